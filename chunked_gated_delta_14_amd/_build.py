@@ -1,0 +1,59 @@
+"""Build of libgdr.so (gfx950) with hipcc, in-tree next to this file."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG_DIR, "libgdr.so")
+SOURCES = ["gdr_api.cpp", "gdr_fwd.hip", "gdr_bwd.hip"]
+HEADERS = ["gdr_device.h", "gdr_kernels.h"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    "-Wno-unused-function",
+    # keep the compiler from forming packed-fp32 VALU ops (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def command(out: str = LIB_PATH) -> list[str]:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    return [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libgdr.so (always recompiles)."""
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libgdr.so")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def stale() -> bool:
+    """True when libgdr.so is missing or older than any of its sources."""
+    if not os.path.exists(LIB_PATH):
+        return True
+    t = os.path.getmtime(LIB_PATH)
+    deps = [os.path.join(CSRC, s) for s in SOURCES + HEADERS] + [os.path.join(INCLUDE, "gdr.h")]
+    return any(os.path.getmtime(d) > t for d in deps if os.path.exists(d))
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,338 @@
+// C ABI of libgdr: host-side validation, the chunk planner, the workspace
+// layout and the launch sequence of each call.  See include/gdr.h for the
+// contract of every entry point.
+#include "gdr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "gdr_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const std::string &msg) {
+  g_last_error = msg;
+  return code;
+}
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kChunk = 64;
+constexpr int64_t kHD = 128;
+
+int64_t round_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Per (chunk, value head) unit bytes of each workspace region.
+constexpr int64_t kFrag64x128 = 16 * 64 * 16;  // 16 fragment tiles of 1 KB
+constexpr int64_t kFrag64x64 = 8 * 64 * 16;
+constexpr int64_t kAcc64x128 = kChunk * kHD * 2;
+constexpr int64_t kGamma = kHD * 4;
+constexpr int64_t kState = kHD * kHD * 2;
+constexpr int64_t kRows = kChunk * kHD * 2;
+
+struct Layout {
+  int64_t WfN, Pf, KbT, Uacc, Oacc, gam;  // forward walk operands
+  int64_t Kb, WTn, QGT, MTs, S, Vn;       // tapes kept for the backward
+  int64_t fwd_bytes, full_bytes;
+};
+
+// Region order keeps WfN|Pf, KbT and Uacc adjacent so that the backward's
+// scratch tapes (dS: 32 KB, dVn, dVnT: 16 KB each per unit) can overlay the
+// forward-walk operands, which are dead once the forward walk has run.
+Layout make_layout(int64_t units) {
+  Layout L{};
+  int64_t off = 0;
+  auto take = [&](int64_t per_unit) {
+    const int64_t at = off;
+    off += round_up(per_unit * units);
+    return at;
+  };
+  L.WfN = take(kFrag64x128);
+  L.Pf = take(kFrag64x128);
+  L.KbT = take(kFrag64x128);
+  L.Uacc = take(kAcc64x128);
+  L.Oacc = take(kAcc64x128);
+  L.gam = take(kGamma);
+  L.fwd_bytes = off;
+  L.Kb = take(kFrag64x128);
+  L.WTn = take(kFrag64x128);
+  L.QGT = take(kFrag64x128);
+  L.MTs = take(kFrag64x64);
+  L.S = take(kState);
+  L.Vn = take(kRows);
+  L.full_bytes = off;
+  return L;
+}
+
+gdr::Workspace bind(const Layout &L, void *base) {
+  char *b = static_cast<char *>(base);
+  gdr::Workspace w{};
+  w.WfN = reinterpret_cast<uint4 *>(b + L.WfN);
+  w.Pf = reinterpret_cast<uint4 *>(b + L.Pf);
+  w.KbT = reinterpret_cast<uint4 *>(b + L.KbT);
+  w.Uacc = reinterpret_cast<uint16_t *>(b + L.Uacc);
+  w.Oacc = reinterpret_cast<uint16_t *>(b + L.Oacc);
+  w.gam = reinterpret_cast<float *>(b + L.gam);
+  w.Kb = reinterpret_cast<uint4 *>(b + L.Kb);
+  w.WTn = reinterpret_cast<uint4 *>(b + L.WTn);
+  w.QGT = reinterpret_cast<uint4 *>(b + L.QGT);
+  w.MTs = reinterpret_cast<uint4 *>(b + L.MTs);
+  w.S = reinterpret_cast<uint16_t *>(b + L.S);
+  w.Vn = reinterpret_cast<uint16_t *>(b + L.Vn);
+  w.dS = reinterpret_cast<uint16_t *>(b + L.WfN);   // over WfN|Pf
+  w.dVn = reinterpret_cast<uint16_t *>(b + L.KbT);  // over KbT
+  w.dVnT = reinterpret_cast<uint16_t *>(b + L.Uacc);// over Uacc
+  return w;
+}
+
+int32_t check_sizes(int32_t variant, int64_t T, int64_t N, int64_t NC, int64_t Hqk, int64_t Hv, int64_t K,
+                    int64_t V) {
+  if (variant != GDR_KDA && variant != GDR_GDN) return fail(GDR_ERR_INVALID_ARG, "unknown variant");
+  if (T < 0 || N < 0 || NC < 0) return fail(GDR_ERR_INVALID_ARG, "T, N and n_chunks must be >= 0");
+  if (Hqk <= 0 || Hv <= 0) return fail(GDR_ERR_INVALID_ARG, "head counts must be positive");
+  if (K != kHD || V != kHD) return fail(GDR_ERR_UNSUPPORTED, "only K = V = 128 is implemented");
+  if (variant == GDR_KDA && Hqk != Hv) return fail(GDR_ERR_UNSUPPORTED, "KDA needs H_qk == H_v");
+  if (variant == GDR_GDN && Hv % Hqk != 0) return fail(GDR_ERR_UNSUPPORTED, "GDN needs H_v to be a multiple of H_qk");
+  if (T > 0 && N == 0) return fail(GDR_ERR_INVALID_ARG, "tokens without documents");
+  // every chunk holds 1..64 tokens of one document, and each document adds at
+  // most one partial chunk
+  if (NC > T || NC < (T + kChunk - 1) / kChunk || NC > (T + kChunk - 1) / kChunk + N)
+    return fail(GDR_ERR_INVALID_ARG, "n_chunks is inconsistent with T and N");
+  // grid sizes are 32-bit: chunk grids use NC blocks, walk grids 8 * N * H_v blocks
+  if (N * Hv > (int64_t(1) << 27) || NC * Hv > (int64_t(1) << 40))
+    return fail(GDR_ERR_UNSUPPORTED, "problem too large");
+  return GDR_OK;
+}
+
+struct DeviceCache {
+  std::mutex mu;
+  std::vector<int> state;  // 0 unknown, 1 gfx950, 2 other
+};
+DeviceCache &device_cache() {
+  static DeviceCache c;
+  return c;
+}
+
+int32_t check_device_impl() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GDR_ERR_HIP, "hipGetDevice failed");
+  DeviceCache &c = device_cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  if ((int)c.state.size() <= dev) c.state.resize(dev + 1, 0);
+  if (c.state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(GDR_ERR_HIP, "hipGetDeviceProperties failed");
+    c.state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  if (c.state[dev] != 1) return fail(GDR_ERR_ARCH, "the current device is not gfx950");
+  return GDR_OK;
+}
+
+int32_t check_problem(int32_t variant, const gdr_problem *p) {
+  if (!p) return fail(GDR_ERR_INVALID_ARG, "problem is NULL");
+  int32_t rc = check_sizes(variant, p->T, p->N, p->n_chunks, p->H_qk, p->H_v, p->K, p->V);
+  if (rc) return rc;
+  if (p->T > 0 && (!p->q || !p->k || !p->v || !p->g || !p->beta))
+    return fail(GDR_ERR_INVALID_ARG, "q, k, v, g and beta must be non-NULL");
+  if (p->N > 0 && (!p->cu_seqlens || !p->chunk_table))
+    return fail(GDR_ERR_INVALID_ARG, "cu_seqlens and chunk_table must be non-NULL");
+  if (!(p->scale == p->scale)) return fail(GDR_ERR_INVALID_ARG, "scale is NaN");
+  return GDR_OK;
+}
+
+int32_t check_workspace(const gdr_problem *p, void *ws, int64_t ws_bytes, bool full, Layout &L) {
+  L = make_layout((int64_t)p->n_chunks * p->H_v);
+  const int64_t need = full ? L.full_bytes : L.fwd_bytes;
+  if (need > 0 && !ws) return fail(GDR_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(GDR_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(GDR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes, got " +
+                                       std::to_string(ws_bytes));
+  return GDR_OK;
+}
+
+gdr::Problem to_internal(const gdr_problem *p) {
+  gdr::Problem q{};
+  q.T = p->T;
+  q.N = p->N;
+  q.Hqk = p->H_qk;
+  q.Hv = p->H_v;
+  q.NC = p->n_chunks;
+  q.q = p->q;
+  q.k = p->k;
+  q.v = p->v;
+  q.g = p->g;
+  q.beta = p->beta;
+  q.cu = p->cu_seqlens;
+  q.table = p->chunk_table;
+  q.h0 = p->h0;
+  q.scale = p->scale;
+  return q;
+}
+
+int32_t hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return GDR_OK;
+  return fail(GDR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int32_t fwd_impl(int32_t variant, const gdr_problem *p, uint16_t *o, float *ht, void *ws, int64_t ws_bytes,
+                 uint32_t flags, void *stream) {
+  int32_t rc = check_problem(variant, p);
+  if (rc) return rc;
+  if (flags & ~GDR_FWD_SAVE) return fail(GDR_ERR_INVALID_ARG, "unknown forward flag");
+  if (p->T > 0 && !o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
+  const bool save = (flags & GDR_FWD_SAVE) != 0;
+  Layout L;
+  if ((rc = check_workspace(p, ws, ws_bytes, save, L))) return rc;
+  if ((rc = check_device_impl())) return rc;
+  const gdr::Problem q = to_internal(p);
+  const gdr::Workspace w = bind(L, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_status(gdr::launch_fwd_prep(variant == GDR_GDN, q, w, save, st), "prep launch"))) return rc;
+  if ((rc = hip_status(gdr::launch_fwd_walk(q, w, o, ht, save, st), "walk launch"))) return rc;
+  g_last_error.clear();
+  return GDR_OK;
+}
+
+int32_t bwd_impl(int32_t variant, const gdr_problem *p, const uint16_t *dout, const float *dht, uint16_t *dq,
+                 uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0, void *ws, int64_t ws_bytes,
+                 void *stream) {
+  int32_t rc = check_problem(variant, p);
+  if (rc) return rc;
+  if (p->T > 0 && (!dout || !dq || !dk || !dv || !dg || !dbeta))
+    return fail(GDR_ERR_INVALID_ARG, "dout, dq, dk, dv, dg and dbeta must be non-NULL");
+  Layout L;
+  if ((rc = check_workspace(p, ws, ws_bytes, true, L))) return rc;
+  if ((rc = check_device_impl())) return rc;
+  const gdr::Problem q = to_internal(p);
+  const gdr::Workspace w = bind(L, ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_status(gdr::launch_bwd_walk(q, w, dout, dht, dh0, st), "adjoint walk launch"))) return rc;
+  if ((rc = hip_status(gdr::launch_bwd_grad(variant == GDR_GDN, q, w, dout, dq, dk, dv, dg, dbeta, st),
+                       "gradient launch")))
+    return rc;
+  g_last_error.clear();
+  return GDR_OK;
+}
+
+int32_t ckpt_impl(int32_t variant, const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout,
+                  const float *dht, uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0,
+                  void *ws, int64_t ws_bytes, void *stream) {
+  // validate everything the three phases need before enqueueing any of them
+  int32_t rc = check_problem(variant, p);
+  if (rc) return rc;
+  if (p->T > 0 && (!o || !dout || !dq || !dk || !dv || !dg || !dbeta))
+    return fail(GDR_ERR_INVALID_ARG, "o, dout, dq, dk, dv, dg and dbeta must be non-NULL");
+  Layout L;
+  if ((rc = check_workspace(p, ws, ws_bytes, true, L))) return rc;
+  if ((rc = fwd_impl(variant, p, o, ht, ws, ws_bytes, 0, stream))) return rc;
+  if ((rc = fwd_impl(variant, p, o, nullptr, ws, ws_bytes, GDR_FWD_SAVE, stream))) return rc;
+  return bwd_impl(variant, p, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdr_plan_chunks(const int32_t *cu, int32_t N, int32_t *table, int64_t capacity, int32_t *n_chunks_out,
+                        int64_t *table_len_out) {
+  if (N < 0) return fail(GDR_ERR_INVALID_ARG, "N must be >= 0");
+  if (!cu) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (cu[0] != 0) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  int64_t nc = 0;
+  for (int32_t n = 0; n < N; ++n) {
+    const int64_t len = (int64_t)cu[n + 1] - cu[n];
+    if (len < 0) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing");
+    nc += (len + kChunk - 1) / kChunk;
+  }
+  if (nc > INT32_MAX / 4) return fail(GDR_ERR_UNSUPPORTED, "too many chunks");
+  const int64_t tlen = 3 * nc + 2 * (int64_t)N + 1;
+  if (n_chunks_out) *n_chunks_out = (int32_t)nc;
+  if (table_len_out) *table_len_out = tlen;
+  if (!table) {
+    g_last_error.clear();
+    return GDR_OK;
+  }
+  if (capacity < tlen) return fail(GDR_ERR_INVALID_ARG, "table capacity too small");
+  int32_t *start = table, *clen = table + nc, *doc = table + 2 * nc, *ptr = table + 3 * nc;
+  int32_t *order = ptr + N + 1;
+  int64_t c = 0;
+  for (int32_t n = 0; n < N; ++n) {
+    ptr[n] = (int32_t)c;
+    for (int64_t t = cu[n]; t < cu[n + 1]; t += kChunk) {
+      start[c] = (int32_t)t;
+      clen[c] = (int32_t)std::min<int64_t>(kChunk, cu[n + 1] - t);
+      doc[c] = n;
+      ++c;
+    }
+  }
+  ptr[N] = (int32_t)c;
+  std::vector<int32_t> idx(N);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](int32_t a, int32_t b) { return ptr[a + 1] - ptr[a] > ptr[b + 1] - ptr[b]; });
+  std::copy(idx.begin(), idx.end(), order);
+  g_last_error.clear();
+  return GDR_OK;
+}
+
+int64_t gdr_workspace_bytes(int32_t variant, int32_t T, int32_t N, int32_t n_chunks, int32_t H_qk, int32_t H_v,
+                            int32_t K, int32_t V, uint32_t flags) {
+  const int32_t rc = check_sizes(variant, T, N, n_chunks, H_qk, H_v, K, V);
+  if (rc) return -(int64_t)rc;
+  if (flags & ~GDR_FWD_SAVE) return -(int64_t)fail(GDR_ERR_INVALID_ARG, "unknown flag");
+  const Layout L = make_layout((int64_t)n_chunks * H_v);
+  return (flags & GDR_FWD_SAVE) ? L.full_bytes : L.fwd_bytes;
+}
+
+int32_t gdr_kda_fwd(const gdr_problem *p, uint16_t *o, float *ht, void *ws, int64_t ws_bytes, uint32_t flags,
+                    void *stream) {
+  return fwd_impl(GDR_KDA, p, o, ht, ws, ws_bytes, flags, stream);
+}
+int32_t gdr_gdn_fwd(const gdr_problem *p, uint16_t *o, float *ht, void *ws, int64_t ws_bytes, uint32_t flags,
+                    void *stream) {
+  return fwd_impl(GDR_GDN, p, o, ht, ws, ws_bytes, flags, stream);
+}
+int32_t gdr_kda_bwd(const gdr_problem *p, const uint16_t *dout, const float *dht, uint16_t *dq, uint16_t *dk,
+                    uint16_t *dv, float *dg, void *dbeta, float *dh0, void *ws, int64_t ws_bytes, void *stream) {
+  return bwd_impl(GDR_KDA, p, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
+}
+int32_t gdr_gdn_bwd(const gdr_problem *p, const uint16_t *dout, const float *dht, uint16_t *dq, uint16_t *dk,
+                    uint16_t *dv, float *dg, void *dbeta, float *dh0, void *ws, int64_t ws_bytes, void *stream) {
+  return bwd_impl(GDR_GDN, p, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
+}
+int32_t gdr_kda_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout, const float *dht,
+                     uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0, void *ws,
+                     int64_t ws_bytes, void *stream) {
+  return ckpt_impl(GDR_KDA, p, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
+}
+int32_t gdr_gdn_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout, const float *dht,
+                     uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0, void *ws,
+                     int64_t ws_bytes, void *stream) {
+  return ckpt_impl(GDR_GDN, p, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
+}
+
+int32_t gdr_check_device(void) { return check_device_impl(); }
+
+const char *gdr_status_string(int32_t s) {
+  switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_INVALID_ARG: return "invalid argument";
+    case GDR_ERR_UNSUPPORTED: return "unsupported problem";
+    case GDR_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case GDR_ERR_HIP: return "HIP runtime error";
+    case GDR_ERR_ARCH: return "device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+const char *gdr_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

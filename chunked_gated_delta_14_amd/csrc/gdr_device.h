@@ -1,0 +1,291 @@
+// Device-side building blocks shared by the gfx950 kernels of libgdr.
+//
+// MFMA conventions (v_mfma_f32_16x16x32_bf16, one 64-lane wavefront):
+//   lane = 16*lg + lr   (lg = lane >> 4 in 0..3, lr = lane & 15)
+//   A fragment (16 x 32, rows m, reduction k): lane holds A[lr][k(lg, i)], i = 0..7
+//   B fragment (32 x 16, reduction k, cols n): lane holds B[k(lg, i)][lr]
+//   D tile     (16 x 16):                      lane holds D[4*lg + j][lr], j = 0..3
+// The instruction pairs A and B positions (lg, i) with the same reduction
+// index, so any permutation k(lg, i) of 0..31 gives the same product as long
+// as both operands use it.  Two permutations are used:
+//   kstd(lg, i) = 8*lg + i        (operands read from LDS or plain row-major memory)
+//   kwalk(lg, i) = 4*lg + i, i<4;  16 + 4*lg + (i-4), i>=4
+// kwalk lines a reduction step up with the rows a lane holds in two stacked
+// accumulator tiles (rows 4lg..4lg+3 of the upper and of the lower 16-row
+// tile), so an accumulator (a state slice, the new values) becomes the next
+// product's B operand in registers, without a trip through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int CH = 64;     // tokens per chunk
+constexpr int HD = 128;    // head dim (K = V)
+constexpr int KP = HD + 8; // LDS row pitch (bf16 elements) of 64 x 128 bf16 tiles
+constexpr int GP = HD + 4; // LDS row pitch (floats) of the 64 x 128 fp32 gate tile
+constexpr int SP = 68;     // LDS row pitch (floats) of 64 x 64 fp32 tiles
+constexpr int MP = 72;     // LDS row pitch (bf16 elements) of 64 x 64 bf16 tiles
+
+// Walk-operand fragment tiles are 64 lanes x 16 bytes = 1 KB each.
+constexpr int FRAG_TILE_U4 = 64;                 // uint4 per tile
+constexpr int FRAG_64x128_U4 = 16 * FRAG_TILE_U4; // 16 tiles: a 64x128 or 128x64 operand
+constexpr int FRAG_64x64_U4 = 8 * FRAG_TILE_U4;   // 8 tiles: a 64x64 operand
+constexpr int ACC_64x128_U16 = CH * HD;           // accumulator-order 64x128 (bf16)
+
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ u16 f2bf(float f) {
+  __bf16 h = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(u16, h);
+}
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ int kwalk(int lg, int i) { return i < 4 ? 4 * lg + i : 12 + 4 * lg + i; }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ uint4 as_u4(bf16x8 x) { return __builtin_bit_cast(uint4, x); }
+
+// Two stacked accumulator tiles -> one kwalk-ordered B fragment.
+__device__ __forceinline__ bf16x8 acc_pair_to_b(f32x4 hi, f32x4 lo) {
+  bf16x8 r;
+  r[0] = (__bf16)hi[0]; r[1] = (__bf16)hi[1]; r[2] = (__bf16)hi[2]; r[3] = (__bf16)hi[3];
+  r[4] = (__bf16)lo[0]; r[5] = (__bf16)lo[1]; r[6] = (__bf16)lo[2]; r[7] = (__bf16)lo[3];
+  return r;
+}
+
+// x ~= hi + lo with both parts bf16: a product against an exact bf16 operand
+// then carries about 16 significant bits instead of 8.
+__device__ __forceinline__ void split_bf16(float x, bf16x8 &hi, bf16x8 &lo, int i) {
+  const __bf16 h = (__bf16)x;
+  hi[i] = h;
+  lo[i] = (__bf16)(x - (float)h);
+}
+
+// 8 contiguous bf16 from LDS/global (16-byte aligned).
+__device__ __forceinline__ bf16x8 ld8(const u16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+// 8 contiguous floats (16-byte aligned) -> bf16.
+__device__ __forceinline__ bf16x8 ld8f(const float *p) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  bf16x8 r;
+  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
+  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk tables (layout documented in gdr.h, gdr_plan_chunks)
+// ---------------------------------------------------------------------------
+struct ChunkTable {
+  const int32_t *start, *len, *doc, *doc_ptr, *order;
+  __device__ __forceinline__ ChunkTable(const int32_t *t, int nc, int n)
+      : start(t), len(t + nc), doc(t + 2 * nc), doc_ptr(t + 3 * nc), order(t + 3 * nc + n + 1) {}
+};
+
+// Walk grid: chain c (= rank of the document in walk order * H_v + head)
+// and value slice s (16 columns) from the block index, placing all slices of
+// one chain on the same XCD (block ids are dealt to the 8 XCDs round-robin),
+// so they share that XCD's L2 copy of the chain's per-chunk operands.
+__device__ __forceinline__ void walk_block(int b, int &chain, int &slice) {
+  const int x = b & 7, m = b >> 3;
+  slice = m & 7;
+  chain = ((m >> 3) << 3) + x;
+}
+
+// ---------------------------------------------------------------------------
+// Shared chunk-local pieces used by the prep and gradient kernels.  They run
+// with NT threads (NW = NT/64 wavefronts) and operate on LDS tiles.
+// ---------------------------------------------------------------------------
+
+// Gate accessor: per-channel (KDA) 64 x GP tile or one scalar per row (GDN).
+template <bool SCALAR>
+struct Gate {
+  const float *s;
+  __device__ __forceinline__ float operator()(int r, int c) const {
+    if constexpr (SCALAR) return s[r];
+    else return s[r * GP + c];
+  }
+};
+
+// Load a chunk's gate rows into LDS (zeros past len) and turn them into the
+// in-chunk inclusive cumulative sum G.  KDA: g row stride H_v*128 floats;
+// GDN: one float per row, stride H_v.
+template <bool SCALAR, int NT = 256>
+__device__ __forceinline__ void load_cumsum_gate(float *sG, const float *g, int start, int len,
+                                                 int Hv, int j, int tid) {
+  if constexpr (SCALAR) {
+    if (tid < 64) {
+      float x = tid < len ? g[(size_t)(start + tid) * Hv + j] : 0.f;
+      // inclusive scan over the 64 lanes of wavefront 0
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(x, o, 64);
+        if (tid >= o) x += y;
+      }
+      sG[tid] = x;
+    }
+    __syncthreads();
+  } else {
+    for (int e = tid; e < CH * HD / 4; e += NT) {
+      const int r = e >> 5, c4 = (e & 31) * 4;
+      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r < len) val = *reinterpret_cast<const float4 *>(g + ((size_t)(start + r) * Hv + j) * HD + c4);
+      *reinterpret_cast<float4 *>(sG + r * GP + c4) = val;
+    }
+    __syncthreads();
+    // NT/128 row bands per channel: scan each band, then add the totals of
+    // the bands above it
+    constexpr int NB = NT / 128, BR = CH / NB;
+    const int c = tid & 127, band = tid >> 7;
+    float run = 0.f;
+    for (int r = BR * band; r < BR * band + BR; ++r) {
+      run += sG[r * GP + c];
+      sG[r * GP + c] = run;
+    }
+    __syncthreads();
+    float base = 0.f;
+    for (int b = 0; b < band; ++b) base += sG[(BR * b + BR - 1) * GP + c];
+    __syncthreads();
+    if (band)
+      for (int r = BR * band; r < BR * band + BR; ++r) sG[r * GP + c] += base;
+    __syncthreads();
+  }
+}
+
+// Copy 64 rows x 128 bf16 (row stride `ld` elements in global memory) into an
+// LDS tile with pitch KP; rows >= len become zeros.
+template <int NT = 256>
+__device__ __forceinline__ void load_rows_bf16(u16 *dst, const u16 *src, size_t ld, int len, int tid) {
+  for (int e = tid; e < CH * 16; e += NT) {
+    const int r = e >> 4, c8 = (e & 15) * 8;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (r < len) val = *reinterpret_cast<const uint4 *>(src + (size_t)r * ld + c8);
+    *reinterpret_cast<uint4 *>(dst + r * KP + c8) = val;
+  }
+}
+
+// The 10 lower block pairs (I, J), J <= I, of a 64 x 64 matrix in 16-row blocks.
+__device__ __forceinline__ void block_pair(int p, int &I, int &J) {
+  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+  I = p >= 6 ? 3 : (p >= 3 ? 2 : (p >= 1 ? 1 : 0));
+  J = p - (I * (I + 1)) / 2;
+}
+
+// Gated key products of one chunk:
+//   E[r][s] = sum_c k_rc k_sc exp(G_rc - G_sc)   (s < r, else 0)     -> sE (fp32, pitch SP)
+//   M[r][s] = sum_c q_rc k_sc exp(G_rc - G_sc)   (s <= r, else 0)    -> sM (bf16, pitch MP), if WITH_M
+// Each 16x16 block pair (I, J) is one MFMA chain over the 128 channels with
+// both factors rescaled around the gate of row 16I+8: the row factor
+// exp(G_r - G_ref) and the column factor exp(G_ref - G_s) stay within
+// exp(+-8*|g|max) in fp32/bf16 range, while the exact exponent G_r - G_s of
+// an entry can reach 64*|g|max, far outside it.
+template <bool SCALAR, bool WITH_M, int NW = 4>
+__device__ __forceinline__ void gated_kk(float *sE, u16 *sM, const u16 *sK, const u16 *sQ,
+                                         const float *sG, int wave, int lane) {
+  const Gate<SCALAR> G{sG};
+  const int lr = lane & 15, lg = lane >> 4;
+  for (int p = wave; p < 10; p += NW) {
+    int I, J;
+    block_pair(p, I, J);
+    const int ref = 16 * I + 8, r = 16 * I + lr, s = 16 * J + lr;
+    f32x4 accE = zero4(), accM = zero4();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int c0 = 32 * kt + 8 * lg;
+      bf16x8 aK, aQ, bK;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = c0 + i;
+        const float gref = G(ref, c);
+        const float er = __expf(G(r, c) - gref);
+        const float es = __expf(gref - G(s, c));
+        aK[i] = (__bf16)(bf2f(sK[r * KP + c]) * er);
+        if constexpr (WITH_M) aQ[i] = (__bf16)(bf2f(sQ[r * KP + c]) * er);
+        bK[i] = (__bf16)(bf2f(sK[s * KP + c]) * es);
+      }
+      accE = mfma(aK, bK, accE);
+      if constexpr (WITH_M) accM = mfma(aQ, bK, accM);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int row = 16 * I + 4 * lg + jj, col = 16 * J + lr;
+      sE[row * SP + col] = col < row ? accE[jj] : 0.f;
+      if constexpr (WITH_M) sM[row * MP + col] = f2bf(col <= row ? accM[jj] : 0.f);
+    }
+  }
+  // upper block pairs are zero
+  for (int e = wave * 64 + lane; e < 6 * 256; e += NW * 64) {
+    const int p = e >> 8, idx = e & 255;
+    const int I = p < 3 ? 0 : (p < 5 ? 1 : 2);
+    const int J = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+    const int row = 16 * I + (idx >> 4), col = 16 * J + (idx & 15);
+    sE[row * SP + col] = 0.f;
+    if constexpr (WITH_M) sM[row * MP + col] = 0;
+  }
+}
+
+// T = (I + diag(beta) E)^-1 (unit lower triangular, fp32) by blocked forward
+// substitution: the four 16x16 diagonal blocks are inverted column by column,
+// then T_IJ = -T_II * sum_{J<=K<I} A_IK T_KJ level by level (I - J = 1, 2, 3).
+// sX: scratch of 3*256 floats.
+template <int NT = 256>
+__device__ __forceinline__ void tri_inverse(float *sT, const float *sE, const float *sB, float *sX,
+                                            int tid) {
+  // zero the strictly upper 16x16 blocks
+  for (int e = tid; e < 6 * 256; e += NT) {
+    const int p = e >> 8, idx = e & 255;
+    const int I = p < 3 ? 0 : (p < 5 ? 1 : 2);
+    const int J = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+    sT[(16 * I + (idx >> 4)) * SP + 16 * J + (idx & 15)] = 0.f;
+  }
+  if (tid < 64) {
+    const int I = tid >> 4, s = tid & 15, base = 16 * I;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (r == s) ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      const float b = sB[base + r];
+      float acc = x[r];
+#pragma unroll
+      for (int t = 0; t < r; ++t) acc -= b * sE[(base + r) * SP + base + t] * x[t];
+      x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(base + r) * SP + base + s] = x[r];
+  }
+  __syncthreads();
+  for (int d = 1; d < 4; ++d) {
+    const int nb = 4 - d;
+    for (int e = tid; e < nb * 256; e += NT) {
+      const int b = e >> 8, idx = e & 255, r = idx >> 4, s = idx & 15;
+      const int I = b + d, J = b;
+      const float beta_r = sB[16 * I + r];
+      float acc = 0.f;
+      for (int K = J; K < I; ++K)
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          acc += beta_r * sE[(16 * I + r) * SP + 16 * K + t] * sT[(16 * K + t) * SP + 16 * J + s];
+      sX[e] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < nb * 256; e += NT) {
+      const int b = e >> 8, idx = e & 255, r = idx >> 4, s = idx & 15;
+      const int I = b + d, J = b;
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) acc += sT[(16 * I + r) * SP + 16 * I + t] * sX[b * 256 + t * 16 + s];
+      sT[(16 * I + r) * SP + 16 * J + s] = -acc;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace gdr

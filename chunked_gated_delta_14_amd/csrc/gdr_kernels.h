@@ -1,0 +1,51 @@
+// Private interface between the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+// Workspace regions; every pointer is a region base, indexed by the unit
+// u = chunk * H_v + value_head (one unit = one chunk of one value head).
+struct Workspace {
+  // forward-walk operands (written by the prep kernel, read by the forward walk)
+  uint4 *WfN;   // -W, A fragments (rows: chunk, k: key), 16 tiles
+  uint4 *Pf;    // scale * (Q.Gamma - M W), A fragments (rows: chunk, k: key)
+  uint4 *KbT;   // Kbar^T, A fragments (rows: key, k: chunk)
+  uint16_t *Uacc;  // U in accumulator order, [u][vslice 8][mtile 4][lane 64][4]
+  uint16_t *Oacc;  // scale * M U in accumulator order
+  float *gam;      // exp(G_last) per channel, [u][128]
+  // backward-walk operands (written by the prep kernel with GDR_FWD_SAVE)
+  uint4 *Kb;    // Kbar, A fragments (rows: chunk, k: key)
+  uint4 *WTn;   // -W^T, A fragments (rows: key, k: chunk)
+  uint4 *QGT;   // scale * (Q.Gamma)^T, A fragments (rows: key, k: chunk)
+  uint4 *MTs;   // scale * M^T, A fragments (rows: chunk, k: chunk), 8 tiles
+  // tapes
+  uint16_t *S;    // entering state of every chunk, bf16 [u][key][v]      (forward walk, SAVE)
+  uint16_t *Vn;   // new values, bf16 [u][row][v]                         (forward walk, SAVE)
+  uint16_t *dS;   // adjoint state leaving every chunk, bf16 [u][key][v]  (backward walk)
+  uint16_t *dVn;  // adjoint of the new values, bf16 [u][row][v]          (backward walk)
+  uint16_t *dVnT; // the same, transposed, bf16 [u][v][row]               (backward walk)
+};
+
+struct Problem {
+  int T, N, Hqk, Hv, NC;
+  const uint16_t *q, *k, *v;
+  const float *g;
+  const void *beta;
+  const int32_t *cu, *table;
+  const float *h0;
+  float scale;
+};
+
+hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, hipStream_t st);
+hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, uint16_t *o, float *ht, bool save,
+                           hipStream_t st);
+hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const uint16_t *dout, const float *dht,
+                           float *dh0, hipStream_t st);
+hipError_t launch_bwd_grad(bool gdn, const Problem &p, const Workspace &w, const uint16_t *dout,
+                           uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta,
+                           hipStream_t st);
+
+}  // namespace gdr

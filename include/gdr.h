@@ -1,0 +1,171 @@
+/*
+ * libgdr -- chunked training of gated delta-rule linear attention on AMD
+ * MI355X (gfx950): Kimi Delta Attention (KDA, per-channel log-gate) and Gated
+ * DeltaNet (GDN, scalar log-decay with grouped Q/K heads), over packed
+ * variable-length sequences at head dim 128.
+ *
+ * What the calls compute.  The FlashInfer pull-request pages this library is
+ * built from name the operation and its operands but print no formula:
+ *   - PR #8218 (description, workload paragraph): KDA training over one packed
+ *     batch described by cu_seqlens; q, k, v BF16 [T,H,128] (q, k
+ *     L2-normalised by the caller), g an FP32 pre-activated log-gate
+ *     [T,H,128], beta BF16 [T,H]; no in-kernel norm, gate or beta activation;
+ *     ops fwd, bwd and ckpt (= forward, recompute and backward);
+ *   - PR #7723 (description): the GDN form -- BF16 q/k/v/out/dout, FP32 scalar
+ *     log-decay g and beta, grouped Q/K heads (H_qk, H_v), dq/dk reduced in
+ *     FP32 over the value heads of each Q/K head and converted once.
+ * The recurrence taken here (per document n and value head j; Q/K head
+ * i = j / (H_v / H_qk); the state restarts at every document start):
+ *     S_0 = h0[n,j] (zeros when h0 is NULL)
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t                    ht[n,j] = S at the last token
+ * with exp(g_t) a 128-vector (KDA) or a scalar (GDN).  The backward returns
+ * the gradients of  sum(o * dout) + sum(ht * dht).
+ *
+ * Conventions for every call below:
+ *   - All tensor pointers are device pointers to caller-owned, contiguous,
+ *     row-major buffers with no padding.  bf16 tensors are passed as uint16_t
+ *     bit patterns.  Token-major layouts: q, k [T, H_qk, K]; v, o, dout
+ *     [T, H_v, V]; states h0, ht, dht, dh0 [N, H_v, K, V] (fp32, K index first).
+ *   - The library never allocates, frees or synchronises: every kernel is
+ *     enqueued on `stream` (a hipStream_t; NULL = the default stream) in call
+ *     order, and the call returns without waiting for the GPU.
+ *   - All argument checks run on the host before anything is enqueued.  A call
+ *     that returns an error has enqueued nothing and left every output
+ *     untouched.  GDR_ERR_HIP reports a launch failure after validation.
+ *   - The workspace is caller-owned device memory of at least
+ *     gdr_workspace_bytes(...) bytes, 256-byte aligned.  Its contents on entry
+ *     do not matter.  A backward call reads what the immediately preceding
+ *     forward with GDR_FWD_SAVE, on the same stream and the same workspace and
+ *     problem, left there; this pairing is the caller's contract and is not
+ *     checked on the device.
+ *   - Outputs must not alias inputs or the workspace.
+ *   - KDA precondition: g >= -8 element-wise (the kernels evaluate
+ *     exp(+-(G_r - G_ref)) for 16-row blocks, which stays finite in fp32 under
+ *     that bound; the pages' gates lie in (-5, 0)).  GDN has no bound.
+ *   - Status codes are plain int32 (enum gdr_status).  gdr_last_error()
+ *     returns a thread-local message for the last failing call on this thread.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gdr_status {
+  GDR_OK = 0,
+  GDR_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, inconsistent table, ... */
+  GDR_ERR_UNSUPPORTED = 2, /* K != 128, V != 128, KDA with H_qk != H_v, GDN with H_v % H_qk != 0 */
+  GDR_ERR_WORKSPACE = 3,   /* workspace smaller than required or not 256-byte aligned */
+  GDR_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  GDR_ERR_ARCH = 5         /* the current device is not gfx950 */
+};
+
+enum gdr_variant { GDR_KDA = 0, GDR_GDN = 1 };
+
+/* Forward flag: also write the tapes a later backward reads (per-chunk
+ * entering states, new values and the backward walk's chunk factors).
+ * Without it the forward writes only o and ht (the first forward of a
+ * checkpointed step). */
+#define GDR_FWD_SAVE 1u
+
+/* One packed problem.  Lifetime: read during the call that receives it. */
+typedef struct gdr_problem {
+  int32_t T;     /* total tokens of the packed batch, >= 0 */
+  int32_t N;     /* documents, >= 0 */
+  int32_t H_qk;  /* Q/K heads (KDA: == H_v) */
+  int32_t H_v;   /* value heads (GDN: multiple of H_qk) */
+  int32_t K;     /* key dim, must be 128 */
+  int32_t V;     /* value dim, must be 128 */
+  const uint16_t *q;         /* bf16 [T, H_qk, K] */
+  const uint16_t *k;         /* bf16 [T, H_qk, K] */
+  const uint16_t *v;         /* bf16 [T, H_v, V] */
+  const float *g;            /* KDA: fp32 [T, H_v, K]; GDN: fp32 [T, H_v] (log-decay) */
+  const void *beta;          /* KDA: bf16 [T, H_v]; GDN: fp32 [T, H_v] */
+  const int32_t *cu_seqlens; /* device int32 [N+1], cu[0] = 0, non-decreasing, cu[N] = T */
+  const int32_t *chunk_table;/* device copy of the table gdr_plan_chunks built from the same cu_seqlens */
+  int32_t n_chunks;          /* the n_chunks gdr_plan_chunks returned for it */
+  const float *h0;           /* fp32 [N, H_v, K, V] initial states, or NULL for zeros */
+  float scale;               /* output scale; 1/sqrt(128) in every workload of the pages */
+} gdr_problem;
+
+/* Chunk planner (host only).  Splits every document of cu_seqlens into
+ * 64-token chunks (the last one of a document may be shorter; chunks never
+ * straddle documents) and orders the documents for the state walks, longest
+ * first.  Table layout (int32), NC = n_chunks:
+ *     [0, NC)             first token of each chunk
+ *     [NC, 2NC)           tokens in each chunk (1..64)
+ *     [2NC, 3NC)          document of each chunk
+ *     [3NC, 3NC+N+1)      first chunk of each document (prefix, last = NC)
+ *     [3NC+N+1, 3NC+2N+1) documents by descending chunk count (ties: lower index first)
+ * cu_seqlens_host: host int32 [N+1].  table_host: host buffer of `capacity`
+ * int32 entries, or NULL to only query the sizes.  Writes n_chunks_out and
+ * table_len_out (both may be NULL).  Errors: GDR_ERR_INVALID_ARG for a bad
+ * cu_seqlens, or a non-NULL table smaller than table_len. */
+int32_t gdr_plan_chunks(const int32_t *cu_seqlens_host, int32_t N, int32_t *table_host,
+                        int64_t capacity, int32_t *n_chunks_out, int64_t *table_len_out);
+
+/* Workspace bytes for a problem (host only).  flags = 0: forward without
+ * tapes; flags = GDR_FWD_SAVE: forward with tapes followed by a backward (the
+ * size every backward needs).  Returns the byte count (a multiple of 256), or
+ * minus a gdr_status on invalid or unsupported sizes. */
+int64_t gdr_workspace_bytes(int32_t variant, int32_t T, int32_t N, int32_t n_chunks,
+                            int32_t H_qk, int32_t H_v, int32_t K, int32_t V, uint32_t flags);
+
+/* KDA forward.  o: bf16 [T, H_v, V] (written).  ht: fp32 [N, H_v, K, V]
+ * final states, or NULL to skip.  flags: 0 or GDR_FWD_SAVE. */
+int32_t gdr_kda_fwd(const gdr_problem *p, uint16_t *o, float *ht, void *workspace,
+                    int64_t workspace_bytes, uint32_t flags, void *stream);
+
+/* KDA backward (after gdr_kda_fwd(..., GDR_FWD_SAVE) on the same workspace).
+ * dout: bf16 [T, H_v, V].  dht: fp32 [N, H_v, K, V] or NULL (= zeros).
+ * Writes dq, dk: bf16 [T, H_qk, K]; dv: bf16 [T, H_v, V]; dg: fp32
+ * [T, H_v, K]; dbeta: bf16 [T, H_v]; dh0: fp32 [N, H_v, K, V] (NULL to skip;
+ * it is the gradient with respect to h0, also when h0 is NULL). */
+int32_t gdr_kda_bwd(const gdr_problem *p, const uint16_t *dout, const float *dht, uint16_t *dq,
+                    uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+
+/* GDN forward: as gdr_kda_fwd with g fp32 [T, H_v] and beta fp32 [T, H_v]. */
+int32_t gdr_gdn_fwd(const gdr_problem *p, uint16_t *o, float *ht, void *workspace,
+                    int64_t workspace_bytes, uint32_t flags, void *stream);
+
+/* GDN backward: as gdr_kda_bwd, except dg is fp32 [T, H_v], dbeta is fp32
+ * [T, H_v], and dq, dk [T, H_qk, K] are the fp32 sums over each Q/K head's
+ * value heads, rounded to bf16 once. */
+int32_t gdr_gdn_bwd(const gdr_problem *p, const uint16_t *dout, const float *dht, uint16_t *dq,
+                    uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0,
+                    void *workspace, int64_t workspace_bytes, void *stream);
+
+/* The checkpointed training step as one call (PR #8218 "ckpt": forward,
+ * recompute and backward): forward without tapes (writes o, ht), forward
+ * again with GDR_FWD_SAVE, then the backward.  Arguments as in the fwd and
+ * bwd calls of the variant; the workspace must hold gdr_workspace_bytes(...,
+ * GDR_FWD_SAVE). */
+int32_t gdr_kda_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout,
+                     const float *dht, uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg,
+                     void *dbeta, float *dh0, void *workspace, int64_t workspace_bytes,
+                     void *stream);
+int32_t gdr_gdn_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout,
+                     const float *dht, uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg,
+                     void *dbeta, float *dh0, void *workspace, int64_t workspace_bytes,
+                     void *stream);
+
+/* Returns GDR_OK when the current HIP device is gfx950, else GDR_ERR_ARCH
+ * (GDR_ERR_HIP when no device can be queried). */
+int32_t gdr_check_device(void);
+
+/* Static description of a status code (never NULL). */
+const char *gdr_status_string(int32_t status);
+
+/* Thread-local detail for the last failing call on this thread ("" if none). */
+const char *gdr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */
