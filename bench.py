@@ -1,0 +1,238 @@
+"""Benchmark of the KDA training hot path on one MI355X.
+
+One step = forward with tapes + backward (every kernel of the path) over the
+4-document pack (42024 / 57573 / 73122 / 88673 tokens, T = 261392) at H = 16,
+K = V = 128, with synthetic seeded inputs already resident in HBM.  Prints one
+JSON line: whole-job throughput in token-heads/s, a roofline entry for the
+dominant kernel (timed with HIP events on the stream the library launches
+on), and the fp64 CPU oracle timed on a bounded sample on this host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--H 16] [--workload 2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA fwd+bwd token-heads/s, H=16, T=261392 (1 GPU); % MFMA & HBM peak"
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+# Per (chunk, value head) unit bytes of the workspace regions.
+FWD_OPERANDS = 16384 * 3 + 16384 * 2 + 512   # -W, P, Kbar^T fragments; U, Oi; gamma
+BWD_OPERANDS = 16384 * 3 + 8192               # Kbar, -W^T, (q Gamma)^T fragments; M^T
+S_TAPE, ROW_TAPE = 32768, 16384
+
+
+def kernel_bytes(name, T, Hqk, Hv, NC, N, gdn, save=True):
+    """Algorithmic bytes of one launch: every input and output byte of the
+    kernel's design counted once (q and k once per Q/K head)."""
+    units = NC * Hv
+    qk = 2 * T * Hqk * 256
+    v = T * Hv * 256
+    g = T * Hv * (4 if gdn else 512)
+    beta = T * Hv * (4 if gdn else 2)
+    if name == "fwd_prep":
+        return qk + v + g + beta + units * (FWD_OPERANDS + (BWD_OPERANDS if save else 0))
+    if name == "fwd_walk":
+        return units * FWD_OPERANDS + v + units * ((S_TAPE + ROW_TAPE) if save else 0) + N * Hv * 65536
+    if name == "bwd_walk":
+        return units * (BWD_OPERANDS + 512 + S_TAPE + 2 * ROW_TAPE) + v + N * Hv * 65536
+    if name == "bwd_grad":
+        return (2 * qk + 3 * v + g * 2 + beta * 2) + units * (2 * S_TAPE + 3 * ROW_TAPE)
+    raise KeyError(name)
+
+
+def kernel_flops(name, NC, Hv):
+    """MFMA flops one launch issues (16x16x32 bf16 MFMA = 16384 flops)."""
+    per_unit = {
+        # E, M: 10 block pairs x 4 k-steps x 2; W, U and P, Oi: 4 strips x 8 tiles x 1.5 k-steps x 2 each
+        "fwd_prep": 10 * 4 * 2 + 2 * (32 * 1.5 * 2),
+        "fwd_walk": 48 * 8,   # 48 MFMAs per chunk per 16-column slice, 8 slices
+        "bwd_walk": 56 * 8,
+        # tape products 3*32*4 + dM 10*4 + dT 10*8 + Y, dA 10*2*2 + T^T dW, T^T dVn 2*32*2
+        # + gated products ~32*10 (hi/lo split) + recomputed E 10*4
+        "bwd_grad": 3 * 32 * 4 + 40 + 80 + 40 + 128 + 320 + 40,
+    }[name]
+    return per_unit * 16384 * NC * Hv
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--H", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8192, help="tokens per document in the CPU sample")
+    return ap.parse_args()
+
+
+def traffic_from_profiles(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    kernel (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), if any."""
+    path = os.path.join(ROOT, "profiles", "%s_traffic.md" % kernel)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", open(path).read())
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(inp, docs, tokens_per_doc):
+    """The fp64 oracle (as it stands) on a bounded sample of the same pack:
+    the first `tokens_per_doc` tokens of every document, all heads."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    cu = np.concatenate([[0], np.cumsum(docs)])
+    take = [min(tokens_per_doc, d) for d in docs]
+    idx = torch.cat([torch.arange(int(cu[i]), int(cu[i]) + take[i]) for i in range(len(docs))])
+    sample = {k: inp[k].index_select(0, idx.to(inp[k].device)).cpu() for k in ("q", "k", "v", "g", "beta", "dout")}
+    scu = np.concatenate([[0], np.cumsum(take)]).astype(np.int32)
+    threads = oracle.default_threads()
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.forward(sample["q"], sample["k"], sample["v"], sample["g"], sample["beta"], scu, threads=threads)
+    t1 = time.perf_counter()
+    oracle.backward(sample["q"], sample["k"], sample["v"], sample["g"], sample["beta"], scu, sample["dout"],
+                    threads=threads)
+    t2 = time.perf_counter()
+    th = int(sum(take)) * int(inp["v"].shape[1])
+    return {"value": th / (t2 - t0), "unit": "token-heads/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d tokens of each of the %d documents, all %d heads (%d token-heads); "
+                      "fwd %.2f s + bwd %.2f s" % (tokens_per_doc, len(docs), inp["v"].shape[1], th,
+                                                   t1 - t0, t2 - t1)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures a single GPU; libgdr has no multi-GPU path. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunked_gated_delta_14_amd as gdr
+    from chunked_gated_delta_14_amd import _build, workloads
+
+    if _build.stale():
+        _build.build()
+    gdr.check_device()
+    dev = torch.device("cuda:0")
+    w = workloads.workload(args.workload, args.H)
+    gdn = w.variant == "gdn"
+    inp = workloads.make_inputs(w, device=dev)
+    prob = gdr.Problem(gdr.GDR_GDN if gdn else gdr.GDR_KDA, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                       inp["cu_seqlens"], inp["h0"])
+    ws = prob.alloc_workspace(gdr.GDR_FWD_SAVE)
+    T, Hqk, Hv, N, NC = prob.T, prob.H_qk, prob.H_v, prob.N, prob.n_chunks
+    bf, f32 = torch.bfloat16, torch.float32
+    o = torch.empty(T, Hv, 128, dtype=bf, device=dev)
+    ht = torch.empty(N, Hv, 128, 128, dtype=f32, device=dev)
+    dq = torch.empty(T, Hqk, 128, dtype=bf, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty(T, Hv, 128, dtype=bf, device=dev)
+    dg = torch.empty(tuple(inp["g"].shape), dtype=f32, device=dev)
+    dbeta = torch.empty(tuple(inp["beta"].shape), dtype=inp["beta"].dtype, device=dev)
+    fwd = gdr.gdn_fwd if gdn else gdr.kda_fwd
+    bwd = gdr.gdn_bwd if gdn else gdr.kda_bwd
+    dout = inp["dout"]
+
+    def step():
+        fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE)
+        bwd(prob, dout, None, dq, dk, dv, dg, dbeta, None, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel HIP events inside the library on the same stream
+    gdr.timing_read(reset=True)
+    gdr.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gdr.timing_enable(False)
+    kern = gdr.timing_read(reset=True)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # separate op timings (events on torch's current stream = the library's stream)
+    def time_op(fn, reps=3):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    ms_fwd = time_op(lambda: fwd(prob, o, ht, ws, 0))
+    ms_fwd_save = time_op(lambda: fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE))
+    fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE)
+    ms_bwd = time_op(lambda: bwd(prob, dout, None, dq, dk, dv, dg, dbeta, None, ws))
+    ckpt = gdr.gdn_ckpt if gdn else gdr.kda_ckpt
+    ms_ckpt = time_op(lambda: ckpt(prob, o, ht, dout, None, dq, dk, dv, dg, dbeta, None, ws))
+
+    kernels = {}
+    total_flops = 0.0
+    for name, (ms, n) in kern.items():
+        if n == 0:
+            continue
+        avg = ms / n
+        b = kernel_bytes(name, T, Hqk, Hv, NC, N, gdn)
+        fl = kernel_flops(name, NC, Hv)
+        total_flops += fl * n / args.steps
+        kernels[name] = {"avg_ms": avg, "launches": n, "bytes": b, "GB_s": b / avg / 1e6,
+                         "hbm_frac": b / avg / 1e6 / HBM_PEAK_GBS, "mfma_TFLOPs": fl / avg / 1e9,
+                         "mfma_frac": fl / avg / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
+    dk_ = kernels[dom]
+    traffic = traffic_from_profiles(dom)
+    token_heads = T * Hv
+    result = {
+        "metric": METRIC,
+        "value": token_heads / (ms_per_step / 1e3),
+        "unit": "token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": w.variant, "T": T, "docs": list(w.docs), "H_qk": Hqk,
+                   "H_v": Hv, "K": 128, "V": 128, "n_chunks": NC,
+                   "step": "forward with tapes + backward (prep, walk, adjoint walk, gradients)"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk_["GB_s"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dk_["GB_s"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "bytes_per_launch": dk_["bytes"], "avg_launch_ms": dk_["avg_ms"]},
+        "ms": {"fwd": ms_fwd, "fwd_save": ms_fwd_save, "bwd": ms_bwd, "ckpt": ms_ckpt},
+        "mfma": {"TFLOPs": total_flops / (ms_per_step / 1e3) / 1e12,
+                 "frac": total_flops / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, list(w.docs), args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

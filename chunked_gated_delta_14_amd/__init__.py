@@ -18,7 +18,7 @@ from . import _build
 __all__ = [
     "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GdrError", "lib", "plan_chunks", "workspace_bytes",
     "Problem", "kda_fwd", "kda_bwd", "gdn_fwd", "gdn_bwd", "kda_ckpt", "gdn_ckpt", "status_string",
-    "check_device", "EXPORTED_SYMBOLS",
+    "check_device", "timing_enable", "timing_read", "EXPORTED_SYMBOLS",
 ]
 
 GDR_KDA = 0
@@ -28,7 +28,7 @@ GDR_FWD_SAVE = 1
 EXPORTED_SYMBOLS = (
     "gdr_plan_chunks", "gdr_workspace_bytes", "gdr_kda_fwd", "gdr_kda_bwd", "gdr_gdn_fwd",
     "gdr_gdn_bwd", "gdr_kda_ckpt", "gdr_gdn_ckpt", "gdr_check_device", "gdr_status_string",
-    "gdr_last_error",
+    "gdr_last_error", "gdr_timing_enable", "gdr_timing_read",
 )
 
 
@@ -82,6 +82,11 @@ def lib():
                 fn = getattr(L, name)
                 fn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
                 fn.restype = i32
+            L.gdr_timing_enable.argtypes = [i32]
+            L.gdr_timing_enable.restype = i32
+            L.gdr_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(i64), i32, ctypes.POINTER(i32), i32]
+            L.gdr_timing_read.restype = i32
             L.gdr_check_device.argtypes = []
             L.gdr_check_device.restype = i32
             L.gdr_status_string.argtypes = [i32]
@@ -103,6 +108,21 @@ def _check(status: int) -> None:
 
 def check_device() -> None:
     _check(lib().gdr_check_device())
+
+
+def timing_enable(on: bool = True) -> None:
+    """Per-kernel event timing inside the library (see gdr_timing_enable)."""
+    _check(lib().gdr_timing_enable(1 if on else 0))
+
+
+def timing_read(reset: bool = True) -> dict:
+    """{kernel name: (total ms, launches)} of the timed launches so far."""
+    names = (ctypes.c_char_p * 4)()
+    ms = (ctypes.c_double * 4)()
+    n_l = (ctypes.c_int64 * 4)()
+    cnt = ctypes.c_int32()
+    _check(lib().gdr_timing_read(names, ms, n_l, 4, ctypes.byref(cnt), 1 if reset else 0))
+    return {names[i].decode(): (float(ms[i]), int(n_l[i])) for i in range(cnt.value)}
 
 
 def plan_chunks(cu_seqlens):

@@ -177,6 +177,55 @@ gdr::Problem to_internal(const gdr_problem *p) {
   return q;
 }
 
+// ---- optional per-kernel timing with events on the call's stream ----
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Pending {
+    int kernel;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  double total_ms[4] = {0, 0, 0, 0};
+  int64_t launches[4] = {0, 0, 0, 0};
+};
+const char *const kKernelNames[4] = {"fwd_prep", "fwd_walk", "bwd_walk", "bwd_grad"};
+Timing &timing() {
+  static Timing t;
+  return t;
+}
+hipEvent_t take_event(Timing &t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (which enqueues one kernel on st), bracketed by events when timing is on.
+template <class F>
+hipError_t timed(int kernel, hipStream_t st, F launch) {
+  Timing &t = timing();
+  if (!t.on) return launch();
+  std::lock_guard<std::mutex> lk(t.mu);
+  hipEvent_t a = take_event(t), b = take_event(t);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, st);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, st);
+  if (e != hipSuccess) {
+    t.pool.push_back(a);
+    t.pool.push_back(b);
+    return e;
+  }
+  t.pending.push_back({kernel, a, b});
+  return hipSuccess;
+}
+
 int32_t hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return GDR_OK;
   return fail(GDR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -195,8 +244,11 @@ int32_t fwd_impl(int32_t variant, const gdr_problem *p, uint16_t *o, float *ht, 
   const gdr::Problem q = to_internal(p);
   const gdr::Workspace w = bind(L, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = hip_status(gdr::launch_fwd_prep(variant == GDR_GDN, q, w, save, st), "prep launch"))) return rc;
-  if ((rc = hip_status(gdr::launch_fwd_walk(q, w, o, ht, save, st), "walk launch"))) return rc;
+  if ((rc = hip_status(timed(0, st, [&] { return gdr::launch_fwd_prep(variant == GDR_GDN, q, w, save, st); }),
+                       "prep launch")))
+    return rc;
+  if ((rc = hip_status(timed(1, st, [&] { return gdr::launch_fwd_walk(q, w, o, ht, save, st); }), "walk launch")))
+    return rc;
   g_last_error.clear();
   return GDR_OK;
 }
@@ -214,9 +266,12 @@ int32_t bwd_impl(int32_t variant, const gdr_problem *p, const uint16_t *dout, co
   const gdr::Problem q = to_internal(p);
   const gdr::Workspace w = bind(L, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = hip_status(gdr::launch_bwd_walk(q, w, dout, dht, dh0, st), "adjoint walk launch"))) return rc;
-  if ((rc = hip_status(gdr::launch_bwd_grad(variant == GDR_GDN, q, w, dout, dq, dk, dv, dg, dbeta, st),
-                       "gradient launch")))
+  if ((rc = hip_status(timed(2, st, [&] { return gdr::launch_bwd_walk(q, w, dout, dht, dh0, st); }),
+                       "adjoint walk launch")))
+    return rc;
+  if ((rc = hip_status(
+           timed(3, st, [&] { return gdr::launch_bwd_grad(variant == GDR_GDN, q, w, dout, dq, dk, dv, dg, dbeta, st); }),
+           "gradient launch")))
     return rc;
   g_last_error.clear();
   return GDR_OK;
@@ -320,6 +375,44 @@ int32_t gdr_gdn_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_
 }
 
 int32_t gdr_check_device(void) { return check_device_impl(); }
+
+int32_t gdr_timing_enable(int32_t on) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = on != 0;
+  return GDR_OK;
+}
+
+int32_t gdr_timing_read(const char **names, double *total_ms, int64_t *launches, int32_t capacity, int32_t *count,
+                        int32_t reset) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  int32_t rc = GDR_OK;
+  for (const auto &pd : t.pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(pd.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pd.a, pd.b);
+    if (e != hipSuccess && rc == GDR_OK) rc = fail(GDR_ERR_HIP, std::string("timing: ") + hipGetErrorString(e));
+    t.total_ms[pd.kernel] += ms;
+    t.launches[pd.kernel] += 1;
+    t.pool.push_back(pd.a);
+    t.pool.push_back(pd.b);
+  }
+  t.pending.clear();
+  const int32_t n = std::min<int32_t>(capacity, 4);
+  for (int32_t i = 0; i < n; ++i) {
+    if (names) names[i] = kKernelNames[i];
+    if (total_ms) total_ms[i] = t.total_ms[i];
+    if (launches) launches[i] = t.launches[i];
+  }
+  if (count) *count = n;
+  if (reset)
+    for (int i = 0; i < 4; ++i) {
+      t.total_ms[i] = 0;
+      t.launches[i] = 0;
+    }
+  return rc;
+}
 
 const char *gdr_status_string(int32_t s) {
   switch (s) {

@@ -154,6 +154,19 @@ int32_t gdr_gdn_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_
                      void *dbeta, float *dh0, void *workspace, int64_t workspace_bytes,
                      void *stream);
 
+/* Kernel timing (diagnostics).  gdr_timing_enable(1) makes every later call
+ * bracket each of its kernel launches with a pair of hipEvents recorded on the
+ * call's stream (the events are created on first use and reused; this is the
+ * one place where the library creates runtime objects).  gdr_timing_read
+ * waits for the recorded events, adds their elapsed times to per-kernel
+ * totals, writes up to `capacity` entries (kernel name, total milliseconds,
+ * number of launches) and, with reset != 0, clears the totals.  Kernel names:
+ * "fwd_prep", "fwd_walk", "bwd_walk", "bwd_grad".  Not thread-safe with
+ * respect to concurrent calls that are being timed. */
+int32_t gdr_timing_enable(int32_t on);
+int32_t gdr_timing_read(const char **names, double *total_ms, int64_t *launches, int32_t capacity,
+                        int32_t *count, int32_t reset);
+
 /* Returns GDR_OK when the current HIP device is gfx950, else GDR_ERR_ARCH
  * (GDR_ERR_HIP when no device can be queried). */
 int32_t gdr_check_device(void);
