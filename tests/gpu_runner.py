@@ -19,8 +19,10 @@ def to_dev(inp, device="cuda"):
     return {k: (v.to(device) if (torch.is_tensor(v) and k != "cu_seqlens") else v) for k, v in inp.items()}
 
 
-def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, nan_workspace=True, workspace=None):
-    """Forward (with tapes) and backward on the GPU.  Returns CPU tensors."""
+def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, nan_workspace=True, workspace=None,
+            on_device=False):
+    """Forward (with tapes) and backward on the GPU.  Returns CPU fp32 tensors
+    (or the device tensors as computed, with on_device=True)."""
     import torch
 
     import chunked_gated_delta_14_amd as gdr
@@ -56,6 +58,8 @@ def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, nan_workspace=
         (gdr.kda_fwd if variant == "kda" else gdr.gdn_fwd)(prob, o, ht, ws, 0)
     torch.cuda.synchronize()
     out.update(o=o, ht=ht)
+    if on_device:
+        return out
     return {k: v.float().cpu() for k, v in out.items()}
 
 
