@@ -40,9 +40,9 @@
  *     problem, left there; this pairing is the caller's contract and is not
  *     checked on the device.
  *   - Outputs must not alias inputs or the workspace.
- *   - KDA precondition: g >= -8 element-wise (the kernels evaluate
- *     exp(+-(G_r - G_ref)) for 16-row blocks, which stays finite in fp32 under
- *     that bound; the pages' gates lie in (-5, 0)).  GDN has no bound.
+ *   - Precondition: g >= -8 element-wise (the kernels evaluate
+ *     exp(+-(G_r - G_ref)) within 16-row blocks, which stays finite in fp32
+ *     under that bound; the pages' gates lie in (-5, 0)).  Not checked.
  *   - Status codes are plain int32 (enum gdr_status).  gdr_last_error()
  *     returns a thread-local message for the last failing call on this thread.
  */
