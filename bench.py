@@ -28,6 +28,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # Per (chunk, value head) unit bytes of the workspace regions.
 FWD_OPERANDS = 16384 * 3 + 16384 * 2 + 512   # -W, P, Kbar^T fragments; U, Oi; gamma
 BWD_OPERANDS = 16384 * 3 + 8192               # Kbar, -W^T, (q Gamma)^T fragments; M^T
+TE_SAVED = 2 * 8192                            # T and E (bf16 64 x 64) for the gradient kernel
 S_TAPE, ROW_TAPE = 32768, 16384
 
 
@@ -40,13 +41,13 @@ def kernel_bytes(name, T, Hqk, Hv, NC, N, gdn, save=True):
     g = T * Hv * (4 if gdn else 512)
     beta = T * Hv * (4 if gdn else 2)
     if name == "fwd_prep":
-        return qk + v + g + beta + units * (FWD_OPERANDS + (BWD_OPERANDS if save else 0))
+        return qk + v + g + beta + units * (FWD_OPERANDS + ((BWD_OPERANDS + TE_SAVED) if save else 0))
     if name == "fwd_walk":
         return units * FWD_OPERANDS + v + units * ((S_TAPE + ROW_TAPE) if save else 0) + N * Hv * 65536
     if name == "bwd_walk":
         return units * (BWD_OPERANDS + 512 + S_TAPE + 2 * ROW_TAPE) + v + N * Hv * 65536
     if name == "bwd_grad":
-        return (2 * qk + 3 * v + g * 2 + beta * 2) + units * (2 * S_TAPE + 3 * ROW_TAPE)
+        return (2 * qk + 3 * v + g * 2 + beta * 2) + units * (2 * S_TAPE + 3 * ROW_TAPE + TE_SAVED)
     raise KeyError(name)
 
 
@@ -58,8 +59,8 @@ def kernel_flops(name, NC, Hv):
         "fwd_walk": 48 * 8,   # 48 MFMAs per chunk per 16-column slice, 8 slices
         "bwd_walk": 56 * 8,
         # tape products 3*32*4 + dM 10*4 + dT 10*8 + Y, dA 10*2*2 + T^T dW, T^T dVn 2*32*2
-        # + gated products ~32*10 (hi/lo split) + recomputed E 10*4
-        "bwd_grad": 3 * 32 * 4 + 40 + 80 + 40 + 128 + 320 + 40,
+        # + gated products ~32*10 (hi/lo split)
+        "bwd_grad": 3 * 32 * 4 + 40 + 80 + 40 + 128 + 320,
     }[name]
     return per_unit * 16384 * NC * Hv
 
@@ -73,6 +74,9 @@ def parse_args():
     ap.add_argument("--H", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="tokens per document in the CPU sample")
+    ap.add_argument("--no-op-timing", action="store_true", help="skip the separate fwd/bwd/ckpt timings")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -130,6 +134,13 @@ def main():
         _build.build()
     gdr.check_device()
     dev = torch.device("cuda:0")
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = workloads.workload(args.workload, args.H)
     gdn = w.variant == "gdn"
     inp = workloads.make_inputs(w, device=dev)
@@ -182,12 +193,14 @@ def main():
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps
 
-    ms_fwd = time_op(lambda: fwd(prob, o, ht, ws, 0))
-    ms_fwd_save = time_op(lambda: fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE))
-    fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE)
-    ms_bwd = time_op(lambda: bwd(prob, dout, None, dq, dk, dv, dg, dbeta, None, ws))
-    ckpt = gdr.gdn_ckpt if gdn else gdr.kda_ckpt
-    ms_ckpt = time_op(lambda: ckpt(prob, o, ht, dout, None, dq, dk, dv, dg, dbeta, None, ws))
+    ops = {}
+    if not args.no_op_timing:
+        ops["fwd"] = time_op(lambda: fwd(prob, o, ht, ws, 0))
+        ops["fwd_save"] = time_op(lambda: fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE))
+        fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE)
+        ops["bwd"] = time_op(lambda: bwd(prob, dout, None, dq, dk, dv, dg, dbeta, None, ws))
+        ckpt = gdr.gdn_ckpt if gdn else gdr.kda_ckpt
+        ops["ckpt"] = time_op(lambda: ckpt(prob, o, ht, dout, None, dq, dk, dv, dg, dbeta, None, ws))
 
     kernels = {}
     total_flops = 0.0
@@ -224,7 +237,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk_["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dk_["GB_s"] / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": dk_["bytes"], "avg_launch_ms": dk_["avg_ms"]},
-        "ms": {"fwd": ms_fwd, "fwd_save": ms_fwd_save, "bwd": ms_bwd, "ckpt": ms_ckpt},
+        "ms": ops,
         "mfma": {"TFLOPs": total_flops / (ms_per_step / 1e3) / 1e12,
                  "frac": total_flops / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "kernels": kernels,

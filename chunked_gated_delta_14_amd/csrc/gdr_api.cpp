@@ -39,7 +39,7 @@ constexpr int64_t kRows = kChunk * kHD * 2;
 
 struct Layout {
   int64_t WfN, Pf, KbT, Uacc, Oacc, gam;  // forward walk operands
-  int64_t Kb, WTn, QGT, MTs, S, Vn;       // tapes kept for the backward
+  int64_t Kb, WTn, QGT, MTs, Tt, Et, S, Vn;  // tapes kept for the backward
   int64_t fwd_bytes, full_bytes;
 };
 
@@ -65,6 +65,8 @@ Layout make_layout(int64_t units) {
   L.WTn = take(kFrag64x128);
   L.QGT = take(kFrag64x128);
   L.MTs = take(kFrag64x64);
+  L.Tt = take(kFrag64x64);
+  L.Et = take(kFrag64x64);
   L.S = take(kState);
   L.Vn = take(kRows);
   L.full_bytes = off;
@@ -84,6 +86,8 @@ gdr::Workspace bind(const Layout &L, void *base) {
   w.WTn = reinterpret_cast<uint4 *>(b + L.WTn);
   w.QGT = reinterpret_cast<uint4 *>(b + L.QGT);
   w.MTs = reinterpret_cast<uint4 *>(b + L.MTs);
+  w.Tt = reinterpret_cast<uint4 *>(b + L.Tt);
+  w.Et = reinterpret_cast<uint4 *>(b + L.Et);
   w.S = reinterpret_cast<uint16_t *>(b + L.S);
   w.Vn = reinterpret_cast<uint16_t *>(b + L.Vn);
   w.dS = reinterpret_cast<uint16_t *>(b + L.WfN);   // over WfN|Pf

@@ -195,7 +195,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int chunk = blockIdx.x, iqk = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const ChunkTable tb(p.table, p.NC, p.N);
   const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
   const int grp = SCALAR ? p.Hv / p.Hqk : 1;  // KDA: H_qk == H_v
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     // loop out of it (that would keep hundreds of values live across it).
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int mt = wave & 3, ch = wave >> 2, nt0 = 4 * ch;
     const int j = iqk * grp + jg;
     const size_t u = (size_t)chunk * Hv + j;
@@ -248,10 +249,18 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       sDB[tid] = 0.f;
     }
     if (tid < 128) sRed[tid] = 0.f;
-    load_cumsum_gate<SCALAR, GNT>(sG, p.g, start, len, p.Hv, j, tid);
-    gated_kk<SCALAR, false, GNW>(sE, nullptr, sK, nullptr, sG, wave, lane);
-    __syncthreads();
-    tri_inverse<GNT>(sT, sE, sB, reinterpret_cast<float *>(sY), tid);
+    // T = (I + diag(beta) E)^-1 and E as the forward's prep saved them (bf16)
+    if (tid < CH * CH / 8) {
+      const int r = tid >> 3, c8 = (tid & 7) * 8;
+      const bf16x8 tv = as_bf16x8(w.Tt[u * FRAG_64x64_U4 + tid]);
+      const bf16x8 ev = as_bf16x8(w.Et[u * FRAG_64x64_U4 + tid]);
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        sT[r * SP + c8 + ii] = (float)tv[ii];
+        sE[r * SP + c8 + ii] = (float)ev[ii];
+      }
+    }
+    load_cumsum_gate<SCALAR, GNT>(sG, p.g, start, len, p.Hv, j, tid);  // ends with a barrier
 
     f32x4 dGA[4];
 #pragma unroll

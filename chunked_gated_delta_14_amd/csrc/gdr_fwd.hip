@@ -32,7 +32,8 @@ template <bool SCALAR>
 __global__ __launch_bounds__(256) void fwd_prep_kernel(Problem p, Workspace w, int save) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int chunk = blockIdx.x, j = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const ChunkTable tb(p.table, p.NC, p.N);
   const int start = tb.start[chunk], len = tb.len[chunk];
   const int i = j / (p.Hv / p.Hqk);
@@ -70,6 +71,20 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Problem p, Workspace w, i
   gated_kk<SCALAR, true>(sE, sM, sK, sQ, sG, wave, lane);
   __syncthreads();
   tri_inverse(sT, sE, sB, sX, tid);
+  if (save) {  // T and E for the gradient kernel, bf16 row-major 64 x 64
+    for (int e = tid; e < CH * CH / 8; e += 256) {
+      const int r = e >> 3, c8 = (e & 7) * 8;
+      bf16x8 tv, ev;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        tv[ii] = (__bf16)sT[r * SP + c8 + ii];
+        ev[ii] = (__bf16)sE[r * SP + c8 + ii];
+      }
+      w.Tt[u * FRAG_64x64_U4 + e] = as_u4(tv);
+      w.Et[u * FRAG_64x64_U4 + e] = as_u4(ev);
+    }
+    __syncthreads();  // sE is reused for W below
+  }
 
   // W = T (beta k exp(G)),  U = T (beta v); wavefront `wave` owns rows 16*wave..+15.
   {

@@ -21,6 +21,8 @@ struct Workspace {
   uint4 *WTn;   // -W^T, A fragments (rows: key, k: chunk)
   uint4 *QGT;   // scale * (Q.Gamma)^T, A fragments (rows: key, k: chunk)
   uint4 *MTs;   // scale * M^T, A fragments (rows: chunk, k: chunk), 8 tiles
+  uint4 *Tt;    // T = (I + diag(beta) E)^-1, bf16 row-major 64 x 64
+  uint4 *Et;    // E (gated k k^T, strictly lower), bf16 row-major 64 x 64
   // tapes
   uint16_t *S;    // entering state of every chunk, bf16 [u][key][v]      (forward walk, SAVE)
   uint16_t *Vn;   // new values, bf16 [u][row][v]                         (forward walk, SAVE)
