@@ -28,7 +28,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # Per (chunk, value head) unit bytes of the workspace regions.
 FWD_OPERANDS = 16384 * 3 + 16384 * 2 + 512   # -W, P, Kbar^T fragments; U, Oi; gamma
 BWD_OPERANDS = 16384 * 3 + 8192               # Kbar, -W^T, (q Gamma)^T fragments; M^T
-TE_SAVED = 2 * 8192                            # T and E (bf16 64 x 64) for the gradient kernel
+TE_SAVED = 8192 + 5120                         # T^T (bf16 64 x 64) and E's 10 lower tiles (bf16)
 S_TAPE, ROW_TAPE = 32768, 16384
 
 
@@ -45,9 +45,9 @@ def kernel_bytes(name, T, Hqk, Hv, NC, N, gdn, save=True):
     if name == "fwd_walk":
         return units * FWD_OPERANDS + v + units * ((S_TAPE + ROW_TAPE) if save else 0) + N * Hv * 65536
     if name == "bwd_walk":
-        return units * (BWD_OPERANDS + 512 + S_TAPE + 2 * ROW_TAPE) + v + N * Hv * 65536
+        return units * (BWD_OPERANDS + 512 + S_TAPE + ROW_TAPE) + v + N * Hv * 65536
     if name == "bwd_grad":
-        return (2 * qk + 3 * v + g * 2 + beta * 2) + units * (2 * S_TAPE + 3 * ROW_TAPE + TE_SAVED)
+        return (2 * qk + 3 * v + g * 2 + beta * 2) + units * (2 * S_TAPE + 2 * ROW_TAPE + TE_SAVED)
     raise KeyError(name)
 
 
@@ -58,9 +58,9 @@ def kernel_flops(name, NC, Hv):
         "fwd_prep": 10 * 4 * 2 + 2 * (32 * 1.5 * 2),
         "fwd_walk": 48 * 8,   # 48 MFMAs per chunk per 16-column slice, 8 slices
         "bwd_walk": 56 * 8,
-        # tape products 3*32*4 + dM 10*4 + dT 10*8 + Y, dA 10*2*2 + T^T dW, T^T dVn 2*32*2
-        # + gated products ~32*10 (hi/lo split)
-        "bwd_grad": 3 * 32 * 4 + 40 + 80 + 40 + 128 + 320,
+        # Y = T^T dVn 8 x (2+2+1+1); tape products 3 x 32 tiles x 4; dM, dA 2 x 10 tiles x 4;
+        # gated products (hi/lo split) 12 per (row block, column tile) x 32
+        "bwd_grad": 48 + 3 * 32 * 4 + 80 + 12 * 32,
     }[name]
     return per_unit * 16384 * NC * Hv
 

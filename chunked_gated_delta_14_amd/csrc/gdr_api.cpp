@@ -44,7 +44,7 @@ struct Layout {
 };
 
 // Region order keeps WfN|Pf, KbT and Uacc adjacent so that the backward's
-// scratch tapes (dS: 32 KB, dVn, dVnT: 16 KB each per unit) can overlay the
+// scratch tapes (dS: 32 KB, dVnT: 16 KB per unit) can overlay the
 // forward-walk operands, which are dead once the forward walk has run.
 Layout make_layout(int64_t units) {
   Layout L{};
@@ -91,7 +91,6 @@ gdr::Workspace bind(const Layout &L, void *base) {
   w.S = reinterpret_cast<uint16_t *>(b + L.S);
   w.Vn = reinterpret_cast<uint16_t *>(b + L.Vn);
   w.dS = reinterpret_cast<uint16_t *>(b + L.WfN);   // over WfN|Pf
-  w.dVn = reinterpret_cast<uint16_t *>(b + L.KbT);  // over KbT
   w.dVnT = reinterpret_cast<uint16_t *>(b + L.Uacc);// over Uacc
   return w;
 }

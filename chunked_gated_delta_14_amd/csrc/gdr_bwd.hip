@@ -6,12 +6,13 @@
 // entering state S, new values Vn and dS' the adjoint of the state leaving it:
 //   walk:   dVn = scale M^T dout + Kbar dS'
 //           dS  = diag(gamma) dS' + scale (q exp G)^T dout - W^T dVn
-//   grads:  dW = -dVn S^T,  dKbar = Vn dS'^T,  dQt = scale dout S^T,
+// The new values are Vn = T R with R = diag(beta) (v - Kt S), Kt = k exp(G).
+// Y = T^T dVn is therefore the adjoint of R, dT = dVn R^T, and with
+// T = (I + A)^-1 the adjoint of A is -T^T dT T^T = -Y (T R)^T = -Y Vn^T:
+//   grads:  Y = T^T dVn,  dv = beta Y,  dKt = -beta (Y S^T),
+//           dA = -Y Vn^T (s < r),  dKbar = Vn dS'^T,  dQt = scale dout S^T,
 //           dM = scale dout Vn^T (s <= r),
-//           dv = beta (T^T dVn),  dKt = beta (T^T dW),
-//           dT = dVn (beta v)^T + dW (beta k exp G)^T,  dA = -T^T dT T^T (s < r),
-//           dbeta_r = sum_v (T^T dVn)_rv v_rv + sum_c (T^T dW)_rc k_rc exp(G_rc)
-//                     + sum_{s<r} dA_rs E_rs,
+//           dbeta_r = sum_v Y_rv v_rv - sum_c (Y S^T)_rc Kt_rc + sum_{s<r} dA_rs E_rs,
 //   and the gated products of dM and dA with k and q give the remaining
 //   dq, dk and the per-row gate gradient dG; dg is the in-chunk reverse
 //   cumulative sum of dG (the gate epilogue).
@@ -106,16 +107,12 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
         Kb[mt][kt] = as_bf16x8(w.Kb[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
       }
     {
-      u16 *rm = w.dVn + u * (CH * HD);
       u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         u16 b[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          b[jj] = f2bf(dV[mt][jj]);
-          rm[(16 * mt + 4 * lg + jj) * HD + vcol] = b[jj];
-        }
+        for (int jj = 0; jj < 4; ++jj) b[jj] = f2bf(dV[mt][jj]);
         uint2 pk;
         pk.x = b[0] | ((uint32_t)b[1] << 16);
         pk.y = b[2] | ((uint32_t)b[3] << 16);
@@ -157,17 +154,37 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 // across them (GDN's group reduction; a single pass for KDA).  Wavefront w
 // owns rows 16*(w&3)..+15 and value/key columns 64*(w>>2)..+63 of every
 // 64 x 128 result, and the 64 x 64 tiles (w&3, nt) with nt&1 == w>>2.
+//
+// q, k and the cumulative gate sit in LDS transposed ([channel][row]), so the
+// exponentially rescaled operands of the gated products, which run down the
+// rows of one channel, are read 8 rows per access.
 // ---------------------------------------------------------------------------
-constexpr int GNT = 512, GNW = 8;
+constexpr int GNT = 512;
+constexpr int QTP = 72;  // LDS pitch (bf16) of the transposed q, k tiles
+constexpr int GTP = 68;  // LDS pitch (floats) of the transposed gate tile
 
 template <bool SCALAR>
 constexpr int grad_smem_bytes() {
-  return 3 * CH * KP * 2      // sK, sQ, sDW
-         + 2 * CH * SP * 4    // sE, sT (later the dG tile)
-         + 3 * CH * MP * 2    // sDM, sDT (later dA), sY (also solve scratch)
-         + (64 + 64 + 128 + 128) * 4
-         + (SCALAR ? 64 * 4 : CH * GP * 4);
+  return 2 * HD * QTP * 2                   // sQT, sKT
+         + CH * KP * 2                      // sY
+         + 4 * CH * MP * 2                  // sDM, sDA, sDMT, sDAT
+         + (64 + 64 + 128 + 128 + 512) * 4  // sB, sDB, sRed, sDgam, sBT
+         + (SCALAR ? 64 * 4 : HD * GTP * 4);  // sG
 }
+
+// Cumulative gate G: per-channel tile [channel][row] (KDA) or one value per row.
+template <bool SCALAR>
+struct GateT {
+  const float *s;
+  __device__ __forceinline__ float at(int r, int c) const {
+    if constexpr (SCALAR) return s[r];
+    else return s[c * GTP + r];
+  }
+  __device__ __forceinline__ float4 at4(int r0, int c) const {  // rows r0..r0+3
+    if constexpr (SCALAR) return *reinterpret_cast<const float4 *>(s + r0);
+    else return *reinterpret_cast<const float4 *>(s + c * GTP + r0);
+  }
+};
 
 // acc[t] += x for a run-time tile index t, without indexing a register array
 // at run time (that would move the array to scratch memory).
@@ -189,42 +206,75 @@ __device__ __forceinline__ float red_lg(float x) {  // sum over the 4 lane group
   x += __shfl_xor(x, 32, 64);
   return x;
 }
+__device__ __forceinline__ float lo_bf(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+__device__ __forceinline__ float bf_at(uint2 x, int jj) {
+  const uint32_t wd = jj < 2 ? x.x : x.y;
+  return (jj & 1) ? hi_bf(wd) : lo_bf(wd);
+}
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  uint2 r;
+  r.x = f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  r.y = f2bf(c) | ((uint32_t)f2bf(d) << 16);
+  return r;
+}
+
+// 64 rows x 128 bf16 (row stride ld) -> LDS [channel][row] (pitch QTP), rows
+// >= len as zeros.  256 threads: thread b moves rows 4(b>>4)..+3 of channels
+// 8(b&15)..+7.
+__device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, size_t ld, int len, int b) {
+  const int r0 = 4 * (b >> 4), c0 = 8 * (b & 15);
+  uint4 x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    x[i] = r0 + i < len ? *reinterpret_cast<const uint4 *>(src + (size_t)(r0 + i) * ld + c0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) {
+    const int sh = (cc & 1) * 16;
+    auto part = [&](const uint4 &v) {
+      const uint32_t wd = (cc >> 1) == 0 ? v.x : ((cc >> 1) == 1 ? v.y : ((cc >> 1) == 2 ? v.z : v.w));
+      return (wd >> sh) & 0xffffu;
+    };
+    uint2 pk;
+    pk.x = part(x[0]) | (part(x[1]) << 16);
+    pk.y = part(x[2]) | (part(x[3]) << 16);
+    *reinterpret_cast<uint2 *>(dst + (c0 + cc) * QTP + r0) = pk;
+  }
+}
 
 template <bool SCALAR>
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int chunk = blockIdx.x, iqk = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const ChunkTable tb(p.table, p.NC, p.N);
   const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
   const int grp = SCALAR ? p.Hv / p.Hqk : 1;  // KDA: H_qk == H_v
   const float scale = p.scale;
   const size_t Hv = p.Hv;
 
-  u16 *sK = reinterpret_cast<u16 *>(smem);
-  u16 *sQ = sK + CH * KP;
-  u16 *sDW = sQ + CH * KP;
-  float *sE = reinterpret_cast<float *>(sDW + CH * KP);
-  float *sT = sE + CH * SP;
-  float *sDG = sE;  // 64 x GP fp32 over sE and sT at the end of each value head
-  u16 *sDM = reinterpret_cast<u16 *>(sT + CH * SP);
-  u16 *sDT = sDM + CH * MP;
-  u16 *sY = sDT + CH * MP;
-  float *sB = reinterpret_cast<float *>(sY + CH * MP);
+  u16 *sQT = reinterpret_cast<u16 *>(smem);
+  u16 *sKT = sQT + HD * QTP;
+  u16 *sY = sKT + HD * QTP;
+  u16 *sDM = sY + CH * KP;
+  u16 *sDA = sDM + CH * MP;
+  u16 *sDMT = sDA + CH * MP;
+  u16 *sDAT = sDMT + CH * MP;
+  float *sB = reinterpret_cast<float *>(sDAT + CH * MP);
   float *sDB = sB + 64;
   float *sRed = sDB + 64;
   float *sDgam = sRed + 128;
-  float *sG = sDgam + 128;
-  const Gate<SCALAR> G{sG};
+  float *sBT = sDgam + 128;  // [4][128] band totals
+  float *sG = sBT + 512;
+  const GateT<SCALAR> G{sG};
 
-  const size_t ldqk = (size_t)p.Hqk * HD;
-  load_rows_bf16<GNT>(sK, p.k + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid);
-  load_rows_bf16<GNT>(sQ, p.q + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid);
+  {
+    const int tid = threadIdx.x;
+    const size_t ldqk = (size_t)p.Hqk * HD;
+    if (tid < 256) load_rows_transposed(sQT, p.q + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid);
+    else load_rows_transposed(sKT, p.k + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid - 256);
+  }
 
-  const int mt = wave & 3, ch = wave >> 2;  // row strip, column half
-  const int nt0 = 4 * ch;                   // first 16-column tile of the half
   f32x4 dqA[4], dkA[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) { dqA[t] = zero4(); dkA[t] = zero4(); }
@@ -236,9 +286,13 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int mt = wave & 3, ch = wave >> 2, nt0 = 4 * ch;
+    const int mt = wave & 3, ch = wave >> 2;  // row strip, column half
     const int j = iqk * grp + jg;
     const size_t u = (size_t)chunk * Hv + j;
+    const int r0 = 16 * mt + 4 * lg;  // first of the 4 accumulator rows of this lane
+    const int ra = 16 * mt + lr;      // operand row of this lane
+
+    // ---- per value head: beta, cleared sums, the cumulative gate ----
     if (tid < 64) {
       float b = 0.f;
       if (tid < len) {
@@ -249,220 +303,179 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       sDB[tid] = 0.f;
     }
     if (tid < 128) sRed[tid] = 0.f;
-    // T = (I + diag(beta) E)^-1 and E as the forward's prep saved them (bf16)
-    if (tid < CH * CH / 8) {
-      const int r = tid >> 3, c8 = (tid & 7) * 8;
-      const bf16x8 tv = as_bf16x8(w.Tt[u * FRAG_64x64_U4 + tid]);
-      const bf16x8 ev = as_bf16x8(w.Et[u * FRAG_64x64_U4 + tid]);
+    // operands of Y = T^T dVn (issued before the barrier)
+    const u16 *dvt = w.dVnT + u * (CH * HD);
+    bf16x8 bT[2], aDV[4][2];
+    {
+      const uint4 *TT = w.Tt + u * FRAG_64x64_U4;  // T^T, bf16 row-major 64 x 64
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        sT[r * SP + c8 + ii] = (float)tv[ii];
-        sE[r * SP + c8 + ii] = (float)ev[ii];
-      }
+      for (int kt = 0; kt < 2; ++kt) bT[kt] = as_bf16x8(TT[ra * 8 + 4 * kt + lg]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) aDV[t][kt] = ld8(dvt + (16 * (4 * ch + t) + lr) * CH + 32 * kt + 8 * lg);
     }
-    load_cumsum_gate<SCALAR, GNT>(sG, p.g, start, len, p.Hv, j, tid);  // ends with a barrier
-
-    f32x4 dGA[4];
+    if constexpr (SCALAR) {
+      if (tid < 64) {
+        float x = tid < len ? p.g[(size_t)(start + tid) * Hv + j] : 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dGA[t] = zero4();
-    float dbp[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int o = 1; o < 64; o <<= 1) {
+          const float y = __shfl_up(x, o, 64);
+          if (tid >= o) x += y;
+        }
+        sG[tid] = x;
+      }
+      __syncthreads();
+    } else {
+      // thread: channel c, band of 16 rows; band sums, then the totals of the bands above
+      const int c = tid & 127, band = tid >> 7;
+      float x[16], run = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 16 * band + i;
+        run += r < len ? p.g[((size_t)(start + r) * Hv + j) * HD + c] : 0.f;
+        x[i] = run;
+      }
+      sBT[band * 128 + c] = run;
+      __syncthreads();
+      float base = 0.f;
+      for (int b = 0; b < band; ++b) base += sBT[b * 128 + c];
+#pragma unroll
+      for (int i = 0; i < 16; i += 4)
+        *reinterpret_cast<float4 *>(sG + c * GTP + 16 * band + i) =
+            make_float4(x[i] + base, x[i + 1] + base, x[i + 2] + base, x[i + 3] + base);
+    }
+
+    // ---- Y = T^T dVn: rows 16mt.., value columns 64ch.. (4 tiles, computed as Y^T) ----
+    {
+      const int kt0 = mt >= 2 ? 1 : 0;  // T^T[r][r'] = 0 for r' < r
+      const float br = sB[ra];
+      float db1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int v0 = 16 * (4 * ch + t) + 4 * lg;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          if (kt >= kt0) acc = mfma(aDV[t][kt], bT[kt], acc);
+        // acc[jj] = Y[ra][v0 + jj]
+        *reinterpret_cast<uint2 *>(sY + ra * KP + v0) = pack4(acc[0], acc[1], acc[2], acc[3]);
+        if (ra < len) {
+          const size_t e = ((size_t)(start + ra) * Hv + j) * HD + v0;
+          const uint2 vv = *reinterpret_cast<const uint2 *>(p.v + e);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) db1 += acc[jj] * bf_at(vv, jj);
+          *reinterpret_cast<uint2 *>(dv + e) = pack4(br * acc[0], br * acc[1], br * acc[2], br * acc[3]);
+        }
+      }
+      db1 = red_lg(db1);
+      if (lg == 0) atomicAdd(&sDB[ra], db1);
+    }
+    __syncthreads();
 
     // ---- products with the state tapes (reduction over the value dim) ----
     const u16 *Sg = w.S + u * (HD * HD);
     const u16 *dSg = w.dS + u * (HD * HD);
     const u16 *Vng = w.Vn + u * (CH * HD);
-    const u16 *dVg = w.dVn + u * (CH * HD);
-    bf16x8 dOa[4];
+    bf16x8 dOa[4], Ya[4], Vna[4];
     {
-    bf16x8 dVa[4], Vna[4];
-    {
-      const int row = 16 * mt + lr;
-      const u16 *dr = dout + ((size_t)(start + row) * Hv + j) * HD;
+      const u16 *dr = dout + ((size_t)(start + ra) * Hv + j) * HD;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const int c0 = 32 * kt + 8 * lg;
-        dOa[kt] = row < len ? ld8(dr + c0) : as_bf16x8(make_uint4(0, 0, 0, 0));
-        dVa[kt] = ld8(dVg + row * HD + c0);
-        Vna[kt] = ld8(Vng + row * HD + c0);
+        dOa[kt] = ra < len ? ld8(dr + c0) : as_bf16x8(make_uint4(0, 0, 0, 0));
+        Ya[kt] = ld8(sY + ra * KP + c0);
+        Vna[kt] = ld8(Vng + ra * HD + c0);
       }
     }
-#pragma unroll 1
-    for (int t = 0; t < 4; ++t) {
-      const int nt = nt0 + t, c = 16 * nt + lr;
-      bf16x8 Sb[4], dSb[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        Sb[kt] = ld8(Sg + c * HD + 32 * kt + 8 * lg);
-        dSb[kt] = ld8(dSg + c * HD + 32 * kt + 8 * lg);
-      }
-      f32x4 aQ = zero4(), aW = zero4(), aK = zero4();
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        aQ = mfma(dOa[kt], Sb[kt], aQ);
-        aW = mfma(dVa[kt], Sb[kt], aW);
-        aK = mfma(Vna[kt], dSb[kt], aK);
-      }
-      const float gl = G(last, c);
-      float colsum = 0.f;
-      f32x4 xq, xk, xg;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * mt + 4 * lg + jj;
-        const float gr = G(r, c);
-        const float qv = bf2f(sQ[r * KP + c]), kv = bf2f(sK[r * KP + c]);
-        const float dqi = scale * __expf(gr) * aQ[jj];
-        const float dkb = __expf(gl - gr) * aK[jj];
-        xq[jj] = dqi;
-        xk[jj] = dkb;
-        xg[jj] = qv * dqi - kv * dkb;
-        colsum += kv * dkb;
-        sDW[r * KP + c] = f2bf(-aW[jj]);
-      }
-      add_tile(dqA, t, xq);
-      add_tile(dkA, t, xk);
-      add_tile(dGA, t, xg);
-      colsum = red_lg(colsum);
-      if (lg == 0) atomicAdd(&sRed[c], colsum);
-      if ((nt >> 1) == mt) {  // sum_v dS'[key][v] S[key][v] for 32 keys per row strip
-        float pr = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int ii = 0; ii < 8; ++ii) pr += (float)Sb[kt][ii] * (float)dSb[kt][ii];
-        pr = red_lg(pr);
-        if (lg == 0) sDgam[c] = pr;
-      }
-    }
-    }
-    for (int nt = ch; nt < 4; nt += 2) {  // dM = scale dout Vn^T, lower (s <= r)
-      f32x4 acc = zero4();
-      if (nt <= mt) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) acc = mfma(dOa[kt], ld8(Vng + (16 * nt + lr) * HD + 32 * kt + 8 * lg), acc);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * mt + 4 * lg + jj, s = 16 * nt + lr;
-        sDM[r * MP + s] = f2bf(nt <= mt && s <= r ? scale * acc[jj] : 0.f);
-      }
-    }
-    __syncthreads();
-
-    // ---- dT = dVn (beta v)^T + dW (beta k exp G)^T, strictly lower ----
+    const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
+    f32x4 dGA[4];
+    float dbp[4] = {0.f, 0.f, 0.f, 0.f};
     {
-      bf16x8 dWa[4], dVa[4];
+      bf16x8 Sb[2][4], dSb[2][4];
+      auto load_tile = [&](int t, bf16x8 (&sb)[4], bf16x8 (&dsb)[4]) {
+        const int c = 16 * (4 * ch + t) + lr;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        dWa[kt] = ld8(sDW + (16 * mt + lr) * KP + 32 * kt + 8 * lg);
-        dVa[kt] = ld8(dVg + (16 * mt + lr) * HD + 32 * kt + 8 * lg);
-      }
-      for (int nt = ch; nt < 4; nt += 2) {
-        f32x4 acc = zero4();
-        if (nt <= mt) {
-          const int s = 16 * nt + lr;
-          const float bs = sB[s];
-          const u16 *vr = p.v + ((size_t)(start + s) * Hv + j) * HD;
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            const int c0 = 32 * kt + 8 * lg;
-            bf16x8 bV, bK;
-            const bf16x8 vraw = s < len ? ld8(vr + c0) : as_bf16x8(make_uint4(0, 0, 0, 0));
-#pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              bV[ii] = (__bf16)(bs * (float)vraw[ii]);
-              bK[ii] = (__bf16)(bs * bf2f(sK[s * KP + c0 + ii]) * __expf(G(s, c0 + ii)));
-            }
-            acc = mfma(dVa[kt], bV, acc);
-            acc = mfma(dWa[kt], bK, acc);
-          }
+        for (int kt = 0; kt < 4; ++kt) {
+          sb[kt] = ld8(Sg + c * HD + 32 * kt + 8 * lg);
+          dsb[kt] = ld8(dSg + c * HD + 32 * kt + 8 * lg);
         }
+      };
+      load_tile(0, Sb[0], dSb[0]);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 16 * mt + 4 * lg + jj, s = 16 * nt + lr;
-          sDT[r * MP + s] = f2bf(nt <= mt && s < r ? acc[jj] : 0.f);
-        }
-      }
-    }
-    __syncthreads();
-    // ---- Y = dT T^T ----
-    for (int nt = ch; nt < 4; nt += 2) {
-      f32x4 acc = zero4();
-      if (nt <= mt) {
-        const int s = 16 * nt + lr;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          acc = mfma(ld8(sDT + (16 * mt + lr) * MP + 32 * kt + 8 * lg), ld8f(sT + s * SP + 32 * kt + 8 * lg), acc);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sY[(16 * mt + 4 * lg + jj) * MP + 16 * nt + lr] = f2bf(acc[jj]);
-    }
-    __syncthreads();
-    // ---- dA = -T^T Y (strictly lower) into sDT; T^T dW and T^T dVn ----
-    bf16x8 aTT[2];  // A = T^T for this row strip
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) aTT[kt][ii] = (__bf16)sT[(32 * kt + 8 * lg + ii) * SP + 16 * mt + lr];
-    for (int nt = ch; nt < 4; nt += 2) {
-      f32x4 acc = zero4();
-      if (nt <= mt) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          bf16x8 bY;
-#pragma unroll
-          for (int ii = 0; ii < 8; ++ii)
-            bY[ii] = __builtin_bit_cast(__bf16, sY[(32 * kt + 8 * lg + ii) * MP + 16 * nt + lr]);
-          acc = mfma(aTT[kt], bY, acc);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * mt + 4 * lg + jj, s = 16 * nt + lr;
-        sDT[r * MP + s] = f2bf(nt <= mt && s < r ? -acc[jj] : 0.f);
-      }
-    }
-#pragma unroll 1
-    for (int t = 0; t < 4; ++t) {  // dKt = beta (T^T dW)
-      const int c = 16 * (nt0 + t) + lr;
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        bf16x8 bW;
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) bW[ii] = __builtin_bit_cast(__bf16, sDW[(32 * kt + 8 * lg + ii) * KP + c]);
-        acc = mfma(aTT[kt], bW, acc);
-      }
-      f32x4 xk, xg;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * mt + 4 * lg + jj;
-        const float e = __expf(G(r, c)), kv = bf2f(sK[r * KP + c]);
-        const float dkt = sB[r] * acc[jj];
-        xk[jj] = e * dkt;
-        xg[jj] = kv * e * dkt;
-        dbp[jj] += acc[jj] * kv * e;
-      }
-      add_tile(dkA, t, xk);
-      add_tile(dGA, t, xg);
-    }
-    {  // dv = beta (T^T dVn)
-      const u16 *dvt = w.dVnT + u * (CH * HD);
-#pragma unroll 1
       for (int t = 0; t < 4; ++t) {
-        const int vc = 16 * (nt0 + t) + lr;
-        f32x4 acc = zero4();
+        const int nt = 4 * ch + t, c = 16 * nt + lr;
+        const bf16x8(&sb)[4] = Sb[t & 1];
+        const bf16x8(&dsb)[4] = dSb[t & 1];
+        if (t + 1 < 4) load_tile(t + 1, Sb[(t + 1) & 1], dSb[(t + 1) & 1]);
+        f32x4 aQ = zero4(), aY = zero4(), aK = zero4();
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) acc = mfma(aTT[kt], ld8(dvt + vc * CH + 32 * kt + 8 * lg), acc);
+        for (int kt = 0; kt < 4; ++kt) {
+          aQ = mfma(dOa[kt], sb[kt], aQ);
+          aY = mfma(Ya[kt], sb[kt], aY);
+          aK = mfma(Vna[kt], dsb[kt], aK);
+        }
+        if ((nt >> 1) == mt) {  // sum_v dS'[key][v] S[key][v] for 32 keys per row strip
+          float pr = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) pr += (float)sb[kt][ii] * (float)dsb[kt][ii];
+          pr = red_lg(pr);
+          if (lg == 0) sDgam[c] = pr;
+        }
+        const float4 g4 = G.at4(r0, c);
+        const float gl = G.at(last, c);
+        const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
+        float colsum = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int r = 16 * mt + 4 * lg + jj;
-          if (r < len) {
-            const size_t e = ((size_t)(start + r) * Hv + j) * HD + vc;
-            dbp[jj] += acc[jj] * bf2f(p.v[e]);
-            dv[e] = f2bf(sB[r] * acc[jj]);
-          }
+          const float gr = g4[jj], qv = bf_at(q4, jj), kv = bf_at(k4, jj);
+          const float eg = __expf(gr), el = __expf(gl - gr);
+          const float dqi = scale * eg * aQ[jj];    // d(q exp G) -> dq
+          const float nb = -b4[jj] * aY[jj];        // dKt = -beta (Y S^T)
+          const float kb = el * aK[jj];             // dKbar exp(G_last - G)
+          const float kt_ = kv * eg;
+          dqA[t][jj] += dqi;
+          dkA[t][jj] += eg * nb + kb;
+          dGA[t][jj] = qv * dqi + kt_ * nb - kv * kb;
+          colsum += kv * kb;
+          dbp[jj] -= kt_ * aY[jj];
         }
+        colsum = red_lg(colsum);
+        if (lg == 0) atomicAdd(&sRed[c], colsum);
       }
+    }
+    // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r), 16 x 16 tiles (mt, nt)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int nt = ch + 2 * q, s = 16 * nt + lr;
+      f32x4 accM = zero4(), accA = zero4();
+      if (nt <= mt) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const bf16x8 vb = ld8(Vng + s * HD + 32 * kt + 8 * lg);
+          accM = mfma(dOa[kt], vb, accM);
+          accA = mfma(Ya[kt], vb, accA);
+        }
+        // E in accumulator order, tile (mt, nt) of the 10 lower tiles
+        const uint2 e4 = reinterpret_cast<const uint2 *>(w.Et + u * FRAG_64x64_U4)[(mt * (mt + 1) / 2 + nt) * 64 + lane];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (s < r0 + jj) dbp[jj] -= accA[jj] * bf_at(e4, jj);
+      }
+      float m[4], a[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = r0 + jj;
+        m[jj] = nt <= mt && s <= r ? scale * accM[jj] : 0.f;
+        a[jj] = nt <= mt && s < r ? -accA[jj] : 0.f;
+        sDM[r * MP + s] = f2bf(m[jj]);
+        sDA[r * MP + s] = f2bf(a[jj]);
+      }
+      *reinterpret_cast<uint2 *>(sDMT + s * MP + r0) = pack4(m[0], m[1], m[2], m[3]);
+      *reinterpret_cast<uint2 *>(sDAT + s * MP + r0) = pack4(a[0], a[1], a[2], a[3]);
     }
     __syncthreads();
 
@@ -475,29 +488,28 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       bf16x8 aM[2], aA[2], aMT[2], aAT[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        aM[kt] = ld8(sDM + (16 * I + lr) * MP + 32 * kt + 8 * lg);
-        aA[kt] = ld8(sDT + (16 * I + lr) * MP + 32 * kt + 8 * lg);
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const int r = 32 * kt + 8 * lg + ii;
-          aMT[kt][ii] = __builtin_bit_cast(__bf16, sDM[r * MP + 16 * I + lr]);
-          aAT[kt][ii] = __builtin_bit_cast(__bf16, sDT[r * MP + 16 * I + lr]);
-        }
+        aM[kt] = ld8(sDM + ra * MP + 32 * kt + 8 * lg);
+        aA[kt] = ld8(sDA + ra * MP + 32 * kt + 8 * lg);
+        aMT[kt] = ld8(sDMT + ra * MP + 32 * kt + 8 * lg);
+        aAT[kt] = ld8(sDAT + ra * MP + 32 * kt + 8 * lg);
       }
 #pragma unroll 1
       for (int t = 0; t < 4; ++t) {
-        const int c = 16 * (nt0 + t) + lr;
-        const float gref = G(ref, c);
+        const int c = 16 * (4 * ch + t) + lr;
+        const float gref = G.at(ref, c);
         // rows r of block I, sums over s <= r (s in blocks <= I)
         f32x4 accM = zero4(), accA = zero4();
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           if (kt > kfirst) continue;
+          const int s0 = 32 * kt + 8 * lg;
+          const bf16x8 k8 = ld8(sKT + c * QTP + s0);
+          const float4 ga = G.at4(s0, c), gb = G.at4(s0 + 4, c);
           bf16x8 bh, bl;
 #pragma unroll
           for (int ii = 0; ii < 8; ++ii) {
-            const int s = 32 * kt + 8 * lg + ii;
-            const float x = s <= 16 * I + 15 ? bf2f(sK[s * KP + c]) * __expf(gref - G(s, c)) : 0.f;
+            const float gs = ii < 4 ? ga[ii] : gb[ii - 4];
+            const float x = s0 + ii <= 16 * I + 15 ? (float)k8[ii] * __expf(gref - gs) : 0.f;
             split_bf16(x, bh, bl, ii);
           }
           accM = mfma(aM[kt], bh, accM);
@@ -510,28 +522,35 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           if (kt < kfirst) continue;
+          const int s0 = 32 * kt + 8 * lg;
+          const bf16x8 q8 = ld8(sQT + c * QTP + s0), k8 = ld8(sKT + c * QTP + s0);
+          const float4 ga = G.at4(s0, c), gb = G.at4(s0 + 4, c);
+          const float4 ba = *reinterpret_cast<const float4 *>(sB + s0);
+          const float4 bb = *reinterpret_cast<const float4 *>(sB + s0 + 4);
           bf16x8 qh, ql, kh, kl;
 #pragma unroll
           for (int ii = 0; ii < 8; ++ii) {
-            const int r = 32 * kt + 8 * lg + ii;
-            const float e = r >= 16 * I ? __expf(G(r, c) - gref) : 0.f;
-            split_bf16(bf2f(sQ[r * KP + c]) * e, qh, ql, ii);
-            split_bf16(sB[r] * bf2f(sK[r * KP + c]) * e, kh, kl, ii);
+            const float gr = ii < 4 ? ga[ii] : gb[ii - 4];
+            const float br = ii < 4 ? ba[ii] : bb[ii - 4];
+            const float e = s0 + ii >= 16 * I ? __expf(gr - gref) : 0.f;
+            split_bf16((float)q8[ii] * e, qh, ql, ii);
+            split_bf16(br * (float)k8[ii] * e, kh, kl, ii);
           }
           accT = mfma(aMT[kt], qh, accT);
           accT = mfma(aMT[kt], ql, accT);
           accT = mfma(aAT[kt], kh, accT);
           accT = mfma(aAT[kt], kl, accT);
         }
+        const float4 g4 = G.at4(r0, c);
+        const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
         f32x4 xq, xk, xg;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int r = 16 * I + 4 * lg + jj;
-          const float gr = G(r, c);
-          const float er = __expf(gr - gref), es = __expf(gref - gr);
-          const float qv = bf2f(sQ[r * KP + c]), kv = bf2f(sK[r * KP + c]);
+          const float er = __expf(g4[jj] - gref), es = __expf(gref - g4[jj]);
+          const float qv = bf_at(q4, jj), kv = bf_at(k4, jj);
           const float qM = er * accM[jj];
-          const float kA = sB[r] * er * accA[jj];
+          const float kA = b4[jj] * er * accA[jj];
           const float kT = es * accT[jj];
           xq[jj] = qM;
           xk[jj] = kA + kT;
@@ -547,55 +566,63 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const float x = red16(dbp[jj]);
-      if (lr == 0) atomicAdd(&sDB[16 * mt + 4 * lg + jj], x);
+      if (lr == 0) atomicAdd(&sDB[r0 + jj], x);
     }
-    __syncthreads();
-    if (tid < 64) {
-      const int r = tid;
-      float acc = sDB[r];
-      for (int s = 0; s < r; ++s) acc += bf2f(sDT[r * MP + s]) * sE[r * SP + s];
-      if (r < len) {
-        const size_t e = (size_t)(start + r) * Hv + j;
-        if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = acc;
-        else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(acc);
-      }
+    __syncthreads();  // also: sRed and sDgam complete
+    if (tid < 64 && tid < len) {
+      const size_t e = (size_t)(start + tid) * Hv + j;
+      if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = sDB[tid];
+      else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(sDB[tid]);
     }
-    __syncthreads();
 
     // ---- gate epilogue: dg = in-chunk reverse cumulative sum of dG ----
+    // The last row also collects the gradient of gamma = exp(G_last) and the
+    // column sums of the Kbar terms.
+    if ((last >> 4) == mt && ((last >> 2) & 3) == lg) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        const int c = 16 * (4 * ch + t) + lr;
+        const float extra = sRed[c] + __expf(G.at(last, c)) * sDgam[c];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sDG[(16 * mt + 4 * lg + jj) * GP + 16 * (nt0 + t) + lr] = dGA[t][jj];
-    __syncthreads();
-    if (tid < 128) sDG[last * GP + tid] += sRed[tid] + __expf(G(last, tid)) * sDgam[tid];
-    __syncthreads();
+        for (int jj = 0; jj < 4; ++jj)
+          if (r0 + jj == last) dGA[t][jj] += extra;
+      }
+    }
     if constexpr (!SCALAR) {
-      // four 16-row bands per channel: reverse-scan each band, then add the
-      // totals of the bands below it
-      const int c = tid & 127, band = tid >> 7;
-      float run = 0.f;
-      for (int r = 16 * band + 15; r >= 16 * band; --r) {
-        run += sDG[r * GP + c];
-        sDG[r * GP + c] = run;
+      // suffix sums inside the lane (4 rows), across the lane groups (16-row
+      // block), then across the row blocks through LDS
+      float hsum[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float s3 = dGA[t][3], s2 = s3 + dGA[t][2], s1 = s2 + dGA[t][1], s0 = s1 + dGA[t][0];
+        const float a = __shfl_down(s0, 16, 64), b = __shfl_down(s0, 32, 64), cc = __shfl_down(s0, 48, 64);
+        const float up = (lg < 3 ? a : 0.f) + (lg < 2 ? b : 0.f) + (lg < 1 ? cc : 0.f);
+        hsum[t][0] = s0 + up; hsum[t][1] = s1 + up; hsum[t][2] = s2 + up; hsum[t][3] = s3 + up;
+        if (lg == 0) sBT[mt * 128 + 16 * (4 * ch + t) + lr] = hsum[t][0];
       }
       __syncthreads();
-      float tail = 0.f;
-      for (int b = band + 1; b < 4; ++b) tail += sDG[16 * b * GP + c];
-      for (int r = 16 * band; r < 16 * band + 16; ++r)
-        if (r < len) dg[((size_t)(start + r) * Hv + j) * HD + c] = sDG[r * GP + c] + tail;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = 16 * (4 * ch + t) + lr;
+        float below = 0.f;
+        for (int b = mt + 1; b < 4; ++b) below += sBT[b * 128 + c];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = r0 + jj;
+          if (r < len) dg[((size_t)(start + r) * Hv + j) * HD + c] = hsum[t][jj] + below;
+        }
+      }
     } else {
-      // channel sums per row (8 threads per row), then a reverse scan over rows
-      const int r = tid >> 3, q8 = tid & 7;
-      float x = 0.f;
-      for (int c = 16 * q8; c < 16 * q8 + 16; ++c) x += sDG[r * GP + c];
-      x += __shfl_xor(x, 1, 64);
-      x += __shfl_xor(x, 2, 64);
-      x += __shfl_xor(x, 4, 64);
-      if (q8 == 0) sDB[r] = x;
+      // row sums over the channels, then a reverse scan over the rows
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float x = dGA[0][jj] + dGA[1][jj] + dGA[2][jj] + dGA[3][jj];
+        x = red16(x);
+        if (lr == 0) sBT[ch * 64 + r0 + jj] = x;
+      }
       __syncthreads();
       if (tid < 64) {
-        float y = sDB[63 - tid];
+        float y = sBT[63 - tid] + sBT[64 + 63 - tid];
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const float z = __shfl_up(y, o, 64);
@@ -609,17 +636,21 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
   }
 
   // dq, dk: fp32 sums over the group's value heads, rounded once
+  {
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), mt = wave & 3, ch = wave >> 2;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int r = 16 * mt + 4 * lg + jj;
-      if (r < len) {
-        const size_t e = ((size_t)(start + r) * p.Hqk + iqk) * HD + 16 * (nt0 + t) + lr;
-        dq[e] = f2bf(dqA[t][jj]);
-        dk[e] = f2bf(dkA[t][jj]);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * mt + 4 * lg + jj;
+        if (r < len) {
+          const size_t e = ((size_t)(start + r) * p.Hqk + iqk) * HD + 16 * (4 * ch + t) + lr;
+          dq[e] = f2bf(dqA[t][jj]);
+          dk[e] = f2bf(dkA[t][jj]);
+        }
       }
-    }
+  }
 }
 
 hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout, const float *dht, float *dh0,

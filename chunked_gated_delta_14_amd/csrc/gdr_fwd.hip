@@ -71,17 +71,22 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(Problem p, Workspace w, i
   gated_kk<SCALAR, true>(sE, sM, sK, sQ, sG, wave, lane);
   __syncthreads();
   tri_inverse(sT, sE, sB, sX, tid);
-  if (save) {  // T and E for the gradient kernel, bf16 row-major 64 x 64
+  if (save) {  // T^T (bf16 row-major) and E (accumulator order) for the gradient kernel
     for (int e = tid; e < CH * CH / 8; e += 256) {
       const int r = e >> 3, c8 = (e & 7) * 8;
-      bf16x8 tv, ev;
+      bf16x8 tv;
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        tv[ii] = (__bf16)sT[r * SP + c8 + ii];
-        ev[ii] = (__bf16)sE[r * SP + c8 + ii];
-      }
+      for (int ii = 0; ii < 8; ++ii) tv[ii] = (__bf16)sT[(c8 + ii) * SP + r];
       w.Tt[u * FRAG_64x64_U4 + e] = as_u4(tv);
-      w.Et[u * FRAG_64x64_U4 + e] = as_u4(ev);
+    }
+    for (int e = tid; e < 10 * 64; e += 256) {  // lower 16x16 tiles (I, J), lane holds rows 4lg..+3
+      int I, J;
+      block_pair(e >> 6, I, J);
+      const int ln = e & 63, row = 16 * I + 4 * (ln >> 4), col = 16 * J + (ln & 15);
+      uint2 pk;
+      pk.x = f2bf(sE[row * SP + col]) | ((uint32_t)f2bf(sE[(row + 1) * SP + col]) << 16);
+      pk.y = f2bf(sE[(row + 2) * SP + col]) | ((uint32_t)f2bf(sE[(row + 3) * SP + col]) << 16);
+      reinterpret_cast<uint2 *>(w.Et + u * FRAG_64x64_U4)[e] = pk;
     }
     __syncthreads();  // sE is reused for W below
   }

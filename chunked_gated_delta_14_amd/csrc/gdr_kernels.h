@@ -21,14 +21,14 @@ struct Workspace {
   uint4 *WTn;   // -W^T, A fragments (rows: key, k: chunk)
   uint4 *QGT;   // scale * (Q.Gamma)^T, A fragments (rows: key, k: chunk)
   uint4 *MTs;   // scale * M^T, A fragments (rows: chunk, k: chunk), 8 tiles
-  uint4 *Tt;    // T = (I + diag(beta) E)^-1, bf16 row-major 64 x 64
-  uint4 *Et;    // E (gated k k^T, strictly lower), bf16 row-major 64 x 64
+  uint4 *Tt;    // T^T, T = (I + diag(beta) E)^-1, bf16 row-major 64 x 64
+  uint4 *Et;    // E (gated k k^T, strictly lower): its 10 lower 16x16 tiles in
+                //   accumulator order, [u][tile][lane 64][4] bf16
   // tapes
   uint16_t *S;    // entering state of every chunk, bf16 [u][key][v]      (forward walk, SAVE)
   uint16_t *Vn;   // new values, bf16 [u][row][v]                         (forward walk, SAVE)
   uint16_t *dS;   // adjoint state leaving every chunk, bf16 [u][key][v]  (backward walk)
-  uint16_t *dVn;  // adjoint of the new values, bf16 [u][row][v]          (backward walk)
-  uint16_t *dVnT; // the same, transposed, bf16 [u][v][row]               (backward walk)
+  uint16_t *dVnT; // adjoint of the new values, bf16 [u][v][row]          (backward walk)
 };
 
 struct Problem {
