@@ -19,216 +19,381 @@
 
 namespace gdr {
 
-template <bool SCALAR>
-constexpr int prep_smem_bytes() {
-  return 4 * CH * KP * 2       // sK, sQ, sV (later P), sU
-         + 2 * CH * SP * 4     // sE (later W), sT
-         + CH * MP * 2         // sM
-         + 64 * 4 + 768 * 4    // sB, solve scratch
-         + (SCALAR ? 64 * 4 : CH * GP * 4);  // sG
+// ---------------------------------------------------------------------------
+// Prep: one workgroup (8 wavefronts) per (chunk, value head).
+//  1. Thread (channel c, band of 16 rows) loads its piece of g, k, q, v,
+//     scans the gate and forms every exponentially rescaled operand once.
+//     For a row r of 16-row block I (reference row 16I+8):
+//       F = exp(G_r - G_ref),  Fi = exp(G_ref - G_r),
+//       exp(G_r) = F exp(G_ref),  exp(G_last - G_r) = Fi exp(G_last - G_ref),
+//     and per channel D_IJ = exp(G_ref(I) - G_ref(J)) for blocks J < I, so a
+//     gated entry exp(G_r - G_s) = F_r D_IJ Fi_s never leaves fp32/bf16 range.
+//  2. E and M per 16x16 block pair as products of (k F) and (q F) with (k Fi D).
+//  3. T = (I + diag(beta) E)^-1.
+//  4. W = T (beta k exp G) together with W^T, and U = T (beta v).
+//  5. P^T = scale (q exp G)^T - scale W^T M^T and Oi = scale M U.
+// Walk operands whose fragment is a pair of stacked accumulator tiles (kwalk
+// order) are stored straight from the accumulators; the rest go through LDS
+// in column form ([channel][row]), where a fragment's rows are contiguous.
+// ---------------------------------------------------------------------------
+constexpr int PNT = 512;
+constexpr int CTP = 72;  // LDS pitch (bf16) of column-form tiles [channel][row]
+
+// LDS map (bytes).  Steps 1-2 use KF, QF, KFi; steps 3-5 reuse that space for
+// the column-form operands, and W, U replace beta k exp(G), beta v in step 4.
+constexpr int P_KF = 0;                    // k F   bf16 [64][KP]
+constexpr int P_QF = P_KF + CH * KP * 2;   // q F   bf16 [64][KP]
+constexpr int P_KFI = P_QF + CH * KP * 2;  // k Fi  fp32 [64][GP]
+constexpr int P_BKG = 0;                   // beta k exp(G)          bf16 [128][CTP]
+constexpr int P_BV = P_BKG + HD * CTP * 2; // beta v
+constexpr int P_QG = P_BV + HD * CTP * 2;  // scale q exp(G)
+constexpr int P_KL = P_QG + HD * CTP * 2;  // Kbar = k exp(G_last - G)
+constexpr int P_WT = P_BKG;                // W (column form)
+constexpr int P_UT = P_BV;                 // U (column form)
+constexpr int P_E = P_KL + HD * CTP * 2;   // E fp32 [64][SP]
+constexpr int P_T = P_E + CH * SP * 4;     // T fp32 [64][SP]
+constexpr int P_M = P_T + CH * SP * 4;     // M bf16 [64][MP]
+constexpr int P_B = P_M + CH * MP * 2;     // beta [64]
+constexpr int P_TOT = P_B + 64 * 4;        // gate band totals [4][128]
+constexpr int P_P8 = P_TOT + 512 * 4;      // band partial sums at the reference rows [4][128]
+constexpr int P_PL = P_P8 + 512 * 4;       // band partial sum at the last row [128]
+constexpr int P_D = P_PL + 128 * 4;        // D_IJ [6][128]
+constexpr int P_X = P_D + 768 * 4;         // solve scratch [768]
+constexpr int P_SMEM = P_X + 768 * 4;
+static_assert(P_KFI + CH * GP * 4 <= P_E, "prep LDS map");
+
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  return f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+__device__ __forceinline__ uint2 pack4bf(const f32x4 &x) {
+  uint2 r;
+  r.x = pack2bf(x[0], x[1]);
+  r.y = pack2bf(x[2], x[3]);
+  return r;
+}
+__device__ __forceinline__ bf16x8 cvt8(float4 a, float4 b) {
+  bf16x8 r;
+  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
+  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
+  return r;
 }
 
 template <bool SCALAR>
-__global__ __launch_bounds__(256) void fwd_prep_kernel(Problem p, Workspace w, int save) {
+__global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int chunk = blockIdx.x, j = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const ChunkTable tb(p.table, p.NC, p.N);
-  const int start = tb.start[chunk], len = tb.len[chunk];
-  const int i = j / (p.Hv / p.Hqk);
+  const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
+  const int iq = j / (p.Hv / p.Hqk);
   const size_t u = (size_t)chunk * p.Hv + j;
+  const size_t Hv = p.Hv;
   const float scale = p.scale;
 
-  u16 *sK = reinterpret_cast<u16 *>(smem);
-  u16 *sQ = sK + CH * KP;
-  u16 *sV = sQ + CH * KP;
-  u16 *sU = sV + CH * KP;
-  float *sE = reinterpret_cast<float *>(sU + CH * KP);
-  float *sT = sE + CH * SP;
-  u16 *sM = reinterpret_cast<u16 *>(sT + CH * SP);
-  float *sB = reinterpret_cast<float *>(sM + CH * MP);
-  float *sX = sB + 64;
-  float *sG = sX + 768;
-  u16 *sW = reinterpret_cast<u16 *>(sE);  // W replaces E once T is built
-  u16 *sP = sV;                           // P replaces V once U is built
-  const Gate<SCALAR> G{sG};
+  u16 *sKF = reinterpret_cast<u16 *>(smem + P_KF);
+  u16 *sQF = reinterpret_cast<u16 *>(smem + P_QF);
+  float *sKFi = reinterpret_cast<float *>(smem + P_KFI);
+  u16 *sBKG = reinterpret_cast<u16 *>(smem + P_BKG);
+  u16 *sBV = reinterpret_cast<u16 *>(smem + P_BV);
+  u16 *sQG = reinterpret_cast<u16 *>(smem + P_QG);
+  u16 *sKL = reinterpret_cast<u16 *>(smem + P_KL);
+  u16 *sWT = reinterpret_cast<u16 *>(smem + P_WT);
+  u16 *sUT = reinterpret_cast<u16 *>(smem + P_UT);
+  float *sE = reinterpret_cast<float *>(smem + P_E);
+  float *sT = reinterpret_cast<float *>(smem + P_T);
+  u16 *sM = reinterpret_cast<u16 *>(smem + P_M);
+  float *sB = reinterpret_cast<float *>(smem + P_B);
+  float *sTot = reinterpret_cast<float *>(smem + P_TOT);
+  float *sP8 = reinterpret_cast<float *>(smem + P_P8);
+  float *sPL = reinterpret_cast<float *>(smem + P_PL);
+  float *sD = reinterpret_cast<float *>(smem + P_D);
+  float *sX = reinterpret_cast<float *>(smem + P_X);
 
-  const size_t ldqk = (size_t)p.Hqk * HD, ldv = (size_t)p.Hv * HD;
-  load_rows_bf16(sK, p.k + ((size_t)start * p.Hqk + i) * HD, ldqk, len, tid);
-  load_rows_bf16(sQ, p.q + ((size_t)start * p.Hqk + i) * HD, ldqk, len, tid);
-  load_rows_bf16(sV, p.v + ((size_t)start * p.Hv + j) * HD, ldv, len, tid);
-  if (tid < 64) {
-    float b = 0.f;
-    if (tid < len) {
-      const size_t e = (size_t)(start + tid) * p.Hv + j;
-      b = SCALAR ? reinterpret_cast<const float *>(p.beta)[e] : bf2f(reinterpret_cast<const u16 *>(p.beta)[e]);
-    }
-    sB[tid] = b;
-  }
-  load_cumsum_gate<SCALAR>(sG, p.g, start, len, p.Hv, j, tid);
-
-  gated_kk<SCALAR, true>(sE, sM, sK, sQ, sG, wave, lane);
-  __syncthreads();
-  tri_inverse(sT, sE, sB, sX, tid);
-  if (save) {  // T^T (bf16 row-major) and E (accumulator order) for the gradient kernel
-    for (int e = tid; e < CH * CH / 8; e += 256) {
-      const int r = e >> 3, c8 = (e & 7) * 8;
-      bf16x8 tv;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) tv[ii] = (__bf16)sT[(c8 + ii) * SP + r];
-      w.Tt[u * FRAG_64x64_U4 + e] = as_u4(tv);
-    }
-    for (int e = tid; e < 10 * 64; e += 256) {  // lower 16x16 tiles (I, J), lane holds rows 4lg..+3
-      int I, J;
-      block_pair(e >> 6, I, J);
-      const int ln = e & 63, row = 16 * I + 4 * (ln >> 4), col = 16 * J + (ln & 15);
-      uint2 pk;
-      pk.x = f2bf(sE[row * SP + col]) | ((uint32_t)f2bf(sE[(row + 1) * SP + col]) << 16);
-      pk.y = f2bf(sE[(row + 2) * SP + col]) | ((uint32_t)f2bf(sE[(row + 3) * SP + col]) << 16);
-      reinterpret_cast<uint2 *>(w.Et + u * FRAG_64x64_U4)[e] = pk;
-    }
-    __syncthreads();  // sE is reused for W below
-  }
-
-  // W = T (beta k exp(G)),  U = T (beta v); wavefront `wave` owns rows 16*wave..+15.
+  // ---- 1. gate scan and rescaled operands: thread = (channel c, 16-row band) ----
+  const int c = tid & 127, band = tid >> 7, rb = 16 * band;
+  uint32_t pkBKG[8], pkBV[8], pkQG[8], pkKL[8];  // column-form values of the 16 rows, bf16 pairs
   {
-    const int mt = wave, kmax = mt >= 2 ? 2 : 1;  // T is lower triangular
-    bf16x8 aT[2];
+    float gs[16];
+    u16 kk[16], qq[16], vv[16];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) aT[kt] = ld8f(sT + (16 * mt + lr) * SP + 32 * kt + 8 * lg);
-    for (int nt = 0; nt < 8; ++nt) {
-      const int c = 16 * nt + lr;
-      f32x4 accW = zero4(), accU = zero4();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        if (kt >= kmax) continue;
-        bf16x8 bW, bU;
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const int s = 32 * kt + 8 * lg + ii;
-          const float bs = sB[s];
-          bW[ii] = (__bf16)(bs * bf2f(sK[s * KP + c]) * __expf(G(s, c)));
-          bU[ii] = (__bf16)(bs * bf2f(sV[s * KP + c]));
-        }
-        accW = mfma(aT[kt], bW, accW);
-        accU = mfma(aT[kt], bU, accU);
+    for (int i = 0; i < 16; ++i) {
+      const int r = rb + i;
+      const bool in = r < len;
+      const size_t t = (size_t)(start + r);
+      gs[i] = in ? (SCALAR ? p.g[t * Hv + j] : p.g[(t * Hv + j) * HD + c]) : 0.f;
+      kk[i] = in ? p.k[(t * p.Hqk + iq) * HD + c] : (u16)0;
+      qq[i] = in ? p.q[(t * p.Hqk + iq) * HD + c] : (u16)0;
+      vv[i] = in ? p.v[(t * Hv + j) * HD + c] : (u16)0;
+    }
+    if (tid < 64) {
+      float b = 0.f;
+      if (tid < len) {
+        const size_t e = (size_t)(start + tid) * Hv + j;
+        b = SCALAR ? reinterpret_cast<const float *>(p.beta)[e] : bf2f(reinterpret_cast<const u16 *>(p.beta)[e]);
       }
-      uint2 pk;
-      u16 ub[4];
+      sB[tid] = b;
+    }
+    float run = 0.f, pl = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      run += gs[i];
+      gs[i] = run;
+      if (i == (last & 15)) pl = run;
+    }
+    sTot[band * 128 + c] = run;
+    sP8[band * 128 + c] = gs[8];
+    if ((last >> 4) == band) sPL[c] = pl;
+    __syncthreads();
+
+    // band bases, reference gates G_ref(I) and G_last of channel c
+    float acc = 0.f, base = 0.f, go = 0.f, gl = 0.f, gref[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      gref[b] = acc + sP8[b * 128 + c];
+      if (b == band) { base = acc; go = gref[b]; }
+      if (b == (last >> 4)) gl = acc + sPL[c];
+      acc += sTot[b * 128 + c];
+    }
+    const float eref = __expf(go), elr = __expf(gl - go);
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      float xb[2], xv[2], xq[2], xl[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = rb + i + h;
+        const float G = gs[i + h] + base;
+        const float F = __expf(G - go), Fi = __expf(go - G);
+        const float kv = bf2f(kk[i + h]), qv = bf2f(qq[i + h]), vx = bf2f(vv[i + h]);
+        const float b = sB[r];
+        sKF[r * KP + c] = f2bf(kv * F);
+        sQF[r * KP + c] = f2bf(qv * F);
+        sKFi[r * GP + c] = kv * Fi;
+        const float eg = F * eref;  // exp(G_r)
+        xb[h] = b * kv * eg;
+        xv[h] = b * vx;
+        xq[h] = scale * qv * eg;
+        xl[h] = kv * (Fi * elr);    // k exp(G_last - G_r)
+      }
+      pkBKG[i >> 1] = pack2bf(xb[0], xb[1]);
+      pkBV[i >> 1] = pack2bf(xv[0], xv[1]);
+      pkQG[i >> 1] = pack2bf(xq[0], xq[1]);
+      pkKL[i >> 1] = pack2bf(xl[0], xl[1]);
+    }
+    if (band == 0) {
+      w.gam[u * HD + c] = __expf(gl);
+      // D_IJ in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): index I(I-1)/2 + J
+      sD[0 * 128 + c] = __expf(gref[1] - gref[0]);
+      sD[1 * 128 + c] = __expf(gref[2] - gref[0]);
+      sD[2 * 128 + c] = __expf(gref[2] - gref[1]);
+      sD[3 * 128 + c] = __expf(gref[3] - gref[0]);
+      sD[4 * 128 + c] = __expf(gref[3] - gref[1]);
+      sD[5 * 128 + c] = __expf(gref[3] - gref[2]);
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. gated products.  Wavefront w: column block J = w >> 1 and row
+  // blocks I in {2kt, 2kt+1}, kt = w & 1; the two accumulator tiles of M are
+  // then exactly the scale M^T fragment (J, kt). ----
+  {
+    const int J = wave >> 1, kt2 = wave & 1, s = 16 * J + lr;
+    f32x4 aE[2] = {zero4(), zero4()}, aMc[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int c0 = 32 * kc + 8 * lg;
+      const float4 fa = *reinterpret_cast<const float4 *>(sKFi + s * GP + c0);
+      const float4 fb = *reinterpret_cast<const float4 *>(sKFi + s * GP + c0 + 4);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int I = 2 * kt2 + h;
+        if (I < J) continue;
+        bf16x8 bk;
+        if (I == J) {
+          bk = cvt8(fa, fb);
+        } else {
+          const float *d = sD + ((I * (I - 1)) / 2 + J) * 128 + c0;
+          const float4 da = *reinterpret_cast<const float4 *>(d), db = *reinterpret_cast<const float4 *>(d + 4);
+          bk = cvt8(make_float4(fa.x * da.x, fa.y * da.y, fa.z * da.z, fa.w * da.w),
+                    make_float4(fb.x * db.x, fb.y * db.y, fb.z * db.z, fb.w * db.w));
+        }
+        aE[h] = mfma(ld8(sKF + (16 * I + lr) * KP + c0), bk, aE[h]);
+        aMc[h] = mfma(ld8(sQF + (16 * I + lr) * KP + c0), bk, aMc[h]);
+      }
+    }
+    f32x4 ms[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int I = 2 * kt2 + h;
+      f32x4 ev;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int row = 16 * mt + 4 * lg + jj;
-        sW[row * KP + c] = f2bf(accW[jj]);
-        ub[jj] = f2bf(accU[jj]);
-        sU[row * KP + c] = ub[jj];
+        const int r = 16 * I + 4 * lg + jj;
+        const float e = (I >= J && s < r) ? aE[h][jj] : 0.f;
+        const float m = (I >= J && s <= r) ? aMc[h][jj] : 0.f;
+        sE[r * SP + s] = e;
+        sM[r * MP + s] = f2bf(m);
+        ev[jj] = e;
+        ms[h][jj] = scale * m;
       }
-      pk.x = ub[0] | ((uint32_t)ub[1] << 16);
-      pk.y = ub[2] | ((uint32_t)ub[3] << 16);
-      *reinterpret_cast<uint2 *>(w.Uacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4) = pk;
+      if (save && I >= J)  // E for the gradient kernel, accumulator order of tile (I, J)
+        reinterpret_cast<uint2 *>(w.Et + u * FRAG_64x64_U4)[((I * (I + 1)) / 2 + J) * 64 + lane] = pack4bf(ev);
     }
+    if (save) w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane] = as_u4(acc_pair_to_b(ms[0], ms[1]));
   }
   __syncthreads();
 
-  // P = scale (q exp(G) - M W),  Oi = scale M U
+  // ---- 3. column-form operands (over the step-1 space), then T ----
   {
-    const int mt = wave, kmax = mt >= 2 ? 2 : 1;  // M is lower triangular
-    bf16x8 aM[2];
+    uint4 *d;
+    d = reinterpret_cast<uint4 *>(sBKG + c * CTP + rb);
+    d[0] = make_uint4(pkBKG[0], pkBKG[1], pkBKG[2], pkBKG[3]);
+    d[1] = make_uint4(pkBKG[4], pkBKG[5], pkBKG[6], pkBKG[7]);
+    d = reinterpret_cast<uint4 *>(sBV + c * CTP + rb);
+    d[0] = make_uint4(pkBV[0], pkBV[1], pkBV[2], pkBV[3]);
+    d[1] = make_uint4(pkBV[4], pkBV[5], pkBV[6], pkBV[7]);
+    d = reinterpret_cast<uint4 *>(sQG + c * CTP + rb);
+    d[0] = make_uint4(pkQG[0], pkQG[1], pkQG[2], pkQG[3]);
+    d[1] = make_uint4(pkQG[4], pkQG[5], pkQG[6], pkQG[7]);
+    d = reinterpret_cast<uint4 *>(sKL + c * CTP + rb);
+    d[0] = make_uint4(pkKL[0], pkKL[1], pkKL[2], pkKL[3]);
+    d[1] = make_uint4(pkKL[4], pkKL[5], pkKL[6], pkKL[7]);
+  }
+  tri_inverse<PNT>(sT, sE, sB, sX, tid);  // ends with a barrier
+
+  // ---- 4. W = T (beta k exp G), W^T, U = T (beta v).  Wavefront: row blocks
+  // {2kp, 2kp+1}, column tiles {2cg, 2cg+1}. ----
+  const int kp = wave & 1, cg = wave >> 1;
+  {
+    bf16x8 aT[2][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) aM[kt] = ld8(sM + (16 * mt + lr) * MP + 32 * kt + 8 * lg);
-    for (int nt = 0; nt < 8; ++nt) {
-      const int c = 16 * nt + lr;
-      f32x4 accP = zero4(), accO = zero4();
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        if (kt <= kp) aT[h][kt] = ld8f(sT + (32 * kp + 16 * h + lr) * SP + 32 * kt + 8 * lg);
+    f32x4 Wd[2][2], Ud[2][2], WTd[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) { Wd[a][b] = zero4(); Ud[a][b] = zero4(); WTd[a][b] = zero4(); }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int cc = 16 * (2 * cg + n) + lr;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        if (kt >= kmax) continue;
-        bf16x8 bW, bU;
+        if (kt > kp) continue;
+        const bf16x8 bw = ld8(sBKG + cc * CTP + 32 * kt + 8 * lg);
+        const bf16x8 bu = ld8(sBV + cc * CTP + 32 * kt + 8 * lg);
 #pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const int s = 32 * kt + 8 * lg + ii;
-          bW[ii] = __builtin_bit_cast(__bf16, sW[s * KP + c]);
-          bU[ii] = __builtin_bit_cast(__bf16, sU[s * KP + c]);
+        for (int h = 0; h < 2; ++h) {
+          Wd[h][n] = mfma(aT[h][kt], bw, Wd[h][n]);
+          Ud[h][n] = mfma(aT[h][kt], bu, Ud[h][n]);
+          WTd[n][h] = mfma(bw, aT[h][kt], WTd[n][h]);  // W^T: rows channel, columns chunk row
         }
-        accP = mfma(aM[kt], bW, accP);
-        accO = mfma(aM[kt], bU, accO);
       }
-      u16 ob[4];
+    }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int row = 16 * mt + 4 * lg + jj;
-        const float pv = scale * (bf2f(sQ[row * KP + c]) * __expf(G(row, c)) - accP[jj]);
-        sP[row * KP + c] = f2bf(pv);
-        ob[jj] = f2bf(scale * accO[jj]);
+    for (int h = 0; h < 2; ++h) {  // -W: rows chunk 16mt.., k: key 32cg + kwalk
+      const int mt = 2 * kp + h;
+      w.WfN[u * FRAG_64x128_U4 + (mt * 4 + cg) * 64 + lane] = as_u4(acc_pair_to_b(-WTd[0][h], -WTd[1][h]));
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int nt = 2 * cg + n;
+        *reinterpret_cast<uint2 *>(w.Uacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4) = pack4bf(Ud[h][n]);
       }
-      uint2 pk;
-      pk.x = ob[0] | ((uint32_t)ob[1] << 16);
-      pk.y = ob[2] | ((uint32_t)ob[3] << 16);
-      *reinterpret_cast<uint2 *>(w.Oacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4) = pk;
+    }
+    if (save)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)  // -W^T: rows key 16nt.., k: chunk 32kp + kwalk
+        w.WTn[u * FRAG_64x128_U4 + ((2 * cg + n) * 2 + kp) * 64 + lane] = as_u4(acc_pair_to_b(-Wd[0][n], -Wd[1][n]));
+    __syncthreads();  // beta k exp(G) and beta v are dead
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int cc = 16 * (2 * cg + n) + lr, r0 = 32 * kp + 16 * h + 4 * lg;
+        *reinterpret_cast<uint2 *>(sWT + cc * CTP + r0) = pack4bf(Wd[h][n]);
+        *reinterpret_cast<uint2 *>(sUT + cc * CTP + r0) = pack4bf(Ud[h][n]);
+      }
+    __syncthreads();
+  }
+
+  // ---- 5. P^T = scale (q exp G)^T - scale W^T M^T,  Oi = scale M U ----
+  {
+    bf16x8 aM[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        if (kt <= kp) aM[h][kt] = ld8(sM + (32 * kp + 16 * h + lr) * MP + 32 * kt + 8 * lg);
+    f32x4 PT[2][2], Oi[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) { PT[a][b] = zero4(); Oi[a][b] = zero4(); }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int cc = 16 * (2 * cg + n) + lr;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        if (kt > kp) continue;
+        const bf16x8 aw = ld8(sWT + cc * CTP + 32 * kt + 8 * lg);
+        const bf16x8 bu = ld8(sUT + cc * CTP + 32 * kt + 8 * lg);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          PT[n][h] = mfma(aw, aM[h][kt], PT[n][h]);
+          Oi[h][n] = mfma(aM[h][kt], bu, Oi[h][n]);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mt = 2 * kp + h, r = 16 * mt + lr;
+      f32x4 pt[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int cc = 16 * (2 * cg + n) + 4 * lg + jj;
+          pt[n][jj] = bf2f(sQG[cc * CTP + r]) - scale * PT[n][h][jj];
+        }
+      w.Pf[u * FRAG_64x128_U4 + (mt * 4 + cg) * 64 + lane] = as_u4(acc_pair_to_b(pt[0], pt[1]));
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int nt = 2 * cg + n;
+        *reinterpret_cast<uint2 *>(w.Oacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4) =
+            pack4bf(scale * Oi[h][n]);
+      }
     }
   }
-  __syncthreads();
 
-  // Walk operands in fragment order (one 16-byte load per lane per tile).
-  const int last = len - 1;
-  if (tid < 128) w.gam[u * HD + tid] = __expf(G(last, tid));
-  for (int slot = tid; slot < 1024; slot += 256) {
+  // ---- remaining walk operands from the column-form tiles ----
+  for (int slot = tid; slot < 1024; slot += PNT) {
     const int tile = slot >> 6, ln = slot & 63, r_ = ln & 15, g_ = ln >> 4;
-    {  // rows: chunk (16 mt + r_), k: key (32 kt + kwalk)
-      const int mt = tile >> 2, kt = tile & 3, row = 16 * mt + r_;
-      bf16x8 wv, pv;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int col = 32 * kt + kwalk(g_, ii);
-        wv[ii] = __builtin_bit_cast(__bf16, (u16)(sW[row * KP + col] ^ 0x8000u));
-        pv[ii] = __builtin_bit_cast(__bf16, sP[row * KP + col]);
-      }
-      w.WfN[u * FRAG_64x128_U4 + slot] = as_u4(wv);
-      w.Pf[u * FRAG_64x128_U4 + slot] = as_u4(pv);
+    {  // rows: key (16 mt + r_), k: chunk (32 kt + kwalk): two 4-row runs of a column-form row
+      const int mt = tile >> 1, kt = tile & 1, key = 16 * mt + r_;
+      const int o = key * CTP + 32 * kt + 4 * g_;
+      const uint2 a = *reinterpret_cast<const uint2 *>(sKL + o), b = *reinterpret_cast<const uint2 *>(sKL + o + 16);
+      w.KbT[u * FRAG_64x128_U4 + slot] = make_uint4(a.x, a.y, b.x, b.y);
       if (save) {
-        bf16x8 kb;
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const int col = 32 * kt + kwalk(g_, ii);
-          kb[ii] = (__bf16)(bf2f(sK[row * KP + col]) * __expf(G(last, col) - G(row, col)));
-        }
-        w.Kb[u * FRAG_64x128_U4 + slot] = as_u4(kb);
+        const uint2 qa = *reinterpret_cast<const uint2 *>(sQG + o), qb = *reinterpret_cast<const uint2 *>(sQG + o + 16);
+        w.QGT[u * FRAG_64x128_U4 + slot] = make_uint4(qa.x, qa.y, qb.x, qb.y);
       }
     }
-    {  // rows: key (16 mt + r_), k: chunk (32 kt + kwalk)
-      const int mt = tile >> 1, kt = tile & 1, key = 16 * mt + r_;
-      const float gl = G(last, key);
-      bf16x8 kbt;
+    if (save) {  // rows: chunk (16 mt + r_), k: key (32 kt + kwalk)
+      const int mt = tile >> 2, kt = tile & 3, row = 16 * mt + r_;
+      bf16x8 kb;
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int r = 32 * kt + kwalk(g_, ii);
-        kbt[ii] = (__bf16)(bf2f(sK[r * KP + key]) * __expf(gl - G(r, key)));
-      }
-      w.KbT[u * FRAG_64x128_U4 + slot] = as_u4(kbt);
-      if (save) {
-        bf16x8 qg, wt;
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const int r = 32 * kt + kwalk(g_, ii);
-          qg[ii] = (__bf16)(scale * bf2f(sQ[r * KP + key]) * __expf(G(r, key)));
-          wt[ii] = __builtin_bit_cast(__bf16, (u16)(sW[r * KP + key] ^ 0x8000u));
-        }
-        w.QGT[u * FRAG_64x128_U4 + slot] = as_u4(qg);
-        w.WTn[u * FRAG_64x128_U4 + slot] = as_u4(wt);
-      }
+      for (int ii = 0; ii < 8; ++ii) kb[ii] = __builtin_bit_cast(__bf16, sKL[(32 * kt + kwalk(g_, ii)) * CTP + row]);
+      w.Kb[u * FRAG_64x128_U4 + slot] = as_u4(kb);
     }
   }
-  if (save) {
-    for (int slot = tid; slot < 512; slot += 256) {  // rows: chunk s, k: chunk r; scale * M[r][s]
-      const int tile = slot >> 6, ln = slot & 63, r_ = ln & 15, g_ = ln >> 4;
-      const int mt = tile >> 1, kt = tile & 1, s = 16 * mt + r_;
-      bf16x8 mv;
+  if (save && tid < CH * CH / 8) {  // T^T, bf16 row-major, for the gradient kernel
+    const int r = tid >> 3, c8 = (tid & 7) * 8;
+    bf16x8 tv;
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int r = 32 * kt + kwalk(g_, ii);
-        mv[ii] = (__bf16)(scale * bf2f(sM[r * MP + s]));
-      }
-      w.MTs[u * FRAG_64x64_U4 + slot] = as_u4(mv);
-    }
+    for (int ii = 0; ii < 8; ++ii) tv[ii] = (__bf16)sT[(c8 + ii) * SP + r];
+    w.Tt[u * FRAG_64x64_U4 + tid] = as_u4(tv);
   }
 }
 
@@ -365,19 +530,12 @@ static int walk_grid(int chains) { return ((chains + 7) / 8) * 64; }
 
 hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, hipStream_t st) {
   if (p.NC == 0) return hipSuccess;
-  const dim3 grid(p.NC, p.Hv), block(256);
-  hipError_t e;
-  if (gdn) {
-    const int sm = prep_smem_bytes<true>();
-    e = hipFuncSetAttribute((const void *)fwd_prep_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
-    if (e != hipSuccess) return e;
-    fwd_prep_kernel<true><<<grid, block, sm, st>>>(p, w, save ? 1 : 0);
-  } else {
-    const int sm = prep_smem_bytes<false>();
-    e = hipFuncSetAttribute((const void *)fwd_prep_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
-    if (e != hipSuccess) return e;
-    fwd_prep_kernel<false><<<grid, block, sm, st>>>(p, w, save ? 1 : 0);
-  }
+  const dim3 grid(p.NC, p.Hv), block(PNT);
+  const void *fn = gdn ? (const void *)fwd_prep_kernel<true> : (const void *)fwd_prep_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
+  if (e != hipSuccess) return e;
+  if (gdn) fwd_prep_kernel<true><<<grid, block, P_SMEM, st>>>(p, w, save ? 1 : 0);
+  else fwd_prep_kernel<false><<<grid, block, P_SMEM, st>>>(p, w, save ? 1 : 0);
   return hipGetLastError();
 }
 
