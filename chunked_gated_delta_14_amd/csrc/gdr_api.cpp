@@ -108,8 +108,8 @@ int32_t check_sizes(int32_t variant, int64_t T, int64_t N, int64_t NC, int64_t H
   // most one partial chunk
   if (NC > T || NC < (T + kChunk - 1) / kChunk || NC > (T + kChunk - 1) / kChunk + N)
     return fail(GDR_ERR_INVALID_ARG, "n_chunks is inconsistent with T and N");
-  // grid sizes are 32-bit: chunk grids use NC blocks, walk grids 8 * N * H_v blocks
-  if (N * Hv > (int64_t(1) << 27) || NC * Hv > (int64_t(1) << 40))
+  // grid sizes are 32-bit: chunk grids use NC * H_v blocks, walk grids 8 * N * H_v
+  if (N * Hv > (int64_t(1) << 27) || NC * Hv > (int64_t(1) << 31) - 1)
     return fail(GDR_ERR_UNSUPPORTED, "problem too large");
   return GDR_OK;
 }

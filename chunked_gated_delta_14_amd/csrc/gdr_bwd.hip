@@ -246,7 +246,8 @@ template <bool SCALAR>
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int chunk = blockIdx.x, iqk = blockIdx.y;
+  // Q/K heads vary fastest over the grid (whole token rows per resident set)
+  const int chunk = blockIdx.x / p.Hqk, iqk = blockIdx.x % p.Hqk;
   const ChunkTable tb(p.table, p.NC, p.N);
   const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
   const int grp = SCALAR ? p.Hv / p.Hqk : 1;  // KDA: H_qk == H_v
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
   float *sDB = sB + 64;
   float *sRed = sDB + 64;
   float *sDgam = sRed + 128;
-  float *sBT = sDgam + 128;  // [4][128] band totals
+  float *sBT = sDgam + 128;  // [4][128] row-block totals of the gate gradient
   float *sG = sBT + 512;
   const GateT<SCALAR> G{sG};
 
@@ -327,23 +328,32 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       }
       __syncthreads();
     } else {
-      // thread: channel c, band of 16 rows; band sums, then the totals of the bands above
-      const int c = tid & 127, band = tid >> 7;
-      float x[16], run = 0.f;
+      // thread: channel octet 8o..8o+7, rows 2pr and 2pr+1, read as 16-byte
+      // pieces; the 32 lanes of a half wavefront scan their octet's 64 rows
+      const int o = tid >> 5, pr = tid & 31, c0 = 8 * o, rp = 2 * pr;
+      float gx[2][8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * band + i;
-        run += r < len ? p.g[((size_t)(start + r) * Hv + j) * HD + c] : 0.f;
-        x[i] = run;
+      for (int h = 0; h < 2; ++h) {
+        float4 ga = make_float4(0.f, 0.f, 0.f, 0.f), gb = ga;
+        if (rp + h < len) {
+          const float *src = p.g + ((size_t)(start + rp + h) * Hv + j) * HD + c0;
+          ga = *reinterpret_cast<const float4 *>(src);
+          gb = *reinterpret_cast<const float4 *>(src + 4);
+        }
+        gx[h][0] = ga.x; gx[h][1] = ga.y; gx[h][2] = ga.z; gx[h][3] = ga.w;
+        gx[h][4] = gb.x; gx[h][5] = gb.y; gx[h][6] = gb.z; gx[h][7] = gb.w;
       }
-      sBT[band * 128 + c] = run;
-      __syncthreads();
-      float base = 0.f;
-      for (int b = 0; b < band; ++b) base += sBT[b * 128 + c];
 #pragma unroll
-      for (int i = 0; i < 16; i += 4)
-        *reinterpret_cast<float4 *>(sG + c * GTP + 16 * band + i) =
-            make_float4(x[i] + base, x[i + 1] + base, x[i + 2] + base, x[i + 3] + base);
+      for (int ii = 0; ii < 8; ++ii) {
+        float incl = gx[0][ii] + gx[1][ii];
+#pragma unroll
+        for (int d = 1; d < 32; d <<= 1) {
+          const float y = __shfl_up(incl, d, 32);
+          if (pr >= d) incl += y;
+        }
+        *reinterpret_cast<float2 *>(sG + (c0 + ii) * GTP + rp) = make_float2(incl - gx[1][ii], incl);
+      }
+      __syncthreads();
     }
 
     // ---- Y = T^T dVn: rows 16mt.., value columns 64ch.. (4 tiles, computed as Y^T) ----
@@ -664,7 +674,7 @@ hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout
 hipError_t launch_bwd_grad(bool gdn, const Problem &p, const Workspace &w, const u16 *dout, u16 *dq, u16 *dk,
                            u16 *dv, float *dg, void *dbeta, hipStream_t st) {
   if (p.NC == 0) return hipSuccess;
-  const dim3 grid(p.NC, p.Hqk), block(GNT);
+  const dim3 grid(p.NC * p.Hqk), block(GNT);
   hipError_t e;
   if (gdn) {
     const int sm = grad_smem_bytes<true>();

@@ -231,58 +231,62 @@ __device__ __forceinline__ void gated_kk(float *sE, u16 *sM, const u16 *sK, cons
   }
 }
 
-// T = (I + diag(beta) E)^-1 (unit lower triangular, fp32) by blocked forward
-// substitution: the four 16x16 diagonal blocks are inverted column by column,
-// then T_IJ = -T_II * sum_{J<=K<I} A_IK T_KJ level by level (I - J = 1, 2, 3).
-// sX: scratch of 3*256 floats.
-template <int NT = 256>
-__device__ __forceinline__ void tri_inverse(float *sT, const float *sE, const float *sB, float *sX,
-                                            int tid) {
-  // zero the strictly upper 16x16 blocks
-  for (int e = tid; e < 6 * 256; e += NT) {
+// fp32 MFMA, 16x16x4: lane holds A[lr][k], B[k][lr] for its reduction index k
+// and D[4lg + j][lr], as the bf16 form.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// T = (I + diag(beta) E)^-1 (unit lower triangular, fp32) for a strictly
+// lower 64 x 64 E (pitch SP) in blocks of 16:
+//  - the four diagonal blocks by right-looking forward substitution, one lane
+//    per column (wavefront 0);
+//  - the off-diagonal blocks level by level (I - J = 1, 2, 3) as
+//      T_IJ = -T_II sum_{J <= K < I} diag(beta_I) E_IK T_KJ,
+//    one wavefront per block with fp32 MFMAs.  The inner sum uses reduction
+//    index k = 4q + lg in step q; the product with T_II uses k = 4lg + q, so
+//    the sum's accumulator is its B operand as it stands.
+template <int NT>
+__device__ __forceinline__ void tri_inverse(float *sT, const float *sE, const float *sB, int tid) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  for (int e = tid; e < 6 * 256; e += NT) {  // strictly upper blocks
     const int p = e >> 8, idx = e & 255;
     const int I = p < 3 ? 0 : (p < 5 ? 1 : 2);
     const int J = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
     sT[(16 * I + (idx >> 4)) * SP + 16 * J + (idx & 15)] = 0.f;
   }
-  if (tid < 64) {
-    const int I = tid >> 4, s = tid & 15, base = 16 * I;
-    float x[16];
+  if (wave == 0) {
+    const int base = 16 * (lane >> 4), s = lane & 15;
+    float x[16], nb[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == s) ? 1.f : 0.f;
-#pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      const float b = sB[base + r];
-      float acc = x[r];
-#pragma unroll
-      for (int t = 0; t < r; ++t) acc -= b * sE[(base + r) * SP + base + t] * x[t];
-      x[r] = acc;
+    for (int r = 0; r < 16; ++r) {
+      x[r] = (r == s) ? 1.f : 0.f;
+      nb[r] = -sB[base + r];
     }
+#pragma unroll
+    for (int t = 0; t < 15; ++t)
+#pragma unroll
+      for (int r = t + 1; r < 16; ++r) x[r] += nb[r] * sE[(base + r) * SP + base + t] * x[t];
 #pragma unroll
     for (int r = 0; r < 16; ++r) sT[(base + r) * SP + base + s] = x[r];
   }
   __syncthreads();
   for (int d = 1; d < 4; ++d) {
-    const int nb = 4 - d;
-    for (int e = tid; e < nb * 256; e += NT) {
-      const int b = e >> 8, idx = e & 255, r = idx >> 4, s = idx & 15;
-      const int I = b + d, J = b;
-      const float beta_r = sB[16 * I + r];
-      float acc = 0.f;
+    if (wave < 4 - d) {
+      const int J = wave, I = J + d, row = 16 * I + lr;
+      const float br = sB[row];
+      f32x4 X = zero4();
       for (int K = J; K < I; ++K)
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
-          acc += beta_r * sE[(16 * I + r) * SP + 16 * K + t] * sT[(16 * K + t) * SP + 16 * J + s];
-      sX[e] = acc;
-    }
-    __syncthreads();
-    for (int e = tid; e < nb * 256; e += NT) {
-      const int b = e >> 8, idx = e & 255, r = idx >> 4, s = idx & 15;
-      const int I = b + d, J = b;
-      float acc = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const int k = 4 * q + lg;
+          X = mfma4(br * sE[row * SP + 16 * K + k], sT[(16 * K + k) * SP + 16 * J + lr], X);
+        }
+      f32x4 Y = zero4();
 #pragma unroll
-      for (int t = 0; t < 16; ++t) acc += sT[(16 * I + r) * SP + 16 * I + t] * sX[b * 256 + t * 16 + s];
-      sT[(16 * I + r) * SP + 16 * J + s] = -acc;
+      for (int q = 0; q < 4; ++q) Y = mfma4(sT[row * SP + 16 * I + 4 * lg + q], X[q], Y);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) sT[(16 * I + 4 * lg + jj) * SP + 16 * J + lr] = -Y[jj];
     }
     __syncthreads();
   }

@@ -21,7 +21,7 @@ namespace gdr {
 
 // ---------------------------------------------------------------------------
 // Prep: one workgroup (8 wavefronts) per (chunk, value head).
-//  1. Thread (channel c, band of 16 rows) loads its piece of g, k, q, v,
+//  1. Thread (channel octet, row pair) loads its piece of g, k, q, v,
 //     scans the gate and forms every exponentially rescaled operand once.
 //     For a row r of 16-row block I (reference row 16I+8):
 //       F = exp(G_r - G_ref),  Fi = exp(G_ref - G_r),
@@ -54,12 +54,8 @@ constexpr int P_E = P_KL + HD * CTP * 2;   // E fp32 [64][SP]
 constexpr int P_T = P_E + CH * SP * 4;     // T fp32 [64][SP]
 constexpr int P_M = P_T + CH * SP * 4;     // M bf16 [64][MP]
 constexpr int P_B = P_M + CH * MP * 2;     // beta [64]
-constexpr int P_TOT = P_B + 64 * 4;        // gate band totals [4][128]
-constexpr int P_P8 = P_TOT + 512 * 4;      // band partial sums at the reference rows [4][128]
-constexpr int P_PL = P_P8 + 512 * 4;       // band partial sum at the last row [128]
-constexpr int P_D = P_PL + 128 * 4;        // D_IJ [6][128]
-constexpr int P_X = P_D + 768 * 4;         // solve scratch [768]
-constexpr int P_SMEM = P_X + 768 * 4;
+constexpr int P_D = P_B + 64 * 4;          // D_IJ [6][128]
+constexpr int P_SMEM = P_D + 768 * 4;
 static_assert(P_KFI + CH * GP * 4 <= P_E, "prep LDS map");
 
 __device__ __forceinline__ uint32_t pack2bf(float a, float b) {
@@ -81,7 +77,9 @@ __device__ __forceinline__ bf16x8 cvt8(float4 a, float4 b) {
 template <bool SCALAR>
 __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int chunk = blockIdx.x, j = blockIdx.y;
+  // heads vary fastest over the grid, so the workgroups resident together read
+  // whole token rows of q, k, v and g
+  const int chunk = blockIdx.x / p.Hv, j = blockIdx.x % p.Hv;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const ChunkTable tb(p.table, p.NC, p.N);
@@ -104,91 +102,109 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
   float *sT = reinterpret_cast<float *>(smem + P_T);
   u16 *sM = reinterpret_cast<u16 *>(smem + P_M);
   float *sB = reinterpret_cast<float *>(smem + P_B);
-  float *sTot = reinterpret_cast<float *>(smem + P_TOT);
-  float *sP8 = reinterpret_cast<float *>(smem + P_P8);
-  float *sPL = reinterpret_cast<float *>(smem + P_PL);
   float *sD = reinterpret_cast<float *>(smem + P_D);
-  float *sX = reinterpret_cast<float *>(smem + P_X);
 
-  // ---- 1. gate scan and rescaled operands: thread = (channel c, 16-row band) ----
-  const int c = tid & 127, band = tid >> 7, rb = 16 * band;
-  uint32_t pkBKG[8], pkBV[8], pkQG[8], pkKL[8];  // column-form values of the 16 rows, bf16 pairs
+  // ---- 1. thread = (channel octet o, row pair pr): rows 2pr, 2pr+1 of
+  // channels 8o..8o+7, read as 16-byte pieces.  The 32 lanes of a half
+  // wavefront hold all 64 rows of their octet, so the gate scan and the
+  // reference gates are in-wave shuffles. ----
+  const int o = tid >> 5, pr = tid & 31, c0 = 8 * o, rp = 2 * pr;
+  uint32_t pkBKG[8], pkBV[8], pkQG[8], pkKL[8];  // channel c0+ii: rows rp, rp+1 as a bf16 pair
   {
-    float gs[16];
-    u16 kk[16], qq[16], vv[16];
+    constexpr int NG = SCALAR ? 1 : 8;  // gate values per row held by a thread
+    bf16x8 kx[2], qx[2], vx[2];
+    float gx[2][NG], bt[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = rb + i;
+    for (int h = 0; h < 2; ++h) {
+      const int r = rp + h;
       const bool in = r < len;
       const size_t t = (size_t)(start + r);
-      gs[i] = in ? (SCALAR ? p.g[t * Hv + j] : p.g[(t * Hv + j) * HD + c]) : 0.f;
-      kk[i] = in ? p.k[(t * p.Hqk + iq) * HD + c] : (u16)0;
-      qq[i] = in ? p.q[(t * p.Hqk + iq) * HD + c] : (u16)0;
-      vv[i] = in ? p.v[(t * Hv + j) * HD + c] : (u16)0;
-    }
-    if (tid < 64) {
-      float b = 0.f;
-      if (tid < len) {
-        const size_t e = (size_t)(start + tid) * Hv + j;
-        b = SCALAR ? reinterpret_cast<const float *>(p.beta)[e] : bf2f(reinterpret_cast<const u16 *>(p.beta)[e]);
+      const bf16x8 z = as_bf16x8(make_uint4(0, 0, 0, 0));
+      kx[h] = in ? ld8(p.k + (t * p.Hqk + iq) * HD + c0) : z;
+      qx[h] = in ? ld8(p.q + (t * p.Hqk + iq) * HD + c0) : z;
+      vx[h] = in ? ld8(p.v + (t * Hv + j) * HD + c0) : z;
+      if constexpr (SCALAR) {
+        gx[h][0] = in ? p.g[t * Hv + j] : 0.f;
+        bt[h] = in ? reinterpret_cast<const float *>(p.beta)[t * Hv + j] : 0.f;
+      } else {
+        float4 ga = make_float4(0.f, 0.f, 0.f, 0.f), gb = ga;
+        if (in) {
+          ga = *reinterpret_cast<const float4 *>(p.g + (t * Hv + j) * HD + c0);
+          gb = *reinterpret_cast<const float4 *>(p.g + (t * Hv + j) * HD + c0 + 4);
+        }
+        gx[h][0] = ga.x; gx[h][1] = ga.y; gx[h][2] = ga.z; gx[h][3] = ga.w;
+        gx[h][4] = gb.x; gx[h][5] = gb.y; gx[h][6] = gb.z; gx[h][7] = gb.w;
+        bt[h] = in ? bf2f(reinterpret_cast<const u16 *>(p.beta)[t * Hv + j]) : 0.f;
       }
-      sB[tid] = b;
     }
-    float run = 0.f, pl = 0.f;
+    if (o == 0) { sB[rp] = bt[0]; sB[rp + 1] = bt[1]; }
+    // inclusive scan of the gate over the 64 rows, reference gates, G_last
+    float G[2][NG], gref[4][NG], gl[NG];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      run += gs[i];
-      gs[i] = run;
-      if (i == (last & 15)) pl = run;
+    for (int ic = 0; ic < NG; ++ic) {
+      float incl = gx[0][ic] + gx[1][ic];
+#pragma unroll
+      for (int d = 1; d < 32; d <<= 1) {
+        const float y = __shfl_up(incl, d, 32);
+        if (pr >= d) incl += y;
+      }
+      G[1][ic] = incl;
+      G[0][ic] = incl - gx[1][ic];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) gref[I][ic] = __shfl(G[0][ic], 8 * I + 4, 32);
+      gl[ic] = (last & 1) ? __shfl(G[1][ic], last >> 1, 32) : __shfl(G[0][ic], last >> 1, 32);
     }
-    sTot[band * 128 + c] = run;
-    sP8[band * 128 + c] = gs[8];
-    if ((last >> 4) == band) sPL[c] = pl;
-    __syncthreads();
-
-    // band bases, reference gates G_ref(I) and G_last of channel c
-    float acc = 0.f, base = 0.f, go = 0.f, gl = 0.f, gref[4];
+    const int Ib = rp >> 4;  // 16-row block of both rows
+    bf16x8 kf[2], qf[2];
+    float kfi[2][8];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      gref[b] = acc + sP8[b * 128 + c];
-      if (b == band) { base = acc; go = gref[b]; }
-      if (b == (last >> 4)) gl = acc + sPL[c];
-      acc += sTot[b * 128 + c];
-    }
-    const float eref = __expf(go), elr = __expf(gl - go);
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int ii = 0; ii < 8; ++ii) {
+      const int ic = SCALAR ? 0 : ii;
+      const float go = Ib == 0 ? gref[0][ic] : (Ib == 1 ? gref[1][ic] : (Ib == 2 ? gref[2][ic] : gref[3][ic]));
+      const float eref = __expf(go), elr = __expf(gl[ic] - go);
       float xb[2], xv[2], xq[2], xl[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int r = rb + i + h;
-        const float G = gs[i + h] + base;
-        const float F = __expf(G - go), Fi = __expf(go - G);
-        const float kv = bf2f(kk[i + h]), qv = bf2f(qq[i + h]), vx = bf2f(vv[i + h]);
-        const float b = sB[r];
-        sKF[r * KP + c] = f2bf(kv * F);
-        sQF[r * KP + c] = f2bf(qv * F);
-        sKFi[r * GP + c] = kv * Fi;
+        const float F = __expf(G[h][ic] - go), Fi = __expf(go - G[h][ic]);
+        const float kv = (float)kx[h][ii], qv = (float)qx[h][ii], vv = (float)vx[h][ii];
+        kf[h][ii] = (__bf16)(kv * F);
+        qf[h][ii] = (__bf16)(qv * F);
+        kfi[h][ii] = kv * Fi;
         const float eg = F * eref;  // exp(G_r)
-        xb[h] = b * kv * eg;
-        xv[h] = b * vx;
+        xb[h] = bt[h] * kv * eg;
+        xv[h] = bt[h] * vv;
         xq[h] = scale * qv * eg;
         xl[h] = kv * (Fi * elr);    // k exp(G_last - G_r)
       }
-      pkBKG[i >> 1] = pack2bf(xb[0], xb[1]);
-      pkBV[i >> 1] = pack2bf(xv[0], xv[1]);
-      pkQG[i >> 1] = pack2bf(xq[0], xq[1]);
-      pkKL[i >> 1] = pack2bf(xl[0], xl[1]);
+      pkBKG[ii] = pack2bf(xb[0], xb[1]);
+      pkBV[ii] = pack2bf(xv[0], xv[1]);
+      pkQG[ii] = pack2bf(xq[0], xq[1]);
+      pkKL[ii] = pack2bf(xl[0], xl[1]);
     }
-    if (band == 0) {
-      w.gam[u * HD + c] = __expf(gl);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = rp + h;
+      *reinterpret_cast<bf16x8 *>(sKF + r * KP + c0) = kf[h];
+      *reinterpret_cast<bf16x8 *>(sQF + r * KP + c0) = qf[h];
+      *reinterpret_cast<float4 *>(sKFi + r * GP + c0) = make_float4(kfi[h][0], kfi[h][1], kfi[h][2], kfi[h][3]);
+      *reinterpret_cast<float4 *>(sKFi + r * GP + c0 + 4) = make_float4(kfi[h][4], kfi[h][5], kfi[h][6], kfi[h][7]);
+    }
+    if (pr == 0) {
+      float e[8];
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) e[ii] = __expf(gl[SCALAR ? 0 : ii]);
+      *reinterpret_cast<float4 *>(w.gam + u * HD + c0) = make_float4(e[0], e[1], e[2], e[3]);
+      *reinterpret_cast<float4 *>(w.gam + u * HD + c0 + 4) = make_float4(e[4], e[5], e[6], e[7]);
       // D_IJ in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): index I(I-1)/2 + J
-      sD[0 * 128 + c] = __expf(gref[1] - gref[0]);
-      sD[1 * 128 + c] = __expf(gref[2] - gref[0]);
-      sD[2 * 128 + c] = __expf(gref[2] - gref[1]);
-      sD[3 * 128 + c] = __expf(gref[3] - gref[0]);
-      sD[4 * 128 + c] = __expf(gref[3] - gref[1]);
-      sD[5 * 128 + c] = __expf(gref[3] - gref[2]);
+#pragma unroll
+      for (int I = 1; I < 4; ++I)
+#pragma unroll
+        for (int J = 0; J < I; ++J)
+#pragma unroll
+          for (int ii = 0; ii < 8; ++ii) {
+            const int ic = SCALAR ? 0 : ii;
+            sD[((I * (I - 1)) / 2 + J) * 128 + c0 + ii] = __expf(gref[I][ic] - gref[J][ic]);
+          }
     }
   }
   __syncthreads();
@@ -244,22 +260,15 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
   __syncthreads();
 
   // ---- 3. column-form operands (over the step-1 space), then T ----
-  {
-    uint4 *d;
-    d = reinterpret_cast<uint4 *>(sBKG + c * CTP + rb);
-    d[0] = make_uint4(pkBKG[0], pkBKG[1], pkBKG[2], pkBKG[3]);
-    d[1] = make_uint4(pkBKG[4], pkBKG[5], pkBKG[6], pkBKG[7]);
-    d = reinterpret_cast<uint4 *>(sBV + c * CTP + rb);
-    d[0] = make_uint4(pkBV[0], pkBV[1], pkBV[2], pkBV[3]);
-    d[1] = make_uint4(pkBV[4], pkBV[5], pkBV[6], pkBV[7]);
-    d = reinterpret_cast<uint4 *>(sQG + c * CTP + rb);
-    d[0] = make_uint4(pkQG[0], pkQG[1], pkQG[2], pkQG[3]);
-    d[1] = make_uint4(pkQG[4], pkQG[5], pkQG[6], pkQG[7]);
-    d = reinterpret_cast<uint4 *>(sKL + c * CTP + rb);
-    d[0] = make_uint4(pkKL[0], pkKL[1], pkKL[2], pkKL[3]);
-    d[1] = make_uint4(pkKL[4], pkKL[5], pkKL[6], pkKL[7]);
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    const int off = (c0 + ii) * CTP + rp;
+    *reinterpret_cast<uint32_t *>(sBKG + off) = pkBKG[ii];
+    *reinterpret_cast<uint32_t *>(sBV + off) = pkBV[ii];
+    *reinterpret_cast<uint32_t *>(sQG + off) = pkQG[ii];
+    *reinterpret_cast<uint32_t *>(sKL + off) = pkKL[ii];
   }
-  tri_inverse<PNT>(sT, sE, sB, sX, tid);  // ends with a barrier
+  tri_inverse<PNT>(sT, sE, sB, tid);  // ends with a barrier
 
   // ---- 4. W = T (beta k exp G), W^T, U = T (beta v).  Wavefront: row blocks
   // {2kp, 2kp+1}, column tiles {2cg, 2cg+1}. ----
@@ -530,7 +539,7 @@ static int walk_grid(int chains) { return ((chains + 7) / 8) * 64; }
 
 hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, hipStream_t st) {
   if (p.NC == 0) return hipSuccess;
-  const dim3 grid(p.NC, p.Hv), block(PNT);
+  const dim3 grid(p.NC * p.Hv), block(PNT);
   const void *fn = gdn ? (const void *)fwd_prep_kernel<true> : (const void *)fwd_prep_kernel<false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
   if (e != hipSuccess) return e;
