@@ -68,6 +68,28 @@ __device__ __forceinline__ void split_bf16(float x, bf16x8 &hi, bf16x8 &lo, int 
   lo[i] = (__bf16)(x - (float)h);
 }
 
+// Inclusive prefix sum over each half wavefront (lanes 0-31 and 32-63) with
+// DPP: shifts within rows of 16 lanes, then lane 15 of rows 0 and 2 added to
+// rows 1 and 3 (row_bcast:15 with row mask 0b1010).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float v) {  // lanes without a source read 0
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float scan32(float x) {
+  x += dpp_move<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_move<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_move<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_move<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_move<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  return x;
+}
+// Value of lane l of this lane's half wavefront (hi: lanes 32-63).
+__device__ __forceinline__ float half_lane(float x, int l, bool hi) {
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32 + l));
+  return hi ? b : a;
+}
+
 // 8 contiguous bf16 from LDS/global (16-byte aligned).
 __device__ __forceinline__ bf16x8 ld8(const u16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 // 8 contiguous floats (16-byte aligned) -> bf16.
@@ -83,10 +105,15 @@ __device__ __forceinline__ bf16x8 ld8f(const float *p) {
 // ---------------------------------------------------------------------------
 // Chunk tables (layout documented in gdr.h, gdr_plan_chunks)
 // ---------------------------------------------------------------------------
+// The table is read-only for the whole launch, so it is read through the
+// constant address space: uniform indices become scalar loads, which do not
+// wait on the vector-memory counter (and so not on a wavefront's stores).
+typedef const __attribute__((address_space(4))) int32_t *ConstI32;
 struct ChunkTable {
-  const int32_t *start, *len, *doc, *doc_ptr, *order;
+  ConstI32 start, len, doc, doc_ptr, order;
   __device__ __forceinline__ ChunkTable(const int32_t *t, int nc, int n)
-      : start(t), len(t + nc), doc(t + 2 * nc), doc_ptr(t + 3 * nc), order(t + 3 * nc + n + 1) {}
+      : start((ConstI32)t), len((ConstI32)(t + nc)), doc((ConstI32)(t + 2 * nc)),
+        doc_ptr((ConstI32)(t + 3 * nc)), order((ConstI32)(t + 3 * nc + n + 1)) {}
 };
 
 // Walk grid: chain c (= rank of the document in walk order * H_v + head)

@@ -24,8 +24,9 @@ namespace gdr {
 //  1. Thread (channel octet, row pair) loads its piece of g, k, q, v,
 //     scans the gate and forms every exponentially rescaled operand once.
 //     For a row r of 16-row block I (reference row 16I+8):
-//       F = exp(G_r - G_ref),  Fi = exp(G_ref - G_r),
-//       exp(G_r) = F exp(G_ref),  exp(G_last - G_r) = Fi exp(G_last - G_ref),
+//       F = exp(G_r - G_ref),  Fi = 1 / F,
+//       exp(G_r) = F exp(G_ref),  exp(G_last - G_r) = Fi exp(G_last - G_ref)
+//     (a factor that underflows there multiplies an entry below exp(-47)),
 //     and per channel D_IJ = exp(G_ref(I) - G_ref(J)) for blocks J < I, so a
 //     gated entry exp(G_r - G_s) = F_r D_IJ Fi_s never leaves fp32/bf16 range.
 //  2. E and M per 16x16 block pair as products of (k F) and (q F) with (k Fi D).
@@ -74,19 +75,66 @@ __device__ __forceinline__ bf16x8 cvt8(float4 a, float4 b) {
   return r;
 }
 
+// One thread's share of a unit's inputs: rows 2pr, 2pr+1 of channels 8o..8o+7
+// (o = tid >> 5, pr = tid & 31), fetched one unit ahead.
+struct PrepIn {
+  bf16x8 k[2], q[2], v[2];
+  f32x4 ga[2], gb[2];  // gate: channels 8o..8o+3, 8o+4..8o+7 (GDN: ga[h][0] only)
+  uint32_t b[2];       // beta as loaded (KDA: bf16 bits, GDN: fp32 bits); nothing
+                       // computes on a fetched value before it is settled
+};
+
+// Wait for a prefetch here (an empty asm that takes the registers as
+// operands): at this point few of the wavefront's stores are outstanding,
+// and the vector-memory counter the wait uses counts stores as well as loads.
+__device__ __forceinline__ void settle(PrepIn &in) {
+  asm volatile("" : "+v"(in.k[0]), "+v"(in.k[1]), "+v"(in.q[0]), "+v"(in.q[1]), "+v"(in.v[0]), "+v"(in.v[1]));
+  asm volatile("" : "+v"(in.ga[0]), "+v"(in.ga[1]), "+v"(in.gb[0]), "+v"(in.gb[1]), "+v"(in.b[0]), "+v"(in.b[1]));
+}
+
 template <bool SCALAR>
-__global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  // heads vary fastest over the grid, so the workgroups resident together read
-  // whole token rows of q, k, v and g
-  const int chunk = blockIdx.x / p.Hv, j = blockIdx.x % p.Hv;
+__device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const ChunkTable &tb, int unit, int tid) {
+  const int chunk = unit / p.Hv, j = unit % p.Hv, iq = j / (p.Hv / p.Hqk);
+  const int start = tb.start[chunk], len = tb.len[chunk];
+  const int c0 = 8 * (tid >> 5), rp = 2 * (tid & 31);
+  const size_t Hv = p.Hv;
+  const bf16x8 z = as_bf16x8(make_uint4(0, 0, 0, 0));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = rp + h;
+    const bool ok = r < len;
+    const size_t t = (size_t)(start + r);
+    in.k[h] = ok ? ld8(p.k + (t * p.Hqk + iq) * HD + c0) : z;
+    in.q[h] = ok ? ld8(p.q + (t * p.Hqk + iq) * HD + c0) : z;
+    in.v[h] = ok ? ld8(p.v + (t * Hv + j) * HD + c0) : z;
+    in.ga[h] = in.gb[h] = zero4();
+    in.b[h] = 0u;
+    if constexpr (SCALAR) {
+      if (ok) {
+        in.ga[h][0] = p.g[t * Hv + j];
+        in.b[h] = reinterpret_cast<const uint32_t *>(p.beta)[t * Hv + j];
+      }
+    } else {
+      if (ok) {
+        in.ga[h] = *reinterpret_cast<const f32x4 *>(p.g + (t * Hv + j) * HD + c0);
+        in.gb[h] = *reinterpret_cast<const f32x4 *>(p.g + (t * Hv + j) * HD + c0 + 4);
+        in.b[h] = reinterpret_cast<const u16 *>(p.beta)[t * Hv + j];
+      }
+    }
+  }
+}
+
+template <bool SCALAR>
+__device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, int save, int unit,
+                                          const PrepIn &in, PrepIn &next, unsigned char *smem) {
+  // heads vary fastest over the units, so the workgroups working together
+  // read whole token rows of q, k, v and g
+  const int chunk = unit / p.Hv, j = unit % p.Hv;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const ChunkTable tb(p.table, p.NC, p.N);
-  const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
-  const int iq = j / (p.Hv / p.Hqk);
+  const int len = tb.len[chunk], last = len - 1;
   const size_t u = (size_t)chunk * p.Hv + j;
-  const size_t Hv = p.Hv;
   const float scale = p.scale;
 
   u16 *sKF = reinterpret_cast<u16 *>(smem + P_KF);
@@ -112,99 +160,76 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
   uint32_t pkBKG[8], pkBV[8], pkQG[8], pkKL[8];  // channel c0+ii: rows rp, rp+1 as a bf16 pair
   {
     constexpr int NG = SCALAR ? 1 : 8;  // gate values per row held by a thread
-    bf16x8 kx[2], qx[2], vx[2];
-    float gx[2][NG], bt[2];
+    const bf16x8 *kx = in.k, *qx = in.q, *vx = in.v;
+    float bt[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bt[h] = SCALAR ? __uint_as_float(in.b[h]) : bf2f((u16)in.b[h]);
+    float gx[2][NG];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int r = rp + h;
-      const bool in = r < len;
-      const size_t t = (size_t)(start + r);
-      const bf16x8 z = as_bf16x8(make_uint4(0, 0, 0, 0));
-      kx[h] = in ? ld8(p.k + (t * p.Hqk + iq) * HD + c0) : z;
-      qx[h] = in ? ld8(p.q + (t * p.Hqk + iq) * HD + c0) : z;
-      vx[h] = in ? ld8(p.v + (t * Hv + j) * HD + c0) : z;
-      if constexpr (SCALAR) {
-        gx[h][0] = in ? p.g[t * Hv + j] : 0.f;
-        bt[h] = in ? reinterpret_cast<const float *>(p.beta)[t * Hv + j] : 0.f;
-      } else {
-        float4 ga = make_float4(0.f, 0.f, 0.f, 0.f), gb = ga;
-        if (in) {
-          ga = *reinterpret_cast<const float4 *>(p.g + (t * Hv + j) * HD + c0);
-          gb = *reinterpret_cast<const float4 *>(p.g + (t * Hv + j) * HD + c0 + 4);
-        }
-        gx[h][0] = ga.x; gx[h][1] = ga.y; gx[h][2] = ga.z; gx[h][3] = ga.w;
-        gx[h][4] = gb.x; gx[h][5] = gb.y; gx[h][6] = gb.z; gx[h][7] = gb.w;
-        bt[h] = in ? bf2f(reinterpret_cast<const u16 *>(p.beta)[t * Hv + j]) : 0.f;
+      gx[h][0] = in.ga[h][0];
+      if constexpr (!SCALAR) {
+        gx[h][1] = in.ga[h][1]; gx[h][2] = in.ga[h][2]; gx[h][3] = in.ga[h][3];
+        gx[h][4] = in.gb[h][0]; gx[h][5] = in.gb[h][1]; gx[h][6] = in.gb[h][2]; gx[h][7] = in.gb[h][3];
       }
     }
     if (o == 0) { sB[rp] = bt[0]; sB[rp + 1] = bt[1]; }
-    // inclusive scan of the gate over the 64 rows, reference gates, G_last
-    float G[2][NG], gref[4][NG], gl[NG];
+    // inclusive scan of the gate over the 64 rows, the reference gates and
+    // G_last (lanes 0-31 and 32-63 hold two different octets)
+    const bool hi = (tid & 32) != 0;
+    const int Ib = pr >> 3;  // 16-row block of this lane's rows
+    float G[2][NG], go[NG], eref[NG], elr[NG];
 #pragma unroll
     for (int ic = 0; ic < NG; ++ic) {
-      float incl = gx[0][ic] + gx[1][ic];
-#pragma unroll
-      for (int d = 1; d < 32; d <<= 1) {
-        const float y = __shfl_up(incl, d, 32);
-        if (pr >= d) incl += y;
-      }
+      const float incl = scan32(gx[0][ic] + gx[1][ic]);
       G[1][ic] = incl;
       G[0][ic] = incl - gx[1][ic];
+      float gr[4];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) gref[I][ic] = __shfl(G[0][ic], 8 * I + 4, 32);
-      gl[ic] = (last & 1) ? __shfl(G[1][ic], last >> 1, 32) : __shfl(G[0][ic], last >> 1, 32);
-    }
-    const int Ib = rp >> 4;  // 16-row block of both rows
-    bf16x8 kf[2], qf[2];
-    float kfi[2][8];
+      for (int I = 0; I < 4; ++I) gr[I] = half_lane(G[0][ic], 8 * I + 4, hi);
+      const float gl = (last & 1) ? half_lane(G[1][ic], last >> 1, hi) : half_lane(G[0][ic], last >> 1, hi);
+      go[ic] = Ib == 0 ? gr[0] : (Ib == 1 ? gr[1] : (Ib == 2 ? gr[2] : gr[3]));
+      eref[ic] = __expf(go[ic]);
+      elr[ic] = __expf(gl - go[ic]);
+      // lanes pr = 0..5: D_IJ, index I(I-1)/2 + J in the order (1,0) (2,0)
+      // (2,1) (3,0) (3,1) (3,2); lane pr = 6: gamma = exp(G_last)
+      const int I = pr >= 3 ? 3 : (pr >= 1 ? 2 : 1);
+      const int J = pr - (I * (I - 1)) / 2;
+      const float a = pr == 6 ? gl : (I == 1 ? gr[1] : (I == 2 ? gr[2] : gr[3]));
+      const float b = pr == 6 ? 0.f : (J == 0 ? gr[0] : (J == 1 ? gr[1] : gr[2]));
+      const float e = __expf(a - b);
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      const int ic = SCALAR ? 0 : ii;
-      const float go = Ib == 0 ? gref[0][ic] : (Ib == 1 ? gref[1][ic] : (Ib == 2 ? gref[2][ic] : gref[3][ic]));
-      const float eref = __expf(go), elr = __expf(gl[ic] - go);
-      float xb[2], xv[2], xq[2], xl[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float F = __expf(G[h][ic] - go), Fi = __expf(go - G[h][ic]);
-        const float kv = (float)kx[h][ii], qv = (float)qx[h][ii], vv = (float)vx[h][ii];
-        kf[h][ii] = (__bf16)(kv * F);
-        qf[h][ii] = (__bf16)(qv * F);
-        kfi[h][ii] = kv * Fi;
-        const float eg = F * eref;  // exp(G_r)
-        xb[h] = bt[h] * kv * eg;
-        xv[h] = bt[h] * vv;
-        xq[h] = scale * qv * eg;
-        xl[h] = kv * (Fi * elr);    // k exp(G_last - G_r)
+      for (int cc = (SCALAR ? 0 : ic); cc < (SCALAR ? 8 : ic + 1); ++cc) {
+        if (pr < 6) sD[pr * 128 + c0 + cc] = e;
+        else if (pr == 6) w.gam[u * HD + c0 + cc] = e;
       }
-      pkBKG[ii] = pack2bf(xb[0], xb[1]);
-      pkBV[ii] = pack2bf(xv[0], xv[1]);
-      pkQG[ii] = pack2bf(xq[0], xq[1]);
-      pkKL[ii] = pack2bf(xl[0], xl[1]);
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pkBKG[i] = pkBV[i] = pkQG[i] = pkKL[i] = 0u;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int r = rp + h;
-      *reinterpret_cast<bf16x8 *>(sKF + r * KP + c0) = kf[h];
-      *reinterpret_cast<bf16x8 *>(sQF + r * KP + c0) = qf[h];
-      *reinterpret_cast<float4 *>(sKFi + r * GP + c0) = make_float4(kfi[h][0], kfi[h][1], kfi[h][2], kfi[h][3]);
-      *reinterpret_cast<float4 *>(sKFi + r * GP + c0 + 4) = make_float4(kfi[h][4], kfi[h][5], kfi[h][6], kfi[h][7]);
-    }
-    if (pr == 0) {
-      float e[8];
+      const int r = rp + h, sh = 16 * h;
+      bf16x8 kf, qf;
+      float kfi[8];
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) e[ii] = __expf(gl[SCALAR ? 0 : ii]);
-      *reinterpret_cast<float4 *>(w.gam + u * HD + c0) = make_float4(e[0], e[1], e[2], e[3]);
-      *reinterpret_cast<float4 *>(w.gam + u * HD + c0 + 4) = make_float4(e[4], e[5], e[6], e[7]);
-      // D_IJ in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): index I(I-1)/2 + J
-#pragma unroll
-      for (int I = 1; I < 4; ++I)
-#pragma unroll
-        for (int J = 0; J < I; ++J)
-#pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const int ic = SCALAR ? 0 : ii;
-            sD[((I * (I - 1)) / 2 + J) * 128 + c0 + ii] = __expf(gref[I][ic] - gref[J][ic]);
-          }
+      for (int ii = 0; ii < 8; ++ii) {
+        const int ic = SCALAR ? 0 : ii;
+        const float F = __expf(G[h][ic] - go[ic]), Fi = __builtin_amdgcn_rcpf(F);
+        const float kv = (float)kx[h][ii], qv = (float)qx[h][ii], vv = (float)vx[h][ii];
+        kf[ii] = (__bf16)(kv * F);
+        qf[ii] = (__bf16)(qv * F);
+        kfi[ii] = kv * Fi;
+        const float eg = F * eref[ic];  // exp(G_r)
+        const float el = Fi * elr[ic];  // exp(G_last - G_r)
+        pkBKG[ii] |= (uint32_t)f2bf(bt[h] * kv * eg) << sh;
+        pkBV[ii] |= (uint32_t)f2bf(bt[h] * vv) << sh;
+        pkQG[ii] |= (uint32_t)f2bf(scale * qv * eg) << sh;
+        pkKL[ii] |= (uint32_t)f2bf(kv * el) << sh;
+      }
+      *reinterpret_cast<bf16x8 *>(sKF + r * KP + c0) = kf;
+      *reinterpret_cast<bf16x8 *>(sQF + r * KP + c0) = qf;
+      *reinterpret_cast<float4 *>(sKFi + r * GP + c0) = make_float4(kfi[0], kfi[1], kfi[2], kfi[3]);
+      *reinterpret_cast<float4 *>(sKFi + r * GP + c0 + 4) = make_float4(kfi[4], kfi[5], kfi[6], kfi[7]);
     }
   }
   __syncthreads();
@@ -258,6 +283,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
     if (save) w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane] = as_u4(acc_pair_to_b(ms[0], ms[1]));
   }
   __syncthreads();
+  settle(next);  // the next unit's inputs, fetched at the start of this one
 
   // ---- 3. column-form operands (over the step-1 space), then T ----
 #pragma unroll
@@ -406,6 +432,26 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
   }
 }
 
+// Persistent: each workgroup walks the units blockIdx.x, blockIdx.x + gridDim.x,
+// ... and fetches the next unit's inputs into registers while it works on
+// the current one.
+template <bool SCALAR>
+__global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const ChunkTable tb(p.table, p.NC, p.N);
+  const int total = p.NC * p.Hv, tid = threadIdx.x;
+  int unit = blockIdx.x;
+  PrepIn nxt;
+  if (unit < total) prep_load<SCALAR>(nxt, p, tb, unit, tid);
+  settle(nxt);  // so that no path into the loop carries an outstanding load
+  for (; unit < total; unit += gridDim.x) {
+    const PrepIn cur = nxt;
+    if (unit + (int)gridDim.x < total) prep_load<SCALAR>(nxt, p, tb, unit + gridDim.x, tid);
+    prep_unit<SCALAR>(p, w, save, unit, cur, nxt, smem);
+    __syncthreads();  // LDS is reused by the next unit
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Forward walk: one wavefront per (document, value head, 16-column value
 // slice).  The 128 x 16 state slice lives in eight accumulator tiles; each
@@ -537,9 +583,22 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
 
 static int walk_grid(int chains) { return ((chains + 7) / 8) * 64; }
 
+static int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, hipStream_t st) {
   if (p.NC == 0) return hipSuccess;
-  const dim3 grid(p.NC * p.Hv), block(PNT);
+  const int total = p.NC * p.Hv;
+  const dim3 grid(total < compute_units() ? total : compute_units()), block(PNT);
   const void *fn = gdn ? (const void *)fwd_prep_kernel<true> : (const void *)fwd_prep_kernel<false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
   if (e != hipSuccess) return e;
