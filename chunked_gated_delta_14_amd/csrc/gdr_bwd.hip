@@ -151,28 +151,56 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 // ---------------------------------------------------------------------------
 // Gradient kernel: one workgroup (8 wavefronts) per (chunk, Q/K head); it
 // loops over the value heads of the group and keeps dq, dk in fp32 registers
-// across them (GDN's group reduction; a single pass for KDA).  Wavefront w
-// owns rows 16*(w&3)..+15 and value/key columns 64*(w>>2)..+63 of every
-// 64 x 128 result, and the 64 x 64 tiles (w&3, nt) with nt&1 == w>>2.
+// across them (GDN's group reduction; a single pass for KDA).
 //
-// q, k and the cumulative gate sit in LDS transposed ([channel][row]), so the
-// exponentially rescaled operands of the gated products, which run down the
-// rows of one channel, are read 8 rows per access.
+// Wavefront w owns key/value column tile w (16 columns) of every 64 x 128
+// result over all 64 rows, for the products with the state tapes and for the
+// gated products alike: it reads only its own 16 rows of S and dS', the gate
+// factors of its lanes are formed once per value head, each rescaled operand
+// of the gated products is built once and serves every row block, and the
+// reverse cumulative sum of dG stays inside the wavefront.  dout, Vn and Y
+// are staged once per workgroup in LDS.  (Y itself is computed by row strip:
+// wavefront w -> rows 16(w&3).., value columns 64(w>>2)..)
+//
+// Gated products with 16-row blocks and reference rows 16I+8: for a lane's
+// column c and rows r of block K, F_r = exp(G_r - G_ref(K)), Fi_r = 1 / F_r,
+// and D_IJ = exp(G_ref(I) - G_ref(J)) for J < I, so that
+//   sum_{s<=r} dM_rs k_s exp(G_r - G_s) = F_r sum_J D_IJ sum_{s in J} dM_rs (k Fi)_s,
+//   sum_{r>=s} dM_rs q_r exp(G_r - G_s) = Fi_s sum_K D_KI sum_{r in K} dM_rs (q F)_r
+// (s in block I): the per-column factor D moves from the operands to the
+// 16x16 partial product of each block.  The rescaled operands (k Fi, q F,
+// beta k F) are split into bf16 hi + lo: each (r, s) pair enters dG twice
+// with opposite signs (row side and column side) and the two must cancel to
+// well below the pair's size.
 // ---------------------------------------------------------------------------
 constexpr int GNT = 512;
 constexpr int QTP = 72;  // LDS pitch (bf16) of the transposed q, k tiles
 constexpr int GTP = 68;  // LDS pitch (floats) of the transposed gate tile
 
-template <bool SCALAR>
-constexpr int grad_smem_bytes() {
-  return 2 * HD * QTP * 2                   // sQT, sKT
-         + CH * KP * 2                      // sY
-         + 4 * CH * MP * 2                  // sDM, sDA, sDMT, sDAT
-         + (64 + 64 + 128 + 128 + 512) * 4  // sB, sDB, sRed, sDgam, sBT
-         + (SCALAR ? 64 * 4 : HD * GTP * 4);  // sG
-}
+// LDS map (bytes)
+constexpr int G_QT = 0;                     // q^T bf16 [128][QTP]
+constexpr int G_KT = G_QT + HD * QTP * 2;   // k^T bf16 [128][QTP]
+constexpr int G_GT = G_KT + HD * QTP * 2;   // cumulative gate: KDA fp32 [128][GTP], GDN [64]
+constexpr int G_DO = G_GT + HD * GTP * 4;   // dout bf16 [64][KP]      (tape products)
+constexpr int G_VN = G_DO + CH * KP * 2;    // Vn
+constexpr int G_Y = G_VN + CH * KP * 2;     // Y
+constexpr int G_DM = G_DO;                  // dM, dA, dM^T, dA^T bf16 [64][MP] (gated products)
+constexpr int G_DA = G_DM + CH * MP * 2;
+constexpr int G_DMT = G_DA + CH * MP * 2;
+constexpr int G_DAT = G_DMT + CH * MP * 2;
+constexpr int G_B = G_Y + CH * KP * 2;      // beta [64]
+constexpr int G_DB = G_B + 64 * 4;          // dbeta partial sums [14][64], added in a fixed order
+constexpr int G_RS = G_DB + 14 * 64 * 4;    // GDN: dG row sums per wavefront [8][64]
+constexpr int G_SMEM = G_RS + 8 * 64 * 4;
+static_assert(G_DAT + CH * MP * 2 <= G_B, "grad LDS map");
 
-// Cumulative gate G: per-channel tile [channel][row] (KDA) or one value per row.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 as_s4(uint2 x) { return __builtin_bit_cast(s16x4, x); }
+
+// Cumulative gate: per-channel tile [channel][row] (KDA) or one value per row.
 template <bool SCALAR>
 struct GateT {
   const float *s;
@@ -185,14 +213,6 @@ struct GateT {
     else return *reinterpret_cast<const float4 *>(s + c * GTP + r0);
   }
 };
-
-// acc[t] += x for a run-time tile index t, without indexing a register array
-// at run time (that would move the array to scratch memory).
-__device__ __forceinline__ void add_tile(f32x4 (&acc)[4], int t, const f32x4 &x) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i == t) acc[i] += x;
-}
 
 __device__ __forceinline__ float red16(float x) {  // sum over the 16 lanes sharing lg
   x += __shfl_xor(x, 1, 64);
@@ -217,6 +237,18 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   r.x = f2bf(a) | ((uint32_t)f2bf(b) << 16);
   r.y = f2bf(c) | ((uint32_t)f2bf(d) << 16);
   return r;
+}
+// x ~= hi + lo, both bf16, four values packed per part
+__device__ __forceinline__ void split4(const f32x4 &x, uint2 &hi, uint2 &lo) {
+  float h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 b = (__bf16)x[i];
+    h[i] = (float)b;
+    l[i] = x[i] - h[i];
+  }
+  hi = pack4(h[0], h[1], h[2], h[3]);
+  lo = pack4(l[0], l[1], l[2], l[3]);
 }
 
 // 64 rows x 128 bf16 (row stride ld) -> LDS [channel][row] (pitch QTP), rows
@@ -244,6 +276,531 @@ __device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, s
 
 template <bool SCALAR>
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
+                                                       u16 *dk, u16 *dv, float *dg, void *dbeta) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  // Q/K heads vary fastest over the grid (whole token rows per resident set)
+  const int chunk = blockIdx.x / p.Hqk, iqk = blockIdx.x % p.Hqk;
+  const ChunkTable tb(p.table, p.NC, p.N);
+  const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
+  const int grp = SCALAR ? p.Hv / p.Hqk : 1;  // KDA: H_qk == H_v
+  const float scale = p.scale;
+  const size_t Hv = p.Hv;
+
+  u16 *sQT = reinterpret_cast<u16 *>(smem + G_QT);
+  u16 *sKT = reinterpret_cast<u16 *>(smem + G_KT);
+  float *sG = reinterpret_cast<float *>(smem + G_GT);
+  u16 *sDo = reinterpret_cast<u16 *>(smem + G_DO);
+  u16 *sVn = reinterpret_cast<u16 *>(smem + G_VN);
+  u16 *sY = reinterpret_cast<u16 *>(smem + G_Y);
+  u16 *sDM = reinterpret_cast<u16 *>(smem + G_DM);
+  u16 *sDA = reinterpret_cast<u16 *>(smem + G_DA);
+  u16 *sDMT = reinterpret_cast<u16 *>(smem + G_DMT);
+  u16 *sDAT = reinterpret_cast<u16 *>(smem + G_DAT);
+  float *sB = reinterpret_cast<float *>(smem + G_B);
+  float *sDB = reinterpret_cast<float *>(smem + G_DB);
+  float *sRS = reinterpret_cast<float *>(smem + G_RS);
+  const GateT<SCALAR> G{sG};
+
+  {
+    const int tid = threadIdx.x;
+    const size_t ldqk = (size_t)p.Hqk * HD;
+    if (tid < 256) load_rows_transposed(sQT, p.q + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid);
+    else load_rows_transposed(sKT, p.k + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid - 256);
+  }
+
+  f32x4 dqA[4], dkA[4];  // [row block I]: rows 16I + 4lg + jj, column 16w + lr
+#pragma unroll
+  for (int t = 0; t < 4; ++t) { dqA[t] = zero4(); dkA[t] = zero4(); }
+
+  for (int jg = 0; jg < grp; ++jg) {
+    // Re-derive the thread coordinates from an opaque copy of the thread id so
+    // the compiler cannot hoist per-element address arithmetic of the group
+    // loop out of it (that would keep hundreds of values live across it).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int j = iqk * grp + jg;
+    const size_t u = (size_t)chunk * Hv + j;
+    const int c = 16 * wave + lr;  // this lane's key/value column
+    const int mtY = wave & 3, chY = wave >> 2, ra = 16 * mtY + lr;  // Y coordinates
+
+    // ---- every load of the iteration, issued up front in the order of use and
+    // unconditionally (rows past the chunk read its last row, zeroed at use) ----
+    float graw[2][8];
+    uint32_t braw = 0u;
+    const int o8 = tid >> 5, pr = tid & 31, c0g = 8 * o8, rp = 2 * pr;  // gate loader coordinates
+    if constexpr (SCALAR) {
+      if (tid < 64) graw[0][0] = p.g[(size_t)(start + (tid < len ? tid : last)) * Hv + j];
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = rp + h < len ? rp + h : last;
+        const float *src = p.g + ((size_t)(start + r) * Hv + j) * HD + c0g;
+        const float4 ga = *reinterpret_cast<const float4 *>(src), gb = *reinterpret_cast<const float4 *>(src + 4);
+        graw[h][0] = ga.x; graw[h][1] = ga.y; graw[h][2] = ga.z; graw[h][3] = ga.w;
+        graw[h][4] = gb.x; graw[h][5] = gb.y; graw[h][6] = gb.z; graw[h][7] = gb.w;
+      }
+    }
+    if (tid < 64) {
+      const size_t e = (size_t)(start + (tid < len ? tid : last)) * Hv + j;
+      braw = SCALAR ? reinterpret_cast<const uint32_t *>(p.beta)[e] : reinterpret_cast<const u16 *>(p.beta)[e];
+    }
+    bf16x8 bT[2], aDV[4][2];
+    uint2 vv[4];
+    {
+      const uint4 *TT = w.Tt + u * FRAG_64x64_U4;  // T^T, bf16 row-major 64 x 64
+      const u16 *dvt = w.dVnT + u * (CH * HD);
+      const int rl = ra < len ? ra : last;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) bT[kt] = as_bf16x8(TT[ra * 8 + 4 * kt + lg]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) aDV[t][kt] = ld8(dvt + (16 * (4 * chY + t) + lr) * CH + 32 * kt + 8 * lg);
+        vv[t] = *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + rl) * Hv + j) * HD + 16 * (4 * chY + t) + 4 * lg);
+      }
+    }
+    // dout and Vn rows for the LDS stage: thread -> rows (tid>>4) and +32, 16-byte segment tid&15
+    uint4 stDo[2], stVn[2];
+    {
+      const u16 *Vng = w.Vn + u * (CH * HD);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = (tid >> 4) + 32 * h, rc = r < len ? r : last, sg = 8 * (tid & 15);
+        stDo[h] = *reinterpret_cast<const uint4 *>(dout + ((size_t)(start + rc) * Hv + j) * HD + sg);
+        stVn[h] = *reinterpret_cast<const uint4 *>(Vng + r * HD + sg);
+      }
+    }
+    // ---- beta, cleared sums, the cumulative gate ----
+    if (tid < 64) sB[tid] = tid < len ? (SCALAR ? __uint_as_float(braw) : bf2f((u16)braw)) : 0.f;
+    if (tid < 256) sDB[10 * 64 + tid] = 0.f;  // E-term slots (not every row block writes every slot)
+    if constexpr (SCALAR) {
+      if (tid < 64) {
+        float x = tid < len ? graw[0][0] : 0.f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const float y = __shfl_up(x, o, 64);
+          if (tid >= o) x += y;
+        }
+        sG[tid] = x;
+      }
+    } else {
+      // the 32 lanes of a half wavefront scan their channel octet's 64 rows
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const float x0 = rp < len ? graw[0][ii] : 0.f, x1 = rp + 1 < len ? graw[1][ii] : 0.f;
+        const float incl = scan32(x0 + x1);
+        *reinterpret_cast<float2 *>(sG + (c0g + ii) * GTP + rp) = make_float2(incl - x1, incl);
+      }
+    }
+    // (issued after the gate scan to bound the registers in flight) this wavefront's rows of the state tapes: S[c][.], dS'[c][.]
+    bf16x8 Sb[4], dSb[4];
+    {
+      const u16 *Sg = w.S + u * (HD * HD) + (size_t)c * HD;
+      const u16 *dSg = w.dS + u * (HD * HD) + (size_t)c * HD;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        Sb[kt] = ld8(Sg + 32 * kt + 8 * lg);
+        dSb[kt] = ld8(dSg + 32 * kt + 8 * lg);
+      }
+    }
+    // E (accumulator order) of the dM, dA tiles of this wavefront: p = w and p = w + 8
+    uint2 eT[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pt = wave + 8 * q < 10 ? wave + 8 * q : wave;
+      eT[q] = reinterpret_cast<const uint2 *>(w.Et + u * FRAG_64x64_U4)[pt * 64 + lane];
+    }
+
+    __syncthreads();
+
+    // ---- Y = T^T dVn (rows 16mtY.., value columns 64chY.., computed as Y^T);
+    // dv = beta Y is kept for the end of the iteration ----
+    uint2 dvv[4];
+    {
+      const int kt0 = mtY >= 2 ? 1 : 0;  // T^T[r][r'] = 0 for r' < r
+      const float br = sB[ra];
+      float db1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int v0 = 16 * (4 * chY + t) + 4 * lg;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          if (kt >= kt0) acc = mfma(aDV[t][kt], bT[kt], acc);
+        // acc[jj] = Y[ra][v0 + jj]
+        *reinterpret_cast<uint2 *>(sY + ra * KP + v0) = pack4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) db1 += acc[jj] * bf_at(vv[t], jj);
+        dvv[t] = pack4(br * acc[0], br * acc[1], br * acc[2], br * acc[3]);
+      }
+      db1 = red_lg(db1);
+      if (lg == 0) sDB[chY * 64 + ra] = db1;  // slots 0, 1
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = (tid >> 4) + 32 * h, sg = 8 * (tid & 15);
+      *reinterpret_cast<uint4 *>(sDo + r * KP + sg) = r < len ? stDo[h] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(sVn + r * KP + sg) = stVn[h];
+    }
+
+    // ---- gate factors of this lane's column c and rows 16I + 4lg + jj ----
+    f32x4 F[4];  // 1 / F, exp(G_ref), exp(G_last - G_ref) and D are formed where used
+    {
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const float gref = G.at(16 * I + 8, c);
+        const float4 g4 = G.at4(16 * I + 4 * lg, c);
+        F[I][0] = __expf(g4.x - gref); F[I][1] = __expf(g4.y - gref);
+        F[I][2] = __expf(g4.z - gref); F[I][3] = __expf(g4.w - gref);
+      }
+    }
+    __syncthreads();
+
+    // ---- products with the state tapes (reduction over the value dim) ----
+    f32x4 dGA[4];
+    float colsum = 0.f, dgam;
+    {
+      float pr_ = 0.f;  // sum_v dS'[c][v] S[c][v]
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) pr_ += (float)Sb[kt][ii] * (float)dSb[kt][ii];
+      dgam = red_lg(pr_);
+    }
+    const float gL = G.at(last, c);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const int r0 = 16 * I + 4 * lg, rA = 16 * I + lr;
+      f32x4 aQ = zero4(), aY = zero4(), aK = zero4();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        __builtin_amdgcn_sched_barrier(0);  // one k-step of operands in flight at a time
+        const int o = rA * KP + 32 * kt + 8 * lg;
+        aQ = mfma(ld8(sDo + o), Sb[kt], aQ);
+        aY = mfma(ld8(sY + o), Sb[kt], aY);
+        aK = mfma(ld8(sVn + o), dSb[kt], aK);
+      }
+      const float gref = G.at(16 * I + 8, c);
+      const float Eref = __expf(gref), Elr = __expf(gL - gref);
+      const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
+      const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
+      const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
+      float db2[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float qv = bf_at(q4, jj), kv = bf_at(k4, jj), bv = jj == 0 ? b4.x : (jj == 1 ? b4.y : (jj == 2 ? b4.z : b4.w));
+        const float eg = F[I][jj] * Eref;  // exp(G_r)
+        const float el = __builtin_amdgcn_rcpf(F[I][jj]) * Elr;  // exp(G_last - G_r)
+        const float dqi = scale * eg * aQ[jj];  // d(q exp G) -> dq
+        const float nb = -bv * aY[jj];          // dKt = -beta (Y S^T)
+        const float kb = el * aK[jj];           // dKbar exp(G_last - G)
+        const float kt_ = kv * eg;
+        dqA[I][jj] += dqi;
+        dkA[I][jj] += eg * nb + kb;
+        dGA[I][jj] = qv * dqi + kt_ * nb - kv * kb;
+        colsum += kv * kb;
+        db2[jj] = -kt_ * aY[jj];
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float x = red16(db2[jj]);
+        if (lr == 0) sDB[(2 + wave) * 64 + r0 + jj] = x;  // slots 2..9
+      }
+    }
+    colsum = red_lg(colsum);
+    // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r): the 10 lower
+    // 16x16 tiles, wavefront w takes tiles w and w + 8
+    f32x4 tM[2], tA[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      tM[q] = zero4(); tA[q] = zero4();
+      const int pt = wave + 8 * q;
+      if (pt < 10) {
+        int I, J;
+        block_pair(pt, I, J);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const bf16x8 vb = ld8(sVn + (16 * J + lr) * KP + 32 * kt + 8 * lg);
+          const int o = (16 * I + lr) * KP + 32 * kt + 8 * lg;
+          tM[q] = mfma(ld8(sDo + o), vb, tM[q]);
+          tA[q] = mfma(ld8(sY + o), vb, tA[q]);
+        }
+        float db3[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 16 * I + 4 * lg + jj, s = 16 * J + lr;
+          db3[jj] = s < r ? -tA[q][jj] * bf_at(eT[q], jj) : 0.f;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float x = red16(db3[jj]);
+          if (lr == 0) sDB[(10 + J) * 64 + 16 * I + 4 * lg + jj] = x;  // slots 10..13
+        }
+      }
+    }
+    __syncthreads();  // dout, Vn, Y are dead: their space takes dM, dA
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pt = wave + 8 * q;
+      if (pt < 10) {
+        int I, J;
+        block_pair(pt, I, J);
+        const int s = 16 * J + lr, r0 = 16 * I + 4 * lg;
+        float m[4], a[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = r0 + jj;
+          m[jj] = s <= r ? scale * tM[q][jj] : 0.f;
+          a[jj] = s < r ? -tA[q][jj] : 0.f;
+          sDM[r * MP + s] = f2bf(m[jj]);
+          sDA[r * MP + s] = f2bf(a[jj]);
+        }
+        *reinterpret_cast<uint2 *>(sDMT + s * MP + r0) = pack4(m[0], m[1], m[2], m[3]);
+        *reinterpret_cast<uint2 *>(sDAT + s * MP + r0) = pack4(a[0], a[1], a[2], a[3]);
+      }
+    }
+    if (wave >= 2) {  // the six upper tiles are zero: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+      const int q = wave - 2;
+      const int I = q < 3 ? 0 : (q < 5 ? 1 : 2), J = q < 3 ? q + 1 : (q < 5 ? q - 1 : 3);
+      const int s = 16 * J + lr, r0 = 16 * I + 4 * lg;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        sDM[(r0 + jj) * MP + s] = 0;
+        sDA[(r0 + jj) * MP + s] = 0;
+      }
+      *reinterpret_cast<uint2 *>(sDMT + s * MP + r0) = make_uint2(0, 0);
+      *reinterpret_cast<uint2 *>(sDAT + s * MP + r0) = make_uint2(0, 0);
+    }
+    __syncthreads();
+
+    float Dm[6];  // D_IJ, index I(I-1)/2 + J: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    {
+      float gref[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        gref[I] = G.at(16 * I + 8, c);
+        const float4 g4 = G.at4(16 * I + 4 * lg, c);  // F again (not kept across the tape products)
+        F[I][0] = __expf(g4.x - gref[I]); F[I][1] = __expf(g4.y - gref[I]);
+        F[I][2] = __expf(g4.z - gref[I]); F[I][3] = __expf(g4.w - gref[I]);
+      }
+      Dm[0] = __expf(gref[1] - gref[0]); Dm[1] = __expf(gref[2] - gref[0]); Dm[2] = __expf(gref[2] - gref[1]);
+      Dm[3] = __expf(gref[3] - gref[0]); Dm[4] = __expf(gref[3] - gref[1]); Dm[5] = __expf(gref[3] - gref[2]);
+    }
+    // ---- gated products of dM and dA for column tile w, all row blocks.
+    // Row side (sums over s <= r), then column side (sums over r >= s); the
+    // rescaled operands of block K sit at rows 16K + 4lg + i of this lane. ----
+    {
+      uint2 xH[4], xL[4];
+#pragma unroll
+      for (int K = 0; K < 4; ++K) {
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + 16 * K + 4 * lg);
+        f32x4 xs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[i] = bf_at(k4, i) * __builtin_amdgcn_rcpf(F[K][i]);  // k Fi
+        split4(xs, xH[K], xL[K]);
+      }
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int rA = 16 * I + lr;
+        f32x4 accM = zero4(), accA = zero4();
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+          const s16x4 aM = as_s4(*reinterpret_cast<const uint2 *>(sDM + rA * MP + 16 * J + 4 * lg));
+          const s16x4 aA = as_s4(*reinterpret_cast<const uint2 *>(sDA + rA * MP + 16 * J + 4 * lg));
+          f32x4 pM = mfma16(aM, as_s4(xH[J]), zero4());
+          pM = mfma16(aM, as_s4(xL[J]), pM);
+          f32x4 pA = mfma16(aA, as_s4(xH[J]), zero4());
+          pA = mfma16(aA, as_s4(xL[J]), pA);
+          const float d = J == I ? 1.f : Dm[(I * (I - 1)) / 2 + J];
+          accM += d * pM;
+          accA += d * pA;
+        }
+        const int r0 = 16 * I + 4 * lg;
+        const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
+        const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float bv = jj == 0 ? b4.x : (jj == 1 ? b4.y : (jj == 2 ? b4.z : b4.w));
+          const float qM = F[I][jj] * accM[jj];
+          const float kA = bv * F[I][jj] * accA[jj];
+          dqA[I][jj] += qM;
+          dkA[I][jj] += kA;
+          dGA[I][jj] += bf_at(q4, jj) * qM + bf_at(k4, jj) * kA;
+        }
+      }
+    }
+    {
+      // column side, block K of the summed rows outermost: its rescaled
+      // operands are formed once and feed the row blocks I <= K
+      f32x4 accT[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) accT[I] = zero4();
+#pragma unroll
+      for (int K = 0; K < 4; ++K) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int r0 = 16 * K + 4 * lg;
+        const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
+        const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
+        f32x4 xq, xk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float bv = i == 0 ? b4.x : (i == 1 ? b4.y : (i == 2 ? b4.z : b4.w));
+          xq[i] = bf_at(q4, i) * F[K][i];       // q F
+          xk[i] = bv * bf_at(k4, i) * F[K][i];  // beta k F
+        }
+        uint2 qH, qL, kH, kL;
+        split4(xq, qH, qL);
+        split4(xk, kH, kL);
+#pragma unroll
+        for (int I = 0; I <= K; ++I) {
+          const int rA = 16 * I + lr;
+          const s16x4 aMT = as_s4(*reinterpret_cast<const uint2 *>(sDMT + rA * MP + 16 * K + 4 * lg));
+          const s16x4 aAT = as_s4(*reinterpret_cast<const uint2 *>(sDAT + rA * MP + 16 * K + 4 * lg));
+          f32x4 pT = mfma16(aMT, as_s4(qH), zero4());
+          pT = mfma16(aMT, as_s4(qL), pT);
+          pT = mfma16(aAT, as_s4(kH), pT);
+          pT = mfma16(aAT, as_s4(kL), pT);
+          const float d = K == I ? 1.f : Dm[(K * (K - 1)) / 2 + I];
+          accT[I] += d * pT;
+        }
+      }
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + 16 * I + 4 * lg);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float kT = __builtin_amdgcn_rcpf(F[I][jj]) * accT[I][jj];
+          dkA[I][jj] += kT;
+          dGA[I][jj] -= bf_at(k4, jj) * kT;
+        }
+      }
+    }
+
+    // ---- gate epilogue: dg = in-chunk reverse cumulative sum of dG ----
+    // The last row also collects the gradient of gamma = exp(G_last) and the
+    // column sums of the Kbar terms.
+    {
+      const float extra = colsum + __expf(G.at(last, c)) * dgam;
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (16 * I + 4 * lg + jj == last) dGA[I][jj] += extra;
+    }
+    if constexpr (!SCALAR) {
+      // suffix sums inside the lane (4 rows), across the lane groups (16-row
+      // block) and across the row blocks, all within the wavefront
+      float tot[4], up[4], blk[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        dGA[I][2] += dGA[I][3];
+        dGA[I][1] += dGA[I][2];
+        dGA[I][0] += dGA[I][1];
+        tot[I] = dGA[I][0];
+        const float a = __shfl_down(tot[I], 16, 64), b = __shfl_down(tot[I], 32, 64), cc = __shfl_down(tot[I], 48, 64);
+        up[I] = (lg < 3 ? a : 0.f) + (lg < 2 ? b : 0.f) + (lg < 1 ? cc : 0.f);
+        blk[I] = red_lg(tot[I]);
+      }
+      float below = 0.f;
+#pragma unroll
+      for (int I = 3; I >= 0; --I) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 16 * I + 4 * lg + jj;
+          if (r < len) dg[((size_t)(start + r) * Hv + j) * HD + c] = dGA[I][jj] + up[I] + below;
+        }
+        below += blk[I];
+      }
+    } else {
+      // row sums over the channels (16 per wavefront, then across the
+      // wavefronts), then a reverse scan over the rows
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float x = red16(dGA[I][jj]);
+          if (lr == 0) sRS[wave * 64 + 16 * I + 4 * lg + jj] = x;
+        }
+    }
+    __syncthreads();  // dbeta partial sums complete (and GDN row sums)
+    if (tid < 64 && tid < len) {
+      float x = 0.f;
+#pragma unroll
+      for (int k = 0; k < 14; ++k) x += sDB[k * 64 + tid];
+      const size_t e = (size_t)(start + tid) * Hv + j;
+      if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = x;
+      else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
+    }
+    if constexpr (SCALAR) {
+      if (tid < 64) {
+        float y = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) y += sRS[ww * 64 + 63 - tid];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const float z = __shfl_up(y, o, 64);
+          if (tid >= o) y += z;
+        }
+        const int rr = 63 - tid;  // y = sum of rows rr..63
+        if (rr < len) dg[(size_t)(start + rr) * Hv + j] = y;
+      }
+    }
+    if (ra < len) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        *reinterpret_cast<uint2 *>(dv + ((size_t)(start + ra) * Hv + j) * HD + 16 * (4 * chY + t) + 4 * lg) = dvv[t];
+    }
+    __syncthreads();
+  }
+
+  // dq, dk: fp32 sums over the group's value heads, rounded once
+  {
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * I + 4 * lg + jj;
+        if (r < len) {
+          const size_t e = ((size_t)(start + r) * p.Hqk + iqk) * HD + 16 * wave + lr;
+          dq[e] = f2bf(dqA[I][jj]);
+          dk[e] = f2bf(dkA[I][jj]);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gradient kernel, row-strip form: wavefront w owns rows 16(w&3).. and column
+// half w>>2 of every result.  Used for GDN, whose value-head loop keeps dq, dk
+// in registers across the group and which this smaller per-iteration register
+// set fits without spilling; the gate factors there are exponentials of
+// per-row scalars.
+// ---------------------------------------------------------------------------
+template <bool SCALAR>
+constexpr int grad_rows_smem_bytes() {
+  return 2 * HD * QTP * 2                   // sQT, sKT
+         + CH * KP * 2                      // sY
+         + 4 * CH * MP * 2                  // sDM, sDA, sDMT, sDAT
+         + (64 + 64 + 128 + 128 + 512) * 4  // sB, sDB, sRed, sDgam, sBT
+         + (SCALAR ? 64 * 4 : HD * GTP * 4);  // sG
+}
+
+// acc[t] += x for a run-time tile index t, without indexing a register array
+// at run time (that would move the array to scratch memory).
+__device__ __forceinline__ void add_tile(f32x4 (&acc)[4], int t, const f32x4 &x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i == t) acc[i] += x;
+}
+
+template <bool SCALAR>
+__global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   extern __shared__ __align__(16) unsigned char smem[];
   // Q/K heads vary fastest over the grid (whole token rows per resident set)
@@ -663,6 +1220,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
   }
 }
 
+
 hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout, const float *dht, float *dh0,
                            hipStream_t st) {
   const int chains = p.N * p.Hv;
@@ -677,15 +1235,14 @@ hipError_t launch_bwd_grad(bool gdn, const Problem &p, const Workspace &w, const
   const dim3 grid(p.NC * p.Hqk), block(GNT);
   hipError_t e;
   if (gdn) {
-    const int sm = grad_smem_bytes<true>();
-    e = hipFuncSetAttribute((const void *)bwd_grad_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
+    const int sm = grad_rows_smem_bytes<true>();
+    e = hipFuncSetAttribute((const void *)bwd_grad_rows_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
     if (e != hipSuccess) return e;
-    bwd_grad_kernel<true><<<grid, block, sm, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
+    bwd_grad_rows_kernel<true><<<grid, block, sm, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
   } else {
-    const int sm = grad_smem_bytes<false>();
-    e = hipFuncSetAttribute((const void *)bwd_grad_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
+    e = hipFuncSetAttribute((const void *)bwd_grad_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, G_SMEM);
     if (e != hipSuccess) return e;
-    bwd_grad_kernel<false><<<grid, block, sm, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
+    bwd_grad_kernel<false><<<grid, block, G_SMEM, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
   }
   return hipGetLastError();
 }
