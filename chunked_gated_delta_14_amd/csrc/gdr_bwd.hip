@@ -159,8 +159,8 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 // factors of its lanes are formed once per value head, each rescaled operand
 // of the gated products is built once and serves every row block, and the
 // reverse cumulative sum of dG stays inside the wavefront.  dout, Vn and Y
-// are staged once per workgroup in LDS.  (Y itself is computed by row strip:
-// wavefront w -> rows 16(w&3).., value columns 64(w>>2)..)
+// are staged once per workgroup in LDS, and so is T^T for Y = T^T dVn, which
+// wavefront w forms for value tile w over all rows.
 //
 // Gated products with 16-row blocks and reference rows 16I+8: for a lane's
 // column c and rows r of block K, F_r = exp(G_r - G_ref(K)), Fi_r = 1 / F_r,
@@ -188,9 +188,10 @@ constexpr int G_DM = G_DO;                  // dM, dA, dM^T, dA^T bf16 [64][MP] 
 constexpr int G_DA = G_DM + CH * MP * 2;
 constexpr int G_DMT = G_DA + CH * MP * 2;
 constexpr int G_DAT = G_DMT + CH * MP * 2;
-constexpr int G_B = G_Y + CH * KP * 2;      // beta [64]
-constexpr int G_DB = G_B + 64 * 4;          // dbeta partial sums [14][64], added in a fixed order
-constexpr int G_RS = G_DB + 14 * 64 * 4;    // GDN: dG row sums per wavefront [8][64]
+constexpr int G_TT = G_Y + CH * KP * 2;     // T^T bf16 [64][MP]             (Y product)
+constexpr int G_B = G_TT + CH * MP * 2;     // beta [64]
+constexpr int G_DB = G_B + 64 * 4;          // dbeta partial sums [20][64], added in a fixed order
+constexpr int G_RS = G_DB + 20 * 64 * 4;    // GDN: dG row sums per wavefront [8][64]
 constexpr int G_SMEM = G_RS + 8 * 64 * 4;
 static_assert(G_DAT + CH * MP * 2 <= G_B, "grad LDS map");
 
@@ -292,6 +293,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
   u16 *sDo = reinterpret_cast<u16 *>(smem + G_DO);
   u16 *sVn = reinterpret_cast<u16 *>(smem + G_VN);
   u16 *sY = reinterpret_cast<u16 *>(smem + G_Y);
+  u16 *sTT = reinterpret_cast<u16 *>(smem + G_TT);
   u16 *sDM = reinterpret_cast<u16 *>(smem + G_DM);
   u16 *sDA = reinterpret_cast<u16 *>(smem + G_DA);
   u16 *sDMT = reinterpret_cast<u16 *>(smem + G_DMT);
@@ -322,7 +324,6 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     const int j = iqk * grp + jg;
     const size_t u = (size_t)chunk * Hv + j;
     const int c = 16 * wave + lr;  // this lane's key/value column
-    const int mtY = wave & 3, chY = wave >> 2, ra = 16 * mtY + lr;  // Y coordinates
 
     // ---- every load of the iteration, issued up front in the order of use and
     // unconditionally (rows past the chunk read its last row, zeroed at use) ----
@@ -345,35 +346,36 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       const size_t e = (size_t)(start + (tid < len ? tid : last)) * Hv + j;
       braw = SCALAR ? reinterpret_cast<const uint32_t *>(p.beta)[e] : reinterpret_cast<const u16 *>(p.beta)[e];
     }
-    bf16x8 bT[2], aDV[4][2];
+    // Y operands: T^T (one 16-byte piece per thread, for the LDS stage), this
+    // wavefront's value tile of dVn^T, and v at the accumulator positions
+    const u32x4 stT = reinterpret_cast<const u32x4 *>(w.Tt + u * FRAG_64x64_U4)[tid];
+    bf16x8 aDV[2];
     uint2 vv[4];
     {
-      const uint4 *TT = w.Tt + u * FRAG_64x64_U4;  // T^T, bf16 row-major 64 x 64
-      const u16 *dvt = w.dVnT + u * (CH * HD);
-      const int rl = ra < len ? ra : last;
+      const u16 *dvt = w.dVnT + u * (CH * HD) + (size_t)c * CH;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) bT[kt] = as_bf16x8(TT[ra * 8 + 4 * kt + lg]);
+      for (int kt = 0; kt < 2; ++kt) aDV[kt] = ld8(dvt + 32 * kt + 8 * lg);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) aDV[t][kt] = ld8(dvt + (16 * (4 * chY + t) + lr) * CH + 32 * kt + 8 * lg);
-        vv[t] = *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + rl) * Hv + j) * HD + 16 * (4 * chY + t) + 4 * lg);
+      for (int mt = 0; mt < 4; ++mt) {
+        const int rl = 16 * mt + lr < len ? 16 * mt + lr : last;
+        vv[mt] = *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + rl) * Hv + j) * HD + 16 * wave + 4 * lg);
       }
     }
     // dout and Vn rows for the LDS stage: thread -> rows (tid>>4) and +32, 16-byte segment tid&15
-    uint4 stDo[2], stVn[2];
+    u32x4 stDo[2], stVn[2];
     {
       const u16 *Vng = w.Vn + u * (CH * HD);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = (tid >> 4) + 32 * h, rc = r < len ? r : last, sg = 8 * (tid & 15);
-        stDo[h] = *reinterpret_cast<const uint4 *>(dout + ((size_t)(start + rc) * Hv + j) * HD + sg);
-        stVn[h] = *reinterpret_cast<const uint4 *>(Vng + r * HD + sg);
+        stDo[h] = *reinterpret_cast<const u32x4 *>(dout + ((size_t)(start + rc) * Hv + j) * HD + sg);
+        stVn[h] = *reinterpret_cast<const u32x4 *>(Vng + r * HD + sg);
       }
     }
     // ---- beta, cleared sums, the cumulative gate ----
     if (tid < 64) sB[tid] = tid < len ? (SCALAR ? __uint_as_float(braw) : bf2f((u16)braw)) : 0.f;
-    if (tid < 256) sDB[10 * 64 + tid] = 0.f;  // E-term slots (not every row block writes every slot)
+    if (tid < 256) sDB[16 * 64 + tid] = 0.f;  // E-term slots (not every row block writes every slot)
+    *reinterpret_cast<u32x4 *>(sTT + (tid >> 3) * MP + 8 * (tid & 7)) = stT;
     if constexpr (SCALAR) {
       if (tid < 64) {
         float x = tid < len ? graw[0][0] : 0.f;
@@ -414,34 +416,34 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 
     __syncthreads();
 
-    // ---- Y = T^T dVn (rows 16mtY.., value columns 64chY.., computed as Y^T);
-    // dv = beta Y is kept for the end of the iteration ----
+    // ---- Y = T^T dVn for value tile w, all rows (computed as Y^T); dv = beta Y
+    // is kept for the end of the iteration ----
     uint2 dvv[4];
     {
-      const int kt0 = mtY >= 2 ? 1 : 0;  // T^T[r][r'] = 0 for r' < r
-      const float br = sB[ra];
-      float db1 = 0.f;
+      const int v0 = 16 * wave + 4 * lg;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int v0 = 16 * (4 * chY + t) + 4 * lg;
+      for (int mt = 0; mt < 4; ++mt) {
+        const int ra = 16 * mt + lr;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          if (kt >= kt0) acc = mfma(aDV[t][kt], bT[kt], acc);
+        for (int kt = (mt >= 2 ? 1 : 0); kt < 2; ++kt)  // T^T[r][r'] = 0 for r' < r
+          acc = mfma(aDV[kt], ld8(sTT + ra * MP + 32 * kt + 8 * lg), acc);
         // acc[jj] = Y[ra][v0 + jj]
         *reinterpret_cast<uint2 *>(sY + ra * KP + v0) = pack4(acc[0], acc[1], acc[2], acc[3]);
+        float db1 = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) db1 += acc[jj] * bf_at(vv[t], jj);
-        dvv[t] = pack4(br * acc[0], br * acc[1], br * acc[2], br * acc[3]);
+        for (int jj = 0; jj < 4; ++jj) db1 += acc[jj] * bf_at(vv[mt], jj);
+        db1 = red_lg(db1);
+        if (lg == 0) sDB[wave * 64 + ra] = db1;  // slots 0..7
+        const float br = sB[ra];
+        dvv[mt] = pack4(br * acc[0], br * acc[1], br * acc[2], br * acc[3]);
       }
-      db1 = red_lg(db1);
-      if (lg == 0) sDB[chY * 64 + ra] = db1;  // slots 0, 1
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = (tid >> 4) + 32 * h, sg = 8 * (tid & 15);
-      *reinterpret_cast<uint4 *>(sDo + r * KP + sg) = r < len ? stDo[h] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(sVn + r * KP + sg) = stVn[h];
+      *reinterpret_cast<u32x4 *>(sDo + r * KP + sg) = r < len ? stDo[h] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(sVn + r * KP + sg) = stVn[h];
     }
 
     // ---- gate factors of this lane's column c and rows 16I + 4lg + jj ----
@@ -505,7 +507,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const float x = red16(db2[jj]);
-        if (lr == 0) sDB[(2 + wave) * 64 + r0 + jj] = x;  // slots 2..9
+        if (lr == 0) sDB[(8 + wave) * 64 + r0 + jj] = x;  // slots 8..15
       }
     }
     colsum = red_lg(colsum);
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const float x = red16(db3[jj]);
-          if (lr == 0) sDB[(10 + J) * 64 + 16 * I + 4 * lg + jj] = x;  // slots 10..13
+          if (lr == 0) sDB[(16 + J) * 64 + 16 * I + 4 * lg + jj] = x;  // slots 16..19
         }
       }
     }
@@ -730,7 +732,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     if (tid < 64 && tid < len) {
       float x = 0.f;
 #pragma unroll
-      for (int k = 0; k < 14; ++k) x += sDB[k * 64 + tid];
+      for (int k = 0; k < 20; ++k) x += sDB[k * 64 + tid];
       const size_t e = (size_t)(start + tid) * Hv + j;
       if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = x;
       else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
@@ -749,11 +751,10 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         if (rr < len) dg[(size_t)(start + rr) * Hv + j] = y;
       }
     }
-    if (ra < len) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        *reinterpret_cast<uint2 *>(dv + ((size_t)(start + ra) * Hv + j) * HD + 16 * (4 * chY + t) + 4 * lg) = dvv[t];
-    }
+    for (int mt = 0; mt < 4; ++mt)
+      if (16 * mt + lr < len)
+        *reinterpret_cast<uint2 *>(dv + ((size_t)(start + 16 * mt + lr) * Hv + j) * HD + 16 * wave + 4 * lg) = dvv[mt];
     __syncthreads();
   }
 

@@ -23,6 +23,7 @@ namespace gdr {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes (stays in registers, unlike HIP's uint4 in arrays)
 typedef uint16_t u16;
 
 constexpr int CH = 64;     // tokens per chunk
