@@ -27,6 +27,7 @@ namespace gdr {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
+  __shared__ __align__(16) float stg[HD * SGP];  // tape stage of this wavefront
   int chain, sl;
   walk_block(blockIdx.x, chain, sl);
   if (chain >= p.N * p.Hv) return;
@@ -81,12 +82,11 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
     bf16x8 dSb[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) dSb[kt] = acc_pair_to_b(dS[2 * kt], dS[2 * kt + 1]);
-    {
-      u16 *tp = w.dS + u * (HD * HD);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) tp[(16 * mt + 4 * lg + jj) * HD + vcol] = f2bf(dS[mt][jj]);
+    {  // this slice's block of the adjoint-state tape
+      u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16);
+      stage_rows<8>(stg, dS, lane, [&](int row, int half, bf16x8 x) {
+        *reinterpret_cast<bf16x8 *>(tp + row * 16 + 8 * half) = x;
+      });
     }
 
     f32x4 dV[4];
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       for (int h = 0; h < 2; ++h) {
         const int r = (tid >> 4) + 32 * h, rc = r < len ? r : last, sg = 8 * (tid & 15);
         stDo[h] = *reinterpret_cast<const u32x4 *>(dout + ((size_t)(start + rc) * Hv + j) * HD + sg);
-        stVn[h] = *reinterpret_cast<const u32x4 *>(Vng + r * HD + sg);
+        stVn[h] = *reinterpret_cast<const u32x4 *>(Vng + tape_r(r, sg));
       }
     }
     // ---- beta, cleared sums, the cumulative gate ----
@@ -398,12 +398,12 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     // (issued after the gate scan to bound the registers in flight) this wavefront's rows of the state tapes: S[c][.], dS'[c][.]
     bf16x8 Sb[4], dSb[4];
     {
-      const u16 *Sg = w.S + u * (HD * HD) + (size_t)c * HD;
-      const u16 *dSg = w.dS + u * (HD * HD) + (size_t)c * HD;
+      const u16 *Sg = w.S + u * (HD * HD);
+      const u16 *dSg = w.dS + u * (HD * HD);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        Sb[kt] = ld8(Sg + 32 * kt + 8 * lg);
-        dSb[kt] = ld8(dSg + 32 * kt + 8 * lg);
+        Sb[kt] = ld8(Sg + tape_s(c, 32 * kt + 8 * lg));
+        dSb[kt] = ld8(dSg + tape_s(c, 32 * kt + 8 * lg));
       }
     }
     // E (accumulator order) of the dM, dA tiles of this wavefront: p = w and p = w + 8
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         const int c0 = 32 * kt + 8 * lg;
         dOa[kt] = ra < len ? ld8(dr + c0) : as_bf16x8(make_uint4(0, 0, 0, 0));
         Ya[kt] = ld8(sY + ra * KP + c0);
-        Vna[kt] = ld8(Vng + ra * HD + c0);
+        Vna[kt] = ld8(Vng + tape_r(ra, c0));
       }
     }
     const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
@@ -965,8 +965,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         const int c = 16 * (4 * ch + t) + lr;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          sb[kt] = ld8(Sg + c * HD + 32 * kt + 8 * lg);
-          dsb[kt] = ld8(dSg + c * HD + 32 * kt + 8 * lg);
+          sb[kt] = ld8(Sg + tape_s(c, 32 * kt + 8 * lg));
+          dsb[kt] = ld8(dSg + tape_s(c, 32 * kt + 8 * lg));
         }
       };
       load_tile(0, Sb[0], dSb[0]);
@@ -1023,7 +1023,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
       if (nt <= mt) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 vb = ld8(Vng + s * HD + 32 * kt + 8 * lg);
+          const bf16x8 vb = ld8(Vng + tape_r(s, 32 * kt + 8 * lg));
           accM = mfma(dOa[kt], vb, accM);
           accA = mfma(Ya[kt], vb, accA);
         }

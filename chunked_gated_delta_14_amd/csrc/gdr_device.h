@@ -91,6 +91,41 @@ __device__ __forceinline__ float half_lane(float x, int l, bool hi) {
   return hi ? b : a;
 }
 
+// Tape layouts.  State tapes (S, dS'): per unit [value slice 8][key 128][16] bf16; row tape (Vn):
+// [value slice 8][row 64][16].  The 16 columns of a value slice are one walk wavefront's share, so
+// each wavefront writes its part of a chunk as one contiguous block, and 8 consecutive values
+// (8-aligned) of one key or row are 16 contiguous bytes.
+__device__ __forceinline__ int tape_s(int key, int v) { return ((v >> 4) * HD + key) * 16 + (v & 15); }
+__device__ __forceinline__ int tape_r(int row, int v) { return ((v >> 4) * CH + row) * 16 + (v & 15); }
+
+__device__ __forceinline__ bf16x8 cvt8(float4 a, float4 b) {
+  bf16x8 r;
+  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
+  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
+  return r;
+}
+
+// Walk wavefront output stage: MT accumulator tiles (rows 16mt + 4lg + j, column lr) go to a
+// wavefront-private fp32 LDS tile [row][SGP] and come back as 16-byte bf16 pieces of 8 columns;
+// put(row, half, piece) stores the piece of columns 8*half..+7.  LDS operations of one wavefront
+// complete in order, so no wait is needed between the two halves or between stages.
+constexpr int SGP = 20;  // stage pitch (floats): rows 4 apart fall 16 banks apart
+template <int MT, typename Put>
+__device__ __forceinline__ void stage_rows(float *stg, const f32x4 (&acc)[MT], int lane, Put put) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) stg[(16 * mt + 4 * lg + jj) * SGP + lr] = acc[mt][jj];
+#pragma unroll
+  for (int pass = 0; pass < MT / 2; ++pass) {  // 32 rows per pass
+    const int row = 32 * pass + (lane >> 1), half = lane & 1;
+    const float4 a = *reinterpret_cast<const float4 *>(stg + row * SGP + 8 * half);
+    const float4 b = *reinterpret_cast<const float4 *>(stg + row * SGP + 8 * half + 4);
+    put(row, half, cvt8(a, b));
+  }
+}
+
 // 8 contiguous bf16 from LDS/global (16-byte aligned).
 __device__ __forceinline__ bf16x8 ld8(const u16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 // 8 contiguous floats (16-byte aligned) -> bf16.

@@ -68,13 +68,6 @@ __device__ __forceinline__ uint2 pack4bf(const f32x4 &x) {
   r.y = pack2bf(x[2], x[3]);
   return r;
 }
-__device__ __forceinline__ bf16x8 cvt8(float4 a, float4 b) {
-  bf16x8 r;
-  r[0] = (__bf16)a.x; r[1] = (__bf16)a.y; r[2] = (__bf16)a.z; r[3] = (__bf16)a.w;
-  r[4] = (__bf16)b.x; r[5] = (__bf16)b.y; r[6] = (__bf16)b.z; r[7] = (__bf16)b.w;
-  return r;
-}
-
 // One thread's share of a unit's inputs: rows 2pr, 2pr+1 of channels 8o..8o+7
 // (o = tid >> 5, pr = tid & 31), fetched one unit ahead.
 struct PrepIn {
@@ -459,6 +452,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
 // fetched one chunk ahead, each register refilled right after its last use.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u16 *o, float *ht, int save) {
+  __shared__ __align__(16) float stg[HD * SGP];  // output stage of this wavefront
   int chain, sl;
   walk_block(blockIdx.x, chain, sl);
   if (chain >= p.N * p.Hv) return;
@@ -506,12 +500,11 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
     bf16x8 Sb[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) Sb[kt] = acc_pair_to_b(S[2 * kt], S[2 * kt + 1]);
-    if (save) {
-      u16 *st = w.S + u * (HD * HD);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) st[(16 * mt + 4 * lg + jj) * HD + vcol] = f2bf(S[mt][jj]);
+    if (save) {  // this slice's block of the state tape
+      u16 *st = w.S + u * (HD * HD) + sl * (HD * 16);
+      stage_rows<8>(stg, S, lane, [&](int row, int half, bf16x8 x) {
+        *reinterpret_cast<bf16x8 *>(st + row * 16 + 8 * half) = x;
+      });
     }
 
     f32x4 Vn[4], Oc[4];
@@ -539,20 +532,17 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
         Pf[mt][kt] = as_bf16x8(w.Pf[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
       }
 
-    u16 *orow = o + ((size_t)row0 * Hv + j) * HD + vcol;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * mt + 4 * lg + jj;
-        if (r < len) orow[(size_t)r * Hv * HD] = f2bf(Oc[mt][jj]);
-      }
+    {
+      u16 *ob = o + ((size_t)row0 * Hv + j) * HD + 16 * sl;
+      stage_rows<4>(stg, Oc, lane, [&](int row, int half, bf16x8 x) {
+        if (row < len) *reinterpret_cast<bf16x8 *>(ob + (size_t)row * Hv * HD + 8 * half) = x;
+      });
+    }
     if (save) {
-      u16 *vt = w.Vn + u * (CH * HD);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) vt[(16 * mt + 4 * lg + jj) * HD + vcol] = f2bf(Vn[mt][jj]);
+      u16 *vt = w.Vn + u * (CH * HD) + sl * (CH * 16);
+      stage_rows<4>(stg, Vn, lane, [&](int row, int half, bf16x8 x) {
+        *reinterpret_cast<bf16x8 *>(vt + row * 16 + 8 * half) = x;
+      });
     }
 
 #pragma unroll

@@ -25,9 +25,9 @@ struct Workspace {
   uint4 *Et;    // E (gated k k^T, strictly lower): its 10 lower 16x16 tiles in
                 //   accumulator order, [u][tile][lane 64][4] bf16
   // tapes
-  uint16_t *S;    // entering state of every chunk, bf16 [u][key][v]      (forward walk, SAVE)
-  uint16_t *Vn;   // new values, bf16 [u][row][v]                         (forward walk, SAVE)
-  uint16_t *dS;   // adjoint state leaving every chunk, bf16 [u][key][v]  (backward walk)
+  uint16_t *S;    // entering state of every chunk, bf16 [u][slice 8][key][16]      (forward walk, SAVE)
+  uint16_t *Vn;   // new values, bf16 [u][slice 8][row][16]                         (forward walk, SAVE)
+  uint16_t *dS;   // adjoint state leaving every chunk, bf16 [u][slice 8][key][16]  (backward walk)
   uint16_t *dVnT; // adjoint of the new values, bf16 [u][v][row]          (backward walk)
 };
 
