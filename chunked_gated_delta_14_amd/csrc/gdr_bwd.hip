@@ -25,9 +25,12 @@ namespace gdr {
 // Adjoint walk: one wavefront per (document, value head, 16-column slice),
 // chunks in reverse.  dS lives in eight accumulator tiles; 56 MFMAs per chunk.
 // ---------------------------------------------------------------------------
+constexpr int DOP = 72;  // pitch (bf16) of the transposed dout tile [column][row]
+
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
-  __shared__ __align__(16) float stg[HD * SGP];  // tape stage of this wavefront
+  __shared__ __align__(16) float stg[HD * SGP];   // tape stage of this wavefront
+  __shared__ __align__(16) u16 sdo[16 * DOP];     // this slice's dout columns, [column][row]
   int chain, sl;
   walk_block(blockIdx.x, chain, sl);
   if (chain >= p.N * p.Hv) return;
@@ -62,22 +65,46 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
     for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(w.gam + u * HD + 16 * mt + 4 * lg);
   }
 
+  // dout of a chunk, this slice's 16 columns, as 16-byte pieces: lane -> rows (lane >> 1) and
+  // 32 + (lane >> 1), columns 8 * (lane & 1)..+7; fetched one chunk ahead (rows past the chunk
+  // read its last row and are zeroed when the tile is formed)
+  u32x4 pdo[2];
+  auto fetch_dout = [&](int n) {
+    const int r0 = tok0 + CH * n, ln = min(CH, tok1 - r0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = (lane >> 1) + 32 * h;
+      pdo[h] = *reinterpret_cast<const u32x4 *>(dout + ((size_t)(r0 + min(r, ln - 1)) * Hv + j) * HD + 16 * sl +
+                                                 8 * (lane & 1));
+    }
+  };
+  if (nch > 0) fetch_dout(nch - 1);
+
   for (int n = nch - 1; n >= 0; --n) {
     const size_t u = (size_t)(first + n) * Hv + j;
     const size_t un = n > 0 ? u - Hv : u;
     const int row0 = tok0 + CH * n;
     const int len = min(CH, tok1 - row0);
 
-    // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns)
-    bf16x8 dOb[2];
-    const u16 *drow = dout + ((size_t)row0 * Hv + j) * HD + vcol;
+    // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns), through the
+    // transposed LDS tile
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int h = 0; h < 2; ++h) {
+      const int r = (lane >> 1) + 32 * h, c0 = 8 * (lane & 1);
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int r = 32 * kt + kwalk(lg, ii);
-        dOb[kt][ii] = __builtin_bit_cast(__bf16, r < len ? drow[(size_t)r * Hv * HD] : (u16)0);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wd = pdo[h][e >> 1];
+        sdo[(c0 + e) * DOP + r] = r < len ? (u16)((e & 1) ? (wd >> 16) : (wd & 0xffffu)) : (u16)0;
       }
+    }
+    fetch_dout(n > 0 ? n - 1 : 0);
+    bf16x8 dOb[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint2 a = *reinterpret_cast<const uint2 *>(sdo + lr * DOP + 32 * kt + 4 * lg);
+      const uint2 b = *reinterpret_cast<const uint2 *>(sdo + lr * DOP + 32 * kt + 16 + 4 * lg);
+      dOb[kt] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+    }
 
     bf16x8 dSb[4];
 #pragma unroll
