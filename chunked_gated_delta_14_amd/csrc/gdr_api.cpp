@@ -111,6 +111,9 @@ int32_t check_sizes(int32_t variant, int64_t T, int64_t N, int64_t NC, int64_t H
   // grid sizes are 32-bit: chunk grids use NC * H_v blocks, walk grids 8 * N * H_v
   if (N * Hv > (int64_t(1) << 27) || NC * Hv > (int64_t(1) << 31) - 1)
     return fail(GDR_ERR_UNSUPPORTED, "problem too large");
+  // the walks address one chunk's rows of o / dout through buffer resources
+  // with a 32-bit byte range: 64 rows of H_v * 128 bf16
+  if (Hv > 65536) return fail(GDR_ERR_UNSUPPORTED, "H_v above 65536");
   return GDR_OK;
 }
 

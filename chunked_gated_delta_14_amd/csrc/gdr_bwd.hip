@@ -24,13 +24,15 @@ namespace gdr {
 // ---------------------------------------------------------------------------
 // Adjoint walk: one wavefront per (document, value head, 16-column slice),
 // chunks in reverse.  dS lives in eight accumulator tiles; 56 MFMAs per chunk.
+// Operands are fetched one chunk ahead in the loop's own issue order.  dout
+// arrives as 8-byte row pieces (rows past the chunk read as zeros) and the
+// dS tape leaves as 8-byte row pieces, both through tile products with the
+// identity on the matrix cores (acc_layout / tile_row4), so the step has no
+// LDS round trip besides the broadcast of the gate factors.
 // ---------------------------------------------------------------------------
-constexpr int DOP = 72;  // pitch (bf16) of the transposed dout tile [column][row]
-
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
-  __shared__ __align__(16) float stg[HD * SGP];   // tape stage of this wavefront
-  __shared__ __align__(16) u16 sdo[16 * DOP];     // this slice's dout columns, [column][row]
+  __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
   int chain, sl;
   walk_block(blockIdx.x, chain, sl);
   if (chain >= p.N * p.Hv) return;
@@ -41,6 +43,8 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int vcol = 16 * sl + lr;
   const size_t Hv = p.Hv;
+  const uint32_t row_bytes = (uint32_t)(Hv * HD * 2);
+  const s16x4 eye = eye16(lane);
 
   f32x4 dS[8];
   const float *dh = dht ? dht + ((size_t)d * Hv + j) * HD * HD : nullptr;
@@ -49,73 +53,79 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) dS[mt][jj] = dh ? dh[(16 * mt + 4 * lg + jj) * HD + vcol] : 0.f;
 
-  bf16x8 Kb[4][4], MT[4][2], QG[8][2], WT[8][2];
-  float4 gm[8];
-  if (nch > 0) {
-    const size_t u = (size_t)(first + nch - 1) * Hv + j;
+  // dout of a chunk, this slice's 16 columns: lane (lr, lg) holds row 16t + lr, columns
+  // 4lg..4lg+3 (the A-operand layout of a 16x16x16 product), rows past the chunk as zeros
+  uint2 pdo[4];
+  auto fetch_dout = [&](int n) {
+    const int r0 = tok0 + CH * n;
+    const RowSource src(dout + ((size_t)r0 * Hv + j) * HD + 16 * sl, (uint32_t)min(CH, tok1 - r0) * row_bytes);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      Kb[t >> 2][t & 3] = as_bf16x8(w.Kb[u * FRAG_64x128_U4 + t * 64 + lane]);
-      QG[t >> 1][t & 1] = as_bf16x8(w.QGT[u * FRAG_64x128_U4 + t * 64 + lane]);
-      WT[t >> 1][t & 1] = as_bf16x8(w.WTn[u * FRAG_64x128_U4 + t * 64 + lane]);
-    }
+    for (int t = 0; t < 4; ++t) pdo[t] = src.get8((uint32_t)(16 * t + lr) * row_bytes + 8 * lg);
+  };
+
+  bf16x8 Kb[4][4], MT[4][2], QG[8][2], WT[8][2];
+  float2 gq = make_float2(0.f, 0.f);  // gamma of keys 2*lane, 2*lane+1 (next chunk)
+  if (nch > 0) {  // issued in the loop's own order: the counter waits at the loop head see one history
+    const size_t u = (size_t)(first + nch - 1) * Hv + j;
+    gq = *reinterpret_cast<const float2 *>(w.gam + u * HD + 2 * lane);
+    fetch_dout(nch - 1);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) QG[t >> 1][t & 1] = as_bf16x8(w.QGT[u * FRAG_64x128_U4 + t * 64 + lane]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) MT[t >> 1][t & 1] = as_bf16x8(w.MTs[u * FRAG_64x64_U4 + t * 64 + lane]);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(w.gam + u * HD + 16 * mt + 4 * lg);
-  }
-
-  // dout of a chunk, this slice's 16 columns, as 16-byte pieces: lane -> rows (lane >> 1) and
-  // 32 + (lane >> 1), columns 8 * (lane & 1)..+7; fetched one chunk ahead (rows past the chunk
-  // read its last row and are zeroed when the tile is formed)
-  u32x4 pdo[2];
-  auto fetch_dout = [&](int n) {
-    const int r0 = tok0 + CH * n, ln = min(CH, tok1 - r0);
+    for (int t = 0; t < 16; ++t) Kb[t >> 2][t & 3] = as_bf16x8(w.Kb[u * FRAG_64x128_U4 + t * 64 + lane]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = (lane >> 1) + 32 * h;
-      pdo[h] = *reinterpret_cast<const u32x4 *>(dout + ((size_t)(r0 + min(r, ln - 1)) * Hv + j) * HD + 16 * sl +
-                                                 8 * (lane & 1));
-    }
-  };
-  if (nch > 0) fetch_dout(nch - 1);
+    for (int t = 0; t < 16; ++t) WT[t >> 1][t & 1] = as_bf16x8(w.WTn[u * FRAG_64x128_U4 + t * 64 + lane]);
+  }
 
   for (int n = nch - 1; n >= 0; --n) {
     const size_t u = (size_t)(first + n) * Hv + j;
     const size_t un = n > 0 ? u - Hv : u;
-    const int row0 = tok0 + CH * n;
-    const int len = min(CH, tok1 - row0);
 
-    // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns), through the
-    // transposed LDS tile
+    *reinterpret_cast<float2 *>(sgam + 2 * lane) = gq;
+    float4 gm[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = (lane >> 1) + 32 * h, c0 = 8 * (lane & 1);
+    for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(sgam + 16 * mt + 4 * lg);
+    gq = *reinterpret_cast<const float2 *>(w.gam + un * HD + 2 * lane);
+
+    // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns)
+    bf16x8 dOb[2];
+    {
+      f32x4 dO[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wd = pdo[h][e >> 1];
-        sdo[(c0 + e) * DOP + r] = r < len ? (u16)((e & 1) ? (wd >> 16) : (wd & 0xffffu)) : (u16)0;
-      }
+      for (int t = 0; t < 4; ++t) dO[t] = mfma16(as_s4(pdo[t]), eye, zero4());
+      dOb[0] = acc_pair_to_b(dO[0], dO[1]);
+      dOb[1] = acc_pair_to_b(dO[2], dO[3]);
     }
     fetch_dout(n > 0 ? n - 1 : 0);
-    bf16x8 dOb[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const uint2 a = *reinterpret_cast<const uint2 *>(sdo + lr * DOP + 32 * kt + 4 * lg);
-      const uint2 b = *reinterpret_cast<const uint2 *>(sdo + lr * DOP + 32 * kt + 16 + 4 * lg);
-      dOb[kt] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-    }
 
     bf16x8 dSb[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) dSb[kt] = acc_pair_to_b(dS[2 * kt], dS[2 * kt + 1]);
-    {  // this slice's block of the adjoint-state tape
-      u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16);
-      stage_rows<8>(stg, dS, lane, [&](int row, int half, bf16x8 x) {
-        *reinterpret_cast<bf16x8 *>(tp + row * 16 + 8 * half) = x;
-      });
+    {  // this slice's block [key][16] of the adjoint-state tape
+      u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + lr * 16 + 4 * lg;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<uint2 *>(tp + mt * 256) = tile_row4(dSb[mt >> 1], mt & 1, eye);
     }
 
+    // dS' = gamma dS + scale (q Gamma)^T dout first (needs only dout), then dVn, then - W^T dVn.
+    // The phases are fenced so that each operand's refill for the next chunk stays beside its
+    // last use instead of collecting at the end of the step.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      dS[mt][0] *= gm[mt].x; dS[mt][1] *= gm[mt].y; dS[mt][2] *= gm[mt].z; dS[mt][3] *= gm[mt].w;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        dS[mt] = mfma(QG[mt][kt], dOb[kt], dS[mt]);
+        QG[mt][kt] = as_bf16x8(w.QGT[un * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
+      }
+
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 dV[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) dV[mt] = zero4();
@@ -133,35 +143,21 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
         dV[mt] = mfma(Kb[mt][kt], dSb[kt], dV[mt]);
         Kb[mt][kt] = as_bf16x8(w.Kb[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
       }
-    {
-      u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH;
+    {  // dVn^T rows of this slice's columns: 4 consecutive chunk rows per lane
+      u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 4 * lg;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        u16 b[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) b[jj] = f2bf(dV[mt][jj]);
-        uint2 pk;
-        pk.x = b[0] | ((uint32_t)b[1] << 16);
-        pk.y = b[2] | ((uint32_t)b[3] << 16);
-        *reinterpret_cast<uint2 *>(tr + 16 * mt + 4 * lg) = pk;
-      }
+      for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<uint2 *>(tr + 16 * mt) = pack_bf16x4(dV[mt]);
     }
 
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 dVb[2];
     dVb[0] = acc_pair_to_b(dV[0], dV[1]);
     dVb[1] = acc_pair_to_b(dV[2], dV[3]);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      dS[mt][0] *= gm[mt].x; dS[mt][1] *= gm[mt].y; dS[mt][2] *= gm[mt].z; dS[mt][3] *= gm[mt].w;
-      gm[mt] = *reinterpret_cast<const float4 *>(w.gam + un * HD + 16 * mt + 4 * lg);
-    }
-#pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        dS[mt] = mfma(QG[mt][kt], dOb[kt], dS[mt]);
         dS[mt] = mfma(WT[mt][kt], dVb[kt], dS[mt]);
-        QG[mt][kt] = as_bf16x8(w.QGT[un * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
         WT[mt][kt] = as_bf16x8(w.WTn[un * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
       }
   }
@@ -222,11 +218,6 @@ constexpr int G_RS = G_DB + 20 * 64 * 4;    // GDN: dG row sums per wavefront [8
 constexpr int G_SMEM = G_RS + 8 * 64 * 4;
 static_assert(G_DAT + CH * MP * 2 <= G_B, "grad LDS map");
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ s16x4 as_s4(uint2 x) { return __builtin_bit_cast(s16x4, x); }
 
 // Cumulative gate: per-channel tile [channel][row] (KDA) or one value per row.
 template <bool SCALAR>

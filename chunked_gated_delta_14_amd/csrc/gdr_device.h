@@ -22,6 +22,7 @@
 namespace gdr {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes (stays in registers, unlike HIP's uint4 in arrays)
 typedef uint16_t u16;
@@ -52,6 +53,42 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
 __device__ __forceinline__ uint4 as_u4(bf16x8 x) { return __builtin_bit_cast(uint4, x); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 as_s4(uint2 x) { return __builtin_bit_cast(s16x4, x); }
+
+// Tile transpose on the matrix cores.  A 16 x 16 accumulator tile, rounded to
+// bf16 (4 values per lane: rows 4lg..4lg+3 of column lr), read as the A operand
+// of a 16x16x16 product is the tile's transpose; times the identity it comes
+// back in accumulator layout with each lane holding row lr, columns
+// 4lg..4lg+3: 8 contiguous bytes of a row-major tile, so 16 lanes x 4 groups
+// store 512 contiguous bytes of a [row][16] block with no LDS round trip.
+// Exact: each output is one bf16 input times 1 plus exact zeros.
+__device__ __forceinline__ s16x4 eye16(int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  s16x4 e;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = (4 * lg + i == lr) ? (short)0x3F80 : (short)0;
+  return e;
+}
+__device__ __forceinline__ uint2 pack_bf16x4(f32x4 x) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 r;
+  r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
+  return __builtin_bit_cast(uint2, r);
+}
+// Half h (tile 2kt + h) of a kwalk-ordered fragment built by acc_pair_to_b.
+__device__ __forceinline__ s16x4 frag_half(bf16x8 f, int h) {
+  const u32x4 q = __builtin_bit_cast(u32x4, f);
+  return h ? as_s4(make_uint2(q.z, q.w)) : as_s4(make_uint2(q.x, q.y));
+}
+// Row lr, columns 4lg..4lg+3 of the tile held (transposed) in fragment half h.
+__device__ __forceinline__ uint2 tile_row4(bf16x8 f, int h, s16x4 eye) {
+  return pack_bf16x4(mfma16(frag_half(f, h), eye, f32x4{0.f, 0.f, 0.f, 0.f}));
+}
 
 // Two stacked accumulator tiles -> one kwalk-ordered B fragment.
 __device__ __forceinline__ bf16x8 acc_pair_to_b(f32x4 hi, f32x4 lo) {
@@ -105,26 +142,35 @@ __device__ __forceinline__ bf16x8 cvt8(float4 a, float4 b) {
   return r;
 }
 
-// Walk wavefront output stage: MT accumulator tiles (rows 16mt + 4lg + j, column lr) go to a
-// wavefront-private fp32 LDS tile [row][SGP] and come back as 16-byte bf16 pieces of 8 columns;
-// put(row, half, piece) stores the piece of columns 8*half..+7.  LDS operations of one wavefront
-// complete in order, so no wait is needed between the two halves or between stages.
-constexpr int SGP = 20;  // stage pitch (floats): rows 4 apart fall 16 banks apart
-template <int MT, typename Put>
-__device__ __forceinline__ void stage_rows(float *stg, const f32x4 (&acc)[MT], int lane, Put put) {
-  const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) stg[(16 * mt + 4 * lg + jj) * SGP + lr] = acc[mt][jj];
-#pragma unroll
-  for (int pass = 0; pass < MT / 2; ++pass) {  // 32 rows per pass
-    const int row = 32 * pass + (lane >> 1), half = lane & 1;
-    const float4 a = *reinterpret_cast<const float4 *>(stg + row * SGP + 8 * half);
-    const float4 b = *reinterpret_cast<const float4 *>(stg + row * SGP + 8 * half + 4);
-    put(row, half, cvt8(a, b));
+// Stores of 16-byte row pieces through a buffer resource whose record count
+// ends at the last valid byte: the hardware drops stores past it, so a ragged
+// final chunk needs no branch (a branch would split the walk's step into
+// separately scheduled blocks).  The base must be wave-uniform.
+struct RowSink {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ RowSink(void *base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ void put(uint32_t byte_off, bf16x8 x) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, (int)byte_off, 0, 0);
   }
-}
+  __device__ __forceinline__ void put8(uint32_t byte_off, uint2 x) const {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, (int)byte_off, 0, 0);
+  }
+};
+
+// Loads of 8-byte row pieces through a buffer resource ending at the last
+// valid byte: pieces past it read as zeros (a ragged final chunk's missing
+// rows), without a branch or a select.  The base must be wave-uniform.
+struct RowSource {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ RowSource(const void *base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ uint2 get8(uint32_t byte_off) const {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0));
+  }
+};
 
 // 8 contiguous bf16 from LDS/global (16-byte aligned).
 __device__ __forceinline__ bf16x8 ld8(const u16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
@@ -153,13 +199,16 @@ struct ChunkTable {
 };
 
 // Walk grid: chain c (= rank of the document in walk order * H_v + head)
-// and value slice s (16 columns) from the block index, placing all slices of
-// one chain on the same XCD (block ids are dealt to the 8 XCDs round-robin),
-// so they share that XCD's L2 copy of the chain's per-chunk operands.
-__device__ __forceinline__ void walk_block(int b, int &chain, int &slice) {
+// and the wavefront's group of NS adjacent 16-column value slices from the
+// block index, placing all groups of one chain on the same XCD (block ids are
+// dealt to the 8 XCDs round-robin), so they share that XCD's L2 copy of the
+// chain's per-chunk operands.  The grid is ceil(chains / 8) * 64 / NS blocks.
+template <int NS = 1>
+__device__ __forceinline__ void walk_block(int b, int &chain, int &group) {
+  constexpr int G = 8 / NS;  // slice groups per chain
   const int x = b & 7, m = b >> 3;
-  slice = m & 7;
-  chain = ((m >> 3) << 3) + x;
+  group = m % G;
+  chain = (m / G) * 8 + x;
 }
 
 // ---------------------------------------------------------------------------
@@ -167,131 +216,11 @@ __device__ __forceinline__ void walk_block(int b, int &chain, int &slice) {
 // with NT threads (NW = NT/64 wavefronts) and operate on LDS tiles.
 // ---------------------------------------------------------------------------
 
-// Gate accessor: per-channel (KDA) 64 x GP tile or one scalar per row (GDN).
-template <bool SCALAR>
-struct Gate {
-  const float *s;
-  __device__ __forceinline__ float operator()(int r, int c) const {
-    if constexpr (SCALAR) return s[r];
-    else return s[r * GP + c];
-  }
-};
-
-// Load a chunk's gate rows into LDS (zeros past len) and turn them into the
-// in-chunk inclusive cumulative sum G.  KDA: g row stride H_v*128 floats;
-// GDN: one float per row, stride H_v.
-template <bool SCALAR, int NT = 256>
-__device__ __forceinline__ void load_cumsum_gate(float *sG, const float *g, int start, int len,
-                                                 int Hv, int j, int tid) {
-  if constexpr (SCALAR) {
-    if (tid < 64) {
-      float x = tid < len ? g[(size_t)(start + tid) * Hv + j] : 0.f;
-      // inclusive scan over the 64 lanes of wavefront 0
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(x, o, 64);
-        if (tid >= o) x += y;
-      }
-      sG[tid] = x;
-    }
-    __syncthreads();
-  } else {
-    for (int e = tid; e < CH * HD / 4; e += NT) {
-      const int r = e >> 5, c4 = (e & 31) * 4;
-      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r < len) val = *reinterpret_cast<const float4 *>(g + ((size_t)(start + r) * Hv + j) * HD + c4);
-      *reinterpret_cast<float4 *>(sG + r * GP + c4) = val;
-    }
-    __syncthreads();
-    // NT/128 row bands per channel: scan each band, then add the totals of
-    // the bands above it
-    constexpr int NB = NT / 128, BR = CH / NB;
-    const int c = tid & 127, band = tid >> 7;
-    float run = 0.f;
-    for (int r = BR * band; r < BR * band + BR; ++r) {
-      run += sG[r * GP + c];
-      sG[r * GP + c] = run;
-    }
-    __syncthreads();
-    float base = 0.f;
-    for (int b = 0; b < band; ++b) base += sG[(BR * b + BR - 1) * GP + c];
-    __syncthreads();
-    if (band)
-      for (int r = BR * band; r < BR * band + BR; ++r) sG[r * GP + c] += base;
-    __syncthreads();
-  }
-}
-
-// Copy 64 rows x 128 bf16 (row stride `ld` elements in global memory) into an
-// LDS tile with pitch KP; rows >= len become zeros.
-template <int NT = 256>
-__device__ __forceinline__ void load_rows_bf16(u16 *dst, const u16 *src, size_t ld, int len, int tid) {
-  for (int e = tid; e < CH * 16; e += NT) {
-    const int r = e >> 4, c8 = (e & 15) * 8;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < len) val = *reinterpret_cast<const uint4 *>(src + (size_t)r * ld + c8);
-    *reinterpret_cast<uint4 *>(dst + r * KP + c8) = val;
-  }
-}
-
 // The 10 lower block pairs (I, J), J <= I, of a 64 x 64 matrix in 16-row blocks.
 __device__ __forceinline__ void block_pair(int p, int &I, int &J) {
   // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
   I = p >= 6 ? 3 : (p >= 3 ? 2 : (p >= 1 ? 1 : 0));
   J = p - (I * (I + 1)) / 2;
-}
-
-// Gated key products of one chunk:
-//   E[r][s] = sum_c k_rc k_sc exp(G_rc - G_sc)   (s < r, else 0)     -> sE (fp32, pitch SP)
-//   M[r][s] = sum_c q_rc k_sc exp(G_rc - G_sc)   (s <= r, else 0)    -> sM (bf16, pitch MP), if WITH_M
-// Each 16x16 block pair (I, J) is one MFMA chain over the 128 channels with
-// both factors rescaled around the gate of row 16I+8: the row factor
-// exp(G_r - G_ref) and the column factor exp(G_ref - G_s) stay within
-// exp(+-8*|g|max) in fp32/bf16 range, while the exact exponent G_r - G_s of
-// an entry can reach 64*|g|max, far outside it.
-template <bool SCALAR, bool WITH_M, int NW = 4>
-__device__ __forceinline__ void gated_kk(float *sE, u16 *sM, const u16 *sK, const u16 *sQ,
-                                         const float *sG, int wave, int lane) {
-  const Gate<SCALAR> G{sG};
-  const int lr = lane & 15, lg = lane >> 4;
-  for (int p = wave; p < 10; p += NW) {
-    int I, J;
-    block_pair(p, I, J);
-    const int ref = 16 * I + 8, r = 16 * I + lr, s = 16 * J + lr;
-    f32x4 accE = zero4(), accM = zero4();
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int c0 = 32 * kt + 8 * lg;
-      bf16x8 aK, aQ, bK;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int c = c0 + i;
-        const float gref = G(ref, c);
-        const float er = __expf(G(r, c) - gref);
-        const float es = __expf(gref - G(s, c));
-        aK[i] = (__bf16)(bf2f(sK[r * KP + c]) * er);
-        if constexpr (WITH_M) aQ[i] = (__bf16)(bf2f(sQ[r * KP + c]) * er);
-        bK[i] = (__bf16)(bf2f(sK[s * KP + c]) * es);
-      }
-      accE = mfma(aK, bK, accE);
-      if constexpr (WITH_M) accM = mfma(aQ, bK, accM);
-    }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int row = 16 * I + 4 * lg + jj, col = 16 * J + lr;
-      sE[row * SP + col] = col < row ? accE[jj] : 0.f;
-      if constexpr (WITH_M) sM[row * MP + col] = f2bf(col <= row ? accM[jj] : 0.f);
-    }
-  }
-  // upper block pairs are zero
-  for (int e = wave * 64 + lane; e < 6 * 256; e += NW * 64) {
-    const int p = e >> 8, idx = e & 255;
-    const int I = p < 3 ? 0 : (p < 5 ? 1 : 2);
-    const int J = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
-    const int row = 16 * I + (idx >> 4), col = 16 * J + (idx & 15);
-    sE[row * SP + col] = 0.f;
-    if constexpr (WITH_M) sM[row * MP + col] = 0;
-  }
 }
 
 // fp32 MFMA, 16x16x4: lane holds A[lr][k], B[k][lr] for its reduction index k

@@ -446,49 +446,69 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
 }
 
 // ---------------------------------------------------------------------------
-// Forward walk: one wavefront per (document, value head, 16-column value
-// slice).  The 128 x 16 state slice lives in eight accumulator tiles; each
-// chunk costs 48 MFMAs (Vn, o and the state update) and its operands are
-// fetched one chunk ahead, each register refilled right after its last use.
+// Forward walk: one wavefront per (document, value head, group of NS adjacent
+// 16-column value slices).  Each 128 x 16 state slice lives in eight
+// accumulator tiles; per chunk a slice costs 48 MFMAs (Vn, o and the state
+// update).  Operands are fetched one chunk ahead, each register refilled right
+// after its last use.  Outputs (o, and with SAVE the state and Vn tapes) leave
+// through tile transposes on the matrix cores as 8-byte row pieces, so the
+// step has no LDS round trip and no branch.  The gate factors gamma arrive as
+// two floats per lane and are spread to the accumulator rows through LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u16 *o, float *ht, int save) {
-  __shared__ __align__(16) float stg[HD * SGP];  // output stage of this wavefront
-  int chain, sl;
-  walk_block(blockIdx.x, chain, sl);
+// Slices per wavefront.  Two slices halve the operand bytes each column pays,
+// but double every wavefront's serial work per chunk; the longest documents
+// end up with one resident wavefront per compute unit, where that serial work
+// sets the pace, so one slice per wavefront is the faster choice for packs of
+// a few long documents.
+constexpr int WALK_NS = 1;
+
+template <int NS, bool SAVE>
+__global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u16 *o, float *ht) {
+  __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
+  int chain, grp;
+  walk_block<NS>(blockIdx.x, chain, grp);
   if (chain >= p.N * p.Hv) return;
   const ChunkTable tb(p.table, p.NC, p.N);
   const int d = tb.order[chain / p.Hv], j = chain % p.Hv;
   const int first = tb.doc_ptr[d], nch = tb.doc_ptr[d + 1] - first;
   const int tok0 = p.cu[d], tok1 = p.cu[d + 1];
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
-  const int vcol = 16 * sl + lr;
+  const int sl0 = NS * grp;  // first slice of this wavefront
   const size_t Hv = p.Hv;
+  const uint32_t row_bytes = (uint32_t)(Hv * HD * 2);
+  const s16x4 eye = eye16(lane);
 
-  f32x4 S[8];
+  f32x4 S[NS][8];
   const float *h0 = p.h0 ? p.h0 + ((size_t)d * Hv + j) * HD * HD : nullptr;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) S[mt][jj] = h0 ? h0[(16 * mt + 4 * lg + jj) * HD + vcol] : 0.f;
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        S[s][mt][jj] = h0 ? h0[(16 * mt + 4 * lg + jj) * HD + 16 * (sl0 + s) + lr] : 0.f;
 
   bf16x8 Wf[4][4], Pf[4][4], KT[8][2];
-  uint2 Ua[4], Oa[4];
-  float4 gm[8];
-  if (nch > 0) {
+  uint2 Ua[NS][4], Oa[NS][4];
+  float2 gq = make_float2(0.f, 0.f);  // gamma of keys 2*lane, 2*lane+1 (next chunk)
+  if (nch > 0) {  // issued in the loop's own order (gamma, U/Oi, W, P, K-bar^T): the
+                  // counter waits at the loop head then see one history
     const size_t u = (size_t)first * Hv + j;
+    gq = *reinterpret_cast<const float2 *>(w.gam + u * HD + 2 * lane);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      Wf[t >> 2][t & 3] = as_bf16x8(w.WfN[u * FRAG_64x128_U4 + t * 64 + lane]);
-      Pf[t >> 2][t & 3] = as_bf16x8(w.Pf[u * FRAG_64x128_U4 + t * 64 + lane]);
-      KT[t >> 1][t & 1] = as_bf16x8(w.KbT[u * FRAG_64x128_U4 + t * 64 + lane]);
-    }
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      Ua[mt] = *reinterpret_cast<const uint2 *>(w.Uacc + u * ACC_64x128_U16 + ((sl * 4 + mt) * 64 + lane) * 4);
-      Oa[mt] = *reinterpret_cast<const uint2 *>(w.Oacc + u * ACC_64x128_U16 + ((sl * 4 + mt) * 64 + lane) * 4);
-    }
+      for (int mt = 0; mt < 4; ++mt) {
+        const size_t off = u * ACC_64x128_U16 + (((sl0 + s) * 4 + mt) * 64 + lane) * 4;
+        Ua[s][mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
+        Oa[s][mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
+      }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(w.gam + u * HD + 16 * mt + 4 * lg);
+    for (int t = 0; t < 16; ++t) Wf[t >> 2][t & 3] = as_bf16x8(w.WfN[u * FRAG_64x128_U4 + t * 64 + lane]);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) Pf[t >> 2][t & 3] = as_bf16x8(w.Pf[u * FRAG_64x128_U4 + t * 64 + lane]);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) KT[t >> 1][t & 1] = as_bf16x8(w.KbT[u * FRAG_64x128_U4 + t * 64 + lane]);
   }
 
   for (int n = 0; n < nch; ++n) {
@@ -497,67 +517,96 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
     const int row0 = tok0 + CH * n;
     const int len = min(CH, tok1 - row0);
 
-    bf16x8 Sb[4];
+    // This chunk's gate factors, laid out as each lane's accumulator rows need them.
+    *reinterpret_cast<float2 *>(sgam + 2 * lane) = gq;
+    float4 gm[8];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) Sb[kt] = acc_pair_to_b(S[2 * kt], S[2 * kt + 1]);
-    if (save) {  // this slice's block of the state tape
-      u16 *st = w.S + u * (HD * HD) + sl * (HD * 16);
-      stage_rows<8>(stg, S, lane, [&](int row, int half, bf16x8 x) {
-        *reinterpret_cast<bf16x8 *>(st + row * 16 + 8 * half) = x;
-      });
+    for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(sgam + 16 * mt + 4 * lg);
+    gq = *reinterpret_cast<const float2 *>(w.gam + un * HD + 2 * lane);
+
+    bf16x8 Sb[NS][4];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) Sb[s][kt] = acc_pair_to_b(S[s][2 * kt], S[s][2 * kt + 1]);
+    if (SAVE) {  // state tape: block [key][16] of each slice
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        u16 *st = w.S + u * (HD * HD) + (sl0 + s) * (HD * 16) + lr * 16 + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+          *reinterpret_cast<uint2 *>(st + mt * 256) = tile_row4(Sb[s][mt >> 1], mt & 1, eye);
+      }
     }
 
-    f32x4 Vn[4], Oc[4];
+    f32x4 Vn[NS][4], Oc[NS][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      Vn[mt][0] = bf2f(Ua[mt].x & 0xffff); Vn[mt][1] = bf2f(Ua[mt].x >> 16);
-      Vn[mt][2] = bf2f(Ua[mt].y & 0xffff); Vn[mt][3] = bf2f(Ua[mt].y >> 16);
-      Oc[mt][0] = bf2f(Oa[mt].x & 0xffff); Oc[mt][1] = bf2f(Oa[mt].x >> 16);
-      Oc[mt][2] = bf2f(Oa[mt].y & 0xffff); Oc[mt][3] = bf2f(Oa[mt].y >> 16);
-      Ua[mt] = *reinterpret_cast<const uint2 *>(w.Uacc + un * ACC_64x128_U16 + ((sl * 4 + mt) * 64 + lane) * 4);
-      Oa[mt] = *reinterpret_cast<const uint2 *>(w.Oacc + un * ACC_64x128_U16 + ((sl * 4 + mt) * 64 + lane) * 4);
-    }
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        Vn[s][mt][0] = bf2f(Ua[s][mt].x & 0xffff); Vn[s][mt][1] = bf2f(Ua[s][mt].x >> 16);
+        Vn[s][mt][2] = bf2f(Ua[s][mt].y & 0xffff); Vn[s][mt][3] = bf2f(Ua[s][mt].y >> 16);
+        Oc[s][mt][0] = bf2f(Oa[s][mt].x & 0xffff); Oc[s][mt][1] = bf2f(Oa[s][mt].x >> 16);
+        Oc[s][mt][2] = bf2f(Oa[s][mt].y & 0xffff); Oc[s][mt][3] = bf2f(Oa[s][mt].y >> 16);
+        const size_t off = un * ACC_64x128_U16 + (((sl0 + s) * 4 + mt) * 64 + lane) * 4;
+        Ua[s][mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
+        Oa[s][mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
+      }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        Vn[mt] = mfma(Wf[mt][kt], Sb[kt], Vn[mt]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) Vn[s][mt] = mfma(Wf[mt][kt], Sb[s][kt], Vn[s][mt]);
         Wf[mt][kt] = as_bf16x8(w.WfN[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
       }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        Oc[mt] = mfma(Pf[mt][kt], Sb[kt], Oc[mt]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) Oc[s][mt] = mfma(Pf[mt][kt], Sb[s][kt], Oc[s][mt]);
         Pf[mt][kt] = as_bf16x8(w.Pf[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
       }
 
-    {
-      u16 *ob = o + ((size_t)row0 * Hv + j) * HD + 16 * sl;
-      stage_rows<4>(stg, Oc, lane, [&](int row, int half, bf16x8 x) {
-        if (row < len) *reinterpret_cast<bf16x8 *>(ob + (size_t)row * Hv * HD + 8 * half) = x;
-      });
+    bf16x8 Vb[NS][2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      Vb[s][0] = acc_pair_to_b(Vn[s][0], Vn[s][1]);
+      Vb[s][1] = acc_pair_to_b(Vn[s][2], Vn[s][3]);
     }
-    if (save) {
-      u16 *vt = w.Vn + u * (CH * HD) + sl * (CH * 16);
-      stage_rows<4>(stg, Vn, lane, [&](int row, int half, bf16x8 x) {
-        *reinterpret_cast<bf16x8 *>(vt + row * 16 + 8 * half) = x;
-      });
+    {  // o rows of this chunk; rows past len fall outside the sink's range
+      const RowSink ob(o + ((size_t)row0 * Hv + j) * HD + 16 * sl0, (uint32_t)len * row_bytes);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 Ob0 = acc_pair_to_b(Oc[s][0], Oc[s][1]), Ob1 = acc_pair_to_b(Oc[s][2], Oc[s][3]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          ob.put8((uint32_t)(16 * mt + lr) * row_bytes + 32 * s + 8 * lg, tile_row4(mt < 2 ? Ob0 : Ob1, mt & 1, eye));
+      }
+    }
+    if (SAVE) {  // Vn tape: block [row][16] of each slice
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        u16 *vt = w.Vn + u * (CH * HD) + (sl0 + s) * (CH * 16) + lr * 16 + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          *reinterpret_cast<uint2 *>(vt + mt * 256) = tile_row4(Vb[s][mt >> 1], mt & 1, eye);
+      }
     }
 
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      S[mt][0] *= gm[mt].x; S[mt][1] *= gm[mt].y; S[mt][2] *= gm[mt].z; S[mt][3] *= gm[mt].w;
-      gm[mt] = *reinterpret_cast<const float4 *>(w.gam + un * HD + 16 * mt + 4 * lg);
-    }
-    bf16x8 Vb[2];
-    Vb[0] = acc_pair_to_b(Vn[0], Vn[1]);
-    Vb[1] = acc_pair_to_b(Vn[2], Vn[3]);
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        S[s][mt][0] *= gm[mt].x; S[s][mt][1] *= gm[mt].y; S[s][mt][2] *= gm[mt].z; S[s][mt][3] *= gm[mt].w;
+      }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        S[mt] = mfma(KT[mt][kt], Vb[kt], S[mt]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) S[s][mt] = mfma(KT[mt][kt], Vb[s][kt], S[s][mt]);
         KT[mt][kt] = as_bf16x8(w.KbT[un * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
       }
   }
@@ -565,13 +614,15 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
   if (ht) {
     float *hp = ht + ((size_t)d * Hv + j) * HD * HD;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) hp[(16 * mt + 4 * lg + jj) * HD + vcol] = S[mt][jj];
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) hp[(16 * mt + 4 * lg + jj) * HD + 16 * (sl0 + s) + lr] = S[s][mt][jj];
   }
 }
 
-static int walk_grid(int chains) { return ((chains + 7) / 8) * 64; }
+static int walk_grid(int chains, int ns) { return ((chains + 7) / 8) * 64 / ns; }
 
 static int compute_units() {
   static int cached[64] = {0};
@@ -600,7 +651,9 @@ hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool 
 hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, u16 *o, float *ht, bool save, hipStream_t st) {
   const int chains = p.N * p.Hv;
   if (chains == 0) return hipSuccess;
-  fwd_walk_kernel<<<walk_grid(chains), 64, 0, st>>>(p, w, o, ht, save ? 1 : 0);
+  constexpr int NS = WALK_NS;
+  if (save) fwd_walk_kernel<NS, true><<<walk_grid(chains, NS), 64, 0, st>>>(p, w, o, ht);
+  else fwd_walk_kernel<NS, false><<<walk_grid(chains, NS), 64, 0, st>>>(p, w, o, ht);
   return hipGetLastError();
 }
 

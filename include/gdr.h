@@ -58,7 +58,8 @@ extern "C" {
 enum gdr_status {
   GDR_OK = 0,
   GDR_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, inconsistent table, ... */
-  GDR_ERR_UNSUPPORTED = 2, /* K != 128, V != 128, KDA with H_qk != H_v, GDN with H_v % H_qk != 0 */
+  GDR_ERR_UNSUPPORTED = 2, /* K != 128, V != 128, KDA with H_qk != H_v, GDN with H_v % H_qk != 0,
+                              H_v > 65536, N * H_v > 2^27 or n_chunks * H_v >= 2^31 */
   GDR_ERR_WORKSPACE = 3,   /* workspace smaller than required or not 256-byte aligned */
   GDR_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
   GDR_ERR_ARCH = 5         /* the current device is not gfx950 */
