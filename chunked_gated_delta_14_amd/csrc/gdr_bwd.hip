@@ -432,7 +432,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       eT[q] = reinterpret_cast<const uint2 *>(w.Et + u * FRAG_64x64_U4)[pt * 64 + lane];
     }
 
-    __syncthreads();
+    lds_barrier();
 
     // ---- Y = T^T dVn for value tile w, all rows (computed as Y^T); dv = beta Y
     // is kept for the end of the iteration ----
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         F[I][2] = __expf(g4.z - gref); F[I][3] = __expf(g4.w - gref);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- products with the state tapes (reduction over the value dim) ----
     f32x4 dGA[4];
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         }
       }
     }
-    __syncthreads();  // dout, Vn, Y are dead: their space takes dM, dA
+    lds_barrier();  // dout, Vn, Y are dead: their space takes dM, dA
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int pt = wave + 8 * q;
@@ -592,7 +592,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       *reinterpret_cast<uint2 *>(sDMT + s * MP + r0) = make_uint2(0, 0);
       *reinterpret_cast<uint2 *>(sDAT + s * MP + r0) = make_uint2(0, 0);
     }
-    __syncthreads();
+    lds_barrier();
 
     float Dm[6];  // D_IJ, index I(I-1)/2 + J: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
     {
@@ -746,7 +746,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
           if (lr == 0) sRS[wave * 64 + 16 * I + 4 * lg + jj] = x;
         }
     }
-    __syncthreads();  // dbeta partial sums complete (and GDN row sums)
+    lds_barrier();  // dbeta partial sums complete (and GDN row sums)
     if (tid < 64 && tid < len) {
       float x = 0.f;
 #pragma unroll
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     for (int mt = 0; mt < 4; ++mt)
       if (16 * mt + lr < len)
         *reinterpret_cast<uint2 *>(dv + ((size_t)(start + 16 * mt + lr) * Hv + j) * HD + 16 * wave + 4 * lg) = dvv[mt];
-    __syncthreads();
+    lds_barrier();
   }
 
   // dq, dk: fp32 sums over the group's value heads, rounded once
@@ -902,7 +902,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         }
         sG[tid] = x;
       }
-      __syncthreads();
+      lds_barrier();
     } else {
       // thread: channel octet 8o..8o+7, rows 2pr and 2pr+1, read as 16-byte
       // pieces; the 32 lanes of a half wavefront scan their octet's 64 rows
@@ -929,7 +929,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         }
         *reinterpret_cast<float2 *>(sG + (c0 + ii) * GTP + rp) = make_float2(incl - gx[1][ii], incl);
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // ---- Y = T^T dVn: rows 16mt.., value columns 64ch.. (4 tiles, computed as Y^T) ----
@@ -957,7 +957,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
       db1 = red_lg(db1);
       if (lg == 0) atomicAdd(&sDB[ra], db1);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- products with the state tapes (reduction over the value dim) ----
     const u16 *Sg = w.S + u * (HD * HD);
@@ -1063,7 +1063,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
       *reinterpret_cast<uint2 *>(sDMT + s * MP + r0) = pack4(m[0], m[1], m[2], m[3]);
       *reinterpret_cast<uint2 *>(sDAT + s * MP + r0) = pack4(a[0], a[1], a[2], a[3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- gated products of dM and dA (16-row blocks, reference row 16I+8) ----
     // The exponentially rescaled operand is split into bf16 hi + lo: each
@@ -1154,7 +1154,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
       const float x = red16(dbp[jj]);
       if (lr == 0) atomicAdd(&sDB[r0 + jj], x);
     }
-    __syncthreads();  // also: sRed and sDgam complete
+    lds_barrier();  // also: sRed and sDgam complete
     if (tid < 64 && tid < len) {
       const size_t e = (size_t)(start + tid) * Hv + j;
       if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = sDB[tid];
@@ -1186,7 +1186,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         hsum[t][0] = s0 + up; hsum[t][1] = s1 + up; hsum[t][2] = s2 + up; hsum[t][3] = s3 + up;
         if (lg == 0) sBT[mt * 128 + 16 * (4 * ch + t) + lr] = hsum[t][0];
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int c = 16 * (4 * ch + t) + lr;
@@ -1206,7 +1206,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         x = red16(x);
         if (lr == 0) sBT[ch * 64 + r0 + jj] = x;
       }
-      __syncthreads();
+      lds_barrier();
       if (tid < 64) {
         float y = sBT[63 - tid] + sBT[64 + 63 - tid];
 #pragma unroll
@@ -1218,7 +1218,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         if (rr < len) dg[(size_t)(start + rr) * Hv + j] = y;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // dq, dk: fp32 sums over the group's value heads, rounded once

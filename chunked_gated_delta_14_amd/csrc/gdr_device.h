@@ -142,6 +142,16 @@ __device__ __forceinline__ bf16x8 cvt8(float4 a, float4 b) {
   return r;
 }
 
+// Workgroup barrier for hand-offs through LDS.  __syncthreads() carries a
+// workgroup-scope release fence, which on this target waits for every global
+// load and store the wavefront has in flight (vmcnt(0)), so loads issued early
+// to overlap later work would be drained at the first barrier.  Data moves
+// between the wavefronts of these kernels only through LDS: completing this
+// wavefront's LDS operations (lgkmcnt(0)) before s_barrier is enough, global
+// loads stay in flight and are waited for where their registers are used.  The
+// memory clobber keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Stores of 16-byte row pieces through a buffer resource whose record count
 // ends at the last valid byte: the hardware drops stores past it, so a ragged
 // final chunk needs no branch (a branch would split the walk's step into
@@ -262,7 +272,7 @@ __device__ __forceinline__ void tri_inverse(float *sT, const float *sE, const fl
 #pragma unroll
     for (int r = 0; r < 16; ++r) sT[(base + r) * SP + base + s] = x[r];
   }
-  __syncthreads();
+  lds_barrier();
   for (int d = 1; d < 4; ++d) {
     if (wave < 4 - d) {
       const int J = wave, I = J + d, row = 16 * I + lr;
@@ -280,7 +290,7 @@ __device__ __forceinline__ void tri_inverse(float *sT, const float *sE, const fl
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) sT[(16 * I + 4 * lg + jj) * SP + 16 * J + lr] = -Y[jj];
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

@@ -225,7 +225,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
       *reinterpret_cast<float4 *>(sKFi + r * GP + c0 + 4) = make_float4(kfi[4], kfi[5], kfi[6], kfi[7]);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- 2. gated products.  Wavefront w: column block J = w >> 1 and row
   // blocks I in {2kt, 2kt+1}, kt = w & 1; the two accumulator tiles of M are
@@ -275,7 +275,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     }
     if (save) w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane] = as_u4(acc_pair_to_b(ms[0], ms[1]));
   }
-  __syncthreads();
+  lds_barrier();
   settle(next);  // the next unit's inputs, fetched at the start of this one
 
   // ---- 3. column-form operands (over the step-1 space), then T ----
@@ -334,7 +334,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 #pragma unroll
       for (int n = 0; n < 2; ++n)  // -W^T: rows key 16nt.., k: chunk 32kp + kwalk
         w.WTn[u * FRAG_64x128_U4 + ((2 * cg + n) * 2 + kp) * 64 + lane] = as_u4(acc_pair_to_b(-Wd[0][n], -Wd[1][n]));
-    __syncthreads();  // beta k exp(G) and beta v are dead
+    lds_barrier();  // beta k exp(G) and beta v are dead
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -343,7 +343,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         *reinterpret_cast<uint2 *>(sWT + cc * CTP + r0) = pack4bf(Wd[h][n]);
         *reinterpret_cast<uint2 *>(sUT + cc * CTP + r0) = pack4bf(Ud[h][n]);
       }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- 5. P^T = scale (q exp G)^T - scale W^T M^T,  Oi = scale M U ----
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
     const PrepIn cur = nxt;
     if (unit + (int)gridDim.x < total) prep_load<SCALAR>(nxt, p, tb, unit + gridDim.x, tid);
     prep_unit<SCALAR>(p, w, save, unit, cur, nxt, smem);
-    __syncthreads();  // LDS is reused by the next unit
+    lds_barrier();  // LDS is reused by the next unit
   }
 }
 
