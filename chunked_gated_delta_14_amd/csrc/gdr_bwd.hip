@@ -25,10 +25,10 @@ namespace gdr {
 // Adjoint walk: one wavefront per (document, value head, 16-column slice),
 // chunks in reverse.  dS lives in eight accumulator tiles; 56 MFMAs per chunk.
 // Operands are fetched one chunk ahead in the loop's own issue order.  dout
-// arrives as 8-byte row pieces (rows past the chunk read as zeros) and the
-// dS tape leaves as 8-byte row pieces, both through tile products with the
-// identity on the matrix cores (acc_layout / tile_row4), so the step has no
-// LDS round trip besides the broadcast of the gate factors.
+// arrives as 16-byte row pieces (rows past the chunk read as zeros) and the dS
+// tape leaves as 16-byte row pieces, both through lane regrouping and tile
+// products with the identity on the matrix cores, so the step has no LDS
+// round trip besides the broadcast of the gate factors.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
@@ -53,14 +53,18 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) dS[mt][jj] = dh ? dh[(16 * mt + 4 * lg + jj) * HD + vcol] : 0.f;
 
-  // dout of a chunk, this slice's 16 columns: lane (lr, lg) holds row 16t + lr, columns
-  // 4lg..4lg+3 (the A-operand layout of a 16x16x16 product), rows past the chunk as zeros
-  uint2 pdo[4];
+  // 16-byte row pieces: lane (lr, lg) carries row 16 (lg >> 1) + lr of a 32-row block,
+  // columns 8 (lg & 1)..+7 of this slice
+  const int prow = 16 * (lg >> 1) + lr, pcol = 8 * (lg & 1);
+  // dout of a chunk, this slice's 16 columns, fetched as 16-byte pieces (rows past the chunk
+  // read as zeros); regrouped at use so that lane (lr, lg) holds row 16t + lr, columns
+  // 4lg..4lg+3 of tile t (the A-operand layout of a 16x16x16 product)
+  u32x4 pdo[2];
   auto fetch_dout = [&](int n) {
     const int r0 = tok0 + CH * n;
     const RowSource src(dout + ((size_t)r0 * Hv + j) * HD + 16 * sl, (uint32_t)min(CH, tok1 - r0) * row_bytes);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pdo[t] = src.get8((uint32_t)(16 * t + lr) * row_bytes + 8 * lg);
+    for (int h = 0; h < 2; ++h) pdo[h] = src.get16((uint32_t)(32 * h + prow) * row_bytes + 2 * pcol);
   };
 
   bf16x8 Kb[4][4], MT[4][2], QG[8][2], WT[8][2];
@@ -94,7 +98,12 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
     {
       f32x4 dO[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) dO[t] = mfma16(as_s4(pdo[t]), eye, zero4());
+      for (int h = 0; h < 2; ++h) {
+        uint2 X, Y;
+        pair_from_rows8(pdo[h], X, Y);
+        dO[2 * h] = mfma16(as_s4(X), eye, zero4());
+        dO[2 * h + 1] = mfma16(as_s4(Y), eye, zero4());
+      }
       dOb[0] = acc_pair_to_b(dO[0], dO[1]);
       dOb[1] = acc_pair_to_b(dO[2], dO[3]);
     }
@@ -104,9 +113,10 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) dSb[kt] = acc_pair_to_b(dS[2 * kt], dS[2 * kt + 1]);
     {  // this slice's block [key][16] of the adjoint-state tape
-      u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + lr * 16 + 4 * lg;
+      u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + prow * 16 + pcol;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<uint2 *>(tp + mt * 256) = tile_row4(dSb[mt >> 1], mt & 1, eye);
+      for (int kt = 0; kt < 4; ++kt)
+        *reinterpret_cast<u32x4 *>(tp + kt * 512) = rows8_from_pair(tile_row4(dSb[kt], 0, eye), tile_row4(dSb[kt], 1, eye));
     }
 
     // dS' = gamma dS + scale (q Gamma)^T dout first (needs only dout), then dVn, then - W^T dVn.
@@ -143,10 +153,11 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
         dV[mt] = mfma(Kb[mt][kt], dSb[kt], dV[mt]);
         Kb[mt][kt] = as_bf16x8(w.Kb[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
       }
-    {  // dVn^T rows of this slice's columns: 4 consecutive chunk rows per lane
-      u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 4 * lg;
+    {  // dVn^T rows of this slice's columns: 8 consecutive chunk rows 32h + 8lg.. per lane
+      u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 8 * lg;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<uint2 *>(tr + 16 * mt) = pack_bf16x4(dV[mt]);
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4 *>(tr + 32 * h) = rows8_from_pair(pack_bf16x4(dV[2 * h]), pack_bf16x4(dV[2 * h + 1]));
     }
 
     __builtin_amdgcn_sched_barrier(0);

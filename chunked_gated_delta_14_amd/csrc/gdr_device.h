@@ -90,6 +90,31 @@ __device__ __forceinline__ uint2 tile_row4(bf16x8 f, int h, s16x4 eye) {
   return pack_bf16x4(mfma16(frag_half(f, h), eye, f32x4{0.f, 0.f, 0.f, 0.f}));
 }
 
+// Regrouping of two 8-byte pieces across the four 16-lane rows (lg) of a
+// wavefront.  X and Y hold, per lane (lr, lg), 4 columns 4lg..4lg+3 of row lr
+// of tiles A and B (the tile_row4 layout).  rows8_from_pair returns, per lane,
+// 8 contiguous columns 8(lg&1)..+7 of row lr of tile A (lg < 2) or B (lg >= 2):
+// one 16-byte piece, so 64 lanes cover 32 rows x 16 columns with 16-byte
+// accesses (half the memory instructions of 8-byte pieces).  Swapping the
+// upper lanes 32..63 of X with the lower 32 of Y and then the odd 16-lane rows
+// of the first result with the even rows of the second moves each piece to
+// its lane; pair_from_rows8 is the inverse (the same swaps in reverse order).
+__device__ __forceinline__ u32x4 rows8_from_pair(uint2 X, uint2 Y) {
+  const auto a = __builtin_amdgcn_permlane32_swap(X.x, Y.x, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(X.y, Y.y, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(b[0], b[1], false, false);
+  return u32x4{c[0], d[0], c[1], d[1]};
+}
+__device__ __forceinline__ void pair_from_rows8(u32x4 r, uint2 &X, uint2 &Y) {
+  const auto c = __builtin_amdgcn_permlane16_swap(r[0], r[2], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(r[1], r[3], false, false);
+  const auto a = __builtin_amdgcn_permlane32_swap(c[0], c[1], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(d[0], d[1], false, false);
+  X = make_uint2(a[0], b[0]);
+  Y = make_uint2(a[1], b[1]);
+}
+
 // Two stacked accumulator tiles -> one kwalk-ordered B fragment.
 __device__ __forceinline__ bf16x8 acc_pair_to_b(f32x4 hi, f32x4 lo) {
   bf16x8 r;
@@ -163,6 +188,9 @@ struct RowSink {
   __device__ __forceinline__ void put(uint32_t byte_off, bf16x8 x) const {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, (int)byte_off, 0, 0);
   }
+  __device__ __forceinline__ void put16(uint32_t byte_off, u32x4 x) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, (int)byte_off, 0, 0);
+  }
   __device__ __forceinline__ void put8(uint32_t byte_off, uint2 x) const {
     typedef int i32x2 __attribute__((ext_vector_type(2)));
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, (int)byte_off, 0, 0);
@@ -176,6 +204,9 @@ struct RowSource {
   __amdgpu_buffer_rsrc_t r;
   __device__ __forceinline__ RowSource(const void *base, uint32_t bytes)
       : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ u32x4 get16(uint32_t byte_off) const {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+  }
   __device__ __forceinline__ uint2 get8(uint32_t byte_off) const {
     typedef int i32x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0));

@@ -451,8 +451,8 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
 // accumulator tiles; per chunk a slice costs 48 MFMAs (Vn, o and the state
 // update).  Operands are fetched one chunk ahead, each register refilled right
 // after its last use.  Outputs (o, and with SAVE the state and Vn tapes) leave
-// through tile transposes on the matrix cores as 8-byte row pieces, so the
-// step has no LDS round trip and no branch.  The gate factors gamma arrive as
+// through tile transposes on the matrix cores, regrouped across lanes into
+// 16-byte row pieces, so the step has no LDS round trip and no branch.  The gate factors gamma arrive as
 // two floats per lane and are spread to the accumulator rows through LDS.
 // ---------------------------------------------------------------------------
 // Slices per wavefront.  Two slices halve the operand bytes each column pays,
@@ -529,13 +529,16 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) Sb[s][kt] = acc_pair_to_b(S[s][2 * kt], S[s][2 * kt + 1]);
+    // 16-byte output pieces: lane (lr, lg) carries row 16 (lg >> 1) + lr of a 32-row
+    // block, columns 8 (lg & 1)..+7 of its slice
+    const int prow = 16 * (lg >> 1) + lr, pcol = 8 * (lg & 1);
     if (SAVE) {  // state tape: block [key][16] of each slice
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        u16 *st = w.S + u * (HD * HD) + (sl0 + s) * (HD * 16) + lr * 16 + 4 * lg;
+        u16 *st = w.S + u * (HD * HD) + (sl0 + s) * (HD * 16) + prow * 16 + pcol;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-          *reinterpret_cast<uint2 *>(st + mt * 256) = tile_row4(Sb[s][mt >> 1], mt & 1, eye);
+        for (int kt = 0; kt < 4; ++kt)
+          *reinterpret_cast<u32x4 *>(st + kt * 512) = rows8_from_pair(tile_row4(Sb[s][kt], 0, eye), tile_row4(Sb[s][kt], 1, eye));
       }
     }
 
@@ -578,20 +581,21 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
     {  // o rows of this chunk; rows past len fall outside the sink's range
       const RowSink ob(o + ((size_t)row0 * Hv + j) * HD + 16 * sl0, (uint32_t)len * row_bytes);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 Ob0 = acc_pair_to_b(Oc[s][0], Oc[s][1]), Ob1 = acc_pair_to_b(Oc[s][2], Oc[s][3]);
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          ob.put8((uint32_t)(16 * mt + lr) * row_bytes + 32 * s + 8 * lg, tile_row4(mt < 2 ? Ob0 : Ob1, mt & 1, eye));
-      }
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 Ob = acc_pair_to_b(Oc[s][2 * h], Oc[s][2 * h + 1]);
+          ob.put16((uint32_t)(32 * h + prow) * row_bytes + 32 * s + 2 * pcol,
+                   rows8_from_pair(tile_row4(Ob, 0, eye), tile_row4(Ob, 1, eye)));
+        }
     }
     if (SAVE) {  // Vn tape: block [row][16] of each slice
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        u16 *vt = w.Vn + u * (CH * HD) + (sl0 + s) * (CH * 16) + lr * 16 + 4 * lg;
+        u16 *vt = w.Vn + u * (CH * HD) + (sl0 + s) * (CH * 16) + prow * 16 + pcol;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          *reinterpret_cast<uint2 *>(vt + mt * 256) = tile_row4(Vb[s][mt >> 1], mt & 1, eye);
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<u32x4 *>(vt + h * 512) = rows8_from_pair(tile_row4(Vb[s][h], 0, eye), tile_row4(Vb[s][h], 1, eye));
       }
     }
 
