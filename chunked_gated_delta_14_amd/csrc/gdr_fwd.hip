@@ -119,7 +119,7 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const Ch
 
 template <bool SCALAR>
 __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, int save, int unit,
-                                          const PrepIn &in, PrepIn &next, unsigned char *smem) {
+                                          const PrepIn &in, PrepIn &next, int next_unit, unsigned char *smem) {
   // heads vary fastest over the units, so the workgroups working together
   // read whole token rows of q, k, v and g
   const int chunk = unit / p.Hv, j = unit % p.Hv;
@@ -226,6 +226,10 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     }
   }
   lds_barrier();
+  // The next unit's inputs: issued once this unit's are in LDS and the previous unit's
+  // final stores have drained (loads issued behind a burst of stores wait for it), and
+  // waited for at the end of this unit.
+  if (next_unit < p.NC * p.Hv) prep_load<SCALAR>(next, p, tb, next_unit, tid);
 
   // ---- 2. gated products.  Wavefront w: column block J = w >> 1 and row
   // blocks I in {2kt, 2kt+1}, kt = w & 1; the two accumulator tiles of M are
@@ -276,7 +280,6 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     if (save) w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane] = as_u4(acc_pair_to_b(ms[0], ms[1]));
   }
   lds_barrier();
-  settle(next);  // the next unit's inputs, fetched at the start of this one
 
   // ---- 3. column-form operands (over the step-1 space), then T ----
 #pragma unroll
@@ -423,11 +426,12 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     for (int ii = 0; ii < 8; ++ii) tv[ii] = (__bf16)sT[(c8 + ii) * SP + r];
     w.Tt[u * FRAG_64x64_U4 + tid] = as_u4(tv);
   }
+  settle(next);  // no path into the next unit carries an outstanding load
 }
 
 // Persistent: each workgroup walks the units blockIdx.x, blockIdx.x + gridDim.x,
 // ... and fetches the next unit's inputs into registers while it works on
-// the current one.
+// the current one (from the end of the current unit's first phase on).
 template <bool SCALAR>
 __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -439,8 +443,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
   settle(nxt);  // so that no path into the loop carries an outstanding load
   for (; unit < total; unit += gridDim.x) {
     const PrepIn cur = nxt;
-    if (unit + (int)gridDim.x < total) prep_load<SCALAR>(nxt, p, tb, unit + gridDim.x, tid);
-    prep_unit<SCALAR>(p, w, save, unit, cur, nxt, smem);
+    prep_unit<SCALAR>(p, w, save, unit, cur, nxt, unit + gridDim.x, smem);
     lds_barrier();  // LDS is reused by the next unit
   }
 }
