@@ -16,7 +16,7 @@ import numpy as np
 from . import _build
 
 __all__ = [
-    "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GdrError", "lib", "plan_chunks", "workspace_bytes",
+    "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GdrError", "lib", "plan_chunks", "workspace_bytes",
     "Problem", "kda_fwd", "kda_bwd", "gdn_fwd", "gdn_bwd", "kda_ckpt", "gdn_ckpt", "status_string",
     "check_device", "timing_enable", "timing_read", "EXPORTED_SYMBOLS",
 ]
@@ -24,6 +24,7 @@ __all__ = [
 GDR_KDA = 0
 GDR_GDN = 1
 GDR_FWD_SAVE = 1
+GDR_FWD_SKIP_OUTPUT = 2  # forward without the output (o may be None): the recompute of a ckpt step
 
 EXPORTED_SYMBOLS = (
     "gdr_plan_chunks", "gdr_workspace_bytes", "gdr_kda_fwd", "gdr_kda_bwd", "gdr_gdn_fwd",

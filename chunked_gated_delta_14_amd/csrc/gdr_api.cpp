@@ -14,6 +14,27 @@
 
 #include "gdr_kernels.h"
 
+namespace gdr {
+hipError_t set_dynamic_lds_once(const void *kernel, int bytes) {
+  struct Entry {
+    int dev;
+    const void *fn;
+    int bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry &x : done)
+    if (x.dev == dev && x.fn == kernel && x.bytes >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.push_back(Entry{dev, kernel, bytes});
+  return e;
+}
+}  // namespace gdr
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -241,19 +262,19 @@ int32_t fwd_impl(int32_t variant, const gdr_problem *p, uint16_t *o, float *ht, 
                  uint32_t flags, void *stream) {
   int32_t rc = check_problem(variant, p);
   if (rc) return rc;
-  if (flags & ~GDR_FWD_SAVE) return fail(GDR_ERR_INVALID_ARG, "unknown forward flag");
-  if (p->T > 0 && !o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
-  const bool save = (flags & GDR_FWD_SAVE) != 0;
+  if (flags & ~(GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT)) return fail(GDR_ERR_INVALID_ARG, "unknown forward flag");
+  const bool save = (flags & GDR_FWD_SAVE) != 0, out = (flags & GDR_FWD_SKIP_OUTPUT) == 0;
+  if (p->T > 0 && out && !o) return fail(GDR_ERR_INVALID_ARG, "o is NULL");
   Layout L;
   if ((rc = check_workspace(p, ws, ws_bytes, save, L))) return rc;
   if ((rc = check_device_impl())) return rc;
   const gdr::Problem q = to_internal(p);
   const gdr::Workspace w = bind(L, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = hip_status(timed(0, st, [&] { return gdr::launch_fwd_prep(variant == GDR_GDN, q, w, save, st); }),
+  if ((rc = hip_status(timed(0, st, [&] { return gdr::launch_fwd_prep(variant == GDR_GDN, q, w, save, out, st); }),
                        "prep launch")))
     return rc;
-  if ((rc = hip_status(timed(1, st, [&] { return gdr::launch_fwd_walk(q, w, o, ht, save, st); }), "walk launch")))
+  if ((rc = hip_status(timed(1, st, [&] { return gdr::launch_fwd_walk(q, w, out ? o : nullptr, ht, save, out, st); }), "walk launch")))
     return rc;
   g_last_error.clear();
   return GDR_OK;
@@ -294,7 +315,9 @@ int32_t ckpt_impl(int32_t variant, const gdr_problem *p, uint16_t *o, float *ht,
   Layout L;
   if ((rc = check_workspace(p, ws, ws_bytes, true, L))) return rc;
   if ((rc = fwd_impl(variant, p, o, ht, ws, ws_bytes, 0, stream))) return rc;
-  if ((rc = fwd_impl(variant, p, o, nullptr, ws, ws_bytes, GDR_FWD_SAVE, stream))) return rc;
+  // the recompute writes the tapes only: o is already there
+  if ((rc = fwd_impl(variant, p, nullptr, nullptr, ws, ws_bytes, GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT, stream)))
+    return rc;
   return bwd_impl(variant, p, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
 }
 
@@ -348,7 +371,7 @@ int64_t gdr_workspace_bytes(int32_t variant, int32_t T, int32_t N, int32_t n_chu
                             int32_t K, int32_t V, uint32_t flags) {
   const int32_t rc = check_sizes(variant, T, N, n_chunks, H_qk, H_v, K, V);
   if (rc) return -(int64_t)rc;
-  if (flags & ~GDR_FWD_SAVE) return -(int64_t)fail(GDR_ERR_INVALID_ARG, "unknown flag");
+  if (flags & ~(GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT)) return -(int64_t)fail(GDR_ERR_INVALID_ARG, "unknown flag");
   const Layout L = make_layout((int64_t)n_chunks * H_v);
   return (flags & GDR_FWD_SAVE) ? L.full_bytes : L.fwd_bytes;
 }

@@ -1266,11 +1266,11 @@ hipError_t launch_bwd_grad(bool gdn, const Problem &p, const Workspace &w, const
   hipError_t e;
   if (gdn) {
     const int sm = grad_rows_smem_bytes<true>();
-    e = hipFuncSetAttribute((const void *)bwd_grad_rows_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
+    e = set_dynamic_lds_once((const void *)bwd_grad_rows_kernel<true>, sm);
     if (e != hipSuccess) return e;
     bwd_grad_rows_kernel<true><<<grid, block, sm, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
   } else {
-    e = hipFuncSetAttribute((const void *)bwd_grad_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, G_SMEM);
+    e = set_dynamic_lds_once((const void *)bwd_grad_kernel<false>, G_SMEM);
     if (e != hipSuccess) return e;
     bwd_grad_kernel<false><<<grid, block, G_SMEM, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
   }

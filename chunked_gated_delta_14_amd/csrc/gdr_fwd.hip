@@ -118,7 +118,7 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const Ch
 }
 
 template <bool SCALAR>
-__device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, int save, int unit,
+__device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, int save, int out, int unit,
                                           const PrepIn &in, PrepIn &next, int next_unit, unsigned char *smem) {
   // heads vary fastest over the units, so the workgroups working together
   // read whole token rows of q, k, v and g
@@ -349,8 +349,9 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     lds_barrier();
   }
 
-  // ---- 5. P^T = scale (q exp G)^T - scale W^T M^T,  Oi = scale M U ----
-  {
+  // ---- 5. P^T = scale (q exp G)^T - scale W^T M^T,  Oi = scale M U (the output's
+  // operands; a recompute that skips the output skips them) ----
+  if (out) {
     bf16x8 aM[2][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -433,7 +434,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 // ... and fetches the next unit's inputs into registers while it works on
 // the current one (from the end of the current unit's first phase on).
 template <bool SCALAR>
-__global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save) {
+__global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save, int out) {
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
   const int total = p.NC * p.Hv, tid = threadIdx.x;
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
   settle(nxt);  // so that no path into the loop carries an outstanding load
   for (; unit < total; unit += gridDim.x) {
     const PrepIn cur = nxt;
-    prep_unit<SCALAR>(p, w, save, unit, cur, nxt, unit + gridDim.x, smem);
+    prep_unit<SCALAR>(p, w, save, out, unit, cur, nxt, unit + gridDim.x, smem);
     lds_barrier();  // LDS is reused by the next unit
   }
 }
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
 // a few long documents.
 constexpr int WALK_NS = 1;
 
-template <int NS, bool SAVE>
+template <int NS, bool SAVE, bool OUT>
 __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u16 *o, float *ht) {
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
   int chain, grp;
@@ -504,12 +505,14 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
       for (int mt = 0; mt < 4; ++mt) {
         const size_t off = u * ACC_64x128_U16 + (((sl0 + s) * 4 + mt) * 64 + lane) * 4;
         Ua[s][mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
-        Oa[s][mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
+        if (OUT) Oa[s][mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
       }
 #pragma unroll
     for (int t = 0; t < 16; ++t) Wf[t >> 2][t & 3] = as_bf16x8(w.WfN[u * FRAG_64x128_U4 + t * 64 + lane]);
+    if (OUT) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) Pf[t >> 2][t & 3] = as_bf16x8(w.Pf[u * FRAG_64x128_U4 + t * 64 + lane]);
+      for (int t = 0; t < 16; ++t) Pf[t >> 2][t & 3] = as_bf16x8(w.Pf[u * FRAG_64x128_U4 + t * 64 + lane]);
+    }
 #pragma unroll
     for (int t = 0; t < 16; ++t) KT[t >> 1][t & 1] = as_bf16x8(w.KbT[u * FRAG_64x128_U4 + t * 64 + lane]);
   }
@@ -552,11 +555,13 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
       for (int mt = 0; mt < 4; ++mt) {
         Vn[s][mt][0] = bf2f(Ua[s][mt].x & 0xffff); Vn[s][mt][1] = bf2f(Ua[s][mt].x >> 16);
         Vn[s][mt][2] = bf2f(Ua[s][mt].y & 0xffff); Vn[s][mt][3] = bf2f(Ua[s][mt].y >> 16);
-        Oc[s][mt][0] = bf2f(Oa[s][mt].x & 0xffff); Oc[s][mt][1] = bf2f(Oa[s][mt].x >> 16);
-        Oc[s][mt][2] = bf2f(Oa[s][mt].y & 0xffff); Oc[s][mt][3] = bf2f(Oa[s][mt].y >> 16);
         const size_t off = un * ACC_64x128_U16 + (((sl0 + s) * 4 + mt) * 64 + lane) * 4;
         Ua[s][mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
-        Oa[s][mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
+        if (OUT) {
+          Oc[s][mt][0] = bf2f(Oa[s][mt].x & 0xffff); Oc[s][mt][1] = bf2f(Oa[s][mt].x >> 16);
+          Oc[s][mt][2] = bf2f(Oa[s][mt].y & 0xffff); Oc[s][mt][3] = bf2f(Oa[s][mt].y >> 16);
+          Oa[s][mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
+        }
       }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -566,14 +571,16 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
         for (int s = 0; s < NS; ++s) Vn[s][mt] = mfma(Wf[mt][kt], Sb[s][kt], Vn[s][mt]);
         Wf[mt][kt] = as_bf16x8(w.WfN[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
       }
+    if (OUT) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) Oc[s][mt] = mfma(Pf[mt][kt], Sb[s][kt], Oc[s][mt]);
-        Pf[mt][kt] = as_bf16x8(w.Pf[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
-      }
+          for (int s = 0; s < NS; ++s) Oc[s][mt] = mfma(Pf[mt][kt], Sb[s][kt], Oc[s][mt]);
+          Pf[mt][kt] = as_bf16x8(w.Pf[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
+        }
+    }
 
     bf16x8 Vb[NS][2];
 #pragma unroll
@@ -581,7 +588,7 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
       Vb[s][0] = acc_pair_to_b(Vn[s][0], Vn[s][1]);
       Vb[s][1] = acc_pair_to_b(Vn[s][2], Vn[s][3]);
     }
-    {  // o rows of this chunk; rows past len fall outside the sink's range
+    if (OUT) {  // o rows of this chunk; rows past len fall outside the sink's range
       const RowSink ob(o + ((size_t)row0 * Hv + j) * HD + 16 * sl0, (uint32_t)len * row_bytes);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -643,24 +650,28 @@ static int compute_units() {
   return cached[dev];
 }
 
-hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, hipStream_t st) {
+hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, bool out, hipStream_t st) {
   if (p.NC == 0) return hipSuccess;
   const int total = p.NC * p.Hv;
   const dim3 grid(total < compute_units() ? total : compute_units()), block(PNT);
   const void *fn = gdn ? (const void *)fwd_prep_kernel<true> : (const void *)fwd_prep_kernel<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
+  hipError_t e = set_dynamic_lds_once(fn, P_SMEM);
   if (e != hipSuccess) return e;
-  if (gdn) fwd_prep_kernel<true><<<grid, block, P_SMEM, st>>>(p, w, save ? 1 : 0);
-  else fwd_prep_kernel<false><<<grid, block, P_SMEM, st>>>(p, w, save ? 1 : 0);
+  if (gdn) fwd_prep_kernel<true><<<grid, block, P_SMEM, st>>>(p, w, save ? 1 : 0, out ? 1 : 0);
+  else fwd_prep_kernel<false><<<grid, block, P_SMEM, st>>>(p, w, save ? 1 : 0, out ? 1 : 0);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, u16 *o, float *ht, bool save, hipStream_t st) {
+hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, u16 *o, float *ht, bool save, bool out,
+                           hipStream_t st) {
   const int chains = p.N * p.Hv;
   if (chains == 0) return hipSuccess;
   constexpr int NS = WALK_NS;
-  if (save) fwd_walk_kernel<NS, true><<<walk_grid(chains, NS), 64, 0, st>>>(p, w, o, ht);
-  else fwd_walk_kernel<NS, false><<<walk_grid(chains, NS), 64, 0, st>>>(p, w, o, ht);
+  const int grid = walk_grid(chains, NS);
+  if (save && out) fwd_walk_kernel<NS, true, true><<<grid, 64, 0, st>>>(p, w, o, ht);
+  else if (save) fwd_walk_kernel<NS, true, false><<<grid, 64, 0, st>>>(p, w, o, ht);
+  else if (out) fwd_walk_kernel<NS, false, true><<<grid, 64, 0, st>>>(p, w, o, ht);
+  else fwd_walk_kernel<NS, false, false><<<grid, 64, 0, st>>>(p, w, o, ht);
   return hipGetLastError();
 }
 

@@ -41,8 +41,13 @@ struct Problem {
   float scale;
 };
 
-hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, hipStream_t st);
-hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, uint16_t *o, float *ht, bool save,
+// Raise a kernel's dynamic-LDS limit, once per (device, kernel, size): the
+// attribute belongs to the function on that device, so later launches
+// (including ones under stream capture) make no runtime call for it.
+hipError_t set_dynamic_lds_once(const void *kernel, int bytes);
+
+hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, bool out, hipStream_t st);
+hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, uint16_t *o, float *ht, bool save, bool out,
                            hipStream_t st);
 hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const uint16_t *dout, const float *dht,
                            float *dh0, hipStream_t st);

@@ -72,6 +72,12 @@ enum gdr_variant { GDR_KDA = 0, GDR_GDN = 1 };
  * Without it the forward writes only o and ht (the first forward of a
  * checkpointed step). */
 #define GDR_FWD_SAVE 1u
+/* Forward without the output: o is neither computed nor written (it may be
+ * NULL) and prep skips the output's operands.  With GDR_FWD_SAVE this is the
+ * recompute of a checkpointed step (PR #8218 section "ckpt": the backward
+ * reuses the recompute's tapes, the output is already known).  ht is still
+ * written when non-NULL. */
+#define GDR_FWD_SKIP_OUTPUT 2u
 
 /* One packed problem.  Lifetime: read during the call that receives it. */
 typedef struct gdr_problem {
@@ -116,8 +122,9 @@ int32_t gdr_plan_chunks(const int32_t *cu_seqlens_host, int32_t N, int32_t *tabl
 int64_t gdr_workspace_bytes(int32_t variant, int32_t T, int32_t N, int32_t n_chunks,
                             int32_t H_qk, int32_t H_v, int32_t K, int32_t V, uint32_t flags);
 
-/* KDA forward.  o: bf16 [T, H_v, V] (written).  ht: fp32 [N, H_v, K, V]
- * final states, or NULL to skip.  flags: 0 or GDR_FWD_SAVE. */
+/* KDA forward.  o: bf16 [T, H_v, V] (written; NULL allowed with
+ * GDR_FWD_SKIP_OUTPUT).  ht: fp32 [N, H_v, K, V] final states, or NULL to
+ * skip.  flags: GDR_FWD_SAVE and/or GDR_FWD_SKIP_OUTPUT. */
 int32_t gdr_kda_fwd(const gdr_problem *p, uint16_t *o, float *ht, void *workspace,
                     int64_t workspace_bytes, uint32_t flags, void *stream);
 
@@ -142,8 +149,9 @@ int32_t gdr_gdn_bwd(const gdr_problem *p, const uint16_t *dout, const float *dht
                     void *workspace, int64_t workspace_bytes, void *stream);
 
 /* The checkpointed training step as one call (PR #8218 "ckpt": forward,
- * recompute and backward): forward without tapes (writes o, ht), forward
- * again with GDR_FWD_SAVE, then the backward.  Arguments as in the fwd and
+ * recompute and backward): forward without tapes (writes o, ht), the
+ * recompute with GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT (tapes only), then the
+ * backward on the recompute's tapes.  Arguments as in the fwd and
  * bwd calls of the variant; the workspace must hold gdr_workspace_bytes(...,
  * GDR_FWD_SAVE). */
 int32_t gdr_kda_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout,

@@ -53,6 +53,80 @@ def test_ckpt_equals_fwd_bwd_bitwise():
         assert torch.equal(a[key], b[key]), key
 
 
+def test_recompute_without_output():
+    """GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT writes the same tapes as GDR_FWD_SAVE and
+    leaves o untouched: the backward after it is bitwise the backward after a full
+    forward."""
+    import chunked_gated_delta_14_amd as gdr
+    from gpu_runner import to_dev
+
+    w = workloads.custom("kda", (170, 64, 33), 2, 2, with_h0=True, seed=8)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    a = run_gdr("kda", inp, dht=inp["dht"])
+    d = to_dev(inp)
+    prob = gdr.Problem(gdr.GDR_KDA, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["h0"])
+    ws = prob.alloc_workspace(gdr.GDR_FWD_SAVE)
+    ws.fill_(0xFF)
+    T, N = prob.T, prob.N
+    sentinel = torch.full((T, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty((N, 2, 128, 128), dtype=torch.float32, device="cuda")
+    gdr.kda_fwd(prob, sentinel, ht, ws, gdr.GDR_FWD_SAVE | gdr.GDR_FWD_SKIP_OUTPUT)
+    gdr.kda_fwd(prob, None, None, ws, gdr.GDR_FWD_SAVE | gdr.GDR_FWD_SKIP_OUTPUT)
+    g = {k: torch.full_like(a[k], float("nan"), device="cuda").to(v.dtype) for k, v in
+         dict(dq=d["q"], dk=d["k"], dv=d["v"], dg=d["g"], dbeta=d["beta"], dh0=ht).items()}
+    gdr.kda_bwd(prob, d["dout"], d["dht"], g["dq"], g["dk"], g["dv"], g["dg"], g["dbeta"], g["dh0"], ws)
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all())
+    assert torch.equal(ht.cpu(), a["ht"])
+    for key in g:
+        assert torch.equal(g[key].float().cpu(), a[key]), key
+
+
+def test_ckpt_graph_replay():
+    """The checkpointed step captured in a HIP graph: three replays, with the
+    program's own eager work and synchronisations between them, each bitwise equal
+    to the eager call."""
+    import chunked_gated_delta_14_amd as gdr
+    from gpu_runner import to_dev
+
+    w = workloads.custom("kda", (150, 90), 2, 2, with_h0=True, seed=9)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    d = to_dev(inp)
+    prob = gdr.Problem(gdr.GDR_KDA, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["h0"])
+    ws = prob.alloc_workspace(gdr.GDR_FWD_SAVE)
+    T, N = prob.T, prob.N
+    bf, f32 = torch.bfloat16, torch.float32
+    outs = dict(o=torch.empty((T, 2, 128), dtype=bf, device="cuda"), ht=torch.empty((N, 2, 128, 128), dtype=f32, device="cuda"),
+                dq=torch.empty((T, 2, 128), dtype=bf, device="cuda"), dk=torch.empty((T, 2, 128), dtype=bf, device="cuda"),
+                dv=torch.empty((T, 2, 128), dtype=bf, device="cuda"), dg=torch.empty((T, 2, 128), dtype=f32, device="cuda"),
+                dbeta=torch.empty((T, 2), dtype=bf, device="cuda"), dh0=torch.empty((N, 2, 128, 128), dtype=f32, device="cuda"))
+
+    def step():
+        gdr.kda_ckpt(prob, outs["o"], outs["ht"], d["dout"], d["dht"], outs["dq"], outs["dk"], outs["dv"],
+                     outs["dg"], outs["dbeta"], outs["dh0"], ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in outs.values():
+            v.fill_(float("nan"))  # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], eager[k]), (rep, k)
+
+
 def test_repeat_bitwise_and_nan_workspace():
     w = workloads.custom("gdn", (100, 180), 1, 3, with_h0=True, seed=4)
     inp = workloads.make_inputs(w, device="cpu", dht=True)

@@ -155,8 +155,22 @@ def test_workspace_checks():
     full = gdr.workspace_bytes(gdr.GDR_KDA, 128, 1, 2, 1, 1, 128, 128, 1)
     rc = L.gdr_kda_bwd(ctypes.byref(p), *([ctypes.c_void_p(4096)] * 8), ctypes.c_void_p(4096), full - 256, None)
     assert rc == 3
-    rc = L.gdr_kda_fwd(ctypes.byref(p), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 1 << 40, 2, None)
+    rc = L.gdr_kda_fwd(ctypes.byref(p), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 1 << 40, 4, None)
     assert rc == 1
+
+
+def test_skip_output_flag_host_checks():
+    """GDR_FWD_SKIP_OUTPUT is a known flag (workspace sizes as without it); o may be
+    NULL only with it.  Only paths that stop before any device call are exercised."""
+    L = gdr.lib()
+    p = _cproblem()
+    for flags in (0, 1):
+        assert gdr.workspace_bytes(gdr.GDR_KDA, 128, 1, 2, 1, 1, 128, 128, flags | gdr.GDR_FWD_SKIP_OUTPUT) == \
+            gdr.workspace_bytes(gdr.GDR_KDA, 128, 1, 2, 1, 1, 128, 128, flags)
+    with pytest.raises(gdr.GdrError):
+        gdr.workspace_bytes(gdr.GDR_KDA, 128, 1, 2, 1, 1, 128, 128, 4)
+    rc = L.gdr_kda_fwd(ctypes.byref(p), None, None, ctypes.c_void_p(4096), 1 << 40, gdr.GDR_FWD_SAVE, None)
+    assert rc == 1 and "o" in L.gdr_last_error().decode()
 
 
 def test_no_cpu_fallback_without_library(monkeypatch, tmp_path):
