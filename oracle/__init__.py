@@ -146,6 +146,72 @@ def backward(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, scale=None, 
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dbeta": dbeta, "dh0": dh0}
 
 
+# ---------------------------------------------------------------------------
+# Input activations (optional, applied before the recurrence)
+#
+# The GDN shapes of PR #8638 (benchmark shapes paragraph) normalise q and k
+# inside the kernel, the inverse norm kept for the backward (its review notes
+# on qk_rstd); PR #8218 (baselines paragraph) names the L2 norm and the beta
+# sigmoid together as in-kernel steps.  No page gives the epsilon, so the
+# plainest reading is
+# taken: q_hat = q * (sum_c q_c^2 + EPS)^(-1/2) with EPS = 1e-6 per (token,
+# head) row, and beta = 1 / (1 + exp(-b)).  The backward is the chain rule
+# through these maps:
+#   d q = rstd * (d q_hat - q_hat * <q_hat, d q_hat>)      (per row)
+#   d b = d beta * beta * (1 - beta)
+# ---------------------------------------------------------------------------
+L2NORM_EPS = 1e-6
+
+
+def l2norm_rows(x):
+    """Rows of x (last axis) scaled to unit L2 norm: returns (x_hat, rstd), fp64."""
+    x = as_f64(x)
+    rstd = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2NORM_EPS)
+    return x * rstd, rstd
+
+
+def l2norm_rows_backward(x_hat, rstd, dx_hat):
+    """Gradient through l2norm_rows, from the normalised rows and their rstd."""
+    dot = np.sum(x_hat * dx_hat, axis=-1, keepdims=True)
+    return rstd * (dx_hat - x_hat * dot)
+
+
+def sigmoid(b):
+    b = as_f64(b)
+    return 1.0 / (1.0 + np.exp(-b))
+
+
+def _activate(q, k, beta, qk_l2norm, beta_sigmoid):
+    q, k, beta = as_f64(q), as_f64(k), as_f64(beta)
+    rq = rk = None
+    if qk_l2norm:
+        q, rq = l2norm_rows(q)
+        k, rk = l2norm_rows(k)
+    if beta_sigmoid:
+        beta = sigmoid(beta)
+    return q, k, beta, rq, rk
+
+
+def forward_act(q, k, v, g, beta, cu_seqlens, h0=None, scale=None, threads=None, qk_l2norm=False,
+                beta_sigmoid=False):
+    """``forward`` with the input activations applied first."""
+    qa, ka, ba, _, _ = _activate(q, k, beta, qk_l2norm, beta_sigmoid)
+    return forward(qa, ka, v, g, ba, cu_seqlens, h0, scale, threads)
+
+
+def backward_act(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, scale=None, threads=None,
+                 qk_l2norm=False, beta_sigmoid=False):
+    """``backward`` with respect to the raw inputs of ``forward_act``."""
+    qa, ka, ba, rq, rk = _activate(q, k, beta, qk_l2norm, beta_sigmoid)
+    grads = backward(qa, ka, v, g, ba, cu_seqlens, dout, h0, dht, scale, threads)
+    if qk_l2norm:
+        grads["dq"] = l2norm_rows_backward(qa, rq, grads["dq"])
+        grads["dk"] = l2norm_rows_backward(ka, rk, grads["dk"])
+    if beta_sigmoid:
+        grads["dbeta"] = grads["dbeta"] * ba * (1.0 - ba)
+    return grads
+
+
 def loss(o, ht, dout, dht=None):
     """The scalar whose gradient ``backward`` returns: sum(o*dout) + sum(ht*dht)."""
     val = float(np.sum(o * as_f64(dout)))

@@ -377,3 +377,66 @@ def test_oracle_rejects_bad_problem():
     p = random_problem(rng, [10, 10], 2, 3, 8, 8, per_channel=False)  # 3 % 2 != 0
     with pytest.raises(ValueError):
         _fwd(p)
+
+
+# --------------------------------------------------------------------------
+# Input activations: in-kernel q/k L2 norm and beta sigmoid
+# --------------------------------------------------------------------------
+def _loss_act(p, **act):
+    o, ht = oracle.forward_act(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu"], p.get("h0"), threads=1, **act)
+    return oracle.loss(o, ht, p["dout"], p.get("dht"))
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn"])
+def test_activations_finite_differences(variant):
+    """d/dq, d/dk, d/dbeta through the L2 norm and the sigmoid, entry by entry."""
+    rng = np.random.default_rng(31 if variant == "kda" else 32)
+    if variant == "kda":
+        p = random_problem(rng, [19, 30], 1, 1, 8, 8, per_channel=True)
+    else:
+        p = random_problem(rng, [19, 30], 1, 3, 8, 8, per_channel=False)
+    p["beta"] = rng.normal(size=p["beta"].shape)  # logits
+    act = dict(qk_l2norm=True, beta_sigmoid=True)
+    grads = oracle.backward_act(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu"], p["dout"], p.get("h0"),
+                                p.get("dht"), threads=1, **act)
+    eps = 1e-6
+    for name, gname in {"q": "dq", "k": "dk", "beta": "dbeta"}.items():
+        x = p[name]
+        flat = x.reshape(-1)
+        fd = np.zeros_like(x)
+        for idx in range(flat.size):
+            keep = flat[idx]
+            flat[idx] = keep + eps
+            lp = _loss_act(p, **act)
+            flat[idx] = keep - eps
+            lm = _loss_act(p, **act)
+            flat[idx] = keep
+            fd.reshape(-1)[idx] = (lp - lm) / (2 * eps)
+        an = grads[gname]
+        assert np.abs(an - fd).max() <= 1e-6 * max(1.0, np.abs(an).max()), name
+
+
+def test_l2norm_scale_invariance_and_orthogonal_gradient():
+    """q -> c q (c > 0) leaves the normalised forward unchanged (up to the epsilon),
+    and each row's gradient is orthogonal to the row: sum_c dq_c q_c equals
+    <q_hat, dq_hat> EPS / (|q|^2 + EPS), which is zero but for the epsilon."""
+    rng = np.random.default_rng(33)
+    p = random_problem(rng, [37, 20], 2, 2, 16, 16, per_channel=True)
+    p["q"] *= 3.0  # rows well away from zero norm
+    p["k"] *= 3.0
+    o1, h1 = oracle.forward_act(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu"], p.get("h0"), qk_l2norm=True)
+    o2, h2 = oracle.forward_act(2.5 * p["q"], 0.4 * p["k"], p["v"], p["g"], p["beta"], p["cu"], p.get("h0"),
+                                qk_l2norm=True)
+    assert np.abs(o1 - o2).max() <= 1e-6 * np.abs(o1).max()
+    assert np.abs(h1 - h2).max() <= 1e-6 * np.abs(h1).max()
+    gr = oracle.backward_act(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu"], p["dout"], p.get("h0"),
+                             p.get("dht"), qk_l2norm=True)
+    for x, d in ((p["q"], gr["dq"]), (p["k"], gr["dk"])):
+        radial = np.sum(x * d, axis=-1)
+        assert np.abs(radial).max() <= 1e-6 * np.abs(d).max() * np.abs(x).max() * x.shape[-1]
+    # unit rows pass through the norm unchanged (to the epsilon)
+    qu = p["q"] / np.linalg.norm(p["q"], axis=-1, keepdims=True)
+    ku = p["k"] / np.linalg.norm(p["k"], axis=-1, keepdims=True)
+    oa, _ = oracle.forward_act(qu, ku, p["v"], p["g"], p["beta"], p["cu"], p.get("h0"), qk_l2norm=True)
+    ob, _ = oracle.forward(qu, ku, p["v"], p["g"], p["beta"], p["cu"], p.get("h0"))
+    assert np.abs(oa - ob).max() <= 1e-5 * np.abs(ob).max()
