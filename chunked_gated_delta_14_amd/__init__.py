@@ -16,7 +16,7 @@ import numpy as np
 from . import _build
 
 __all__ = [
-    "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GdrError", "lib", "plan_chunks", "workspace_bytes",
+    "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GDR_IN_QK_L2NORM", "GDR_IN_BETA_SIGMOID", "GdrError", "lib", "plan_chunks", "workspace_bytes",
     "Problem", "kda_fwd", "kda_bwd", "gdn_fwd", "gdn_bwd", "kda_ckpt", "gdn_ckpt", "status_string",
     "check_device", "timing_enable", "timing_read", "EXPORTED_SYMBOLS",
 ]
@@ -25,6 +25,8 @@ GDR_KDA = 0
 GDR_GDN = 1
 GDR_FWD_SAVE = 1
 GDR_FWD_SKIP_OUTPUT = 2  # forward without the output (o may be None): the recompute of a ckpt step
+GDR_IN_QK_L2NORM = 1     # Problem input flag: q, k rows scaled to unit L2 norm inside the kernels
+GDR_IN_BETA_SIGMOID = 2  # Problem input flag: beta holds logits, sigmoid applied inside the kernels
 
 EXPORTED_SYMBOLS = (
     "gdr_plan_chunks", "gdr_workspace_bytes", "gdr_kda_fwd", "gdr_kda_bwd", "gdr_gdn_fwd",
@@ -46,7 +48,7 @@ class _CProblem(ctypes.Structure):
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("chunk_table", ctypes.c_void_p), ("n_chunks", ctypes.c_int32), ("h0", ctypes.c_void_p),
-        ("scale", ctypes.c_float),
+        ("scale", ctypes.c_float), ("input_flags", ctypes.c_uint32),
     ]
 
 
@@ -167,9 +169,10 @@ class Problem:
     q, k: bf16 [T, H_qk, 128]; v: bf16 [T, H_v, 128]; g: fp32 [T, H_v, 128] (KDA)
     or [T, H_v] (GDN); beta: bf16 [T, H_v] (KDA) or fp32 [T, H_v] (GDN);
     cu_seqlens: host sequence or tensor of N+1 ints; h0: fp32 [N, H_v, 128, 128] or None.
+    input_flags: GDR_IN_QK_L2NORM and/or GDR_IN_BETA_SIGMOID (activations applied in the kernels).
     """
 
-    def __init__(self, variant, q, k, v, g, beta, cu_seqlens, h0=None, scale=None):
+    def __init__(self, variant, q, k, v, g, beta, cu_seqlens, h0=None, scale=None, input_flags=0):
         import torch
 
         self.variant = variant
@@ -190,7 +193,8 @@ class Problem:
         self._c = _CProblem(self.T, self.N, self.H_qk, self.H_v, self.K, self.V,
                             q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                             self.cu.data_ptr(), self.table.data_ptr(), nc,
-                            h0.data_ptr() if h0 is not None else None, self.scale)
+                            h0.data_ptr() if h0 is not None else None, self.scale, int(input_flags))
+        self.input_flags = int(input_flags)
 
     def workspace_bytes(self, flags=GDR_FWD_SAVE) -> int:
         return workspace_bytes(self.variant, self.T, self.N, self.n_chunks, self.H_qk, self.H_v,

@@ -171,6 +171,8 @@ int32_t check_problem(int32_t variant, const gdr_problem *p) {
   if (p->N > 0 && (!p->cu_seqlens || !p->chunk_table))
     return fail(GDR_ERR_INVALID_ARG, "cu_seqlens and chunk_table must be non-NULL");
   if (!(p->scale == p->scale)) return fail(GDR_ERR_INVALID_ARG, "scale is NaN");
+  if (p->input_flags & ~(GDR_IN_QK_L2NORM | GDR_IN_BETA_SIGMOID))
+    return fail(GDR_ERR_INVALID_ARG, "unknown input flag");
   return GDR_OK;
 }
 
@@ -201,6 +203,7 @@ gdr::Problem to_internal(const gdr_problem *p) {
   q.table = p->chunk_table;
   q.h0 = p->h0;
   q.scale = p->scale;
+  q.inflags = (int)p->input_flags;
   return q;
 }
 

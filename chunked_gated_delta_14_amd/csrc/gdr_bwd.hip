@@ -226,7 +226,8 @@ constexpr int G_TT = G_Y + CH * KP * 2;     // T^T bf16 [64][MP]             (Y 
 constexpr int G_B = G_TT + CH * MP * 2;     // beta [64]
 constexpr int G_DB = G_B + 64 * 4;          // dbeta partial sums [20][64], added in a fixed order
 constexpr int G_RS = G_DB + 20 * 64 * 4;    // GDN: dG row sums per wavefront [8][64]
-constexpr int G_SMEM = G_RS + 8 * 64 * 4;
+constexpr int G_NRM = G_RS + 8 * 64 * 4;     // q, k row norms [2][64], then row dots [64][2][8]
+constexpr int G_SMEM = G_NRM + (128 + 64 * 16) * 4;
 static_assert(G_DAT + CH * MP * 2 <= G_B, "grad LDS map");
 
 
@@ -304,6 +305,63 @@ __device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, s
   }
 }
 
+// q and k rows of a chunk into the transposed LDS tiles, as load_rows_transposed
+// (threads 0..255: q, 256..511: k).  With IN_QK_L2NORM every row is first scaled
+// to unit L2 norm, x (sum x^2 + eps)^(-1/2), the 16 partial sums of squares of a
+// row (one per 8-channel group) added in a fixed order through sPart (2 x 64 x 16
+// floats of scratch), and the inverse norms kept in sRstd [2][64] for the
+// backward through the norm.
+__device__ __forceinline__ void load_qk_rows(u16 *sQT, u16 *sKT, const Problem &p, int start, int iqk, int len,
+                                             int tid, float *sPart, float *sRstd) {
+  const int isk = tid >> 8, b = tid & 255;
+  const u16 *src = (isk ? p.k : p.q) + ((size_t)start * p.Hqk + iqk) * HD;
+  const size_t ld = (size_t)p.Hqk * HD;
+  if (!(p.inflags & IN_QK_L2NORM)) {
+    load_rows_transposed(isk ? sKT : sQT, src, ld, len, b);
+    return;
+  }
+  const int r0 = 4 * (b >> 4), c0 = 8 * (b & 15);
+  float x[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 raw = r0 + i < len ? *reinterpret_cast<const uint4 *>(src + (size_t)(r0 + i) * ld + c0)
+                                   : make_uint4(0, 0, 0, 0);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[i][e] = bf2f((u16)((e & 1) ? (wd[e >> 1] >> 16) : (wd[e >> 1] & 0xffffu)));
+      ss += x[i][e] * x[i][e];
+    }
+    sPart[(isk * 64 + r0 + i) * 16 + (b & 15)] = ss;
+  }
+  lds_barrier();
+  u16 *dst = isk ? sKT : sQT;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 *pp = reinterpret_cast<const float4 *>(sPart + (isk * 64 + r0 + i) * 16);
+    float t = 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 v4 = pp[q4];
+      t += v4.x; t += v4.y; t += v4.z; t += v4.w;
+    }
+    const float rs = rsqrtf(t + L2NORM_EPS);
+    if ((b & 15) == 0) sRstd[isk * 64 + r0 + i] = rs;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[i][e] *= rs;
+  }
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) {
+    uint2 pk;
+    pk.x = (uint32_t)f2bf(x[0][cc]) | ((uint32_t)f2bf(x[1][cc]) << 16);
+    pk.y = (uint32_t)f2bf(x[2][cc]) | ((uint32_t)f2bf(x[3][cc]) << 16);
+    *reinterpret_cast<uint2 *>(dst + (c0 + cc) * QTP + r0) = pk;
+  }
+}
+
+__device__ __forceinline__ float sigmoidf_(float b) { return 1.f / (1.f + __expf(-b)); }
+
 template <bool SCALAR>
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
@@ -332,12 +390,9 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
   float *sRS = reinterpret_cast<float *>(smem + G_RS);
   const GateT<SCALAR> G{sG};
 
-  {
-    const int tid = threadIdx.x;
-    const size_t ldqk = (size_t)p.Hqk * HD;
-    if (tid < 256) load_rows_transposed(sQT, p.q + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid);
-    else load_rows_transposed(sKT, p.k + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid - 256);
-  }
+  float *sNrm = reinterpret_cast<float *>(smem + G_NRM);
+  // (the dout stage is free until the first iteration's loads: scratch of the row norms)
+  load_qk_rows(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(smem + G_DO), sNrm);
 
   f32x4 dqA[4], dkA[4];  // [row block I]: rows 16I + 4lg + jj, column 16w + lr
 #pragma unroll
@@ -402,7 +457,11 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       }
     }
     // ---- beta, cleared sums, the cumulative gate ----
-    if (tid < 64) sB[tid] = tid < len ? (SCALAR ? __uint_as_float(braw) : bf2f((u16)braw)) : 0.f;
+    if (tid < 64) {
+      float b = SCALAR ? __uint_as_float(braw) : bf2f((u16)braw);
+      if (p.inflags & IN_BETA_SIGMOID) b = sigmoidf_(b);
+      sB[tid] = tid < len ? b : 0.f;
+    }
     if (tid < 256) sDB[16 * 64 + tid] = 0.f;  // E-term slots (not every row block writes every slot)
     *reinterpret_cast<u32x4 *>(sTT + (tid >> 3) * MP + 8 * (tid & 7)) = stT;
     if constexpr (SCALAR) {
@@ -762,6 +821,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       float x = 0.f;
 #pragma unroll
       for (int k = 0; k < 20; ++k) x += sDB[k * 64 + tid];
+      if (p.inflags & IN_BETA_SIGMOID) x *= sB[tid] * (1.f - sB[tid]);  // to the logit
       const size_t e = (size_t)(start + tid) * Hv + j;
       if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = x;
       else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
@@ -791,6 +851,31 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
   {
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (p.inflags & IN_QK_L2NORM) {  // back through the norm: d x = rstd (d x_hat - x_hat <x_hat, d x_hat>)
+      const int c = 16 * wave + lr;
+      float *sDot = sNrm + 128;  // [row][q, k][wavefront]
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 16 * I + 4 * lg + jj;
+          const float pq = red16(bf2f(sQT[c * QTP + r]) * dqA[I][jj]);
+          const float pk = red16(bf2f(sKT[c * QTP + r]) * dkA[I][jj]);
+          if (lr == 0) { sDot[(r * 2) * 8 + wave] = pq; sDot[(r * 2 + 1) * 8 + wave] = pk; }
+        }
+      lds_barrier();
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 16 * I + 4 * lg + jj;
+          float dotq = 0.f, dotk = 0.f;
+#pragma unroll
+          for (int v8 = 0; v8 < 8; ++v8) { dotq += sDot[(r * 2) * 8 + v8]; dotk += sDot[(r * 2 + 1) * 8 + v8]; }
+          dqA[I][jj] = sNrm[r] * (dqA[I][jj] - bf2f(sQT[c * QTP + r]) * dotq);
+          dkA[I][jj] = sNrm[64 + r] * (dkA[I][jj] - bf2f(sKT[c * QTP + r]) * dotk);
+        }
+    }
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -818,6 +903,7 @@ constexpr int grad_rows_smem_bytes() {
          + CH * KP * 2                      // sY
          + 4 * CH * MP * 2                  // sDM, sDA, sDMT, sDAT
          + (64 + 64 + 128 + 128 + 512) * 4  // sB, sDB, sRed, sDgam, sBT
+         + (128 + 64 * 4) * 4               // q, k row norms [2][64], row dots [64][2][2]
          + (SCALAR ? 64 * 4 : HD * GTP * 4);  // sG
 }
 
@@ -854,14 +940,11 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
   float *sDgam = sRed + 128;
   float *sBT = sDgam + 128;  // [4][128] row-block totals of the gate gradient
   float *sG = sBT + 512;
+  float *sNrm = sG + (SCALAR ? 64 : HD * GTP);  // q, k row norms [2][64], then row dots [64][2][2]
   const GateT<SCALAR> G{sG};
 
-  {
-    const int tid = threadIdx.x;
-    const size_t ldqk = (size_t)p.Hqk * HD;
-    if (tid < 256) load_rows_transposed(sQT, p.q + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid);
-    else load_rows_transposed(sKT, p.k + ((size_t)start * p.Hqk + iqk) * HD, ldqk, len, tid - 256);
-  }
+  // (the Y stage is free until the first iteration: scratch of the row norms)
+  load_qk_rows(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(sY), sNrm);
 
   f32x4 dqA[4], dkA[4];
 #pragma unroll
@@ -886,6 +969,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
       if (tid < len) {
         const size_t e = (size_t)(start + tid) * Hv + j;
         b = SCALAR ? reinterpret_cast<const float *>(p.beta)[e] : bf2f(reinterpret_cast<const u16 *>(p.beta)[e]);
+        if (p.inflags & IN_BETA_SIGMOID) b = sigmoidf_(b);
       }
       sB[tid] = b;
       sDB[tid] = 0.f;
@@ -1168,8 +1252,10 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
     lds_barrier();  // also: sRed and sDgam complete
     if (tid < 64 && tid < len) {
       const size_t e = (size_t)(start + tid) * Hv + j;
-      if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = sDB[tid];
-      else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(sDB[tid]);
+      float x = sDB[tid];
+      if (p.inflags & IN_BETA_SIGMOID) x *= sB[tid] * (1.f - sB[tid]);  // to the logit
+      if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = x;
+      else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
     }
 
     // ---- gate epilogue: dg = in-chunk reverse cumulative sum of dG ----
@@ -1236,6 +1322,36 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
   {
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), mt = wave & 3, ch = wave >> 2;
+    if (p.inflags & IN_QK_L2NORM) {  // back through the norm: d x = rstd (d x_hat - x_hat <x_hat, d x_hat>)
+      float *sDot = sNrm + 128;  // [row][q, k][column half]
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * mt + 4 * lg + jj;
+        float pq = 0.f, pk = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int c = 16 * (4 * ch + t) + lr;
+          pq += bf2f(sQT[c * QTP + r]) * dqA[t][jj];
+          pk += bf2f(sKT[c * QTP + r]) * dkA[t][jj];
+        }
+        pq = red16(pq);
+        pk = red16(pk);
+        if (lr == 0) { sDot[(r * 2) * 2 + ch] = pq; sDot[(r * 2 + 1) * 2 + ch] = pk; }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * mt + 4 * lg + jj;
+        const float dotq = sDot[(r * 2) * 2] + sDot[(r * 2) * 2 + 1];
+        const float dotk = sDot[(r * 2 + 1) * 2] + sDot[(r * 2 + 1) * 2 + 1];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int c = 16 * (4 * ch + t) + lr;
+          dqA[t][jj] = sNrm[r] * (dqA[t][jj] - bf2f(sQT[c * QTP + r]) * dotq);
+          dkA[t][jj] = sNrm[64 + r] * (dkA[t][jj] - bf2f(sKT[c * QTP + r]) * dotk);
+        }
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll

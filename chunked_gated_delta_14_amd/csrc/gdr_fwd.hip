@@ -117,7 +117,7 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const Ch
   }
 }
 
-template <bool SCALAR>
+template <bool SCALAR, bool ACT>
 __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, int save, int out, int unit,
                                           const PrepIn &in, PrepIn &next, int next_unit, unsigned char *smem) {
   // heads vary fastest over the units, so the workgroups working together
@@ -156,7 +156,42 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     const bf16x8 *kx = in.k, *qx = in.q, *vx = in.v;
     float bt[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) bt[h] = SCALAR ? __uint_as_float(in.b[h]) : bf2f((u16)in.b[h]);
+    for (int h = 0; h < 2; ++h) {
+      bt[h] = SCALAR ? __uint_as_float(in.b[h]) : bf2f((u16)in.b[h]);
+      if (ACT && (p.inflags & IN_BETA_SIGMOID)) bt[h] = rp + h < len ? 1.f / (1.f + __expf(-bt[h])) : 0.f;
+    }
+    // q, k rows to unit L2 norm (optional): the 16 channel octets' partial sums of
+    // squares meet in LDS (the T tile is free until step 3) and are added in a fixed order
+    float rq[2] = {1.f, 1.f}, rk[2] = {1.f, 1.f};
+    if (ACT && (p.inflags & IN_QK_L2NORM)) {
+      float *sPart = sT;  // [q, k][row][octet]
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const float a = (float)qx[h][ii], c = (float)kx[h][ii];
+          sq += a * a;
+          sk += c * c;
+        }
+        sPart[(rp + h) * 16 + o] = sq;
+        sPart[(64 + rp + h) * 16 + o] = sk;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float tq = 0.f, tk = 0.f;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 a = reinterpret_cast<const float4 *>(sPart + (rp + h) * 16)[q4];
+          const float4 c = reinterpret_cast<const float4 *>(sPart + (64 + rp + h) * 16)[q4];
+          tq += a.x; tq += a.y; tq += a.z; tq += a.w;
+          tk += c.x; tk += c.y; tk += c.z; tk += c.w;
+        }
+        rq[h] = rsqrtf(tq + L2NORM_EPS);
+        rk[h] = rsqrtf(tk + L2NORM_EPS);
+      }
+    }
     float gx[2][NG];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -208,7 +243,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
       for (int ii = 0; ii < 8; ++ii) {
         const int ic = SCALAR ? 0 : ii;
         const float F = __expf(G[h][ic] - go[ic]), Fi = __builtin_amdgcn_rcpf(F);
-        const float kv = (float)kx[h][ii], qv = (float)qx[h][ii], vv = (float)vx[h][ii];
+        const float kv = (float)kx[h][ii] * rk[h], qv = (float)qx[h][ii] * rq[h], vv = (float)vx[h][ii];
         kf[ii] = (__bf16)(kv * F);
         qf[ii] = (__bf16)(qv * F);
         kfi[ii] = kv * Fi;
@@ -433,7 +468,9 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 // Persistent: each workgroup walks the units blockIdx.x, blockIdx.x + gridDim.x,
 // ... and fetches the next unit's inputs into registers while it works on
 // the current one (from the end of the current unit's first phase on).
-template <bool SCALAR>
+// ACT: input activations requested (q/k L2 norm, beta sigmoid); the instantiation
+// without them carries none of their code.
+template <bool SCALAR, bool ACT>
 __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save, int out) {
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
@@ -444,7 +481,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
   settle(nxt);  // so that no path into the loop carries an outstanding load
   for (; unit < total; unit += gridDim.x) {
     const PrepIn cur = nxt;
-    prep_unit<SCALAR>(p, w, save, out, unit, cur, nxt, unit + gridDim.x, smem);
+    prep_unit<SCALAR, ACT>(p, w, save, out, unit, cur, nxt, unit + gridDim.x, smem);
     lds_barrier();  // LDS is reused by the next unit
   }
 }
@@ -654,11 +691,16 @@ hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool 
   if (p.NC == 0) return hipSuccess;
   const int total = p.NC * p.Hv;
   const dim3 grid(total < compute_units() ? total : compute_units()), block(PNT);
-  const void *fn = gdn ? (const void *)fwd_prep_kernel<true> : (const void *)fwd_prep_kernel<false>;
+  const bool act = p.inflags != 0;
+  const void *fn = gdn ? (act ? (const void *)fwd_prep_kernel<true, true> : (const void *)fwd_prep_kernel<true, false>)
+                       : (act ? (const void *)fwd_prep_kernel<false, true> : (const void *)fwd_prep_kernel<false, false>);
   hipError_t e = set_dynamic_lds_once(fn, P_SMEM);
   if (e != hipSuccess) return e;
-  if (gdn) fwd_prep_kernel<true><<<grid, block, P_SMEM, st>>>(p, w, save ? 1 : 0, out ? 1 : 0);
-  else fwd_prep_kernel<false><<<grid, block, P_SMEM, st>>>(p, w, save ? 1 : 0, out ? 1 : 0);
+  const int sv = save ? 1 : 0, ov = out ? 1 : 0;
+  if (gdn && act) fwd_prep_kernel<true, true><<<grid, block, P_SMEM, st>>>(p, w, sv, ov);
+  else if (gdn) fwd_prep_kernel<true, false><<<grid, block, P_SMEM, st>>>(p, w, sv, ov);
+  else if (act) fwd_prep_kernel<false, true><<<grid, block, P_SMEM, st>>>(p, w, sv, ov);
+  else fwd_prep_kernel<false, false><<<grid, block, P_SMEM, st>>>(p, w, sv, ov);
   return hipGetLastError();
 }
 

@@ -39,7 +39,10 @@ struct Problem {
   const int32_t *cu, *table;
   const float *h0;
   float scale;
+  int inflags;  // bit 0: q, k rows to unit L2 norm; bit 1: beta = sigmoid(beta)
 };
+constexpr int IN_QK_L2NORM = 1, IN_BETA_SIGMOID = 2;
+constexpr float L2NORM_EPS = 1e-6f;
 
 // Raise a kernel's dynamic-LDS limit, once per (device, kernel, size): the
 // attribute belongs to the function on that device, so later launches

@@ -97,7 +97,18 @@ typedef struct gdr_problem {
   int32_t n_chunks;          /* the n_chunks gdr_plan_chunks returned for it */
   const float *h0;           /* fp32 [N, H_v, K, V] initial states, or NULL for zeros */
   float scale;               /* output scale; 1/sqrt(128) in every workload of the pages */
+  uint32_t input_flags;      /* GDR_IN_* bits below; 0 = q, k, beta used as given */
 } gdr_problem;
+
+/* Input activations applied inside the kernels (gdr_problem.input_flags).
+ * GDR_IN_QK_L2NORM: every (token, head) row of q and of k is scaled to unit L2
+ * norm, x * (sum x^2 + 1e-6)^(-1/2), before use (PR #8638 shapes paragraph);
+ * dq and dk are then gradients with respect to the raw rows.
+ * GDR_IN_BETA_SIGMOID: beta holds logits; the kernels use sigmoid(beta) and
+ * dbeta is the gradient with respect to the logits.
+ * The forward and backward of one problem must use the same flags. */
+#define GDR_IN_QK_L2NORM 1u
+#define GDR_IN_BETA_SIGMOID 2u
 
 /* Chunk planner (host only).  Splits every document of cu_seqlens into
  * 64-token chunks (the last one of a document may be shorter; chunks never

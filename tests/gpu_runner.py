@@ -20,7 +20,7 @@ def to_dev(inp, device="cuda"):
 
 
 def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, nan_workspace=True, workspace=None,
-            on_device=False):
+            on_device=False, input_flags=0):
     """Forward (with tapes) and backward on the GPU.  Returns CPU fp32 tensors
     (or the device tensors as computed, with on_device=True)."""
     import torch
@@ -29,7 +29,8 @@ def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, nan_workspace=
 
     d = to_dev(inp)
     code = gdr.GDR_KDA if variant == "kda" else gdr.GDR_GDN
-    prob = gdr.Problem(code, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d.get("h0"))
+    prob = gdr.Problem(code, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d.get("h0"),
+                       input_flags=input_flags)
     T, Hqk, Hv, N = prob.T, prob.H_qk, prob.H_v, prob.N
     ws = workspace if workspace is not None else prob.alloc_workspace(gdr.GDR_FWD_SAVE)
     if nan_workspace:
@@ -63,13 +64,15 @@ def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, nan_workspace=
     return {k: v.float().cpu() for k, v in out.items()}
 
 
-def oracle_all(variant, inp, dht=None, backward=True, threads=None):
-    o, ht = oracle.forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"].numpy(),
-                           inp.get("h0"), threads=threads)
+def oracle_all(variant, inp, dht=None, backward=True, threads=None, qk_l2norm=False, beta_sigmoid=False):
+    act = dict(qk_l2norm=qk_l2norm, beta_sigmoid=beta_sigmoid)
+    o, ht = oracle.forward_act(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"].numpy(),
+                               inp.get("h0"), threads=threads, **act)
     ref = {"o": o, "ht": ht}
     if backward:
-        ref.update(oracle.backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
-                                   inp["cu_seqlens"].numpy(), inp["dout"], inp.get("h0"), dht, threads=threads))
+        ref.update(oracle.backward_act(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                       inp["cu_seqlens"].numpy(), inp["dout"], inp.get("h0"), dht, threads=threads,
+                                       **act))
     return ref
 
 

@@ -36,6 +36,35 @@ def test_small_pack_parity(case):
     compare(got, ref, label=w.name)
 
 
+ACT = [
+    # (variant, docs, H_qk, H_v): raw q, k rows of varying norm, beta as logits
+    ("kda", (1, 63, 64, 65, 130, 7), 2, 2),
+    ("gdn", (130, 1, 200), 1, 3),
+    ("gdn", (77, 64, 129), 2, 6),
+]
+
+
+@pytest.mark.parametrize("case", ACT, ids=lambda c: "%s_%s_h%d_%d" % (c[0], "-".join(map(str, c[1])), c[2], c[3]))
+def test_input_activations_parity(case):
+    """In-kernel q/k L2 norm and beta sigmoid (GDR_IN_QK_L2NORM | GDR_IN_BETA_SIGMOID)
+    against the oracle with the same activations, forward and backward."""
+    import chunked_gated_delta_14_amd as gdr
+
+    variant, docs, hqk, hv = case
+    w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=sum(docs) + 7 * hv)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    gen = torch.Generator().manual_seed(sum(docs))
+    T = w.T
+    for name in ("q", "k"):
+        x = inp[name].float()
+        inp[name] = (x * (0.25 + 4.0 * torch.rand((T, hqk, 1), generator=gen))).to(torch.bfloat16)
+    inp["beta"] = torch.randn(tuple(inp["beta"].shape), generator=gen).to(inp["beta"].dtype)
+    print("[case]", w.name, "activations", flush=True)
+    got = run_gdr(variant, inp, dht=inp["dht"], input_flags=gdr.GDR_IN_QK_L2NORM | gdr.GDR_IN_BETA_SIGMOID)
+    ref = oracle_all(variant, inp, dht=inp["dht"], qk_l2norm=True, beta_sigmoid=True)
+    compare(got, ref, label=w.name + "_act")
+
+
 def test_workload0_parity():
     w = workloads.workload(0)
     inp = workloads.make_inputs(w, device="cpu")

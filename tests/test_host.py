@@ -159,6 +159,14 @@ def test_workspace_checks():
     assert rc == 1
 
 
+def test_unknown_input_flag_rejected_on_host():
+    L = gdr.lib()
+    p = _cproblem()
+    p.input_flags = 4
+    rc = L.gdr_kda_fwd(ctypes.byref(p), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 1 << 40, 0, None)
+    assert rc == 1 and "input flag" in L.gdr_last_error().decode()
+
+
 def test_skip_output_flag_host_checks():
     """GDR_FWD_SKIP_OUTPUT is a known flag (workspace sizes as without it); o may be
     NULL only with it.  Only paths that stop before any device call are exercised."""
