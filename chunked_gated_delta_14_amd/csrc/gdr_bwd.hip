@@ -795,14 +795,17 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         up[I] = (lg < 3 ? a : 0.f) + (lg < 2 ? b : 0.f) + (lg < 1 ? cc : 0.f);
         blk[I] = red_lg(tot[I]);
       }
+      // dg leaves as 16-byte row pieces: each 16 x 16 block transposed on the matrix cores
+      // (rows past the chunk fall outside the sink's range)
+      const uint32_t rowb = (uint32_t)(Hv * HD * 4);
+      const RowSink sg(dg + ((size_t)start * Hv + j) * HD + 16 * wave, (uint32_t)len * rowb);
       float below = 0.f;
 #pragma unroll
       for (int I = 3; I >= 0; --I) {
+        f32x4 x;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 16 * I + 4 * lg + jj;
-          if (r < len) dg[((size_t)(start + r) * Hv + j) * HD + c] = dGA[I][jj] + up[I] + below;
-        }
+        for (int jj = 0; jj < 4; ++jj) x[jj] = dGA[I][jj] + up[I] + below;
+        sg.put16((uint32_t)(16 * I + lr) * rowb + 16 * lg, __builtin_bit_cast(u32x4, tile_row4_f32(x, lane)));
         below += blk[I];
       }
     } else {
@@ -840,10 +843,14 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         if (rr < len) dg[(size_t)(start + rr) * Hv + j] = y;
       }
     }
+    {  // dv: pairs of row blocks regrouped into 16-byte row pieces
+      const uint32_t rowb = (uint32_t)(Hv * HD * 2);
+      const RowSink sv(dv + ((size_t)start * Hv + j) * HD + 16 * wave, (uint32_t)len * rowb);
+      const int prow = 16 * (lg >> 1) + lr, pcol = 8 * (lg & 1);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      if (16 * mt + lr < len)
-        *reinterpret_cast<uint2 *>(dv + ((size_t)(start + 16 * mt + lr) * Hv + j) * HD + 16 * wave + 4 * lg) = dvv[mt];
+      for (int h = 0; h < 2; ++h)
+        sv.put16((uint32_t)(32 * h + prow) * rowb + 2 * pcol, rows8_from_pair(dvv[2 * h], dvv[2 * h + 1]));
+    }
     lds_barrier();
   }
 
@@ -876,17 +883,18 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
           dkA[I][jj] = sNrm[64 + r] * (dkA[I][jj] - bf2f(sKT[c * QTP + r]) * dotk);
         }
     }
+    // 16-byte row pieces: pairs of 16-row blocks transposed on the matrix cores and regrouped
+    const s16x4 eye = eye16(lane);
+    const uint32_t rowb = (uint32_t)(p.Hqk * HD * 2);
+    const size_t base = ((size_t)start * p.Hqk + iqk) * HD + 16 * wave;
+    const RowSink sq(dq + base, (uint32_t)len * rowb), sk(dk + base, (uint32_t)len * rowb);
+    const int prow = 16 * (lg >> 1) + lr, pcol = 8 * (lg & 1);
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * I + 4 * lg + jj;
-        if (r < len) {
-          const size_t e = ((size_t)(start + r) * p.Hqk + iqk) * HD + 16 * wave + lr;
-          dq[e] = f2bf(dqA[I][jj]);
-          dk[e] = f2bf(dkA[I][jj]);
-        }
-      }
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 fq = acc_pair_to_b(dqA[2 * h], dqA[2 * h + 1]), fk = acc_pair_to_b(dkA[2 * h], dkA[2 * h + 1]);
+      sq.put16((uint32_t)(32 * h + prow) * rowb + 2 * pcol, rows8_from_pair(tile_row4(fq, 0, eye), tile_row4(fq, 1, eye)));
+      sk.put16((uint32_t)(32 * h + prow) * rowb + 2 * pcol, rows8_from_pair(tile_row4(fk, 0, eye), tile_row4(fk, 1, eye)));
+    }
   }
 }
 

@@ -270,6 +270,19 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Transpose of a 16 x 16 fp32 accumulator tile on the matrix cores, exact: the
+// result holds, per lane (lr, lg), row lr, columns 4lg..4lg+3 of the tile (16
+// contiguous bytes of a row-major tile).  Step jj of four 16x16x4 products takes
+// A[i][k] = X[4k + jj][i] (the lane's element jj) against B[k][j] = (4k + jj == j),
+// so D[i][j] = X[j][i]; every output is one input times 1 plus zeros.
+__device__ __forceinline__ f32x4 tile_row4_f32(f32x4 x, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) d = mfma4(x[jj], (4 * lg + jj == lr) ? 1.f : 0.f, d);
+  return d;
+}
+
 // T = (I + diag(beta) E)^-1 (unit lower triangular, fp32) for a strictly
 // lower 64 x 64 E (pitch SP) in blocks of 16:
 //  - the four diagonal blocks by right-looking forward substitution, one lane
