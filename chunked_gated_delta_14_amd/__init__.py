@@ -48,7 +48,7 @@ class _CProblem(ctypes.Structure):
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("chunk_table", ctypes.c_void_p), ("n_chunks", ctypes.c_int32), ("h0", ctypes.c_void_p),
-        ("scale", ctypes.c_float), ("input_flags", ctypes.c_uint32),
+        ("scale", ctypes.c_float), ("input_flags", ctypes.c_uint32), ("walk_segments", ctypes.c_int32),
     ]
 
 
@@ -170,9 +170,10 @@ class Problem:
     or [T, H_v] (GDN); beta: bf16 [T, H_v] (KDA) or fp32 [T, H_v] (GDN);
     cu_seqlens: host sequence or tensor of N+1 ints; h0: fp32 [N, H_v, 128, 128] or None.
     input_flags: GDR_IN_QK_L2NORM and/or GDR_IN_BETA_SIGMOID (activations applied in the kernels).
+    walk_segments: 0 = automatic segmentation of the state walks, n >= 1 = at most n segments.
     """
 
-    def __init__(self, variant, q, k, v, g, beta, cu_seqlens, h0=None, scale=None, input_flags=0):
+    def __init__(self, variant, q, k, v, g, beta, cu_seqlens, h0=None, scale=None, input_flags=0, walk_segments=0):
         import torch
 
         self.variant = variant
@@ -193,7 +194,8 @@ class Problem:
         self._c = _CProblem(self.T, self.N, self.H_qk, self.H_v, self.K, self.V,
                             q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                             self.cu.data_ptr(), self.table.data_ptr(), nc,
-                            h0.data_ptr() if h0 is not None else None, self.scale, int(input_flags))
+                            h0.data_ptr() if h0 is not None else None, self.scale, int(input_flags),
+                            int(walk_segments))
         self.input_flags = int(input_flags)
 
     def workspace_bytes(self, flags=GDR_FWD_SAVE) -> int:

@@ -58,7 +58,17 @@ constexpr int64_t kGamma = kHD * 4;
 constexpr int64_t kState = kHD * kHD * 2;
 constexpr int64_t kRows = kChunk * kHD * 2;
 
+// Walk segments per document: more than one only when the chains (documents x
+// value heads, 8 wavefronts each) would leave the compute units underfilled and
+// some document spans two chunks.
+int walk_segments(int64_t N, int64_t Hv, int64_t NC) {
+  const int64_t waves = 8 * N * Hv;
+  if (waves == 0 || waves >= 512 || NC <= N) return 1;
+  return (int)std::min<int64_t>(4, std::max<int64_t>(1, 512 / waves));
+}
+
 struct Layout {
+  int64_t carry;                          // segment carries (segmented walks only)
   int64_t WfN, Pf, KbT, Uacc, Oacc, gam;  // forward walk operands
   int64_t Kb, WTn, QGT, MTs, Tt, Et, S, Vn;  // tapes kept for the backward
   int64_t fwd_bytes, full_bytes;
@@ -67,7 +77,7 @@ struct Layout {
 // Region order keeps WfN|Pf, KbT and Uacc adjacent so that the backward's
 // scratch tapes (dS: 32 KB, dVnT: 16 KB per unit) can overlay the
 // forward-walk operands, which are dead once the forward walk has run.
-Layout make_layout(int64_t units) {
+Layout make_layout(int64_t units, int64_t N, int64_t Hv) {
   Layout L{};
   int64_t off = 0;
   auto take = [&](int64_t per_unit) {
@@ -75,6 +85,8 @@ Layout make_layout(int64_t units) {
     off += round_up(per_unit * units);
     return at;
   };
+  L.carry = off;
+  off += round_up((int64_t)(walk_segments(N, Hv, units / Hv) - 1) * N * Hv * 2 * kHD * kHD * 4);
   L.WfN = take(kFrag64x128);
   L.Pf = take(kFrag64x128);
   L.KbT = take(kFrag64x128);
@@ -113,6 +125,7 @@ gdr::Workspace bind(const Layout &L, void *base) {
   w.Vn = reinterpret_cast<uint16_t *>(b + L.Vn);
   w.dS = reinterpret_cast<uint16_t *>(b + L.WfN);   // over WfN|Pf
   w.dVnT = reinterpret_cast<uint16_t *>(b + L.Uacc);// over Uacc
+  w.carry = reinterpret_cast<float *>(b + L.carry);
   return w;
 }
 
@@ -173,11 +186,12 @@ int32_t check_problem(int32_t variant, const gdr_problem *p) {
   if (!(p->scale == p->scale)) return fail(GDR_ERR_INVALID_ARG, "scale is NaN");
   if (p->input_flags & ~(GDR_IN_QK_L2NORM | GDR_IN_BETA_SIGMOID))
     return fail(GDR_ERR_INVALID_ARG, "unknown input flag");
+  if (p->walk_segments < 0) return fail(GDR_ERR_INVALID_ARG, "walk_segments < 0");
   return GDR_OK;
 }
 
 int32_t check_workspace(const gdr_problem *p, void *ws, int64_t ws_bytes, bool full, Layout &L) {
-  L = make_layout((int64_t)p->n_chunks * p->H_v);
+  L = make_layout((int64_t)p->n_chunks * p->H_v, p->N, p->H_v);
   const int64_t need = full ? L.full_bytes : L.fwd_bytes;
   if (need > 0 && !ws) return fail(GDR_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(GDR_ERR_WORKSPACE, "workspace is not 256-byte aligned");
@@ -204,6 +218,8 @@ gdr::Problem to_internal(const gdr_problem *p) {
   q.h0 = p->h0;
   q.scale = p->scale;
   q.inflags = (int)p->input_flags;
+  q.P = walk_segments(p->N, p->H_v, p->n_chunks);
+  if (p->walk_segments > 0 && p->walk_segments < q.P) q.P = p->walk_segments;
   return q;
 }
 
@@ -375,7 +391,7 @@ int64_t gdr_workspace_bytes(int32_t variant, int32_t T, int32_t N, int32_t n_chu
   const int32_t rc = check_sizes(variant, T, N, n_chunks, H_qk, H_v, K, V);
   if (rc) return -(int64_t)rc;
   if (flags & ~(GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT)) return -(int64_t)fail(GDR_ERR_INVALID_ARG, "unknown flag");
-  const Layout L = make_layout((int64_t)n_chunks * H_v);
+  const Layout L = make_layout((int64_t)n_chunks * H_v, N, H_v);
   return (flags & GDR_FWD_SAVE) ? L.full_bytes : L.fwd_bytes;
 }
 

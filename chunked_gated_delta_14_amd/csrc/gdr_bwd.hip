@@ -18,6 +18,7 @@
 //   cumulative sum of dG (the gate epilogue).
 #include "gdr_device.h"
 #include "gdr_kernels.h"
+#include "gdr_walk.h"
 
 namespace gdr {
 
@@ -30,16 +31,26 @@ namespace gdr {
 // products with the identity on the matrix cores, so the step has no LDS
 // round trip besides the broadcast of the gate factors.
 // ---------------------------------------------------------------------------
+// Segmented like the forward walk (gdr_walk.h), in reverse: the adjoint walk over
+// segment s maps the adjoint entering it at its last chunk to the one leaving it
+// at its first, dS_out = Phi' dS_in + Psi'.  Pass 1 computes the carries of
+// segments 1 .. P_d - 1 (MODE_CARRY: zero start, dout as given; MODE_TRANSFER:
+// identity start, dout = 0); pass 2 starts segment s from dht carried back
+// through segments P_d - 1 .. s + 1 and writes the tapes; dh0 comes from segment 0.
+template <int MODE = MODE_WALK>
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
+  static_assert(MODE != MODE_TRANSFER, "transfer walks run in the second half of a MODE_CARRY launch");
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
+  const bool transfer = MODE == MODE_CARRY && blockIdx.x >= gridDim.x / 2;
   int chain, sl;
-  walk_block(blockIdx.x, chain, sl);
-  if (chain >= p.N * p.Hv) return;
+  walk_block(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, chain, sl);
   const ChunkTable tb(p.table, p.NC, p.N);
-  const int d = tb.order[chain / p.Hv], j = chain % p.Hv;
-  const int first = tb.doc_ptr[d], nch = tb.doc_ptr[d + 1] - first;
-  const int tok0 = p.cu[d], tok1 = p.cu[d + 1];
+  WalkChain wc;
+  if (!walk_chain(p, tb, chain, MODE == MODE_WALK ? p.P : p.P - 1, MODE != MODE_WALK, wc, MODE == MODE_WALK ? 0 : 1))
+    return;
+  const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
+  const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int vcol = 16 * sl + lr;
   const size_t Hv = p.Hv;
@@ -47,11 +58,20 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
   const s16x4 eye = eye16(lane);
 
   f32x4 dS[8];
-  const float *dh = dht ? dht + ((size_t)d * Hv + j) * HD * HD : nullptr;
+  const float *dh = (MODE == MODE_WALK && dht) ? dht + ((size_t)d * Hv + j) * HD * HD : nullptr;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dS[mt][jj] = dh ? dh[(16 * mt + 4 * lg + jj) * HD + vcol] : 0.f;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int row = 16 * mt + 4 * lg + jj;
+      dS[mt][jj] = transfer ? (row == vcol ? 1.f : 0.f) : (dh ? dh[row * HD + vcol] : 0.f);
+    }
+  if constexpr (MODE == MODE_WALK) {
+    for (int t = wc.Pd - 1; t > wc.s; --t) {  // adjoint entering segment s: back through the later segments
+      const float *cb = carry_of(p, w, d, t - 1, j);
+      apply_carry(dS, cb, cb + HD * HD, 16 * sl, lane);
+    }
+  }
 
   // 16-byte row pieces: lane (lr, lg) carries row 16 (lg >> 1) + lr of a 32-row block,
   // columns 8 (lg & 1)..+7 of this slice
@@ -101,6 +121,7 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
       for (int h = 0; h < 2; ++h) {
         uint2 X, Y;
         pair_from_rows8(pdo[h], X, Y);
+        if (transfer) X = Y = make_uint2(0u, 0u);
         dO[2 * h] = mfma16(as_s4(X), eye, zero4());
         dO[2 * h + 1] = mfma16(as_s4(Y), eye, zero4());
       }
@@ -112,7 +133,7 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
     bf16x8 dSb[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) dSb[kt] = acc_pair_to_b(dS[2 * kt], dS[2 * kt + 1]);
-    {  // this slice's block [key][16] of the adjoint-state tape
+    if (MODE == MODE_WALK) {  // this slice's block [key][16] of the adjoint-state tape
       u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + prow * 16 + pcol;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -153,7 +174,7 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
         dV[mt] = mfma(Kb[mt][kt], dSb[kt], dV[mt]);
         Kb[mt][kt] = as_bf16x8(w.Kb[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
       }
-    {  // dVn^T rows of this slice's columns: 8 consecutive chunk rows 32h + 8lg.. per lane
+    if (MODE == MODE_WALK) {  // dVn^T rows of this slice's columns: 8 consecutive chunk rows 32h + 8lg.. per lane
       u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 8 * lg;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -173,8 +194,13 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
       }
   }
 
-  if (dh0) {
-    float *hp = dh0 + ((size_t)d * Hv + j) * HD * HD;
+  float *hp = nullptr;
+  if (MODE == MODE_WALK) {
+    if (dh0 && wc.s == 0) hp = dh0 + ((size_t)d * Hv + j) * HD * HD;
+  } else {
+    hp = const_cast<float *>(carry_of(p, w, d, wc.s - 1, j)) + (transfer ? HD * HD : 0);
+  }
+  if (hp) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -1379,7 +1405,11 @@ hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout
                            hipStream_t st) {
   const int chains = p.N * p.Hv;
   if (chains == 0) return hipSuccess;
-  bwd_walk_kernel<<<((chains + 7) / 8) * 64, 64, 0, st>>>(p, w, dout, dht, dh0);
+  if (p.P > 1) {  // pass 1: the segments' carries
+    const int g1 = ((chains * (p.P - 1) + 7) / 8) * 64;
+    bwd_walk_kernel<MODE_CARRY><<<2 * g1, 64, 0, st>>>(p, w, dout, nullptr, nullptr);
+  }
+  bwd_walk_kernel<MODE_WALK><<<((chains * p.P + 7) / 8) * 64, 64, 0, st>>>(p, w, dout, dht, dh0);
   return hipGetLastError();
 }
 

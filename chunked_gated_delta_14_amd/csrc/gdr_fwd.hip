@@ -16,6 +16,7 @@
 // pass over q, k and the gates.)
 #include "gdr_device.h"
 #include "gdr_kernels.h"
+#include "gdr_walk.h"
 
 namespace gdr {
 
@@ -503,16 +504,21 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
 // a few long documents.
 constexpr int WALK_NS = 1;
 
-template <int NS, bool SAVE, bool OUT>
+// MODE_CARRY launches run the carry walks in the first half of the grid and the
+// transfer walks in the second, so the two proceed together.
+template <int NS, bool SAVE, bool OUT, int MODE = MODE_WALK>
 __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u16 *o, float *ht) {
+  static_assert(MODE != MODE_TRANSFER, "transfer walks run in the second half of a MODE_CARRY launch");
+  static_assert(MODE == MODE_WALK || (NS == 1 && !SAVE && !OUT), "pass-1 walks carry one slice, no outputs");
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
+  const bool transfer = MODE == MODE_CARRY && blockIdx.x >= gridDim.x / 2;
   int chain, grp;
-  walk_block<NS>(blockIdx.x, chain, grp);
-  if (chain >= p.N * p.Hv) return;
+  walk_block<NS>(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, chain, grp);
   const ChunkTable tb(p.table, p.NC, p.N);
-  const int d = tb.order[chain / p.Hv], j = chain % p.Hv;
-  const int first = tb.doc_ptr[d], nch = tb.doc_ptr[d + 1] - first;
-  const int tok0 = p.cu[d], tok1 = p.cu[d + 1];
+  WalkChain wc;
+  if (!walk_chain(p, tb, chain, MODE == MODE_WALK ? p.P : p.P - 1, MODE != MODE_WALK, wc)) return;
+  const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
+  const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int sl0 = NS * grp;  // first slice of this wavefront
   const size_t Hv = p.Hv;
@@ -520,14 +526,24 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
   const s16x4 eye = eye16(lane);
 
   f32x4 S[NS][8];
-  const float *h0 = p.h0 ? p.h0 + ((size_t)d * Hv + j) * HD * HD : nullptr;
+  const float *h0 = (MODE == MODE_WALK && p.h0) ? p.h0 + ((size_t)d * Hv + j) * HD * HD : nullptr;
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        S[s][mt][jj] = h0 ? h0[(16 * mt + 4 * lg + jj) * HD + 16 * (sl0 + s) + lr] : 0.f;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int row = 16 * mt + 4 * lg + jj, col = 16 * (sl0 + s) + lr;
+        S[s][mt][jj] = transfer ? (row == col ? 1.f : 0.f) : (h0 ? h0[row * HD + col] : 0.f);
+      }
+  if constexpr (MODE == MODE_WALK) {
+    if (NS == 1) {
+      for (int b = 0; b < wc.s; ++b) {  // entering state of segment s: through the earlier segments
+        const float *cb = carry_of(p, w, d, b, j);
+        apply_carry(S[0], cb, cb + HD * HD, 16 * sl0, lane);
+      }
+    }
+  }
 
   bf16x8 Wf[4][4], Pf[4][4], KT[8][2];
   uint2 Ua[NS][4], Oa[NS][4];
@@ -592,6 +608,7 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
       for (int mt = 0; mt < 4; ++mt) {
         Vn[s][mt][0] = bf2f(Ua[s][mt].x & 0xffff); Vn[s][mt][1] = bf2f(Ua[s][mt].x >> 16);
         Vn[s][mt][2] = bf2f(Ua[s][mt].y & 0xffff); Vn[s][mt][3] = bf2f(Ua[s][mt].y >> 16);
+        if (transfer) Vn[s][mt] = zero4();
         const size_t off = un * ACC_64x128_U16 + (((sl0 + s) * 4 + mt) * 64 + lane) * 4;
         Ua[s][mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
         if (OUT) {
@@ -662,8 +679,13 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
       }
   }
 
-  if (ht) {
-    float *hp = ht + ((size_t)d * Hv + j) * HD * HD;
+  float *hp = nullptr;
+  if (MODE == MODE_WALK) {
+    if (ht && wc.s == wc.Pd - 1) hp = ht + ((size_t)d * Hv + j) * HD * HD;
+  } else {
+    hp = const_cast<float *>(carry_of(p, w, d, wc.s, j)) + (transfer ? HD * HD : 0);
+  }
+  if (hp) {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -709,7 +731,12 @@ hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, u16 *o, float *
   const int chains = p.N * p.Hv;
   if (chains == 0) return hipSuccess;
   constexpr int NS = WALK_NS;
-  const int grid = walk_grid(chains, NS);
+  static_assert(NS == 1, "segmented walks form entering states per 16-column slice");
+  if (p.P > 1) {  // pass 1: the segments' carries
+    const int g1 = walk_grid(chains * (p.P - 1), 1);
+    fwd_walk_kernel<1, false, false, MODE_CARRY><<<2 * g1, 64, 0, st>>>(p, w, nullptr, nullptr);
+  }
+  const int grid = walk_grid(chains * p.P, NS);
   if (save && out) fwd_walk_kernel<NS, true, true><<<grid, 64, 0, st>>>(p, w, o, ht);
   else if (save) fwd_walk_kernel<NS, true, false><<<grid, 64, 0, st>>>(p, w, o, ht);
   else if (out) fwd_walk_kernel<NS, false, true><<<grid, 64, 0, st>>>(p, w, o, ht);

@@ -29,6 +29,10 @@ struct Workspace {
   uint16_t *Vn;   // new values, bf16 [u][slice 8][row][16]                         (forward walk, SAVE)
   uint16_t *dS;   // adjoint state leaving every chunk, bf16 [u][slice 8][key][16]  (backward walk)
   uint16_t *dVnT; // adjoint of the new values, bf16 [u][v][row]          (backward walk)
+  // segmented walks: per (document, segment boundary b < P-1, value head) the
+  // affine carry of a segment, fp32 [128][128] each: Psi (end state from a zero
+  // start) then Phi (the segment's transfer matrix)
+  float *carry;
 };
 
 struct Problem {
@@ -40,6 +44,7 @@ struct Problem {
   const float *h0;
   float scale;
   int inflags;  // bit 0: q, k rows to unit L2 norm; bit 1: beta = sigmoid(beta)
+  int P;        // walk segments per document (1: one chain per document and head)
 };
 constexpr int IN_QK_L2NORM = 1, IN_BETA_SIGMOID = 2;
 constexpr float L2NORM_EPS = 1e-6f;

@@ -98,6 +98,8 @@ typedef struct gdr_problem {
   const float *h0;           /* fp32 [N, H_v, K, V] initial states, or NULL for zeros */
   float scale;               /* output scale; 1/sqrt(128) in every workload of the pages */
   uint32_t input_flags;      /* GDR_IN_* bits below; 0 = q, k, beta used as given */
+  int32_t walk_segments;     /* segments per document of the state walks: 0 = automatic (see
+                                gdr_workspace_bytes), n >= 1 = at most n and at most the automatic count */
 } gdr_problem;
 
 /* Input activations applied inside the kernels (gdr_problem.input_flags).
@@ -128,7 +130,12 @@ int32_t gdr_plan_chunks(const int32_t *cu_seqlens_host, int32_t N, int32_t *tabl
 
 /* Workspace bytes for a problem (host only).  flags = 0: forward without
  * tapes; flags = GDR_FWD_SAVE: forward with tapes followed by a backward (the
- * size every backward needs).  Returns the byte count (a multiple of 256), or
+ * size every backward needs).  When the walks' chains (documents x value
+ * heads, 8 wavefronts each) number fewer than 512 wavefronts and some document
+ * spans two chunks (n_chunks > N), each document's walk is split into
+ * P = min(4, 512 / (8 N H_v)) segments run in parallel
+ * (the segments' affine carries, 2 x 64 KB per segment boundary and value
+ * head, are part of the workspace).  Returns the byte count (a multiple of 256), or
  * minus a gdr_status on invalid or unsupported sizes. */
 int64_t gdr_workspace_bytes(int32_t variant, int32_t T, int32_t N, int32_t n_chunks,
                             int32_t H_qk, int32_t H_v, int32_t K, int32_t V, uint32_t flags);
