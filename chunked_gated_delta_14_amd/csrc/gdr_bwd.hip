@@ -34,13 +34,13 @@ namespace gdr {
 // Segmented like the forward walk (gdr_walk.h), in reverse: the adjoint walk over
 // segment s maps the adjoint entering it at its last chunk to the one leaving it
 // at its first, dS_out = Phi' dS_in + Psi'.  Pass 1 computes the carries of
-// segments 1 .. P_d - 1 (MODE_CARRY: zero start, dout as given; MODE_TRANSFER:
-// identity start, dout = 0); pass 2 starts segment s from dht carried back
+// segments 1 .. P_d - 1 in one MODE_CARRY launch (first half of the grid: zero
+// start, dout as given; second half: identity start, dout = 0); pass 2 starts
+// segment s from dht carried back
 // through segments P_d - 1 .. s + 1 and writes the tapes; dh0 comes from segment 0.
 template <int MODE = MODE_WALK>
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
-  static_assert(MODE != MODE_TRANSFER, "transfer walks run in the second half of a MODE_CARRY launch");
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
   const bool transfer = MODE == MODE_CARRY && blockIdx.x >= gridDim.x / 2;
   int chain, sl;

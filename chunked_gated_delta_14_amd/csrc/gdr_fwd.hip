@@ -508,7 +508,6 @@ constexpr int WALK_NS = 1;
 // transfer walks in the second, so the two proceed together.
 template <int NS, bool SAVE, bool OUT, int MODE = MODE_WALK>
 __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u16 *o, float *ht) {
-  static_assert(MODE != MODE_TRANSFER, "transfer walks run in the second half of a MODE_CARRY launch");
   static_assert(MODE == MODE_WALK || (NS == 1 && !SAVE && !OUT), "pass-1 walks carry one slice, no outputs");
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
   const bool transfer = MODE == MODE_CARRY && blockIdx.x >= gridDim.x / 2;

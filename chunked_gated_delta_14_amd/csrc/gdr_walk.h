@@ -8,14 +8,15 @@ namespace gdr {
 
 // Segmented walks.  With P > 1 segments per document (P_d = min(P, chunks of
 // the document), at least 1, equal shares of its chunks), the walk over a segment is an
-// affine map of the state entering it: S_end = Phi S_start + Psi.  Pass 1 runs
-// every segment but the last twice in parallel: MODE_CARRY from a zero state
-// (its end state is Psi) and MODE_TRANSFER from the identity with U = 0 (its end
-// state is Phi: each step then applies S <- (diag(gamma) - Kbar^T W) S).  Pass 2
-// (MODE_WALK) runs every segment with its true entering state, which each
-// wavefront forms for its own 16 columns from h0 through the earlier segments'
-// carries (fp32 16x16x4 MFMAs), and writes the outputs and tapes.
-constexpr int MODE_WALK = 0, MODE_CARRY = 1, MODE_TRANSFER = 2;  // (transfer: second half of a carry launch)
+// affine map of the state entering it: S_end = Phi S_start + Psi.  Pass 1
+// (MODE_CARRY) walks every segment but the last twice, in one launch: the first
+// half of the grid from a zero state (its end state is Psi), the second half
+// from the identity with U = 0 (its end state is Phi: each step then applies
+// S <- (diag(gamma) - Kbar^T W) S).  Pass 2 (MODE_WALK) runs every segment with
+// its true entering state, which each wavefront forms for its own 16 columns
+// from h0 through the earlier segments' carries (fp32 16x16x4 MFMAs), and
+// writes the outputs and tapes.
+constexpr int MODE_WALK = 0, MODE_CARRY = 1;
 
 // Chain c of a walk launch over Q segments per document: the document (walk
 // order), segment and value head, and the segment's chunk range; false if the

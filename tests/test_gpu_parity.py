@@ -10,6 +10,7 @@ import torch
 
 from chunked_gated_delta_14_amd import workloads
 from gpu_runner import compare, oracle_all, run_gdr
+from helpers import rel_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +64,37 @@ def test_input_activations_parity(case):
     got = run_gdr(variant, inp, dht=inp["dht"], input_flags=gdr.GDR_IN_QK_L2NORM | gdr.GDR_IN_BETA_SIGMOID)
     ref = oracle_all(variant, inp, dht=inp["dht"], qk_l2norm=True, beta_sigmoid=True)
     compare(got, ref, label=w.name + "_act")
+
+
+SEGMENTED = [
+    # (variant, docs, H_qk, H_v): few wavefronts, so the walks cut documents into
+    # segments; documents shorter than the segment count and empty ones included
+    ("kda", (1000, 130, 0, 1, 257), 1, 1),
+    ("gdn", (700, 64, 3), 1, 3),
+]
+
+
+@pytest.mark.parametrize("case", SEGMENTED, ids=lambda c: "%s_%s_h%d_%d" % (c[0], "-".join(map(str, c[1])), c[2], c[3]))
+def test_segmented_walks(case):
+    """Walks split into 2, 3 and 4 segments per document (carry and transfer
+    walks, composed at the segment starts) against the oracle, and against the
+    unsegmented walk: the two differ only by fp32 rounding of the composition,
+    which reaches the bf16 outputs and tapes as rare last-place flips."""
+    variant, docs, hqk, hv = case
+    w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=sum(docs) + 11 * hv)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    ref = oracle_all(variant, inp, dht=inp["dht"])
+    base = None
+    for P in (1, 2, 3, 4):
+        print("[case]", w.name, "walk_segments", P, flush=True)
+        got = run_gdr(variant, inp, dht=inp["dht"], walk_segments=P)
+        compare(got, ref, label="%s_P%d" % (w.name, P))
+        if base is None:
+            base = got
+            continue
+        for name, x in got.items():
+            r = rel_rms(x.double().numpy(), base[name].double().numpy())
+            assert r <= 1e-3, "%s P=%d vs P=1: rel-RMS %.3g" % (name, P, r)
 
 
 def test_workload0_parity():
