@@ -271,17 +271,36 @@ struct GateT {
   }
 };
 
+// Butterfly sums without the LDS crossbar: each step adds the value of a partner
+// lane (lane ^ 1, ^ 2, then the neighbouring quad, then the other half row), and
+// since a + b == b + a every lane of a 16-lane row ends with the same bits.
 __device__ __forceinline__ float red16(float x) {  // sum over the 16 lanes sharing lg
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
+  x += dpp_move<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
+  x += dpp_move<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
+  x += dpp_move<0x141, 0xf>(x);  // row_half_mirror: quads 0 <-> 1, 2 <-> 3
+  x += dpp_move<0x140, 0xf>(x);  // row_mirror: the two halves of the row
   return x;
 }
+// The same across the four 16-lane rows: rows (0,1), (2,3) exchanged, then the
+// two halves of the wavefront.
 __device__ __forceinline__ float red_lg(float x) {  // sum over the 4 lane groups sharing lr
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// Sum of x over the lane groups above this lane's (lg' > lg), same lr.
+__device__ __forceinline__ float sum_above_lg(float x, int lg) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float pair = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // x(2m) + x(2m + 1)
+  const float nxt = (lg & 1) ? 0.f : __uint_as_float(a[1]);             // x(lg + 1) for even lg
+  const uint32_t v = __float_as_uint(pair);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const float other = (lg < 2) ? __uint_as_float(b[1]) : 0.f;  // the upper pair's sum
+  return nxt + other;
 }
 __device__ __forceinline__ float lo_bf(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -817,8 +836,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         dGA[I][1] += dGA[I][2];
         dGA[I][0] += dGA[I][1];
         tot[I] = dGA[I][0];
-        const float a = __shfl_down(tot[I], 16, 64), b = __shfl_down(tot[I], 32, 64), cc = __shfl_down(tot[I], 48, 64);
-        up[I] = (lg < 3 ? a : 0.f) + (lg < 2 ? b : 0.f) + (lg < 1 ? cc : 0.f);
+        up[I] = sum_above_lg(tot[I], lg);
         blk[I] = red_lg(tot[I]);
       }
       // dg leaves as 16-byte row pieces: each 16 x 16 block transposed on the matrix cores
@@ -1312,8 +1330,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float s3 = dGA[t][3], s2 = s3 + dGA[t][2], s1 = s2 + dGA[t][1], s0 = s1 + dGA[t][0];
-        const float a = __shfl_down(s0, 16, 64), b = __shfl_down(s0, 32, 64), cc = __shfl_down(s0, 48, 64);
-        const float up = (lg < 3 ? a : 0.f) + (lg < 2 ? b : 0.f) + (lg < 1 ? cc : 0.f);
+        const float up = sum_above_lg(s0, lg);
         hsum[t][0] = s0 + up; hsum[t][1] = s1 + up; hsum[t][2] = s2 + up; hsum[t][3] = s3 + up;
         if (lg == 0) sBT[mt * 128 + 16 * (4 * ch + t) + lr] = hsum[t][0];
       }
