@@ -234,27 +234,31 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 // well below the pair's size.
 // ---------------------------------------------------------------------------
 constexpr int GNT = 512;
-constexpr int QTP = 72;  // LDS pitch (bf16) of the transposed q, k tiles
+constexpr int QTP = 72;  // LDS pitch (bf16) of the transposed q, k tiles read 16 bytes at a time
 constexpr int GTP = 68;  // LDS pitch (floats) of the transposed gate tile
+// Pitches of the tiles the column-tile kernel reads 8 bytes at a time: 136-byte
+// rows put the 16 lanes of a read (16 consecutive rows) on distinct bank pairs.
+constexpr int KQTP = 68;  // q^T, k^T
+constexpr int DMP = 68;   // dM, dA, dM^T, dA^T
 
 // LDS map (bytes)
-constexpr int G_QT = 0;                     // q^T bf16 [128][QTP]
-constexpr int G_KT = G_QT + HD * QTP * 2;   // k^T bf16 [128][QTP]
-constexpr int G_GT = G_KT + HD * QTP * 2;   // cumulative gate: KDA fp32 [128][GTP], GDN [64]
+constexpr int G_QT = 0;                     // q^T bf16 [128][KQTP]
+constexpr int G_KT = G_QT + HD * KQTP * 2;  // k^T bf16 [128][KQTP]
+constexpr int G_GT = G_KT + HD * KQTP * 2;  // cumulative gate: KDA fp32 [128][GTP], GDN [64]
 constexpr int G_DO = G_GT + HD * GTP * 4;   // dout bf16 [64][KP]      (tape products)
 constexpr int G_VN = G_DO + CH * KP * 2;    // Vn
 constexpr int G_Y = G_VN + CH * KP * 2;     // Y
-constexpr int G_DM = G_DO;                  // dM, dA, dM^T, dA^T bf16 [64][MP] (gated products)
-constexpr int G_DA = G_DM + CH * MP * 2;
-constexpr int G_DMT = G_DA + CH * MP * 2;
-constexpr int G_DAT = G_DMT + CH * MP * 2;
+constexpr int G_DM = G_DO;                  // dM, dA, dM^T, dA^T bf16 [64][DMP] (gated products)
+constexpr int G_DA = G_DM + CH * DMP * 2;
+constexpr int G_DMT = G_DA + CH * DMP * 2;
+constexpr int G_DAT = G_DMT + CH * DMP * 2;
 constexpr int G_TT = G_Y + CH * KP * 2;     // T^T bf16 [64][MP]             (Y product)
 constexpr int G_B = G_TT + CH * MP * 2;     // beta [64]
 constexpr int G_DB = G_B + 64 * 4;          // dbeta partial sums [20][64], added in a fixed order
 constexpr int G_RS = G_DB + 20 * 64 * 4;    // GDN: dG row sums per wavefront [8][64]
 constexpr int G_NRM = G_RS + 8 * 64 * 4;     // q, k row norms [2][64], then row dots [64][2][8]
 constexpr int G_SMEM = G_NRM + (128 + 64 * 16) * 4;
-static_assert(G_DAT + CH * MP * 2 <= G_B, "grad LDS map");
+static_assert(G_DAT + CH * DMP * 2 <= G_B, "grad LDS map");
 
 
 // Cumulative gate: per-channel tile [channel][row] (KDA) or one value per row.
@@ -330,8 +334,11 @@ __device__ __forceinline__ void split4(const f32x4 &x, uint2 &hi, uint2 &lo) {
 // 64 rows x 128 bf16 (row stride ld) -> LDS [channel][row] (pitch QTP), rows
 // >= len as zeros.  256 threads: thread b moves rows 4(b>>4)..+3 of channels
 // 8(b&15)..+7.
+template <int PITCH>
 __device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, size_t ld, int len, int b) {
-  const int r0 = 4 * (b >> 4), c0 = 8 * (b & 15);
+  // rows vary fastest over the lanes, so that the 8-byte transposed writes of 16
+  // lanes (rows 4l..4l+3 of one channel) are consecutive in LDS
+  const int r0 = 4 * (b & 15), c0 = 8 * (b >> 4);
   uint4 x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -346,7 +353,7 @@ __device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, s
     uint2 pk;
     pk.x = part(x[0]) | (part(x[1]) << 16);
     pk.y = part(x[2]) | (part(x[3]) << 16);
-    *reinterpret_cast<uint2 *>(dst + (c0 + cc) * QTP + r0) = pk;
+    *reinterpret_cast<uint2 *>(dst + (c0 + cc) * PITCH + r0) = pk;
   }
 }
 
@@ -356,13 +363,14 @@ __device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, s
 // row (one per 8-channel group) added in a fixed order through sPart (2 x 64 x 16
 // floats of scratch), and the inverse norms kept in sRstd [2][64] for the
 // backward through the norm.
+template <int PITCH>
 __device__ __forceinline__ void load_qk_rows(u16 *sQT, u16 *sKT, const Problem &p, int start, int iqk, int len,
                                              int tid, float *sPart, float *sRstd) {
   const int isk = tid >> 8, b = tid & 255;
   const u16 *src = (isk ? p.k : p.q) + ((size_t)start * p.Hqk + iqk) * HD;
   const size_t ld = (size_t)p.Hqk * HD;
   if (!(p.inflags & IN_QK_L2NORM)) {
-    load_rows_transposed(isk ? sKT : sQT, src, ld, len, b);
+    load_rows_transposed<PITCH>(isk ? sKT : sQT, src, ld, len, b);
     return;
   }
   const int r0 = 4 * (b >> 4), c0 = 8 * (b & 15);
@@ -401,7 +409,7 @@ __device__ __forceinline__ void load_qk_rows(u16 *sQT, u16 *sKT, const Problem &
     uint2 pk;
     pk.x = (uint32_t)f2bf(x[0][cc]) | ((uint32_t)f2bf(x[1][cc]) << 16);
     pk.y = (uint32_t)f2bf(x[2][cc]) | ((uint32_t)f2bf(x[3][cc]) << 16);
-    *reinterpret_cast<uint2 *>(dst + (c0 + cc) * QTP + r0) = pk;
+    *reinterpret_cast<uint2 *>(dst + (c0 + cc) * PITCH + r0) = pk;
   }
 }
 
@@ -437,7 +445,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 
   float *sNrm = reinterpret_cast<float *>(smem + G_NRM);
   // (the dout stage is free until the first iteration's loads: scratch of the row norms)
-  load_qk_rows(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(smem + G_DO), sNrm);
+  load_qk_rows<KQTP>(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(smem + G_DO), sNrm);
 
   f32x4 dqA[4], dkA[4];  // [row block I]: rows 16I + 4lg + jj, column 16w + lr
 #pragma unroll
@@ -618,8 +626,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       }
       const float gref = G.at(16 * I + 8, c);
       const float Eref = __expf(gref), Elr = __expf(gL - gref);
-      const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
-      const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
+      const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * KQTP + r0);
+      const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * KQTP + r0);
       const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
       float db2[4];
 #pragma unroll
@@ -688,11 +696,11 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
           const int r = r0 + jj;
           m[jj] = s <= r ? scale * tM[q][jj] : 0.f;
           a[jj] = s < r ? -tA[q][jj] : 0.f;
-          sDM[r * MP + s] = f2bf(m[jj]);
-          sDA[r * MP + s] = f2bf(a[jj]);
+          sDM[r * DMP + s] = f2bf(m[jj]);
+          sDA[r * DMP + s] = f2bf(a[jj]);
         }
-        *reinterpret_cast<uint2 *>(sDMT + s * MP + r0) = pack4(m[0], m[1], m[2], m[3]);
-        *reinterpret_cast<uint2 *>(sDAT + s * MP + r0) = pack4(a[0], a[1], a[2], a[3]);
+        *reinterpret_cast<uint2 *>(sDMT + s * DMP + r0) = pack4(m[0], m[1], m[2], m[3]);
+        *reinterpret_cast<uint2 *>(sDAT + s * DMP + r0) = pack4(a[0], a[1], a[2], a[3]);
       }
     }
     if (wave >= 2) {  // the six upper tiles are zero: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
@@ -701,11 +709,11 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       const int s = 16 * J + lr, r0 = 16 * I + 4 * lg;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        sDM[(r0 + jj) * MP + s] = 0;
-        sDA[(r0 + jj) * MP + s] = 0;
+        sDM[(r0 + jj) * DMP + s] = 0;
+        sDA[(r0 + jj) * DMP + s] = 0;
       }
-      *reinterpret_cast<uint2 *>(sDMT + s * MP + r0) = make_uint2(0, 0);
-      *reinterpret_cast<uint2 *>(sDAT + s * MP + r0) = make_uint2(0, 0);
+      *reinterpret_cast<uint2 *>(sDMT + s * DMP + r0) = make_uint2(0, 0);
+      *reinterpret_cast<uint2 *>(sDAT + s * DMP + r0) = make_uint2(0, 0);
     }
     lds_barrier();
 
@@ -729,7 +737,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       uint2 xH[4], xL[4];
 #pragma unroll
       for (int K = 0; K < 4; ++K) {
-        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + 16 * K + 4 * lg);
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * KQTP + 16 * K + 4 * lg);
         f32x4 xs;
 #pragma unroll
         for (int i = 0; i < 4; ++i) xs[i] = bf_at(k4, i) * __builtin_amdgcn_rcpf(F[K][i]);  // k Fi
@@ -742,8 +750,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         f32x4 accM = zero4(), accA = zero4();
 #pragma unroll
         for (int J = 0; J <= I; ++J) {
-          const s16x4 aM = as_s4(*reinterpret_cast<const uint2 *>(sDM + rA * MP + 16 * J + 4 * lg));
-          const s16x4 aA = as_s4(*reinterpret_cast<const uint2 *>(sDA + rA * MP + 16 * J + 4 * lg));
+          const s16x4 aM = as_s4(*reinterpret_cast<const uint2 *>(sDM + rA * DMP + 16 * J + 4 * lg));
+          const s16x4 aA = as_s4(*reinterpret_cast<const uint2 *>(sDA + rA * DMP + 16 * J + 4 * lg));
           f32x4 pM = mfma16(aM, as_s4(xH[J]), zero4());
           pM = mfma16(aM, as_s4(xL[J]), pM);
           f32x4 pA = mfma16(aA, as_s4(xH[J]), zero4());
@@ -753,8 +761,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
           accA += d * pA;
         }
         const int r0 = 16 * I + 4 * lg;
-        const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
-        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
+        const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * KQTP + r0);
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * KQTP + r0);
         const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -777,8 +785,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       for (int K = 0; K < 4; ++K) {
         __builtin_amdgcn_sched_barrier(0);
         const int r0 = 16 * K + 4 * lg;
-        const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
-        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
+        const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * KQTP + r0);
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * KQTP + r0);
         const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
         f32x4 xq, xk;
 #pragma unroll
@@ -793,8 +801,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 #pragma unroll
         for (int I = 0; I <= K; ++I) {
           const int rA = 16 * I + lr;
-          const s16x4 aMT = as_s4(*reinterpret_cast<const uint2 *>(sDMT + rA * MP + 16 * K + 4 * lg));
-          const s16x4 aAT = as_s4(*reinterpret_cast<const uint2 *>(sDAT + rA * MP + 16 * K + 4 * lg));
+          const s16x4 aMT = as_s4(*reinterpret_cast<const uint2 *>(sDMT + rA * DMP + 16 * K + 4 * lg));
+          const s16x4 aAT = as_s4(*reinterpret_cast<const uint2 *>(sDAT + rA * DMP + 16 * K + 4 * lg));
           f32x4 pT = mfma16(aMT, as_s4(qH), zero4());
           pT = mfma16(aMT, as_s4(qL), pT);
           pT = mfma16(aAT, as_s4(kH), pT);
@@ -805,7 +813,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       }
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + 16 * I + 4 * lg);
+        const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * KQTP + 16 * I + 4 * lg);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const float kT = __builtin_amdgcn_rcpf(F[I][jj]) * accT[I][jj];
@@ -910,8 +918,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int r = 16 * I + 4 * lg + jj;
-          const float pq = red16(bf2f(sQT[c * QTP + r]) * dqA[I][jj]);
-          const float pk = red16(bf2f(sKT[c * QTP + r]) * dkA[I][jj]);
+          const float pq = red16(bf2f(sQT[c * KQTP + r]) * dqA[I][jj]);
+          const float pk = red16(bf2f(sKT[c * KQTP + r]) * dkA[I][jj]);
           if (lr == 0) { sDot[(r * 2) * 8 + wave] = pq; sDot[(r * 2 + 1) * 8 + wave] = pk; }
         }
       lds_barrier();
@@ -923,8 +931,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
           float dotq = 0.f, dotk = 0.f;
 #pragma unroll
           for (int v8 = 0; v8 < 8; ++v8) { dotq += sDot[(r * 2) * 8 + v8]; dotk += sDot[(r * 2 + 1) * 8 + v8]; }
-          dqA[I][jj] = sNrm[r] * (dqA[I][jj] - bf2f(sQT[c * QTP + r]) * dotq);
-          dkA[I][jj] = sNrm[64 + r] * (dkA[I][jj] - bf2f(sKT[c * QTP + r]) * dotk);
+          dqA[I][jj] = sNrm[r] * (dqA[I][jj] - bf2f(sQT[c * KQTP + r]) * dotq);
+          dkA[I][jj] = sNrm[64 + r] * (dkA[I][jj] - bf2f(sKT[c * KQTP + r]) * dotk);
         }
     }
     // 16-byte row pieces: pairs of 16-row blocks transposed on the matrix cores and regrouped
@@ -996,7 +1004,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
   const GateT<SCALAR> G{sG};
 
   // (the Y stage is free until the first iteration: scratch of the row norms)
-  load_qk_rows(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(sY), sNrm);
+  load_qk_rows<QTP>(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(sY), sNrm);
 
   f32x4 dqA[4], dkA[4];
 #pragma unroll
