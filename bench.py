@@ -15,6 +15,7 @@ import argparse
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -30,6 +31,10 @@ FWD_OPERANDS = 16384 * 3 + 16384 * 2 + 512   # -W, P, Kbar^T fragments; U, Oi; g
 BWD_OPERANDS = 16384 * 3 + 8192               # Kbar, -W^T, (q Gamma)^T fragments; M^T
 TE_SAVED = 8192 + 5120                         # T^T (bf16 64 x 64) and E's 10 lower tiles (bf16)
 S_TAPE, ROW_TAPE = 32768, 16384
+# Bytes per token-head that the method must move for fwd + bwd with bf16 state
+# tapes: inputs and outputs of both passes plus one 128 x 128 tape per 64 tokens.
+FLOOR_BYTES_PER_TOKEN_HEAD = {"kda": 5382.0, "gdn": 2840.0}
+FLUSH_BYTES = 512 << 20  # written before every timed call: larger than L2 (8 x 4 MB) and MALL (256 MB)
 
 
 def kernel_bytes(name, T, Hqk, Hv, NC, N, gdn, save=True):
@@ -79,6 +84,7 @@ def parse_args():
                     help="gdr_problem.input_flags: 1 = in-kernel q/k L2 norm, 2 = beta sigmoid (logits as input)")
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="tokens per document in the CPU sample")
     ap.add_argument("--no-op-timing", action="store_true", help="skip the separate fwd/bwd/ckpt timings")
+    ap.add_argument("--no-smi", action="store_true", help="do not sample clock and power with amd-smi")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (HBM counter calibration)")
     return ap.parse_args()
@@ -92,6 +98,126 @@ def traffic_from_profiles(kernel):
         return None
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", open(path).read())
     return float(m.group(1)) if m else None
+
+
+def protocol_cells(ops, dev, groups=3, iters=8):
+    """Per-op timing cells: one untimed call, then `groups` groups of `iters`
+    calls, each after writing a 512 MB buffer (so no input is cached) and a
+    device synchronisation, timed with events around the call on the stream
+    the library launches on.  Cell = median of the group medians; drift =
+    (last - first group median) / first; the first op is visited a second
+    time at the end and its ratio to the first visit reported."""
+    import torch
+
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def visit(fn):
+        fn()
+        torch.cuda.synchronize()
+        meds = []
+        for g in range(groups):
+            ts = []
+            for i in range(iters):
+                flush.fill_((g * iters + i) & 0xFF)
+                torch.cuda.synchronize()
+                s.record()
+                fn()
+                e.record()
+                torch.cuda.synchronize()
+                ts.append(s.elapsed_time(e))
+            meds.append(statistics.median(ts))
+        return {"ms": statistics.median(meds), "group_medians": meds, "drift": (meds[-1] - meds[0]) / meds[0]}
+
+    cells = {}
+    for name, fn in ops:
+        t0 = time.perf_counter()
+        cells[name] = visit(fn)
+        cells[name]["window"] = (t0, time.perf_counter())
+    name0, fn0 = ops[0]
+    cells[name0]["control_ratio"] = visit(fn0)["ms"] / cells[name0]["ms"]
+    del flush
+    return cells
+
+
+class SmiSampler:
+    """Samples the GPU's clock and socket power with `amd-smi metric` (run as a
+    child process) from a background thread while the timed work runs.  A
+    missing or failing tool is recorded, never raised."""
+
+    def __init__(self, period_s=0.25):
+        import threading
+
+        self.samples, self.error, self.period = [], None, period_s
+        self.path, self.error = self.available()
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def available():
+        """amd-smi is a Python script: run it with this interpreter (no shebang
+        hop).  Not under a profiler: its preloaded tool library would start the
+        GPU runtime in the child before that child starts the interpreter."""
+        import shutil
+
+        if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+            return None, "not sampled under a profiler"
+        path = shutil.which("amd-smi")
+        return (path, None) if path else (None, "amd-smi not found")
+
+    def _one(self):
+        import subprocess
+
+        r = subprocess.run([sys.executable, self.path, "metric", "-c", "-p", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        g = json.loads(r.stdout)["gpu_data"][0]
+        clks = [v["clk"]["value"] for k, v in g["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        pw = g["power"]["socket_power"]["value"]
+        return {"t": time.perf_counter(), "sclk_mhz": sum(clks) / len(clks) if clks else None,
+                "power_w": pw if isinstance(pw, (int, float)) else None}
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._one())
+            except Exception as ex:  # noqa: BLE001 - the tool is optional
+                self.error = "%s: %s" % (type(ex).__name__, str(ex)[:200])
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join(timeout=30)
+
+    def summary(self, t0=None, t1=None):
+        xs = [x for x in self.samples if (t0 is None or x["t"] >= t0) and (t1 is None or x["t"] <= t1)]
+        clk = [x["sclk_mhz"] for x in xs if x["sclk_mhz"] is not None]
+        pw = [x["power_w"] for x in xs if x["power_w"] is not None]
+        out = {"samples": len(xs)}
+        if clk:
+            out.update(sclk_mhz_median=statistics.median(clk), sclk_mhz_min=min(clk), sclk_mhz_max=max(clk))
+        if pw:
+            out.update(power_w_median=statistics.median(pw), power_w_max=max(pw))
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(inp, docs, tokens_per_doc):
@@ -117,6 +243,7 @@ def cpu_baseline(inp, docs, tokens_per_doc):
     t2 = time.perf_counter()
     th = int(sum(take)) * int(inp["v"].shape[1])
     return {"value": th / (t2 - t0), "unit": "token-heads/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "first %d tokens of each of the %d documents, all %d heads (%d token-heads); "
                       "fwd %.2f s + bwd %.2f s" % (tokens_per_doc, len(docs), inp["v"].shape[1], th,
                                                    t1 - t0, t2 - t1)}
@@ -172,6 +299,14 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    smi = SmiSampler()
+    if args.no_smi:
+        smi.path, smi.error = None, "disabled (--no-smi)"
+    smi.__enter__()
+    if smi.path:
+        time.sleep(1.0)  # let the first sample land before the timed region
+    smi_t0 = time.perf_counter()
+
     # timed region: K steps, per-kernel HIP events inside the library on the same stream
     gdr.timing_read(reset=True)
     gdr.timing_enable(True)
@@ -185,26 +320,22 @@ def main():
     kern = gdr.timing_read(reset=True)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # separate op timings (events on torch's current stream = the library's stream)
-    def time_op(fn, reps=3):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        torch.cuda.synchronize()
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / reps
-
+    # per-op cells (events on torch's current stream = the library's stream); the
+    # backward reuses the tapes of one untimed forward with GDR_FWD_SAVE
     ops = {}
     if not args.no_op_timing:
-        ops["fwd"] = time_op(lambda: fwd(prob, o, ht, ws, 0))
-        ops["fwd_save"] = time_op(lambda: fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE))
-        fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE)
-        ops["bwd"] = time_op(lambda: bwd(prob, dout, None, dq, dk, dv, dg, dbeta, None, ws))
         ckpt = gdr.gdn_ckpt if gdn else gdr.kda_ckpt
-        ops["ckpt"] = time_op(lambda: ckpt(prob, o, ht, dout, None, dq, dk, dv, dg, dbeta, None, ws))
+        fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE)
+        ops = protocol_cells([
+            ("fwd", lambda: fwd(prob, o, ht, ws, 0)),
+            ("fwd_save", lambda: fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE)),
+            ("bwd", lambda: bwd(prob, dout, None, dq, dk, dv, dg, dbeta, None, ws)),
+            ("ckpt", lambda: ckpt(prob, o, ht, dout, None, dq, dk, dv, dg, dbeta, None, ws)),
+        ], dev)
+
+    smi.__exit__()
+    for c in ops.values():
+        c["smi"] = smi.summary(*c.pop("window"))
 
     kernels = {}
     total_flops = 0.0
@@ -219,6 +350,13 @@ def main():
                          "hbm_frac": b / avg / 1e6 / HBM_PEAK_GBS, "mfma_TFLOPs": fl / avg / 1e9,
                          "mfma_frac": fl / avg / 1e9 / MFMA_BF16_PEAK_TFLOPS}
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
+    # dependent steps of the walks: chunks of the longest document (unsegmented
+    # walks: 8 N H_v >= 512 wavefronts, or one chunk per document at most)
+    longest = max((d + 63) // 64 for d in w.docs)
+    unsegmented = args.walk_segments == 1 or 8 * N * Hv >= 512 or NC <= N
+    walk_us = {k: kernels[k]["avg_ms"] * 1e3 / longest for k in ("fwd_walk", "bwd_walk")
+               if k in kernels and unsegmented}
+    floor_ms = T * Hv * FLOOR_BYTES_PER_TOKEN_HEAD[w.variant] / (HBM_PEAK_GBS * 1e6)
     dk_ = kernels[dom]
     traffic = traffic_from_profiles(dom)
     token_heads = T * Hv
@@ -242,7 +380,14 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk_["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dk_["GB_s"] / HBM_PEAK_GBS, "traffic": traffic,
                      "bytes_per_launch": dk_["bytes"], "avg_launch_ms": dk_["avg_ms"]},
-        "ms": ops,
+        "ms": {k: v["ms"] for k, v in ops.items()},
+        "cells": ops,
+        "path_floor": {"ms": floor_ms, "frac": floor_ms / ms_per_step,
+                       "bytes_per_token_head": FLOOR_BYTES_PER_TOKEN_HEAD[w.variant]},
+        "us_per_walk_step": walk_us,
+        "smi": dict(smi.summary(smi_t0), note="amd-smi metric: mean gfx clock over the XCDs, socket power; "
+                    "samples from the start of the timed steps to the end of the per-op cells"),
+        "longest_chain_chunks": longest,
         "mfma": {"TFLOPs": total_flops / (ms_per_step / 1e3) / 1e12,
                  "frac": total_flops / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "kernels": kernels,
