@@ -1212,6 +1212,13 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         const int r = r0 + jj;
         m[jj] = nt <= mt && s <= r ? scale * accM[jj] : 0.f;
         a[jj] = nt <= mt && s < r ? -accA[jj] : 0.f;
+        if constexpr (SCALAR) {
+          // one gate per row: the decay exp(G_r - G_s) (<= 1 for s <= r) and, for
+          // dA, beta_r go into the tiles, and the gated products below are plain
+          const float gam = nt <= mt && s <= r ? __expf(G.at(r, 0) - G.at(s, 0)) : 0.f;
+          m[jj] *= gam;
+          a[jj] *= b4[jj] * gam;
+        }
         sDM[r * MP + s] = f2bf(m[jj]);
         sDA[r * MP + s] = f2bf(a[jj]);
       }
@@ -1220,12 +1227,13 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
     }
     lds_barrier();
 
-    // ---- gated products of dM and dA (16-row blocks, reference row 16I+8) ----
-    // The exponentially rescaled operand is split into bf16 hi + lo: each
-    // (r, s) pair enters dG twice with opposite signs (row side and column
-    // side) and the two must cancel to well below the pair's size.
-    {
-      const int I = mt, ref = 16 * I + 8, kfirst = I >> 1;
+    if constexpr (SCALAR) {
+      // ---- gated products with the decay and beta folded into the tiles:
+      // P_M = dM o Gamma, P_A = diag(beta) (dA o Gamma) (rows r, columns s <= r).
+      //   dq_r += sum_s P_M[r][s] k_s,   dk_r += sum_s P_A[r][s] k_s (row side)
+      //   dk_s += sum_r P_M[r][s] q_r + P_A[r][s] k_r               (column side)
+      // Both sides of every (r, s) pair of dG read the same rounded P. ----
+      const int I = mt, kfirst = I >> 1;
       bf16x8 aM[2], aA[2], aMT[2], aAT[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -1237,70 +1245,118 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
 #pragma unroll 1
       for (int t = 0; t < 4; ++t) {
         const int c = 16 * (4 * ch + t) + lr;
-        const float gref = G.at(ref, c);
-        // rows r of block I, sums over s <= r (s in blocks <= I)
-        f32x4 accM = zero4(), accA = zero4();
+        f32x4 accM = zero4(), accA = zero4(), accT = zero4();
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          if (kt > kfirst) continue;
           const int s0 = 32 * kt + 8 * lg;
           const bf16x8 k8 = ld8(sKT + c * QTP + s0);
-          const float4 ga = G.at4(s0, c), gb = G.at4(s0 + 4, c);
-          bf16x8 bh, bl;
-#pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const float gs = ii < 4 ? ga[ii] : gb[ii - 4];
-            const float x = s0 + ii <= 16 * I + 15 ? (float)k8[ii] * __expf(gref - gs) : 0.f;
-            split_bf16(x, bh, bl, ii);
+          if (kt <= kfirst) {  // row side: s in blocks <= I
+            accM = mfma(aM[kt], k8, accM);
+            accA = mfma(aA[kt], k8, accA);
           }
-          accM = mfma(aM[kt], bh, accM);
-          accM = mfma(aM[kt], bl, accM);
-          accA = mfma(aA[kt], bh, accA);
-          accA = mfma(aA[kt], bl, accA);
-        }
-        // rows s of block I, sums over r >= s (r in blocks >= I)
-        f32x4 accT = zero4();
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          if (kt < kfirst) continue;
-          const int s0 = 32 * kt + 8 * lg;
-          const bf16x8 q8 = ld8(sQT + c * QTP + s0), k8 = ld8(sKT + c * QTP + s0);
-          const float4 ga = G.at4(s0, c), gb = G.at4(s0 + 4, c);
-          const float4 ba = *reinterpret_cast<const float4 *>(sB + s0);
-          const float4 bb = *reinterpret_cast<const float4 *>(sB + s0 + 4);
-          bf16x8 qh, ql, kh, kl;
-#pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const float gr = ii < 4 ? ga[ii] : gb[ii - 4];
-            const float br = ii < 4 ? ba[ii] : bb[ii - 4];
-            const float e = s0 + ii >= 16 * I ? __expf(gr - gref) : 0.f;
-            split_bf16((float)q8[ii] * e, qh, ql, ii);
-            split_bf16(br * (float)k8[ii] * e, kh, kl, ii);
+          if (kt >= kfirst) {  // column side: r in blocks >= I
+            accT = mfma(aMT[kt], ld8(sQT + c * QTP + s0), accT);
+            accT = mfma(aAT[kt], k8, accT);
           }
-          accT = mfma(aMT[kt], qh, accT);
-          accT = mfma(aMT[kt], ql, accT);
-          accT = mfma(aAT[kt], kh, accT);
-          accT = mfma(aAT[kt], kl, accT);
         }
-        const float4 g4 = G.at4(r0, c);
         const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
         const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
         f32x4 xq, xk, xg;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float er = __expf(g4[jj] - gref), es = __expf(gref - g4[jj]);
           const float qv = bf_at(q4, jj), kv = bf_at(k4, jj);
-          const float qM = er * accM[jj];
-          const float kA = b4[jj] * er * accA[jj];
-          const float kT = es * accT[jj];
-          xq[jj] = qM;
-          xk[jj] = kA + kT;
-          xg[jj] = qv * qM + kv * (kA - kT);
+          xq[jj] = accM[jj];
+          xk[jj] = accA[jj] + accT[jj];
+          xg[jj] = qv * accM[jj] + kv * (accA[jj] - accT[jj]);
         }
         add_tile(dqA, t, xq);
         add_tile(dkA, t, xk);
         add_tile(dGA, t, xg);
       }
+    } else {
+    // ---- gated products of dM and dA (16-row blocks, reference row 16I+8) ----
+      // The exponentially rescaled operand is split into bf16 hi + lo: each
+      // (r, s) pair enters dG twice with opposite signs (row side and column
+      // side) and the two must cancel to well below the pair's size.
+      {
+        const int I = mt, ref = 16 * I + 8, kfirst = I >> 1;
+        bf16x8 aM[2], aA[2], aMT[2], aAT[2];
+  #pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          aM[kt] = ld8(sDM + ra * MP + 32 * kt + 8 * lg);
+          aA[kt] = ld8(sDA + ra * MP + 32 * kt + 8 * lg);
+          aMT[kt] = ld8(sDMT + ra * MP + 32 * kt + 8 * lg);
+          aAT[kt] = ld8(sDAT + ra * MP + 32 * kt + 8 * lg);
+        }
+  #pragma unroll 1
+        for (int t = 0; t < 4; ++t) {
+          const int c = 16 * (4 * ch + t) + lr;
+          const float gref = G.at(ref, c);
+          // rows r of block I, sums over s <= r (s in blocks <= I)
+          f32x4 accM = zero4(), accA = zero4();
+  #pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            if (kt > kfirst) continue;
+            const int s0 = 32 * kt + 8 * lg;
+            const bf16x8 k8 = ld8(sKT + c * QTP + s0);
+            const float4 ga = G.at4(s0, c), gb = G.at4(s0 + 4, c);
+            bf16x8 bh, bl;
+  #pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+              const float gs = ii < 4 ? ga[ii] : gb[ii - 4];
+              const float x = s0 + ii <= 16 * I + 15 ? (float)k8[ii] * __expf(gref - gs) : 0.f;
+              split_bf16(x, bh, bl, ii);
+            }
+            accM = mfma(aM[kt], bh, accM);
+            accM = mfma(aM[kt], bl, accM);
+            accA = mfma(aA[kt], bh, accA);
+            accA = mfma(aA[kt], bl, accA);
+          }
+          // rows s of block I, sums over r >= s (r in blocks >= I)
+          f32x4 accT = zero4();
+  #pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            if (kt < kfirst) continue;
+            const int s0 = 32 * kt + 8 * lg;
+            const bf16x8 q8 = ld8(sQT + c * QTP + s0), k8 = ld8(sKT + c * QTP + s0);
+            const float4 ga = G.at4(s0, c), gb = G.at4(s0 + 4, c);
+            const float4 ba = *reinterpret_cast<const float4 *>(sB + s0);
+            const float4 bb = *reinterpret_cast<const float4 *>(sB + s0 + 4);
+            bf16x8 qh, ql, kh, kl;
+  #pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+              const float gr = ii < 4 ? ga[ii] : gb[ii - 4];
+              const float br = ii < 4 ? ba[ii] : bb[ii - 4];
+              const float e = s0 + ii >= 16 * I ? __expf(gr - gref) : 0.f;
+              split_bf16((float)q8[ii] * e, qh, ql, ii);
+              split_bf16(br * (float)k8[ii] * e, kh, kl, ii);
+            }
+            accT = mfma(aMT[kt], qh, accT);
+            accT = mfma(aMT[kt], ql, accT);
+            accT = mfma(aAT[kt], kh, accT);
+            accT = mfma(aAT[kt], kl, accT);
+          }
+          const float4 g4 = G.at4(r0, c);
+          const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
+          const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
+          f32x4 xq, xk, xg;
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float er = __expf(g4[jj] - gref), es = __expf(gref - g4[jj]);
+            const float qv = bf_at(q4, jj), kv = bf_at(k4, jj);
+            const float qM = er * accM[jj];
+            const float kA = b4[jj] * er * accA[jj];
+            const float kT = es * accT[jj];
+            xq[jj] = qM;
+            xk[jj] = kA + kT;
+            xg[jj] = qv * qM + kv * (kA - kT);
+          }
+          add_tile(dqA, t, xq);
+          add_tile(dkA, t, xk);
+          add_tile(dGA, t, xg);
+        }
+      }
+  
     }
 
     // ---- dbeta ----
