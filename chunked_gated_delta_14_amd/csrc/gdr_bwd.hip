@@ -415,7 +415,6 @@ __device__ __forceinline__ void load_qk_rows(u16 *sQT, u16 *sKT, const Problem &
 
 __device__ __forceinline__ float sigmoidf_(float b) { return 1.f / (1.f + __expf(-b)); }
 
-template <bool SCALAR>
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -423,7 +422,6 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
   const int chunk = blockIdx.x / p.Hqk, iqk = blockIdx.x % p.Hqk;
   const ChunkTable tb(p.table, p.NC, p.N);
   const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
-  const int grp = SCALAR ? p.Hv / p.Hqk : 1;  // KDA: H_qk == H_v
   const float scale = p.scale;
   const size_t Hv = p.Hv;
 
@@ -441,7 +439,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
   float *sB = reinterpret_cast<float *>(smem + G_B);
   float *sDB = reinterpret_cast<float *>(smem + G_DB);
   float *sRS = reinterpret_cast<float *>(smem + G_RS);
-  const GateT<SCALAR> G{sG};
+  const GateT<false> G{sG};
 
   float *sNrm = reinterpret_cast<float *>(smem + G_NRM);
   // (the dout stage is free until the first iteration's loads: scratch of the row norms)
@@ -451,14 +449,14 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 #pragma unroll
   for (int t = 0; t < 4; ++t) { dqA[t] = zero4(); dkA[t] = zero4(); }
 
-  for (int jg = 0; jg < grp; ++jg) {
+  {
     // Re-derive the thread coordinates from an opaque copy of the thread id so
-    // the compiler cannot hoist per-element address arithmetic of the group
-    // loop out of it (that would keep hundreds of values live across it).
+    // the compiler cannot hoist per-element address arithmetic out of this
+    // block (that would keep hundreds of values live across it).
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int j = iqk * grp + jg;
+    const int j = iqk;  // H_qk == H_v
     const size_t u = (size_t)chunk * Hv + j;
     const int c = 16 * wave + lr;  // this lane's key/value column
 
@@ -467,9 +465,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     float graw[2][8];
     uint32_t braw = 0u;
     const int o8 = tid >> 5, pr = tid & 31, c0g = 8 * o8, rp = 2 * pr;  // gate loader coordinates
-    if constexpr (SCALAR) {
-      if (tid < 64) graw[0][0] = p.g[(size_t)(start + (tid < len ? tid : last)) * Hv + j];
-    } else {
+    {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = rp + h < len ? rp + h : last;
@@ -481,7 +477,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     }
     if (tid < 64) {
       const size_t e = (size_t)(start + (tid < len ? tid : last)) * Hv + j;
-      braw = SCALAR ? reinterpret_cast<const uint32_t *>(p.beta)[e] : reinterpret_cast<const u16 *>(p.beta)[e];
+      braw = reinterpret_cast<const u16 *>(p.beta)[e];
     }
     // Y operands: T^T (one 16-byte piece per thread, for the LDS stage), this
     // wavefront's value tile of dVn^T, and v at the accumulator positions
@@ -511,23 +507,13 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     }
     // ---- beta, cleared sums, the cumulative gate ----
     if (tid < 64) {
-      float b = SCALAR ? __uint_as_float(braw) : bf2f((u16)braw);
+      float b = bf2f((u16)braw);
       if (p.inflags & IN_BETA_SIGMOID) b = sigmoidf_(b);
       sB[tid] = tid < len ? b : 0.f;
     }
     if (tid < 256) sDB[16 * 64 + tid] = 0.f;  // E-term slots (not every row block writes every slot)
     *reinterpret_cast<u32x4 *>(sTT + (tid >> 3) * MP + 8 * (tid & 7)) = stT;
-    if constexpr (SCALAR) {
-      if (tid < 64) {
-        float x = tid < len ? graw[0][0] : 0.f;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float y = __shfl_up(x, o, 64);
-          if (tid >= o) x += y;
-        }
-        sG[tid] = x;
-      }
-    } else {
+    {
       // the 32 lanes of a half wavefront scan their channel octet's 64 rows
 #pragma unroll
       for (int ii = 0; ii < 8; ++ii) {
@@ -834,7 +820,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         for (int jj = 0; jj < 4; ++jj)
           if (16 * I + 4 * lg + jj == last) dGA[I][jj] += extra;
     }
-    if constexpr (!SCALAR) {
+    {
       // suffix sums inside the lane (4 rows), across the lane groups (16-row
       // block) and across the row blocks, all within the wavefront
       float tot[4], up[4], blk[4];
@@ -860,16 +846,6 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
         sg.put16((uint32_t)(16 * I + lr) * rowb + 16 * lg, __builtin_bit_cast(u32x4, tile_row4_f32(x, lane)));
         below += blk[I];
       }
-    } else {
-      // row sums over the channels (16 per wavefront, then across the
-      // wavefronts), then a reverse scan over the rows
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float x = red16(dGA[I][jj]);
-          if (lr == 0) sRS[wave * 64 + 16 * I + 4 * lg + jj] = x;
-        }
     }
     lds_barrier();  // dbeta partial sums complete (and GDN row sums)
     if (tid < 64 && tid < len) {
@@ -878,22 +854,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
       for (int k = 0; k < 20; ++k) x += sDB[k * 64 + tid];
       if (p.inflags & IN_BETA_SIGMOID) x *= sB[tid] * (1.f - sB[tid]);  // to the logit
       const size_t e = (size_t)(start + tid) * Hv + j;
-      if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = x;
-      else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
-    }
-    if constexpr (SCALAR) {
-      if (tid < 64) {
-        float y = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < 8; ++ww) y += sRS[ww * 64 + 63 - tid];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float z = __shfl_up(y, o, 64);
-          if (tid >= o) y += z;
-        }
-        const int rr = 63 - tid;  // y = sum of rows rr..63
-        if (rr < len) dg[(size_t)(start + rr) * Hv + j] = y;
-      }
+      reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
     }
     {  // dv: pairs of row blocks regrouped into 16-byte row pieces
       const uint32_t rowb = (uint32_t)(Hv * HD * 2);
@@ -957,14 +918,13 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 // set fits without spilling; the gate factors there are exponentials of
 // per-row scalars.
 // ---------------------------------------------------------------------------
-template <bool SCALAR>
 constexpr int grad_rows_smem_bytes() {
   return 2 * HD * QTP * 2                   // sQT, sKT
          + CH * KP * 2                      // sY
          + 4 * CH * MP * 2                  // sDM, sDA, sDMT, sDAT
          + (64 + 64 + 128 + 128 + 512) * 4  // sB, sDB, sRed, sDgam, sBT
          + (128 + 64 * 4) * 4               // q, k row norms [2][64], row dots [64][2][2]
-         + (SCALAR ? 64 * 4 : HD * GTP * 4);  // sG
+         + 64 * 4;                          // sG
 }
 
 // acc[t] += x for a run-time tile index t, without indexing a register array
@@ -975,7 +935,6 @@ __device__ __forceinline__ void add_tile(f32x4 (&acc)[4], int t, const f32x4 &x)
     if (i == t) acc[i] += x;
 }
 
-template <bool SCALAR>
 __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -983,7 +942,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
   const int chunk = blockIdx.x / p.Hqk, iqk = blockIdx.x % p.Hqk;
   const ChunkTable tb(p.table, p.NC, p.N);
   const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
-  const int grp = SCALAR ? p.Hv / p.Hqk : 1;  // KDA: H_qk == H_v
+  const int grp = p.Hv / p.Hqk;  // value heads of the Q/K head
   const float scale = p.scale;
   const size_t Hv = p.Hv;
 
@@ -1000,8 +959,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
   float *sDgam = sRed + 128;
   float *sBT = sDgam + 128;  // [4][128] row-block totals of the gate gradient
   float *sG = sBT + 512;
-  float *sNrm = sG + (SCALAR ? 64 : HD * GTP);  // q, k row norms [2][64], then row dots [64][2][2]
-  const GateT<SCALAR> G{sG};
+  float *sNrm = sG + 64;  // q, k row norms [2][64], then row dots [64][2][2]
+  const GateT<true> G{sG};
 
   // (the Y stage is free until the first iteration: scratch of the row norms)
   load_qk_rows<QTP>(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(sY), sNrm);
@@ -1028,7 +987,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
       float b = 0.f;
       if (tid < len) {
         const size_t e = (size_t)(start + tid) * Hv + j;
-        b = SCALAR ? reinterpret_cast<const float *>(p.beta)[e] : bf2f(reinterpret_cast<const u16 *>(p.beta)[e]);
+        b = reinterpret_cast<const float *>(p.beta)[e];
         if (p.inflags & IN_BETA_SIGMOID) b = sigmoidf_(b);
       }
       sB[tid] = b;
@@ -1047,7 +1006,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) aDV[t][kt] = ld8(dvt + (16 * (4 * ch + t) + lr) * CH + 32 * kt + 8 * lg);
     }
-    if constexpr (SCALAR) {
+    {
       if (tid < 64) {
         float x = tid < len ? p.g[(size_t)(start + tid) * Hv + j] : 0.f;
 #pragma unroll
@@ -1056,33 +1015,6 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
           if (tid >= o) x += y;
         }
         sG[tid] = x;
-      }
-      lds_barrier();
-    } else {
-      // thread: channel octet 8o..8o+7, rows 2pr and 2pr+1, read as 16-byte
-      // pieces; the 32 lanes of a half wavefront scan their octet's 64 rows
-      const int o = tid >> 5, pr = tid & 31, c0 = 8 * o, rp = 2 * pr;
-      float gx[2][8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float4 ga = make_float4(0.f, 0.f, 0.f, 0.f), gb = ga;
-        if (rp + h < len) {
-          const float *src = p.g + ((size_t)(start + rp + h) * Hv + j) * HD + c0;
-          ga = *reinterpret_cast<const float4 *>(src);
-          gb = *reinterpret_cast<const float4 *>(src + 4);
-        }
-        gx[h][0] = ga.x; gx[h][1] = ga.y; gx[h][2] = ga.z; gx[h][3] = ga.w;
-        gx[h][4] = gb.x; gx[h][5] = gb.y; gx[h][6] = gb.z; gx[h][7] = gb.w;
-      }
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        float incl = gx[0][ii] + gx[1][ii];
-#pragma unroll
-        for (int d = 1; d < 32; d <<= 1) {
-          const float y = __shfl_up(incl, d, 32);
-          if (pr >= d) incl += y;
-        }
-        *reinterpret_cast<float2 *>(sG + (c0 + ii) * GTP + rp) = make_float2(incl - gx[1][ii], incl);
       }
       lds_barrier();
     }
@@ -1212,7 +1144,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         const int r = r0 + jj;
         m[jj] = nt <= mt && s <= r ? scale * accM[jj] : 0.f;
         a[jj] = nt <= mt && s < r ? -accA[jj] : 0.f;
-        if constexpr (SCALAR) {
+        {
           // one gate per row: the decay exp(G_r - G_s) (<= 1 for s <= r) and, for
           // dA, beta_r go into the tiles, and the gated products below are plain
           const float gam = nt <= mt && s <= r ? __expf(G.at(r, 0) - G.at(s, 0)) : 0.f;
@@ -1227,7 +1159,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
     }
     lds_barrier();
 
-    if constexpr (SCALAR) {
+    {
       // ---- gated products with the decay and beta folded into the tiles:
       // P_M = dM o Gamma, P_A = diag(beta) (dA o Gamma) (rows r, columns s <= r).
       //   dq_r += sum_s P_M[r][s] k_s,   dk_r += sum_s P_A[r][s] k_s (row side)
@@ -1273,90 +1205,6 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
         add_tile(dkA, t, xk);
         add_tile(dGA, t, xg);
       }
-    } else {
-    // ---- gated products of dM and dA (16-row blocks, reference row 16I+8) ----
-      // The exponentially rescaled operand is split into bf16 hi + lo: each
-      // (r, s) pair enters dG twice with opposite signs (row side and column
-      // side) and the two must cancel to well below the pair's size.
-      {
-        const int I = mt, ref = 16 * I + 8, kfirst = I >> 1;
-        bf16x8 aM[2], aA[2], aMT[2], aAT[2];
-  #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          aM[kt] = ld8(sDM + ra * MP + 32 * kt + 8 * lg);
-          aA[kt] = ld8(sDA + ra * MP + 32 * kt + 8 * lg);
-          aMT[kt] = ld8(sDMT + ra * MP + 32 * kt + 8 * lg);
-          aAT[kt] = ld8(sDAT + ra * MP + 32 * kt + 8 * lg);
-        }
-  #pragma unroll 1
-        for (int t = 0; t < 4; ++t) {
-          const int c = 16 * (4 * ch + t) + lr;
-          const float gref = G.at(ref, c);
-          // rows r of block I, sums over s <= r (s in blocks <= I)
-          f32x4 accM = zero4(), accA = zero4();
-  #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            if (kt > kfirst) continue;
-            const int s0 = 32 * kt + 8 * lg;
-            const bf16x8 k8 = ld8(sKT + c * QTP + s0);
-            const float4 ga = G.at4(s0, c), gb = G.at4(s0 + 4, c);
-            bf16x8 bh, bl;
-  #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              const float gs = ii < 4 ? ga[ii] : gb[ii - 4];
-              const float x = s0 + ii <= 16 * I + 15 ? (float)k8[ii] * __expf(gref - gs) : 0.f;
-              split_bf16(x, bh, bl, ii);
-            }
-            accM = mfma(aM[kt], bh, accM);
-            accM = mfma(aM[kt], bl, accM);
-            accA = mfma(aA[kt], bh, accA);
-            accA = mfma(aA[kt], bl, accA);
-          }
-          // rows s of block I, sums over r >= s (r in blocks >= I)
-          f32x4 accT = zero4();
-  #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            if (kt < kfirst) continue;
-            const int s0 = 32 * kt + 8 * lg;
-            const bf16x8 q8 = ld8(sQT + c * QTP + s0), k8 = ld8(sKT + c * QTP + s0);
-            const float4 ga = G.at4(s0, c), gb = G.at4(s0 + 4, c);
-            const float4 ba = *reinterpret_cast<const float4 *>(sB + s0);
-            const float4 bb = *reinterpret_cast<const float4 *>(sB + s0 + 4);
-            bf16x8 qh, ql, kh, kl;
-  #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              const float gr = ii < 4 ? ga[ii] : gb[ii - 4];
-              const float br = ii < 4 ? ba[ii] : bb[ii - 4];
-              const float e = s0 + ii >= 16 * I ? __expf(gr - gref) : 0.f;
-              split_bf16((float)q8[ii] * e, qh, ql, ii);
-              split_bf16(br * (float)k8[ii] * e, kh, kl, ii);
-            }
-            accT = mfma(aMT[kt], qh, accT);
-            accT = mfma(aMT[kt], ql, accT);
-            accT = mfma(aAT[kt], kh, accT);
-            accT = mfma(aAT[kt], kl, accT);
-          }
-          const float4 g4 = G.at4(r0, c);
-          const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * QTP + r0);
-          const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * QTP + r0);
-          f32x4 xq, xk, xg;
-  #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float er = __expf(g4[jj] - gref), es = __expf(gref - g4[jj]);
-            const float qv = bf_at(q4, jj), kv = bf_at(k4, jj);
-            const float qM = er * accM[jj];
-            const float kA = b4[jj] * er * accA[jj];
-            const float kT = es * accT[jj];
-            xq[jj] = qM;
-            xk[jj] = kA + kT;
-            xg[jj] = qv * qM + kv * (kA - kT);
-          }
-          add_tile(dqA, t, xq);
-          add_tile(dkA, t, xk);
-          add_tile(dGA, t, xg);
-        }
-      }
-  
     }
 
     // ---- dbeta ----
@@ -1370,8 +1218,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
       const size_t e = (size_t)(start + tid) * Hv + j;
       float x = sDB[tid];
       if (p.inflags & IN_BETA_SIGMOID) x *= sB[tid] * (1.f - sB[tid]);  // to the logit
-      if (SCALAR) reinterpret_cast<float *>(dbeta)[e] = x;
-      else reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
+      reinterpret_cast<float *>(dbeta)[e] = x;
     }
 
     // ---- gate epilogue: dg = in-chunk reverse cumulative sum of dG ----
@@ -1387,30 +1234,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
           if (r0 + jj == last) dGA[t][jj] += extra;
       }
     }
-    if constexpr (!SCALAR) {
-      // suffix sums inside the lane (4 rows), across the lane groups (16-row
-      // block), then across the row blocks through LDS
-      float hsum[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float s3 = dGA[t][3], s2 = s3 + dGA[t][2], s1 = s2 + dGA[t][1], s0 = s1 + dGA[t][0];
-        const float up = sum_above_lg(s0, lg);
-        hsum[t][0] = s0 + up; hsum[t][1] = s1 + up; hsum[t][2] = s2 + up; hsum[t][3] = s3 + up;
-        if (lg == 0) sBT[mt * 128 + 16 * (4 * ch + t) + lr] = hsum[t][0];
-      }
-      lds_barrier();
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = 16 * (4 * ch + t) + lr;
-        float below = 0.f;
-        for (int b = mt + 1; b < 4; ++b) below += sBT[b * 128 + c];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = r0 + jj;
-          if (r < len) dg[((size_t)(start + r) * Hv + j) * HD + c] = hsum[t][jj] + below;
-        }
-      }
-    } else {
+    {
       // row sums over the channels, then a reverse scan over the rows
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -1500,14 +1324,14 @@ hipError_t launch_bwd_grad(bool gdn, const Problem &p, const Workspace &w, const
   const dim3 grid(p.NC * p.Hqk), block(GNT);
   hipError_t e;
   if (gdn) {
-    const int sm = grad_rows_smem_bytes<true>();
-    e = set_dynamic_lds_once((const void *)bwd_grad_rows_kernel<true>, sm);
+    const int sm = grad_rows_smem_bytes();
+    e = set_dynamic_lds_once((const void *)bwd_grad_rows_kernel, sm);
     if (e != hipSuccess) return e;
-    bwd_grad_rows_kernel<true><<<grid, block, sm, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
+    bwd_grad_rows_kernel<<<grid, block, sm, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
   } else {
-    e = set_dynamic_lds_once((const void *)bwd_grad_kernel<false>, G_SMEM);
+    e = set_dynamic_lds_once((const void *)bwd_grad_kernel, G_SMEM);
     if (e != hipSuccess) return e;
-    bwd_grad_kernel<false><<<grid, block, G_SMEM, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
+    bwd_grad_kernel<<<grid, block, G_SMEM, st>>>(p, w, dout, dq, dk, dv, dg, dbeta);
   }
   return hipGetLastError();
 }
