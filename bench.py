@@ -26,7 +26,7 @@ METRIC = "KDA fwd+bwd token-heads/s, H=16, T=261392 (1 GPU); % MFMA & HBM peak"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
-# Per (chunk, value head) unit bytes of the workspace regions (see DESIGN.md).
+# Per (chunk, value head) unit bytes of the workspace regions.
 FWD_OPERANDS = 16384 * 3 + 16384 * 2 + 512   # -W, P, Kbar^T fragments; U, Oi; gamma
 BWD_OPERANDS = 16384 * 3 + 8192               # Kbar, -W^T, (q Gamma)^T fragments; M^T
 TE_SAVED = 8192 + 5120                         # T^T (bf16 64 x 64) and E's 10 lower tiles (bf16)

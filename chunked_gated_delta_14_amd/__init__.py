@@ -16,7 +16,7 @@ import numpy as np
 from . import _build
 
 __all__ = [
-    "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GDR_IN_QK_L2NORM", "GDR_IN_BETA_SIGMOID", "GdrError", "lib", "plan_chunks", "workspace_bytes",
+    "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GDR_IN_QK_L2NORM", "GDR_IN_BETA_SIGMOID", "GDR_WALK_AUTO", "GDR_WALK_SLICES", "GDR_WALK_RINGS", "GdrError", "lib", "plan_chunks", "max_doc_chunks", "workspace_bytes",
     "Problem", "kda_fwd", "kda_bwd", "gdn_fwd", "gdn_bwd", "kda_ckpt", "gdn_ckpt", "status_string",
     "check_device", "timing_enable", "timing_read", "EXPORTED_SYMBOLS",
 ]
@@ -27,6 +27,7 @@ GDR_FWD_SAVE = 1
 GDR_FWD_SKIP_OUTPUT = 2  # forward without the output (o may be None): the recompute of a ckpt step
 GDR_IN_QK_L2NORM = 1     # Problem input flag: q, k rows scaled to unit L2 norm inside the kernels
 GDR_IN_BETA_SIGMOID = 2  # Problem input flag: beta holds logits, sigmoid applied inside the kernels
+GDR_WALK_AUTO, GDR_WALK_SLICES, GDR_WALK_RINGS = 0, 1, 2  # Problem walk_layout
 
 EXPORTED_SYMBOLS = (
     "gdr_plan_chunks", "gdr_workspace_bytes", "gdr_kda_fwd", "gdr_kda_bwd", "gdr_gdn_fwd",
@@ -49,6 +50,7 @@ class _CProblem(ctypes.Structure):
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("chunk_table", ctypes.c_void_p), ("n_chunks", ctypes.c_int32), ("h0", ctypes.c_void_p),
         ("scale", ctypes.c_float), ("input_flags", ctypes.c_uint32), ("walk_segments", ctypes.c_int32),
+        ("max_doc_chunks", ctypes.c_int32), ("walk_layout", ctypes.c_int32),
     ]
 
 
@@ -163,6 +165,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def max_doc_chunks(table, N, n_chunks) -> int:
+    """Chunks of the longest document, from the planner's per-document first-chunk section."""
+    if N == 0 or n_chunks == 0:
+        return 0
+    doc_ptr = np.asarray(table[3 * n_chunks:3 * n_chunks + N + 1], dtype=np.int64)
+    return int(np.max(np.diff(doc_ptr)))
+
+
 class Problem:
     """A packed problem: the input tensors (device), cu_seqlens and its chunk table.
 
@@ -171,9 +181,11 @@ class Problem:
     cu_seqlens: host sequence or tensor of N+1 ints; h0: fp32 [N, H_v, 128, 128] or None.
     input_flags: GDR_IN_QK_L2NORM and/or GDR_IN_BETA_SIGMOID (activations applied in the kernels).
     walk_segments: 0 = automatic segmentation of the state walks, n >= 1 = at most n segments.
+    walk_layout: GDR_WALK_AUTO, GDR_WALK_SLICES or GDR_WALK_RINGS (launch layout of the walks).
     """
 
-    def __init__(self, variant, q, k, v, g, beta, cu_seqlens, h0=None, scale=None, input_flags=0, walk_segments=0):
+    def __init__(self, variant, q, k, v, g, beta, cu_seqlens, h0=None, scale=None, input_flags=0, walk_segments=0,
+                 walk_layout=GDR_WALK_AUTO):
         import torch
 
         self.variant = variant
@@ -195,7 +207,7 @@ class Problem:
                             q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                             self.cu.data_ptr(), self.table.data_ptr(), nc,
                             h0.data_ptr() if h0 is not None else None, self.scale, int(input_flags),
-                            int(walk_segments))
+                            int(walk_segments), max_doc_chunks(table, self.N, nc), int(walk_layout))
         self.input_flags = int(input_flags)
 
     def workspace_bytes(self, flags=GDR_FWD_SAVE) -> int:

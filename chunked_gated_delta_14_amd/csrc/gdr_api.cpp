@@ -187,6 +187,10 @@ int32_t check_problem(int32_t variant, const gdr_problem *p) {
   if (p->input_flags & ~(GDR_IN_QK_L2NORM | GDR_IN_BETA_SIGMOID))
     return fail(GDR_ERR_INVALID_ARG, "unknown input flag");
   if (p->walk_segments < 0) return fail(GDR_ERR_INVALID_ARG, "walk_segments < 0");
+  if (p->max_doc_chunks < 0 || p->max_doc_chunks > p->n_chunks)
+    return fail(GDR_ERR_INVALID_ARG, "max_doc_chunks outside [0, n_chunks]");
+  if (p->walk_layout != GDR_WALK_AUTO && p->walk_layout != GDR_WALK_SLICES && p->walk_layout != GDR_WALK_RINGS)
+    return fail(GDR_ERR_INVALID_ARG, "unknown walk_layout");
   return GDR_OK;
 }
 
@@ -220,6 +224,8 @@ gdr::Problem to_internal(const gdr_problem *p) {
   q.inflags = (int)p->input_flags;
   q.P = walk_segments(p->N, p->H_v, p->n_chunks);
   if (p->walk_segments > 0 && p->walk_segments < q.P) q.P = p->walk_segments;
+  q.L = p->max_doc_chunks > 0 ? p->max_doc_chunks : p->n_chunks;
+  q.layout = p->walk_layout;
   return q;
 }
 

@@ -208,6 +208,170 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
   }
 }
 
+// Adjoint walk with the slice wavefronts of a chain in workgroups of NW, as
+// fwd_walk_wg_kernel: the chain's shared per-chunk operands ((q Gamma)^T, M^T,
+// Kbar, -W^T fragments and the gate factors: 56 tiles) pass once per chunk
+// through a two-slot LDS ring (three slots would not fit); each wavefront
+// fetches 56 / NW tiles of the next chunk into registers at the top of a step
+// and writes them to the free slot at its end.  dout stays a per-slice register
+// prefetch.  Same products in the same order as bwd_walk_kernel.
+constexpr int WGB_TILES = 56;                                    // QGT 0..15, MTs 16..23, Kb 24..39, WTn 40..55
+constexpr int WGB_SLOT = WGB_TILES * FRAG_TILE_U4 * 16 + HD * 4;  // bytes per ring slot (+ gamma)
+constexpr int WGB_SMEM = 2 * WGB_SLOT;
+constexpr int WGB_NW = 4;
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspace w, const u16 *dout,
+                                                              const float *dht, float *dh0) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const ChunkTable tb(p.table, p.NC, p.N);
+  int chain, half;
+  walk_block<NW>(blockIdx.x, chain, half);  // the 8 / NW workgroups of a chain on one XCD
+  WalkChain wc;
+  if (!walk_chain(p, tb, chain, p.P, false, wc)) return;  // uniform over the workgroup
+  const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
+  const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sl = NW * half + wv;  // this wavefront's slice
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int vcol = 16 * sl + lr;
+  const size_t Hv = p.Hv;
+  const uint32_t row_bytes = (uint32_t)(Hv * HD * 2);
+  const s16x4 eye = eye16(lane);
+  constexpr int PER = WGB_TILES / NW;
+
+  f32x4 dS[8];
+  const float *dh = dht ? dht + ((size_t)d * Hv + j) * HD * HD : nullptr;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dS[mt][jj] = dh ? dh[(16 * mt + 4 * lg + jj) * HD + vcol] : 0.f;
+  for (int t = wc.Pd - 1; t > wc.s; --t) {  // adjoint entering segment s: back through the later segments
+    const float *cb = carry_of(p, w, d, t - 1, j);
+    apply_carry(dS, cb, cb + HD * HD, 16 * sl, lane);
+  }
+
+  const int prow = 16 * (lg >> 1) + lr, pcol = 8 * (lg & 1);
+  u32x4 pdo[2];
+  auto fetch_dout = [&](int n) {
+    const int r0 = tok0 + CH * n;
+    const RowSource src(dout + ((size_t)r0 * Hv + j) * HD + 16 * sl, (uint32_t)min(CH, tok1 - r0) * row_bytes);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pdo[h] = src.get16((uint32_t)(32 * h + prow) * row_bytes + 2 * pcol);
+  };
+  auto tile_src = [&](size_t u, int t) -> const uint4 * {
+    if (t < 16) return w.QGT + u * FRAG_64x128_U4 + t * 64 + lane;
+    if (t < 24) return w.MTs + u * FRAG_64x64_U4 + (t - 16) * 64 + lane;
+    return (t < 40 ? w.Kb : w.WTn) + u * FRAG_64x128_U4 + ((t - 24) & 15) * 64 + lane;
+  };
+  u32x4 stage[PER];
+  float4 gst = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fetch = [&](size_t u) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) stage[i] = __builtin_bit_cast(u32x4, *tile_src(u, wv + NW * i));
+    if (wv == 0 && lane < 32) gst = *reinterpret_cast<const float4 *>(w.gam + u * HD + 4 * lane);
+  };
+  auto put = [&](int slot) {
+    unsigned char *base = smem + slot * WGB_SLOT;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) *reinterpret_cast<u32x4 *>(base + (wv + NW * i) * 1024 + lane * 16) = stage[i];
+    if (wv == 0 && lane < 32) *reinterpret_cast<float4 *>(base + WGB_TILES * 1024 + lane * 16) = gst;
+  };
+  auto frag = [&](int slot, int t) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8 *>(smem + slot * WGB_SLOT + t * 1024 + lane * 16);
+  };
+
+  if (nch > 0) {
+    fetch((size_t)(first + nch - 1) * Hv + j);
+    fetch_dout(nch - 1);
+    put(0);
+  }
+  lds_barrier();
+
+  for (int n = nch - 1, it = 0; n >= 0; --n, ++it) {
+    const size_t u = (size_t)(first + n) * Hv + j;
+    const size_t un = n > 0 ? u - Hv : u;
+    const int slot = it & 1;
+    if (n > 0) fetch(un);
+
+    float4 gm[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      gm[mt] = *reinterpret_cast<const float4 *>(smem + slot * WGB_SLOT + WGB_TILES * 1024 + (16 * mt + 4 * lg) * 4);
+
+    bf16x8 dOb[2];  // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns)
+    {
+      f32x4 dO[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint2 X, Y;
+        pair_from_rows8(pdo[h], X, Y);
+        dO[2 * h] = mfma16(as_s4(X), eye, zero4());
+        dO[2 * h + 1] = mfma16(as_s4(Y), eye, zero4());
+      }
+      dOb[0] = acc_pair_to_b(dO[0], dO[1]);
+      dOb[1] = acc_pair_to_b(dO[2], dO[3]);
+    }
+    fetch_dout(n > 0 ? n - 1 : 0);
+
+    bf16x8 dSb[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) dSb[kt] = acc_pair_to_b(dS[2 * kt], dS[2 * kt + 1]);
+    {  // this slice's block [key][16] of the adjoint-state tape
+      u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + prow * 16 + pcol;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        *reinterpret_cast<u32x4 *>(tp + kt * 512) = rows8_from_pair(tile_row4(dSb[kt], 0, eye), tile_row4(dSb[kt], 1, eye));
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      dS[mt][0] *= gm[mt].x; dS[mt][1] *= gm[mt].y; dS[mt][2] *= gm[mt].z; dS[mt][3] *= gm[mt].w;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(frag(slot, mt * 2 + kt), dOb[kt], dS[mt]);
+
+    f32x4 dV[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) dV[mt] = zero4();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 16 + mt * 2 + kt), dOb[kt], dV[mt]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 24 + mt * 4 + kt), dSb[kt], dV[mt]);
+    {  // dVn^T rows of this slice's columns: 8 consecutive chunk rows 32h + 8lg.. per lane
+      u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 8 * lg;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4 *>(tr + 32 * h) = rows8_from_pair(pack_bf16x4(dV[2 * h]), pack_bf16x4(dV[2 * h + 1]));
+    }
+
+    bf16x8 dVb[2];
+    dVb[0] = acc_pair_to_b(dV[0], dV[1]);
+    dVb[1] = acc_pair_to_b(dV[2], dV[3]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(frag(slot, 40 + mt * 2 + kt), dVb[kt], dS[mt]);
+
+    if (n > 0) put(slot ^ 1);  // the slot every wavefront finished reading a step ago
+    lds_barrier();
+  }
+
+  if (dh0 && wc.s == 0) {
+    float *hp = dh0 + ((size_t)d * Hv + j) * HD * HD;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) hp[(16 * mt + 4 * lg + jj) * HD + vcol] = dS[mt][jj];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Gradient kernel: one workgroup (8 wavefronts) per (chunk, Q/K head); it
 // loops over the value heads of the group and keeps dq, dk in fp32 registers
@@ -1313,6 +1477,12 @@ hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout
   if (p.P > 1) {  // pass 1: the segments' carries
     const int g1 = ((chains * (p.P - 1) + 7) / 8) * 64;
     bwd_walk_kernel<MODE_CARRY><<<2 * g1, 64, 0, st>>>(p, w, dout, nullptr, nullptr);
+  }
+  if (walk_uses_rings(p, compute_units())) {
+    hipError_t e = set_dynamic_lds_once((const void *)bwd_walk_wg_kernel<WGB_NW>, WGB_SMEM);
+    if (e != hipSuccess) return e;
+    bwd_walk_wg_kernel<WGB_NW><<<((chains * p.P + 7) / 8) * 64 / WGB_NW, 64 * WGB_NW, WGB_SMEM, st>>>(p, w, dout, dht, dh0);
+    return hipGetLastError();
   }
   bwd_walk_kernel<MODE_WALK><<<((chains * p.P + 7) / 8) * 64, 64, 0, st>>>(p, w, dout, dht, dh0);
   return hipGetLastError();

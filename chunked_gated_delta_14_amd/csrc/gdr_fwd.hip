@@ -694,9 +694,186 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
   }
 }
 
+// Forward walk with one workgroup per chain: wavefront w walks value slice w
+// (16 columns), and the chain's shared per-chunk operands (-W, P, Kbar^T
+// fragments and the gate factors) pass once per chunk through a two-slot LDS
+// ring instead of once per slice wavefront through its own memory pipeline.
+// Each wavefront fetches a sixth of the next chunk's 48 fragment tiles into
+// registers at the top of a step and writes them to the free slot at its end;
+// one LDS barrier per step then hands the slot over.  Per-slice operands (U, Oi)
+// stay a register prefetch, and the outputs leave as in fwd_walk_kernel.
+constexpr int WG_TILES = 48;                                  // -W, P, Kbar^T: 16 tiles each
+constexpr int WG_SLOT = WG_TILES * FRAG_TILE_U4 * 16 + HD * 4;  // bytes per ring slot (+ gamma)
+constexpr int WG_NW = 4;    // slice wavefronts per ring workgroup (two workgroups per chain)
+constexpr int WG_RING = 3;  // slots: the chunk in use, the next one, the one after in flight
+constexpr int WG_SMEM = WG_RING * WG_SLOT;
+
+template <bool SAVE, bool OUT, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspace w, u16 *o, float *ht) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const ChunkTable tb(p.table, p.NC, p.N);
+  int chain, half;
+  walk_block<NW>(blockIdx.x, chain, half);  // the 8 / NW workgroups of a chain on one XCD
+  WalkChain wc;
+  if (!walk_chain(p, tb, chain, p.P, false, wc)) return;  // uniform over the workgroup
+  const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
+  const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sl0 = NW * half + wv;  // this wavefront's slice
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const size_t Hv = p.Hv;
+  const uint32_t row_bytes = (uint32_t)(Hv * HD * 2);
+  const s16x4 eye = eye16(lane);
+  constexpr int NT = OUT ? 48 : 32;  // tiles fetched per chunk (P only with the output)
+  constexpr int PER = NT / NW;       // tiles per wavefront
+
+  f32x4 S[8];
+  const float *h0 = p.h0 ? p.h0 + ((size_t)d * Hv + j) * HD * HD : nullptr;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) S[mt][jj] = h0 ? h0[(16 * mt + 4 * lg + jj) * HD + 16 * sl0 + lr] : 0.f;
+  for (int b = 0; b < wc.s; ++b) {  // entering state of segment s: through the earlier segments
+    const float *cb = carry_of(p, w, d, b, j);
+    apply_carry(S, cb, cb + HD * HD, 16 * sl0, lane);
+  }
+
+  // tile t of a chunk: -W (0..15), Kbar^T (16..31), P (32..47); wavefront w takes t = w + 8i
+  auto tile_src = [&](size_t u, int t) -> const uint4 * {
+    const uint4 *base = t < 16 ? w.WfN : (t < 32 ? w.KbT : w.Pf);
+    return base + u * FRAG_64x128_U4 + (t & 15) * 64 + lane;
+  };
+  // two register stage sets: the chunk after next is fetched while the next one waits for its slot
+  u32x4 stA[PER], stB[PER];
+  float4 gA = make_float4(0.f, 0.f, 0.f, 0.f), gB = gA;
+  auto fetch = [&](size_t u, u32x4 (&st)[PER], float4 &gs) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) st[i] = __builtin_bit_cast(u32x4, *tile_src(u, wv + NW * i));
+    if (wv == 0 && lane < 32) gs = *reinterpret_cast<const float4 *>(w.gam + u * HD + 4 * lane);
+  };
+  auto put = [&](int slot, const u32x4 (&st)[PER], const float4 &gs) {
+    unsigned char *base = smem + slot * WG_SLOT;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) *reinterpret_cast<u32x4 *>(base + (wv + NW * i) * 1024 + lane * 16) = st[i];
+    if (wv == 0 && lane < 32) *reinterpret_cast<float4 *>(base + WG_TILES * 1024 + lane * 16) = gs;
+  };
+  auto frag = [&](int slot, int t) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8 *>(smem + slot * WG_SLOT + t * 1024 + lane * 16);
+  };
+
+  uint2 Ua[4], Oa[4];
+  if (nch > 0) {
+    const size_t u = (size_t)first * Hv + j;
+    fetch(u, stA, gA);
+    if (nch > 1) fetch(u + Hv, stB, gB);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const size_t off = u * ACC_64x128_U16 + ((sl0 * 4 + mt) * 64 + lane) * 4;
+      Ua[mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
+      if (OUT) Oa[mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
+    }
+    put(0, stA, gA);
+  }
+  lds_barrier();
+
+  // step n: chunk n in slot n % 3; chunk n + 1 in one stage set (fetched a step
+  // ago), chunk n + 2 fetched into the other; at the end chunk n + 1 goes to its
+  // slot, which every wavefront finished reading two steps ago.
+  auto step = [&](int n, u32x4 (&st_next)[PER], float4 &g_next, u32x4 (&st_after)[PER], float4 &g_after) {
+    const size_t u = (size_t)(first + n) * Hv + j;
+    const size_t un = n + 1 < nch ? u + Hv : u;
+    const int slot = n % WG_RING;
+    const int row0 = tok0 + CH * n;
+    const int len = min(CH, tok1 - row0);
+    if (n + 2 < nch) fetch(u + 2 * Hv, st_after, g_after);
+
+    float4 gm[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      gm[mt] = *reinterpret_cast<const float4 *>(smem + slot * WG_SLOT + WG_TILES * 1024 + (16 * mt + 4 * lg) * 4);
+
+    bf16x8 Sb[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) Sb[kt] = acc_pair_to_b(S[2 * kt], S[2 * kt + 1]);
+    const int prow = 16 * (lg >> 1) + lr, pcol = 8 * (lg & 1);
+    if (SAVE) {  // state tape: block [key][16] of each slice
+      u16 *st = w.S + u * (HD * HD) + sl0 * (HD * 16) + prow * 16 + pcol;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        *reinterpret_cast<u32x4 *>(st + kt * 512) = rows8_from_pair(tile_row4(Sb[kt], 0, eye), tile_row4(Sb[kt], 1, eye));
+    }
+
+    f32x4 Vn[4], Oc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      Vn[mt][0] = bf2f(Ua[mt].x & 0xffff); Vn[mt][1] = bf2f(Ua[mt].x >> 16);
+      Vn[mt][2] = bf2f(Ua[mt].y & 0xffff); Vn[mt][3] = bf2f(Ua[mt].y >> 16);
+      const size_t off = un * ACC_64x128_U16 + ((sl0 * 4 + mt) * 64 + lane) * 4;
+      Ua[mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
+      if (OUT) {
+        Oc[mt][0] = bf2f(Oa[mt].x & 0xffff); Oc[mt][1] = bf2f(Oa[mt].x >> 16);
+        Oc[mt][2] = bf2f(Oa[mt].y & 0xffff); Oc[mt][3] = bf2f(Oa[mt].y >> 16);
+        Oa[mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) Vn[mt] = mfma(frag(slot, mt * 4 + kt), Sb[kt], Vn[mt]);
+    if (OUT) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Oc[mt] = mfma(frag(slot, 32 + mt * 4 + kt), Sb[kt], Oc[mt]);
+    }
+
+    bf16x8 Vb[2];
+    Vb[0] = acc_pair_to_b(Vn[0], Vn[1]);
+    Vb[1] = acc_pair_to_b(Vn[2], Vn[3]);
+    if (OUT) {  // o rows of this chunk; rows past len fall outside the sink's range
+      const RowSink ob(o + ((size_t)row0 * Hv + j) * HD + 16 * sl0, (uint32_t)len * row_bytes);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 Ob = acc_pair_to_b(Oc[2 * h], Oc[2 * h + 1]);
+        ob.put16((uint32_t)(32 * h + prow) * row_bytes + 2 * pcol, rows8_from_pair(tile_row4(Ob, 0, eye), tile_row4(Ob, 1, eye)));
+      }
+    }
+    if (SAVE) {  // Vn tape: block [row][16] of each slice
+      u16 *vt = w.Vn + u * (CH * HD) + sl0 * (CH * 16) + prow * 16 + pcol;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4 *>(vt + h * 512) = rows8_from_pair(tile_row4(Vb[h], 0, eye), tile_row4(Vb[h], 1, eye));
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      S[mt][0] *= gm[mt].x; S[mt][1] *= gm[mt].y; S[mt][2] *= gm[mt].z; S[mt][3] *= gm[mt].w;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) S[mt] = mfma(frag(slot, 16 + mt * 2 + kt), Vb[kt], S[mt]);
+
+    if (n + 1 < nch) put((n + 1) % WG_RING, st_next, g_next);
+    lds_barrier();
+  };
+  for (int n = 0; n < nch; n += 2) {  // unrolled by two: the stage sets swap roles
+    step(n, stB, gB, stA, gA);
+    if (n + 1 < nch) step(n + 1, stA, gA, stB, gB);
+  }
+
+  if (ht && wc.s == wc.Pd - 1) {
+    float *hp = ht + ((size_t)d * Hv + j) * HD * HD;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) hp[(16 * mt + 4 * lg + jj) * HD + 16 * sl0 + lr] = S[mt][jj];
+  }
+}
+
 static int walk_grid(int chains, int ns) { return ((chains + 7) / 8) * 64 / ns; }
 
-static int compute_units() {
+int compute_units() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -734,6 +911,19 @@ hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, u16 *o, float *
   if (p.P > 1) {  // pass 1: the segments' carries
     const int g1 = walk_grid(chains * (p.P - 1), 1);
     fwd_walk_kernel<1, false, false, MODE_CARRY><<<2 * g1, 64, 0, st>>>(p, w, nullptr, nullptr);
+  }
+  if (walk_uses_rings(p, compute_units())) {  // slice wavefronts of a chain in workgroups of WG_NW
+    constexpr int NW = WG_NW;
+    const void *fn = save ? (out ? (const void *)fwd_walk_wg_kernel<true, true, NW> : (const void *)fwd_walk_wg_kernel<true, false, NW>)
+                          : (out ? (const void *)fwd_walk_wg_kernel<false, true, NW> : (const void *)fwd_walk_wg_kernel<false, false, NW>);
+    hipError_t e = set_dynamic_lds_once(fn, WG_SMEM);
+    if (e != hipSuccess) return e;
+    const int g = walk_grid(chains * p.P, NW);
+    if (save && out) fwd_walk_wg_kernel<true, true, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
+    else if (save) fwd_walk_wg_kernel<true, false, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
+    else if (out) fwd_walk_wg_kernel<false, true, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
+    else fwd_walk_wg_kernel<false, false, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
+    return hipGetLastError();
   }
   const int grid = walk_grid(chains * p.P, NS);
   if (save && out) fwd_walk_kernel<NS, true, true><<<grid, 64, 0, st>>>(p, w, o, ht);

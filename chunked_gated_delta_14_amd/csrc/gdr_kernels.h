@@ -1,6 +1,8 @@
 // Private interface between the C-ABI layer and the kernel translation units.
 #pragma once
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,7 +47,23 @@ struct Problem {
   float scale;
   int inflags;  // bit 0: q, k rows to unit L2 norm; bit 1: beta = sigmoid(beta)
   int P;        // walk segments per document (1: one chain per document and head)
+  int L;        // chunks of the longest document (an upper bound; only steers the walk layout)
+  int layout;   // walk layout: 0 automatic, 1 slice wavefronts, 2 workgroup rings
 };
+
+// Walk layout.  Slice wavefronts finish a chain step in about 3.7 K cycles, but a
+// compute unit retires only about one slice step per 3.5 K cycles however many of
+// them it holds.  A ring workgroup (four slice wavefronts sharing the chain's
+// operands through LDS) needs about 6.5 K cycles per chain step, 8.5 K with every
+// compute unit busy, and holds a compute unit alone.  Each layout's time is the
+// larger of its longest chain and its work per compute unit; the smaller wins.
+inline bool walk_uses_rings(const Problem &p, int cus) {
+  if (p.layout != 0) return p.layout == 2;
+  const double units = (double)p.NC * p.Hv, chain = (double)((p.L + p.P - 1) / p.P);
+  const double slices = std::max(chain * 3.7, 8.0 * units / cus * 3.5);
+  const double rings = std::max(chain * 6.5, 2.0 * units / cus * 8.5);
+  return rings < slices;
+}
 constexpr int IN_QK_L2NORM = 1, IN_BETA_SIGMOID = 2;
 constexpr float L2NORM_EPS = 1e-6f;
 
@@ -53,6 +71,9 @@ constexpr float L2NORM_EPS = 1e-6f;
 // attribute belongs to the function on that device, so later launches
 // (including ones under stream capture) make no runtime call for it.
 hipError_t set_dynamic_lds_once(const void *kernel, int bytes);
+
+// Compute units of the current device (cached per device).
+int compute_units();
 
 hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, bool out, hipStream_t st);
 hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, uint16_t *o, float *ht, bool save, bool out,

@@ -100,7 +100,26 @@ typedef struct gdr_problem {
   uint32_t input_flags;      /* GDR_IN_* bits below; 0 = q, k, beta used as given */
   int32_t walk_segments;     /* segments per document of the state walks: 0 = automatic (see
                                 gdr_workspace_bytes), n >= 1 = at most n and at most the automatic count */
+  int32_t max_doc_chunks;    /* chunks of the longest document (the largest step of the table's
+                                per-document first-chunk section), or 0 = unknown (taken as n_chunks).
+                                A hint for the walks' launch layout: results never depend on it */
+  int32_t walk_layout;       /* GDR_WALK_AUTO, GDR_WALK_SLICES or GDR_WALK_RINGS (below) */
 } gdr_problem;
+
+/* Launch layout of the state walks (gdr_problem.walk_layout).  Both run the same
+ * products in the same order for every 16-column slice of the state, so they
+ * give the same bits.
+ * GDR_WALK_SLICES: one wavefront per (chain, slice), each reading the chain's
+ *   per-chunk operands through its own memory pipeline: the shortest chain step,
+ *   but a compute unit retires about one slice step at a time.
+ * GDR_WALK_RINGS: the slice wavefronts of a chain in workgroups of four that
+ *   pass each chunk's shared operands through a three-slot LDS ring (146 KB):
+ *   a longer chain step, about four times the work per compute unit.
+ * GDR_WALK_AUTO: the layout with the smaller estimated walk time, from the
+ *   longest chain (max_doc_chunks) and the work per compute unit. */
+#define GDR_WALK_AUTO 0
+#define GDR_WALK_SLICES 1
+#define GDR_WALK_RINGS 2
 
 /* Input activations applied inside the kernels (gdr_problem.input_flags).
  * GDR_IN_QK_L2NORM: every (token, head) row of q and of k is scaled to unit L2

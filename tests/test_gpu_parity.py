@@ -97,6 +97,36 @@ def test_segmented_walks(case):
             assert r <= 1e-3, "%s P=%d vs P=1: rel-RMS %.3g" % (name, P, r)
 
 
+LAYOUTS = [
+    # (variant, docs, H_qk, H_v, walk_segments): ragged packs, segmented and not
+    ("kda", (1, 63, 64, 65, 130, 7), 2, 2, 1),
+    ("kda", (1000, 130, 0, 1, 257), 1, 1, 3),
+    ("gdn", (77, 64, 129), 2, 6, 1),
+    ("gdn", (700, 64, 3), 1, 3, 4),
+]
+
+
+@pytest.mark.parametrize("case", LAYOUTS, ids=lambda c: "%s_%s_h%d_%d_P%d" % (c[0], "-".join(map(str, c[1])), c[2], c[3], c[4]))
+def test_walk_layouts_agree(case):
+    """The two launch layouts of the walks (one wavefront per slice; slice
+    wavefronts in workgroups sharing the chain's operands through LDS) run the
+    same products in the same order: every output is bitwise equal, and the
+    ring layout matches the oracle."""
+    import chunked_gated_delta_14_amd as gdr
+
+    variant, docs, hqk, hv, P = case
+    w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=sum(docs) + 13 * hv)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    print("[case]", w.name, "walk layouts, segments", P, flush=True)
+    slices = run_gdr(variant, inp, dht=inp["dht"], walk_segments=P, walk_layout=gdr.GDR_WALK_SLICES)
+    rings = run_gdr(variant, inp, dht=inp["dht"], walk_segments=P, walk_layout=gdr.GDR_WALK_RINGS)
+    for name in slices:
+        assert torch.equal(slices[name], rings[name]), "%s differs between walk layouts" % name
+    fwd_only = run_gdr(variant, inp, backward=False, walk_segments=P, walk_layout=gdr.GDR_WALK_RINGS)
+    assert torch.equal(fwd_only["o"], rings["o"]) and torch.equal(fwd_only["ht"], rings["ht"])
+    compare(rings, oracle_all(variant, inp, dht=inp["dht"]), label=w.name + "_rings")
+
+
 def test_workload0_parity():
     w = workloads.workload(0)
     inp = workloads.make_inputs(w, device="cpu")

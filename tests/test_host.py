@@ -167,6 +167,24 @@ def test_unknown_input_flag_rejected_on_host():
     assert rc == 1 and "input flag" in L.gdr_last_error().decode()
 
 
+def test_walk_layout_fields_checked_on_host():
+    """walk_layout must name a layout and max_doc_chunks lie in [0, n_chunks]."""
+    L = gdr.lib()
+    for field, value, msg in (("walk_layout", 3, "walk_layout"), ("walk_layout", -1, "walk_layout"),
+                              ("max_doc_chunks", -1, "max_doc_chunks"), ("max_doc_chunks", 3, "max_doc_chunks")):
+        p = _cproblem()
+        setattr(p, field, value)
+        rc = L.gdr_kda_fwd(ctypes.byref(p), ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), 1 << 40, 0, None)
+        assert rc == 1 and msg in L.gdr_last_error().decode()
+
+
+@pytest.mark.parametrize("docs", [[200, 312], [0, 5, 0], [88673, 42024, 73122, 57573]])
+def test_max_doc_chunks_from_table(docs):
+    cu = np.concatenate([[0], np.cumsum(docs)]).astype(np.int32)
+    table, nc = gdr.plan_chunks(cu)
+    assert gdr.max_doc_chunks(table, len(docs), nc) == max(-(-d // 64) for d in docs)
+
+
 def test_skip_output_flag_host_checks():
     """GDR_FWD_SKIP_OUTPUT is a known flag (workspace sizes as without it); o may be
     NULL only with it.  Only paths that stop before any device call are exercised."""
