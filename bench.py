@@ -90,13 +90,18 @@ def parse_args():
     return ap.parse_args()
 
 
-def traffic_from_profiles(kernel):
+def traffic_from_profiles(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this
-    kernel (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), if any."""
+    kernel (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), if
+    one exists for this workload."""
     path = os.path.join(ROOT, "profiles", "%s_traffic.md" % kernel)
     if not os.path.exists(path):
         return None
-    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", open(path).read())
+    text = open(path).read()
+    w = re.search(r"traffic_workload:\s*(\S+)", text)
+    if not w or w.group(1) != workload:
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     return float(m.group(1)) if m else None
 
 
@@ -358,7 +363,7 @@ def main():
                if k in kernels and unsegmented}
     floor_ms = T * Hv * FLOOR_BYTES_PER_TOKEN_HEAD[w.variant] / (HBM_PEAK_GBS * 1e6)
     dk_ = kernels[dom]
-    traffic = traffic_from_profiles(dom)
+    traffic = traffic_from_profiles(dom, w.name)
     token_heads = T * Hv
     result = {
         "metric": METRIC,
