@@ -579,11 +579,15 @@ __device__ __forceinline__ void load_qk_rows(u16 *sQT, u16 *sKT, const Problem &
 
 __device__ __forceinline__ float sigmoidf_(float b) { return 1.f / (1.f + __expf(-b)); }
 
-__global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
-                                                       u16 *dk, u16 *dv, float *dg, void *dbeta) {
+__device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace &w, const u16 *dout, u16 *dq,
+                                             u16 *dk, u16 *dv, float *dg, void *dbeta, int unit) {
   extern __shared__ __align__(16) unsigned char smem[];
-  // Q/K heads vary fastest over the grid (whole token rows per resident set)
-  const int chunk = blockIdx.x / p.Hqk, iqk = blockIdx.x % p.Hqk;
+  // Q/K heads vary fastest over the units (whole token rows per resident set)
+  const int chunk = unit / p.Hqk, iqk = unit % p.Hqk;
+  // the thread id as a value the compiler cannot prove loop-invariant, so that no
+  // per-thread address arithmetic is hoisted out of the persistent loop
+  int tid0 = threadIdx.x;
+  asm volatile("" : "+v"(tid0));
   const ChunkTable tb(p.table, p.NC, p.N);
   const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
   const float scale = p.scale;
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 
   float *sNrm = reinterpret_cast<float *>(smem + G_NRM);
   // (the dout stage is free until the first iteration's loads: scratch of the row norms)
-  load_qk_rows<KQTP>(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(smem + G_DO), sNrm);
+  load_qk_rows<KQTP>(sQT, sKT, p, start, iqk, len, tid0, reinterpret_cast<float *>(smem + G_DO), sNrm);
 
   f32x4 dqA[4], dkA[4];  // [row block I]: rows 16I + 4lg + jj, column 16w + lr
 #pragma unroll
@@ -617,7 +621,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
     // Re-derive the thread coordinates from an opaque copy of the thread id so
     // the compiler cannot hoist per-element address arithmetic out of this
     // block (that would keep hundreds of values live across it).
-    int tid = threadIdx.x;
+    int tid = tid0;
     asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int j = iqk;  // H_qk == H_v
@@ -1033,7 +1037,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 
   // dq, dk: fp32 sums over the group's value heads, rounded once
   {
-    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int tid = tid0, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (p.inflags & IN_QK_L2NORM) {  // back through the norm: d x = rstd (d x_hat - x_hat <x_hat, d x_hat>)
       const int c = 16 * wave + lr;
@@ -1099,11 +1103,13 @@ __device__ __forceinline__ void add_tile(f32x4 (&acc)[4], int t, const f32x4 &x)
     if (i == t) acc[i] += x;
 }
 
-__global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
-                                                       u16 *dk, u16 *dv, float *dg, void *dbeta) {
+__device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Workspace &w, const u16 *dout, u16 *dq,
+                                             u16 *dk, u16 *dv, float *dg, void *dbeta, int unit) {
   extern __shared__ __align__(16) unsigned char smem[];
-  // Q/K heads vary fastest over the grid (whole token rows per resident set)
-  const int chunk = blockIdx.x / p.Hqk, iqk = blockIdx.x % p.Hqk;
+  // Q/K heads vary fastest over the units (whole token rows per resident set)
+  const int chunk = unit / p.Hqk, iqk = unit % p.Hqk;
+  int tid0 = threadIdx.x;  // opaque: nothing per-thread is hoisted out of the persistent loop
+  asm volatile("" : "+v"(tid0));
   const ChunkTable tb(p.table, p.NC, p.N);
   const int start = tb.start[chunk], len = tb.len[chunk], last = len - 1;
   const int grp = p.Hv / p.Hqk;  // value heads of the Q/K head
@@ -1127,7 +1133,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
   const GateT<true> G{sG};
 
   // (the Y stage is free until the first iteration: scratch of the row norms)
-  load_qk_rows<QTP>(sQT, sKT, p, start, iqk, len, threadIdx.x, reinterpret_cast<float *>(sY), sNrm);
+  load_qk_rows<QTP>(sQT, sKT, p, start, iqk, len, tid0, reinterpret_cast<float *>(sY), sNrm);
 
   f32x4 dqA[4], dkA[4];
 #pragma unroll
@@ -1137,7 +1143,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
     // Re-derive the thread coordinates from an opaque copy of the thread id so
     // the compiler cannot hoist per-element address arithmetic of the group
     // loop out of it (that would keep hundreds of values live across it).
-    int tid = threadIdx.x;
+    int tid = tid0;
     asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int mt = wave & 3, ch = wave >> 2;  // row strip, column half
@@ -1423,7 +1429,7 @@ __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace
 
   // dq, dk: fp32 sums over the group's value heads, rounded once
   {
-    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int tid = tid0, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), mt = wave & 3, ch = wave >> 2;
     if (p.inflags & IN_QK_L2NORM) {  // back through the norm: d x = rstd (d x_hat - x_hat <x_hat, d x_hat>)
       float *sDot = sNrm + 128;  // [row][q, k][column half]
@@ -1488,10 +1494,31 @@ hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout
   return hipGetLastError();
 }
 
+// Persistent gradient kernels: one workgroup per compute unit (the LDS map allows
+// no second) walks the units blockIdx.x, + gridDim.x, ...; consecutive
+// workgroups take consecutive units, as a one-unit-per-workgroup grid would.
+__global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
+                                                       u16 *dk, u16 *dv, float *dg, void *dbeta) {
+  const int units = p.NC * p.Hqk;
+  for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    bwd_grad_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit);
+    lds_barrier();  // LDS is reused by the next unit
+  }
+}
+__global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
+                                                            u16 *dk, u16 *dv, float *dg, void *dbeta) {
+  const int units = p.NC * p.Hqk;
+  for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    bwd_grad_rows_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit);
+    lds_barrier();  // LDS is reused by the next unit
+  }
+}
+
 hipError_t launch_bwd_grad(bool gdn, const Problem &p, const Workspace &w, const u16 *dout, u16 *dq, u16 *dk,
                            u16 *dv, float *dg, void *dbeta, hipStream_t st) {
   if (p.NC == 0) return hipSuccess;
-  const dim3 grid(p.NC * p.Hqk), block(GNT);
+  const int units = p.NC * p.Hqk;
+  const dim3 grid(units < compute_units() ? units : compute_units()), block(GNT);
   hipError_t e;
   if (gdn) {
     const int sm = grad_rows_smem_bytes();
