@@ -27,22 +27,44 @@ FLAGS = [
 ]
 
 
-def command(out: str = LIB_PATH) -> list[str]:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    return [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", out]
+# Per-source device code-generation options.  The adjoint-walk and gradient
+# source keeps MFMA accumulators in ordinary VGPRs (no accumulator-register
+# moves around the VALU work on them); the forward source leaves the choice to
+# the compiler, whose accumulator registers relieve the forward walks' pressure.
+EXTRA = {"gdr_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def commands(out: str = LIB_PATH, objdir: str | None = None) -> list[list[str]]:
+    """hipcc -c for every source, then the link into the shared library."""
+    objdir = objdir or os.path.dirname(out)
+    objs, cmds = [], []
+    common = [f for f in FLAGS if f != "-shared"]
+    for src in SOURCES:
+        obj = os.path.join(objdir, "%s.%d.o" % (src, os.getpid()))
+        cmds.append([HIPCC, *common, *EXTRA.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    cmds.append([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out])
+    return cmds
 
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libgdr.so (always recompiles)."""
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libgdr.so")
-    os.replace(tmp, LIB_PATH)
+    cmds = commands(tmp, PKG_DIR)
+    try:
+        for cmd in cmds:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError("hipcc failed building libgdr.so")
+        os.replace(tmp, LIB_PATH)
+    finally:
+        for obj in cmds[-1][4:-2]:
+            if os.path.exists(obj):
+                os.remove(obj)
     return LIB_PATH
 
 
