@@ -173,17 +173,19 @@ def test_recompute_without_output():
         assert torch.equal(g[key].float().cpu(), a[key]), key
 
 
-def test_ckpt_graph_replay():
-    """The checkpointed step captured in a HIP graph: three replays, with the
-    program's own eager work and synchronisations between them, each bitwise equal
-    to the eager call."""
+@pytest.mark.parametrize("walk_layout", [1, 2], ids=["slices", "rings"])
+def test_ckpt_graph_replay(walk_layout):
+    """The checkpointed step captured in a HIP graph, with either walk layout:
+    three replays, with the program's own eager work and synchronisations between
+    them, each bitwise equal to the eager call."""
     import chunked_gated_delta_14_amd as gdr
     from gpu_runner import to_dev
 
     w = workloads.custom("kda", (150, 90), 2, 2, with_h0=True, seed=9)
     inp = workloads.make_inputs(w, device="cpu", dht=True)
     d = to_dev(inp)
-    prob = gdr.Problem(gdr.GDR_KDA, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["h0"])
+    prob = gdr.Problem(gdr.GDR_KDA, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["h0"],
+                       walk_layout=walk_layout)
     ws = prob.alloc_workspace(gdr.GDR_FWD_SAVE)
     T, N = prob.T, prob.N
     bf, f32 = torch.bfloat16, torch.float32
