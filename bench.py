@@ -87,6 +87,7 @@ def parse_args():
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="tokens per document in the CPU sample")
     ap.add_argument("--no-op-timing", action="store_true", help="skip the separate fwd/bwd/ckpt timings")
     ap.add_argument("--no-smi", action="store_true", help="do not sample clock and power with amd-smi")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and HBM peak probes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (HBM counter calibration)")
     return ap.parse_args()
@@ -215,6 +216,60 @@ class SmiSampler:
         if self.error:
             out["error"] = self.error
         return out
+
+
+def measured_peaks(dev, gib=2):
+    """Rates measured on this device with the probe kernels (libgdr_probe.so): a
+    pure bf16 MFMA loop (eight independent 16x16x32 chains per wavefront, two
+    wavefronts per SIMD) and 16-byte grid-stride copy / read / fill kernels over
+    `gib` GiB buffers; each timed with events on the current stream, best of 3."""
+    import ctypes
+
+    import torch
+
+    from chunked_gated_delta_14_amd import _build
+
+    if not os.path.exists(_build.PROBE_PATH):
+        _build.build_probe()
+    L = ctypes.CDLL(_build.PROBE_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.gdr_probe_mfma.argtypes = [vp, i32, i32, i32, vp]
+    L.gdr_probe_stream.argtypes = [i32, vp, vp, vp, i64, i32, vp]
+    st = vp(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def best(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return min(out)
+
+    blocks, iters = 2 * cus, 40000  # 4 wavefronts per block: two per SIMD
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    ms16 = best(lambda: L.gdr_probe_mfma(vp(sink.data_ptr()), blocks, iters, 0, st))
+    ms32 = best(lambda: L.gdr_probe_mfma(vp(sink.data_ptr()), blocks, iters, 1, st))
+    tf16 = blocks * 4 * iters * 8 * 16384 / (ms16 / 1e3) / 1e12
+    tf32 = blocks * 4 * iters * 4 * 32768 / (ms32 / 1e3) / 1e12
+    n = gib << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    s32 = torch.zeros(1, dtype=torch.int32, device=dev)
+    rates = {}
+    for mode, name, mult in ((0, "copy", 2), (1, "read", 1), (2, "write", 1)):
+        ms = best(lambda: L.gdr_probe_stream(mode, vp(src.data_ptr()), vp(dst.data_ptr()), vp(s32.data_ptr()),
+                                             n, 8 * cus, st))
+        rates[name + "_GB_s"] = mult * n / (ms / 1e3) / 1e9
+    del src, dst
+    torch.cuda.synchronize()
+    return dict(mfma_bf16_TFLOPs=max(tf16, tf32), mfma_16x16x32_TFLOPs=tf16, mfma_32x32x16_TFLOPs=tf32, **rates,
+                note="probe kernels on this device; copy counts read + write bytes; best of 3")
 
 
 def cpu_model():
@@ -400,6 +455,12 @@ def main():
                  "frac": total_flops / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "kernels": kernels,
     }
+    if not args.no_peaks:
+        peaks = measured_peaks(dev)
+        result["measured_peaks"] = peaks
+        result["roofline"]["measured_copy_GB_s"] = peaks["copy_GB_s"]
+        result["roofline"]["frac_of_measured_copy"] = dk_["GB_s"] / peaks["copy_GB_s"]
+        result["mfma"]["frac_of_measured"] = result["mfma"]["TFLOPs"] / peaks["mfma_bf16_TFLOPs"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, list(w.docs), args.cpu_tokens)
     print(json.dumps(result), flush=True)

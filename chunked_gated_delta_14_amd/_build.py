@@ -68,6 +68,24 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+PROBE_SRC = "gdr_probe.hip"
+PROBE_PATH = os.path.join(PKG_DIR, "libgdr_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The peak probes used by bench.py (a library of their own, outside libgdr's ABI)."""
+    tmp = PROBE_PATH + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, PROBE_SRC), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libgdr_probe.so")
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
+
+
 def stale() -> bool:
     """True when libgdr.so is missing or older than any of its sources."""
     if not os.path.exists(LIB_PATH):
@@ -79,3 +97,4 @@ def stale() -> bool:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))
