@@ -694,13 +694,15 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
   }
 }
 
-// Forward walk with one workgroup per chain: wavefront w walks value slice w
-// (16 columns), and the chain's shared per-chunk operands (-W, P, Kbar^T
-// fragments and the gate factors) pass once per chunk through a two-slot LDS
-// ring instead of once per slice wavefront through its own memory pipeline.
-// Each wavefront fetches a sixth of the next chunk's 48 fragment tiles into
-// registers at the top of a step and writes them to the free slot at its end;
-// one LDS barrier per step then hands the slot over.  Per-slice operands (U, Oi)
+// Forward walk in ring workgroups: the 8 / NW workgroups of a chain each hold
+// NW slice wavefronts (wavefront w of workgroup h walks the 16-column value
+// slice NW h + w), and the chain's shared per-chunk operands (-W, P, Kbar^T
+// fragments and the gate factors) pass once per chunk and workgroup through a
+// three-slot LDS ring instead of once per slice wavefront through its own
+// memory pipeline.  At the top of step n each wavefront fetches 1 / NW of chunk
+// n + 2's fragment tiles into one of two register stage sets; at the end it
+// writes the other set (chunk n + 1, fetched a step earlier) to that chunk's
+// slot, and one LDS barrier per step hands it over.  Per-slice operands (U, Oi)
 // stay a register prefetch, and the outputs leave as in fwd_walk_kernel.
 constexpr int WG_TILES = 48;                                  // -W, P, Kbar^T: 16 tiles each
 constexpr int WG_SLOT = WG_TILES * FRAG_TILE_U4 * 16 + HD * 4;  // bytes per ring slot (+ gamma)
