@@ -57,8 +57,11 @@ struct Problem {
 // operands through LDS) needs about 6.5 K cycles per chain step, 8.5 K with every
 // compute unit busy, and holds a compute unit alone.  Each layout's time is the
 // larger of its longest chain and its work per compute unit; the smaller wins.
+// Segmented walks keep the slices: segments are cut only when the chains leave
+// the compute units underfilled, where the shorter slice step wins.
 inline bool walk_uses_rings(const Problem &p, int cus) {
   if (p.layout != 0) return p.layout == 2;
+  if (p.P > 1) return false;
   const double units = (double)p.NC * p.Hv, chain = (double)((p.L + p.P - 1) / p.P);
   const double slices = std::max(chain * 3.7, 8.0 * units / cus * 3.5);
   const double rings = std::max(chain * 6.5, 2.0 * units / cus * 8.5);

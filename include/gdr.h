@@ -117,7 +117,8 @@ typedef struct gdr_problem {
  *   slots, 146 KB; adjoint walk: two slots, 113 KB): a longer chain step, about
  *   four times the work per compute unit.
  * GDR_WALK_AUTO: the layout with the smaller estimated walk time, from the
- *   longest chain (max_doc_chunks) and the work per compute unit. */
+ *   longest chain (max_doc_chunks) and the work per compute unit; segmented
+ *   walks (see walk_segments) always use slices. */
 #define GDR_WALK_AUTO 0
 #define GDR_WALK_SLICES 1
 #define GDR_WALK_RINGS 2
