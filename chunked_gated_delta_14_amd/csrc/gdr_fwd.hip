@@ -86,8 +86,11 @@ __device__ __forceinline__ void settle(PrepIn &in) {
   asm volatile("" : "+v"(in.ga[0]), "+v"(in.ga[1]), "+v"(in.gb[0]), "+v"(in.gb[1]), "+v"(in.b[0]), "+v"(in.b[1]));
 }
 
+// reuse: the current unit's inputs when the fetched unit reads the same Q/K head
+// (the next value head of its group): q and k are then copied, not reloaded.
 template <bool SCALAR>
-__device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const ChunkTable &tb, int unit, int tid) {
+__device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const ChunkTable &tb, int unit, int tid,
+                                          const PrepIn *reuse) {
   const int chunk = unit / p.Hv, j = unit % p.Hv, iq = j / (p.Hv / p.Hqk);
   const int start = tb.start[chunk], len = tb.len[chunk];
   const int c0 = 8 * (tid >> 5), rp = 2 * (tid & 31);
@@ -98,8 +101,13 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const Ch
     const int r = rp + h;
     const bool ok = r < len;
     const size_t t = (size_t)(start + r);
-    in.k[h] = ok ? ld8(p.k + (t * p.Hqk + iq) * HD + c0) : z;
-    in.q[h] = ok ? ld8(p.q + (t * p.Hqk + iq) * HD + c0) : z;
+    if (reuse) {
+      in.k[h] = reuse->k[h];
+      in.q[h] = reuse->q[h];
+    } else {
+      in.k[h] = ok ? ld8(p.k + (t * p.Hqk + iq) * HD + c0) : z;
+      in.q[h] = ok ? ld8(p.q + (t * p.Hqk + iq) * HD + c0) : z;
+    }
     in.v[h] = ok ? ld8(p.v + (t * Hv + j) * HD + c0) : z;
     in.ga[h] = in.gb[h] = zero4();
     in.b[h] = 0u;
@@ -120,7 +128,8 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const Ch
 
 template <bool SCALAR, bool ACT>
 __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, int save, int out, int unit,
-                                          const PrepIn &in, PrepIn &next, int next_unit, unsigned char *smem) {
+                                          const PrepIn &in, PrepIn &next, int next_unit, bool next_same_qk,
+                                          unsigned char *smem) {
   // heads vary fastest over the units, so the workgroups working together
   // read whole token rows of q, k, v and g
   const int chunk = unit / p.Hv, j = unit % p.Hv;
@@ -265,7 +274,10 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   // The next unit's inputs: issued once this unit's are in LDS and the previous unit's
   // final stores have drained (loads issued behind a burst of stores wait for it), and
   // waited for at the end of this unit.
-  if (next_unit < p.NC * p.Hv) prep_load<SCALAR>(next, p, tb, next_unit, tid);
+  if (next_unit < p.NC * p.Hv) {
+    if constexpr (SCALAR) prep_load<SCALAR>(next, p, tb, next_unit, tid, next_same_qk ? &in : nullptr);
+    else prep_load<SCALAR>(next, p, tb, next_unit, tid, nullptr);
+  }
 
   // ---- 2. gated products.  Wavefront w: column block J = w >> 1 and row
   // blocks I in {2kt, 2kt+1}, kt = w & 1; the two accumulator tiles of M are
@@ -476,14 +488,36 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
   const int total = p.NC * p.Hv, tid = threadIdx.x;
-  int unit = blockIdx.x;
+  if constexpr (!SCALAR) {  // KDA: units blockIdx.x, + gridDim.x, ...
+    int unit = blockIdx.x;
+    PrepIn nxt;
+    if (unit < total) prep_load<SCALAR>(nxt, p, tb, unit, tid, nullptr);
+    settle(nxt);  // so that no path into the loop carries an outstanding load
+    for (; unit < total; unit += gridDim.x) {
+      const PrepIn cur = nxt;
+      prep_unit<SCALAR, ACT>(p, w, save, out, unit, cur, nxt, unit + gridDim.x, false, smem);
+      lds_barrier();  // LDS is reused by the next unit
+    }
+    return;
+  }
+  // GDN: the workgroup walks (chunk, Q/K head) groups blockIdx.x, + gridDim.x, ...,
+  // each group's value heads back to back, so consecutive units of a group share
+  // q and k (fetched once per group).
+  const int groups = p.NC * p.Hqk, grp = p.Hv / p.Hqk;
+  auto unit_of = [&](int g, int jg) { return (g / p.Hqk) * p.Hv + (g % p.Hqk) * grp + jg; };
+  int g = blockIdx.x, jg = 0;
   PrepIn nxt;
-  if (unit < total) prep_load<SCALAR>(nxt, p, tb, unit, tid);
+  if (g < groups) prep_load<SCALAR>(nxt, p, tb, unit_of(g, 0), tid, nullptr);
   settle(nxt);  // so that no path into the loop carries an outstanding load
-  for (; unit < total; unit += gridDim.x) {
+  while (g < groups) {
+    int ng = g, nj = jg + 1;
+    if (nj == grp) { ng = g + gridDim.x; nj = 0; }
     const PrepIn cur = nxt;
-    prep_unit<SCALAR, ACT>(p, w, save, out, unit, cur, nxt, unit + gridDim.x, smem);
+    prep_unit<SCALAR, ACT>(p, w, save, out, unit_of(g, jg), cur, nxt, ng < groups ? unit_of(ng, nj) : total, nj != 0,
+                           smem);
     lds_barrier();  // LDS is reused by the next unit
+    g = ng;
+    jg = nj;
   }
 }
 
@@ -889,8 +923,8 @@ int compute_units() {
 
 hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, bool out, hipStream_t st) {
   if (p.NC == 0) return hipSuccess;
-  const int total = p.NC * p.Hv;
-  const dim3 grid(total < compute_units() ? total : compute_units()), block(PNT);
+  const int items = gdn ? p.NC * p.Hqk : p.NC * p.Hv;  // GDN: (chunk, Q/K head) groups; KDA: units
+  const dim3 grid(items < compute_units() ? items : compute_units()), block(PNT);
   const bool act = p.inflags != 0;
   const void *fn = gdn ? (act ? (const void *)fwd_prep_kernel<true, true> : (const void *)fwd_prep_kernel<true, false>)
                        : (act ? (const void *)fwd_prep_kernel<false, true> : (const void *)fwd_prep_kernel<false, false>);
