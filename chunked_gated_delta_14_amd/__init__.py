@@ -18,7 +18,7 @@ from . import _build
 __all__ = [
     "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GDR_IN_QK_L2NORM", "GDR_IN_BETA_SIGMOID", "GDR_WALK_AUTO", "GDR_WALK_SLICES", "GDR_WALK_RINGS", "GdrError", "lib", "plan_chunks", "max_doc_chunks", "workspace_bytes",
     "Problem", "kda_fwd", "kda_bwd", "gdn_fwd", "gdn_bwd", "kda_ckpt", "gdn_ckpt", "status_string",
-    "check_device", "timing_enable", "timing_read", "EXPORTED_SYMBOLS",
+    "check_device", "walk_layout_chosen", "timing_enable", "timing_read", "EXPORTED_SYMBOLS",
 ]
 
 GDR_KDA = 0
@@ -32,7 +32,7 @@ GDR_WALK_AUTO, GDR_WALK_SLICES, GDR_WALK_RINGS = 0, 1, 2  # Problem walk_layout
 EXPORTED_SYMBOLS = (
     "gdr_plan_chunks", "gdr_workspace_bytes", "gdr_kda_fwd", "gdr_kda_bwd", "gdr_gdn_fwd",
     "gdr_gdn_bwd", "gdr_kda_ckpt", "gdr_gdn_ckpt", "gdr_check_device", "gdr_status_string",
-    "gdr_last_error", "gdr_timing_enable", "gdr_timing_read",
+    "gdr_last_error", "gdr_timing_enable", "gdr_timing_read", "gdr_walk_layout_chosen",
 )
 
 
@@ -92,6 +92,8 @@ def lib():
             L.gdr_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(i64), i32, ctypes.POINTER(i32), i32]
             L.gdr_timing_read.restype = i32
+            L.gdr_walk_layout_chosen.argtypes = [i32, P, i32, ctypes.POINTER(i32)]
+            L.gdr_walk_layout_chosen.restype = i32
             L.gdr_check_device.argtypes = []
             L.gdr_check_device.restype = i32
             L.gdr_status_string.argtypes = [i32]
@@ -113,6 +115,16 @@ def _check(status: int) -> None:
 
 def check_device() -> None:
     _check(lib().gdr_check_device())
+
+
+def walk_layout_chosen(variant, problem, compute_units=0) -> int:
+    """GDR_WALK_SLICES or GDR_WALK_RINGS: the walks' launch layout for `problem`
+    (a Problem or a _CProblem) on a device with `compute_units` CUs (0: current)."""
+    code = variant if isinstance(variant, int) else (GDR_KDA if variant == "kda" else GDR_GDN)
+    c = problem.cstruct if hasattr(problem, "cstruct") else ctypes.byref(problem)
+    out = ctypes.c_int32()
+    _check(lib().gdr_walk_layout_chosen(code, c, int(compute_units), ctypes.byref(out)))
+    return out.value
 
 
 def timing_enable(on: bool = True) -> None:

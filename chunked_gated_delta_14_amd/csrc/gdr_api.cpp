@@ -428,6 +428,17 @@ int32_t gdr_gdn_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_
   return ckpt_impl(GDR_GDN, p, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
 }
 
+int32_t gdr_walk_layout_chosen(int32_t variant, const gdr_problem *p, int32_t compute_units, int32_t *layout) {
+  int32_t rc = check_problem(variant, p);
+  if (rc) return rc;
+  if (!layout) return fail(GDR_ERR_INVALID_ARG, "layout is NULL");
+  if (compute_units < 0) return fail(GDR_ERR_INVALID_ARG, "compute_units < 0");
+  const gdr::Problem q = to_internal(p);
+  *layout = gdr::walk_uses_rings(q, compute_units > 0 ? compute_units : gdr::compute_units()) ? GDR_WALK_RINGS
+                                                                                              : GDR_WALK_SLICES;
+  return GDR_OK;
+}
+
 int32_t gdr_check_device(void) { return check_device_impl(); }
 
 int32_t gdr_timing_enable(int32_t on) {

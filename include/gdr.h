@@ -215,6 +215,14 @@ int32_t gdr_timing_enable(int32_t on);
 int32_t gdr_timing_read(const char **names, double *total_ms, int64_t *launches, int32_t capacity,
                         int32_t *count, int32_t reset);
 
+/* Launch layout the state walks of problem *p (variant GDR_KDA or GDR_GDN) take
+ * on a device with `compute_units` compute units (0: the current device, 256 if
+ * none can be queried): writes GDR_WALK_SLICES or GDR_WALK_RINGS to *layout.
+ * Host only; the problem is validated as by the forward, and no device call is
+ * made when compute_units > 0.  GDR_ERR_INVALID_ARG for a NULL layout or a
+ * negative unit count. */
+int32_t gdr_walk_layout_chosen(int32_t variant, const gdr_problem *p, int32_t compute_units, int32_t *layout);
+
 /* Returns GDR_OK when the current HIP device is gfx950, else GDR_ERR_ARCH
  * (GDR_ERR_HIP when no device can be queried). */
 int32_t gdr_check_device(void);

@@ -185,6 +185,33 @@ def test_max_doc_chunks_from_table(docs):
     assert gdr.max_doc_chunks(table, len(docs), nc) == max(-(-d // 64) for d in docs)
 
 
+@pytest.mark.parametrize("index,H,expected", [
+    (2, 16, "slices"),  # four long chains per head: the chain step decides
+    (2, 64, "rings"),   # 256 chains: the work per compute unit decides
+    (2, 4, "slices"),   # segmented walks keep the slices
+    (1, 16, "slices"),  # one 511-chunk document, four segments
+    (3, None, "rings"),  # GDN, 288 chains
+])
+def test_walk_layout_policy(index, H, expected):
+    """The automatic walk layout at each workload's shape, on a 256-CU device
+    (host only: no device call), and the forced layouts."""
+    from chunked_gated_delta_14_amd import workloads
+
+    w = workloads.workload(index, H)
+    cu = np.concatenate([[0], np.cumsum(w.docs)]).astype(np.int32)
+    table, nc = gdr.plan_chunks(cu)
+    p = _cproblem(T=w.T, N=len(w.docs), Hqk=w.H_qk, Hv=w.H_v, nc=nc)
+    p.max_doc_chunks = gdr.max_doc_chunks(table, len(w.docs), nc)
+    code = gdr.GDR_KDA if w.variant == "kda" else gdr.GDR_GDN
+    want = gdr.GDR_WALK_RINGS if expected == "rings" else gdr.GDR_WALK_SLICES
+    assert gdr.walk_layout_chosen(code, p, 256) == want
+    for forced in (gdr.GDR_WALK_SLICES, gdr.GDR_WALK_RINGS):
+        p.walk_layout = forced
+        assert gdr.walk_layout_chosen(code, p, 256) == forced
+    with pytest.raises(gdr.GdrError):
+        gdr.walk_layout_chosen(code, p, -1)
+
+
 def test_skip_output_flag_host_checks():
     """GDR_FWD_SKIP_OUTPUT is a known flag (workspace sizes as without it); o may be
     NULL only with it.  Only paths that stop before any device call are exercised."""
