@@ -419,8 +419,7 @@ constexpr int G_DAT = G_DMT + CH * DMP * 2;
 constexpr int G_TT = G_Y + CH * KP * 2;     // T^T bf16 [64][MP]             (Y product)
 constexpr int G_B = G_TT + CH * MP * 2;     // beta [64]
 constexpr int G_DB = G_B + 64 * 4;          // dbeta partial sums [20][64], added in a fixed order
-constexpr int G_RS = G_DB + 20 * 64 * 4;    // GDN: dG row sums per wavefront [8][64]
-constexpr int G_NRM = G_RS + 8 * 64 * 4;     // q, k row norms [2][64], then row dots [64][2][8]
+constexpr int G_NRM = G_DB + 20 * 64 * 4;   // q, k row norms [2][64], then row dots [64][2][8]
 constexpr int G_SMEM = G_NRM + (128 + 64 * 16) * 4;
 static_assert(G_DAT + CH * DMP * 2 <= G_B, "grad LDS map");
 
@@ -606,7 +605,6 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
   u16 *sDAT = reinterpret_cast<u16 *>(smem + G_DAT);
   float *sB = reinterpret_cast<float *>(smem + G_B);
   float *sDB = reinterpret_cast<float *>(smem + G_DB);
-  float *sRS = reinterpret_cast<float *>(smem + G_RS);
   const GateT<false> G{sG};
 
   float *sNrm = reinterpret_cast<float *>(smem + G_NRM);

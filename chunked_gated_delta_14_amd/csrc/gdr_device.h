@@ -208,7 +208,6 @@ struct RowSource {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
   }
   __device__ __forceinline__ uint2 get8(uint32_t byte_off) const {
-    typedef int i32x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0));
   }
 };
