@@ -23,6 +23,8 @@ SMALL = [
     ("gdn", (64,), 1, 1, False, False),
     ("gdn", (130, 1, 200), 1, 3, True, True),
     ("gdn", (77, 64, 129), 2, 6, False, True),
+    ("gdn", (70, 190), 2, 4, True, True),   # groups of 2 value heads
+    ("gdn", (130, 65), 1, 4, False, True),  # one group of 4
 ]
 
 
