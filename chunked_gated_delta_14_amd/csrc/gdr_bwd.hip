@@ -1162,9 +1162,25 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
       sDB[tid] = 0.f;
     }
     if (tid < 128) sRed[tid] = 0.f;
-    // operands of Y = T^T dVn (issued before the barrier)
+    // operands of Y = T^T dVn, v for dbeta and dv, and the dout / Vn rows of the tape
+    // products, all issued before the barrier
     const u16 *dvt = w.dVnT + u * (CH * HD);
-    bf16x8 bT[2], aDV[4][2];
+    bf16x8 bT[2], aDV[4][2], dOa[4], Vna[4];
+    uint2 vvs[4];
+    {
+      const u16 *dr = dout + ((size_t)(start + ra) * Hv + j) * HD;
+      const u16 *Vng = w.Vn + u * (CH * HD);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int c0 = 32 * kt + 8 * lg;
+        dOa[kt] = ra < len ? ld8(dr + c0) : as_bf16x8(make_uint4(0, 0, 0, 0));
+        Vna[kt] = ld8(Vng + tape_r(ra, c0));
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        vvs[t] = ra < len ? *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + ra) * Hv + j) * HD + 16 * (4 * ch + t) + 4 * lg)
+                          : make_uint2(0u, 0u);
+    }
     {
       const uint4 *TT = w.Tt + u * FRAG_64x64_U4;  // T^T, bf16 row-major 64 x 64
 #pragma unroll
@@ -1203,7 +1219,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
         *reinterpret_cast<uint2 *>(sY + ra * KP + v0) = pack4(acc[0], acc[1], acc[2], acc[3]);
         if (ra < len) {
           const size_t e = ((size_t)(start + ra) * Hv + j) * HD + v0;
-          const uint2 vv = *reinterpret_cast<const uint2 *>(p.v + e);
+          const uint2 vv = vvs[t];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) db1 += acc[jj] * bf_at(vv, jj);
           *reinterpret_cast<uint2 *>(dv + e) = pack4(br * acc[0], br * acc[1], br * acc[2], br * acc[3]);
@@ -1218,17 +1234,9 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
     const u16 *Sg = w.S + u * (HD * HD);
     const u16 *dSg = w.dS + u * (HD * HD);
     const u16 *Vng = w.Vn + u * (CH * HD);
-    bf16x8 dOa[4], Ya[4], Vna[4];
-    {
-      const u16 *dr = dout + ((size_t)(start + ra) * Hv + j) * HD;
+    bf16x8 Ya[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int c0 = 32 * kt + 8 * lg;
-        dOa[kt] = ra < len ? ld8(dr + c0) : as_bf16x8(make_uint4(0, 0, 0, 0));
-        Ya[kt] = ld8(sY + ra * KP + c0);
-        Vna[kt] = ld8(Vng + tape_r(ra, c0));
-      }
-    }
+    for (int kt = 0; kt < 4; ++kt) Ya[kt] = ld8(sY + ra * KP + 32 * kt + 8 * lg);
     const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
     f32x4 dGA[4];
     float dbp[4] = {0.f, 0.f, 0.f, 0.f};
