@@ -1090,7 +1090,8 @@ constexpr int grad_rows_smem_bytes() {
          + 4 * CH * MP * 2                  // sDM, sDA, sDMT, sDAT
          + (64 + 64 + 128 + 128 + 512) * 4  // sB, sDB, sRed, sDgam, sBT
          + (128 + 64 * 4) * 4               // q, k row norms [2][64], row dots [64][2][2]
-         + 64 * 4;                          // sG
+         + 64 * 4                           // sG
+         + CH * HD * 2;                     // sVn: the value head's Vn tile, tape layout
 }
 
 // acc[t] += x for a run-time tile index t, without indexing a register array
@@ -1128,6 +1129,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
   float *sBT = sDgam + 128;  // [4][128] row-block totals of the gate gradient
   float *sG = sBT + 512;
   float *sNrm = sG + 64;  // q, k row norms [2][64], then row dots [64][2][2]
+  u16 *sVn = reinterpret_cast<u16 *>(sNrm + 128 + 64 * 4);  // Vn tile of the current value head
   const GateT<true> G{sG};
 
   // (the Y stage is free until the first iteration: scratch of the row norms)
@@ -1165,17 +1167,15 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
     // operands of Y = T^T dVn, v for dbeta and dv, and the dout / Vn rows of the tape
     // products, all issued before the barrier
     const u16 *dvt = w.dVnT + u * (CH * HD);
-    bf16x8 bT[2], aDV[4][2], dOa[4], Vna[4];
+    bf16x8 bT[2], aDV[4][2], dOa[4];
     uint2 vvs[4];
+    // the Vn tile (16 KB) for the LDS stage: 32 contiguous bytes per thread
+    const uint4 *vnsrc = reinterpret_cast<const uint4 *>(w.Vn + u * (CH * HD));
+    const uint4 vn0 = vnsrc[2 * tid], vn1 = vnsrc[2 * tid + 1];
     {
       const u16 *dr = dout + ((size_t)(start + ra) * Hv + j) * HD;
-      const u16 *Vng = w.Vn + u * (CH * HD);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int c0 = 32 * kt + 8 * lg;
-        dOa[kt] = ra < len ? ld8(dr + c0) : as_bf16x8(make_uint4(0, 0, 0, 0));
-        Vna[kt] = ld8(Vng + tape_r(ra, c0));
-      }
+      for (int kt = 0; kt < 4; ++kt) dOa[kt] = ra < len ? ld8(dr + 32 * kt + 8 * lg) : as_bf16x8(make_uint4(0, 0, 0, 0));
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         vvs[t] = ra < len ? *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + ra) * Hv + j) * HD + 16 * (4 * ch + t) + 4 * lg)
@@ -1200,6 +1200,8 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
         }
         sG[tid] = x;
       }
+      reinterpret_cast<uint4 *>(sVn)[2 * tid] = vn0;
+      reinterpret_cast<uint4 *>(sVn)[2 * tid + 1] = vn1;
       lds_barrier();
     }
 
@@ -1233,10 +1235,12 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
     // ---- products with the state tapes (reduction over the value dim) ----
     const u16 *Sg = w.S + u * (HD * HD);
     const u16 *dSg = w.dS + u * (HD * HD);
-    const u16 *Vng = w.Vn + u * (CH * HD);
-    bf16x8 Ya[4];
+    bf16x8 Ya[4], Vna[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) Ya[kt] = ld8(sY + ra * KP + 32 * kt + 8 * lg);
+    for (int kt = 0; kt < 4; ++kt) {
+      Ya[kt] = ld8(sY + ra * KP + 32 * kt + 8 * lg);
+      Vna[kt] = ld8(sVn + tape_r(ra, 32 * kt + 8 * lg));
+    }
     const float4 b4 = *reinterpret_cast<const float4 *>(sB + r0);
     f32x4 dGA[4];
     float dbp[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1304,7 +1308,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
       if (nt <= mt) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 vb = ld8(Vng + tape_r(s, 32 * kt + 8 * lg));
+          const bf16x8 vb = ld8(sVn + tape_r(s, 32 * kt + 8 * lg));
           accM = mfma(dOa[kt], vb, accM);
           accA = mfma(Ya[kt], vb, accA);
         }
