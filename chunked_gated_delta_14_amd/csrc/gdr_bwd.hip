@@ -1168,7 +1168,12 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
     // products, all issued before the barrier
     const u16 *dvt = w.dVnT + u * (CH * HD);
     bf16x8 bT[2], aDV[4][2], dOa[4];
-    uint2 vvs[4];
+    uint2 vvs[4], e4s[2];
+    // E tiles (mt, ch + 2q) of the dA products (read only where ch + 2q <= mt; every index
+    // lies in the 10 lower tiles)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      e4s[q] = reinterpret_cast<const uint2 *>(w.Et + u * FRAG_64x64_U4)[(mt * (mt + 1) / 2 + ch + 2 * q) * 64 + lane];
     // the Vn tile (16 KB) for the LDS stage: 32 contiguous bytes per thread
     const uint4 *vnsrc = reinterpret_cast<const uint4 *>(w.Vn + u * (CH * HD));
     const uint4 vn0 = vnsrc[2 * tid], vn1 = vnsrc[2 * tid + 1];
@@ -1313,7 +1318,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
           accA = mfma(Ya[kt], vb, accA);
         }
         // E in accumulator order, tile (mt, nt) of the 10 lower tiles
-        const uint2 e4 = reinterpret_cast<const uint2 *>(w.Et + u * FRAG_64x64_U4)[(mt * (mt + 1) / 2 + nt) * 64 + lane];
+        const uint2 e4 = e4s[q];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
           if (s < r0 + jj) dbp[jj] -= accA[jj] * bf_at(e4, jj);
