@@ -1210,18 +1210,38 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
       lds_barrier();
     }
 
+    // the state tapes' first tile of the tape products below, fetched once the Y
+    // product has consumed its operands (before the stores and the barrier of that phase)
+    const u16 *Sg = w.S + u * (HD * HD);
+    const u16 *dSg = w.dS + u * (HD * HD);
+    bf16x8 Sb[2][4], dSb[2][4];
+    auto load_tile = [&](int t, bf16x8 (&sb)[4], bf16x8 (&dsb)[4]) {
+      const int c = 16 * (4 * ch + t) + lr;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sb[kt] = ld8(Sg + tape_s(c, 32 * kt + 8 * lg));
+        dsb[kt] = ld8(dSg + tape_s(c, 32 * kt + 8 * lg));
+      }
+    };
+
     // ---- Y = T^T dVn: rows 16mt.., value columns 64ch.. (4 tiles, computed as Y^T) ----
     {
       const int kt0 = mt >= 2 ? 1 : 0;  // T^T[r][r'] = 0 for r' < r
       const float br = sB[ra];
       float db1 = 0.f;
+      f32x4 accs[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        accs[t] = zero4();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          if (kt >= kt0) accs[t] = mfma(aDV[t][kt], bT[kt], accs[t]);
+      }
+      load_tile(0, Sb[0], dSb[0]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int v0 = 16 * (4 * ch + t) + 4 * lg;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          if (kt >= kt0) acc = mfma(aDV[t][kt], bT[kt], acc);
+        const f32x4 acc = accs[t];
         // acc[jj] = Y[ra][v0 + jj]
         *reinterpret_cast<uint2 *>(sY + ra * KP + v0) = pack4(acc[0], acc[1], acc[2], acc[3]);
         if (ra < len) {
@@ -1238,8 +1258,6 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
     lds_barrier();
 
     // ---- products with the state tapes (reduction over the value dim) ----
-    const u16 *Sg = w.S + u * (HD * HD);
-    const u16 *dSg = w.dS + u * (HD * HD);
     bf16x8 Ya[4], Vna[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -1250,16 +1268,6 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
     f32x4 dGA[4];
     float dbp[4] = {0.f, 0.f, 0.f, 0.f};
     {
-      bf16x8 Sb[2][4], dSb[2][4];
-      auto load_tile = [&](int t, bf16x8 (&sb)[4], bf16x8 (&dsb)[4]) {
-        const int c = 16 * (4 * ch + t) + lr;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          sb[kt] = ld8(Sg + tape_s(c, 32 * kt + 8 * lg));
-          dsb[kt] = ld8(dSg + tape_s(c, 32 * kt + 8 * lg));
-        }
-      };
-      load_tile(0, Sb[0], dSb[0]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int nt = 4 * ch + t, c = 16 * nt + lr;
