@@ -439,6 +439,8 @@ def main():
         "config": {"workload": w.name, "variant": w.variant, "T": T, "docs": list(w.docs), "H_qk": Hqk,
                    "H_v": Hv, "K": 128, "V": 128, "n_chunks": NC, "input_flags": args.input_flags,
                    "walk_segments": args.walk_segments, "walk_layout": args.walk_layout,
+                   "walk_layout_run": "rings" if gdr.walk_layout_chosen(gdr.GDR_GDN if gdn else gdr.GDR_KDA, prob)
+                   == gdr.GDR_WALK_RINGS else "slices",
                    "step": "forward with tapes + backward (prep, walk, adjoint walk, gradients)"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk_["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dk_["GB_s"] / HBM_PEAK_GBS, "traffic": traffic,
