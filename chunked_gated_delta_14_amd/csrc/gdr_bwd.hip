@@ -578,8 +578,20 @@ __device__ __forceinline__ void load_qk_rows(u16 *sQT, u16 *sKT, const Problem &
 
 __device__ __forceinline__ float sigmoidf_(float b) { return 1.f / (1.f + __expf(-b)); }
 
+// This wavefront's rows of a unit's state tapes, S[c][.] and dS'[c][.] (c = 16 wave + lr).
+__device__ __forceinline__ void load_grad_tape(const u16 *tape, size_t u, int tid, bf16x8 (&Sb)[4]) {
+  const int lane = tid & 63, c = 16 * (tid >> 6) + (lane & 15), lg = lane >> 4;
+  const u16 *Sg = tape + u * (HD * HD);
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) Sb[kt] = ld8(Sg + tape_s(c, 32 * kt + 8 * lg));
+}
+
+// Sb, dSb arrive holding this unit's state-tape rows (load_grad_tapes) and leave
+// holding those of unit `next` (if next >= 0), loaded once this unit is done with
+// them, so that their latency overlaps the rest of the unit.
 __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace &w, const u16 *dout, u16 *dq,
-                                             u16 *dk, u16 *dv, float *dg, void *dbeta, int unit) {
+                                             u16 *dk, u16 *dv, float *dg, void *dbeta, int unit,
+                                             bf16x8 (&Sb)[4], int next) {
   extern __shared__ __align__(16) unsigned char smem[];
   // Q/K heads vary fastest over the units (whole token rows per resident set)
   const int chunk = unit / p.Hqk, iqk = unit % p.Hqk;
@@ -688,17 +700,8 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         *reinterpret_cast<float2 *>(sG + (c0g + ii) * GTP + rp) = make_float2(incl - x1, incl);
       }
     }
-    // (issued after the gate scan to bound the registers in flight) this wavefront's rows of the state tapes: S[c][.], dS'[c][.]
-    bf16x8 Sb[4], dSb[4];
-    {
-      const u16 *Sg = w.S + u * (HD * HD);
-      const u16 *dSg = w.dS + u * (HD * HD);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        Sb[kt] = ld8(Sg + tape_s(c, 32 * kt + 8 * lg));
-        dSb[kt] = ld8(dSg + tape_s(c, 32 * kt + 8 * lg));
-      }
-    }
+    bf16x8 dSb[4];
+    load_grad_tape(w.dS, u, tid, dSb);
     // E (accumulator order) of the dM, dA tiles of this wavefront: p = w and p = w + 8
     uint2 eT[2];
 #pragma unroll
@@ -803,6 +806,7 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         if (lr == 0) sDB[(8 + wave) * 64 + r0 + jj] = x;  // slots 8..15
       }
     }
+    if (next >= 0) load_grad_tape(w.S, (size_t)(next / p.Hqk) * Hv + next % p.Hqk, tid, Sb);
     colsum = red_lg(colsum);
     // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r): the 10 lower
     // 16x16 tiles, wavefront w takes tiles w and w + 8
@@ -1523,8 +1527,12 @@ hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   const int units = p.NC * p.Hqk;
+  bf16x8 Sb[4];
+  if ((int)blockIdx.x < units)
+    load_grad_tape(w.S, (size_t)(blockIdx.x / p.Hqk) * p.Hv + blockIdx.x % p.Hqk, threadIdx.x, Sb);
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    bwd_grad_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit);
+    const int next = unit + (int)gridDim.x < units ? unit + (int)gridDim.x : -1;
+    bwd_grad_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit, Sb, next);
     lds_barrier();  // LDS is reused by the next unit
   }
 }
