@@ -88,9 +88,13 @@ __device__ __forceinline__ void settle(PrepIn &in) {
 
 // reuse: the current unit's inputs when the fetched unit reads the same Q/K head
 // (the next value head of its group): q and k are then copied, not reloaded.
-template <bool SCALAR>
+// PARTS selects what to fetch: PF_K, PF_Q, PF_V, PF_GA (KDA: gate channels
+// 8o..8o+3; GDN: the scalar gate) and PF_GB (KDA: channels 8o+4..8o+7; beta).
+constexpr int PF_K = 1, PF_Q = 2, PF_V = 4, PF_GA = 8, PF_GB = 16, PF_ALL = 31;
+template <bool SCALAR, int PARTS = PF_ALL>
 __device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const ChunkTable &tb, int unit, int tid,
                                           const PrepIn *reuse) {
+  if constexpr (PARTS == 0) return;
   const int chunk = unit / p.Hv, j = unit % p.Hv, iq = j / (p.Hv / p.Hqk);
   const int start = tb.start[chunk], len = tb.len[chunk];
   const int c0 = 8 * (tid >> 5), rp = 2 * (tid & 31);
@@ -101,26 +105,26 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const Ch
     const int r = rp + h;
     const bool ok = r < len;
     const size_t t = (size_t)(start + r);
-    if (reuse) {
-      in.k[h] = reuse->k[h];
-      in.q[h] = reuse->q[h];
-    } else {
-      in.k[h] = ok ? ld8(p.k + (t * p.Hqk + iq) * HD + c0) : z;
-      in.q[h] = ok ? ld8(p.q + (t * p.Hqk + iq) * HD + c0) : z;
-    }
-    in.v[h] = ok ? ld8(p.v + (t * Hv + j) * HD + c0) : z;
-    in.ga[h] = in.gb[h] = zero4();
-    in.b[h] = 0u;
-    if constexpr (SCALAR) {
+    if constexpr ((PARTS & PF_K) != 0) in.k[h] = reuse ? reuse->k[h] : ok ? ld8(p.k + (t * p.Hqk + iq) * HD + c0) : z;
+    if constexpr ((PARTS & PF_Q) != 0) in.q[h] = reuse ? reuse->q[h] : ok ? ld8(p.q + (t * p.Hqk + iq) * HD + c0) : z;
+    if constexpr ((PARTS & PF_V) != 0) in.v[h] = ok ? ld8(p.v + (t * Hv + j) * HD + c0) : z;
+    if constexpr ((PARTS & PF_GA) != 0) {
+      in.ga[h] = zero4();
       if (ok) {
-        in.ga[h][0] = p.g[t * Hv + j];
-        in.b[h] = reinterpret_cast<const uint32_t *>(p.beta)[t * Hv + j];
+        if constexpr (SCALAR) in.ga[h][0] = p.g[t * Hv + j];
+        else in.ga[h] = *reinterpret_cast<const f32x4 *>(p.g + (t * Hv + j) * HD + c0);
       }
-    } else {
+    }
+    if constexpr ((PARTS & PF_GB) != 0) {
+      in.gb[h] = zero4();
+      in.b[h] = 0u;
       if (ok) {
-        in.ga[h] = *reinterpret_cast<const f32x4 *>(p.g + (t * Hv + j) * HD + c0);
-        in.gb[h] = *reinterpret_cast<const f32x4 *>(p.g + (t * Hv + j) * HD + c0 + 4);
-        in.b[h] = reinterpret_cast<const u16 *>(p.beta)[t * Hv + j];
+        if constexpr (SCALAR) {
+          in.b[h] = reinterpret_cast<const uint32_t *>(p.beta)[t * Hv + j];
+        } else {
+          in.gb[h] = *reinterpret_cast<const f32x4 *>(p.g + (t * Hv + j) * HD + c0 + 4);
+          in.b[h] = reinterpret_cast<const u16 *>(p.beta)[t * Hv + j];
+        }
       }
     }
   }
@@ -271,13 +275,16 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     }
   }
   lds_barrier();
-  // The next unit's inputs: issued once this unit's are in LDS and the previous unit's
-  // final stores have drained (loads issued behind a burst of stores wait for it), and
-  // waited for at the end of this unit.
-  if (next_unit < p.NC * p.Hv) {
-    if constexpr (SCALAR) prep_load<SCALAR>(next, p, tb, next_unit, tid, next_same_qk ? &in : nullptr);
-    else prep_load<SCALAR>(next, p, tb, next_unit, tid, nullptr);
-  }
+  // The next unit's inputs, fetched in four parts: k here (this unit's inputs are in
+  // LDS), q and v after step 2, the first gate half after the inverse, the second
+  // half and beta before step 5; waited for at the end of this unit.  A wavefront
+  // that issues the whole fetch at once stalls at issue until the memory pipeline
+  // takes it, so spreading it lets the steps run in between.
+  constexpr int PF_A = PF_K, PF_B = PF_Q | PF_V, PF_C = PF_GA, PF_D = PF_GB;
+  static_assert((PF_A | PF_B | PF_C | PF_D) == PF_ALL && (PF_A + PF_B + PF_C + PF_D) == PF_ALL, "prefetch parts");
+  const bool has_next = next_unit < p.NC * p.Hv;
+  const PrepIn *reuse_in = SCALAR && next_same_qk ? &in : nullptr;
+  if (has_next) prep_load<SCALAR, PF_A>(next, p, tb, next_unit, tid, reuse_in);
 
   // ---- 2. gated products.  Wavefront w: column block J = w >> 1 and row
   // blocks I in {2kt, 2kt+1}, kt = w & 1; the two accumulator tiles of M are
@@ -328,6 +335,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     if (save) w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane] = as_u4(acc_pair_to_b(ms[0], ms[1]));
   }
   lds_barrier();
+  if (has_next) prep_load<SCALAR, PF_B>(next, p, tb, next_unit, tid, reuse_in);
 
   // ---- 3. column-form operands (over the step-1 space), then T ----
 #pragma unroll
@@ -339,6 +347,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     *reinterpret_cast<uint32_t *>(sKL + off) = pkKL[ii];
   }
   tri_inverse<PNT>(sT, sE, sB, tid);  // ends with a barrier
+  if (has_next) prep_load<SCALAR, PF_C>(next, p, tb, next_unit, tid, reuse_in);
 
   // ---- 4. W = T (beta k exp G), W^T, U = T (beta v).  Wavefront: row blocks
   // {2kp, 2kp+1}, column tiles {2cg, 2cg+1}. ----
@@ -396,6 +405,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
       }
     lds_barrier();
   }
+  if (has_next) prep_load<SCALAR, PF_D>(next, p, tb, next_unit, tid, reuse_in);
 
   // ---- 5. P^T = scale (q exp G)^T - scale W^T M^T,  Oi = scale M U (the output's
   // operands; a recompute that skips the output skips them) ----
@@ -480,7 +490,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 
 // Persistent: each workgroup walks the units blockIdx.x, blockIdx.x + gridDim.x,
 // ... and fetches the next unit's inputs into registers while it works on
-// the current one (from the end of the current unit's first phase on).
+// the current one (in parts, from the end of the current unit's first phase on).
 // ACT: input activations requested (q/k L2 norm, beta sigmoid); the instantiation
 // without them carries none of their code.
 template <bool SCALAR, bool ACT>
