@@ -497,15 +497,20 @@ __device__ __forceinline__ void split4(const f32x4 &x, uint2 &hi, uint2 &lo) {
 // 64 rows x 128 bf16 (row stride ld) -> LDS [channel][row] (pitch QTP), rows
 // >= len as zeros.  256 threads: thread b moves rows 4(b>>4)..+3 of channels
 // 8(b&15)..+7.
+// rows vary fastest over the lanes, so that the 8-byte transposed writes of 16
+// lanes (rows 4l..4l+3 of one channel) are consecutive in LDS
+__device__ __forceinline__ void fetch_rows(u32x4 (&x)[4], const u16 *src, size_t ld, int len, int b) {
+  const int r0 = 4 * (b & 15), c0 = 8 * (b >> 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    x[i] = r0 + i < len ? *reinterpret_cast<const u32x4 *>(src + (size_t)(r0 + i) * ld + c0) : u32x4{0u, 0u, 0u, 0u};
+}
 template <int PITCH>
-__device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, size_t ld, int len, int b) {
-  // rows vary fastest over the lanes, so that the 8-byte transposed writes of 16
-  // lanes (rows 4l..4l+3 of one channel) are consecutive in LDS
+__device__ __forceinline__ void store_rows_transposed(u16 *dst, const u32x4 (&xr)[4], int b) {
   const int r0 = 4 * (b & 15), c0 = 8 * (b >> 4);
   uint4 x[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    x[i] = r0 + i < len ? *reinterpret_cast<const uint4 *>(src + (size_t)(r0 + i) * ld + c0) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 4; ++i) x[i] = make_uint4(xr[i][0], xr[i][1], xr[i][2], xr[i][3]);
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) {
     const int sh = (cc & 1) * 16;
@@ -518,6 +523,21 @@ __device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, s
     pk.y = part(x[2]) | (part(x[3]) << 16);
     *reinterpret_cast<uint2 *>(dst + (c0 + cc) * PITCH + r0) = pk;
   }
+}
+template <int PITCH>
+__device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, size_t ld, int len, int b) {
+  u32x4 x[4];
+  fetch_rows(x, src, ld, len, b);
+  store_rows_transposed<PITCH>(dst, x, b);
+}
+
+// The raw q (threads 0..255) or k (256..511) rows of a KDA gradient unit, for
+// store_rows_transposed (inputs without the q/k L2 norm).
+__device__ __forceinline__ void fetch_qk_unit(const Problem &p, int unit, int tid, u32x4 (&x)[4]) {
+  const ChunkTable tb(p.table, p.NC, p.N);
+  const int chunk = unit / p.Hqk, iqk = unit % p.Hqk;
+  const int start = tb.start[chunk], len = tb.len[chunk], isk = tid >> 8;
+  fetch_rows(x, (isk ? p.k : p.q) + ((size_t)start * p.Hqk + iqk) * HD, (size_t)p.Hqk * HD, len, tid & 255);
 }
 
 // q and k rows of a chunk into the transposed LDS tiles, as load_rows_transposed
@@ -578,7 +598,7 @@ __device__ __forceinline__ void load_qk_rows(u16 *sQT, u16 *sKT, const Problem &
 
 __device__ __forceinline__ float sigmoidf_(float b) { return 1.f / (1.f + __expf(-b)); }
 
-// This wavefront's rows of a unit's state tapes, S[c][.] and dS'[c][.] (c = 16 wave + lr).
+// This wavefront's rows of one of a unit's state tapes (S or dS'): tape[c][.], c = 16 wave + lr.
 __device__ __forceinline__ void load_grad_tape(const u16 *tape, size_t u, int tid, bf16x8 (&Sb)[4]) {
   const int lane = tid & 63, c = 16 * (tid >> 6) + (lane & 15), lg = lane >> 4;
   const u16 *Sg = tape + u * (HD * HD);
@@ -586,12 +606,13 @@ __device__ __forceinline__ void load_grad_tape(const u16 *tape, size_t u, int ti
   for (int kt = 0; kt < 4; ++kt) Sb[kt] = ld8(Sg + tape_s(c, 32 * kt + 8 * lg));
 }
 
-// Sb, dSb arrive holding this unit's state-tape rows (load_grad_tapes) and leave
-// holding those of unit `next` (if next >= 0), loaded once this unit is done with
-// them, so that their latency overlaps the rest of the unit.
+// qkx arrives holding this unit's raw q/k rows (fetch_qk_unit) and leaves holding
+// those of unit `next` (if next >= 0), fetched once this unit's tape products are
+// done, so that their latency overlaps the rest of the unit.  With the q/k L2 norm
+// the unit loads its rows itself and qkx is unused.
 __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace &w, const u16 *dout, u16 *dq,
                                              u16 *dk, u16 *dv, float *dg, void *dbeta, int unit,
-                                             bf16x8 (&Sb)[4], int next) {
+                                             u32x4 (&qkx)[4], int next) {
   extern __shared__ __align__(16) unsigned char smem[];
   // Q/K heads vary fastest over the units (whole token rows per resident set)
   const int chunk = unit / p.Hqk, iqk = unit % p.Hqk;
@@ -621,7 +642,8 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
 
   float *sNrm = reinterpret_cast<float *>(smem + G_NRM);
   // (the dout stage is free until the first iteration's loads: scratch of the row norms)
-  load_qk_rows<KQTP>(sQT, sKT, p, start, iqk, len, tid0, reinterpret_cast<float *>(smem + G_DO), sNrm);
+  if (p.inflags & IN_QK_L2NORM) load_qk_rows<KQTP>(sQT, sKT, p, start, iqk, len, tid0, reinterpret_cast<float *>(smem + G_DO), sNrm);
+  else store_rows_transposed<KQTP>((tid0 >> 8) ? sKT : sQT, qkx, tid0 & 255);
 
   f32x4 dqA[4], dkA[4];  // [row block I]: rows 16I + 4lg + jj, column 16w + lr
 #pragma unroll
@@ -700,7 +722,9 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         *reinterpret_cast<float2 *>(sG + (c0g + ii) * GTP + rp) = make_float2(incl - x1, incl);
       }
     }
-    bf16x8 dSb[4];
+    // (issued after the gate scan to bound the registers in flight)
+    bf16x8 Sb[4], dSb[4];
+    load_grad_tape(w.S, u, tid, Sb);
     load_grad_tape(w.dS, u, tid, dSb);
     // E (accumulator order) of the dM, dA tiles of this wavefront: p = w and p = w + 8
     uint2 eT[2];
@@ -806,7 +830,7 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         if (lr == 0) sDB[(8 + wave) * 64 + r0 + jj] = x;  // slots 8..15
       }
     }
-    if (next >= 0) load_grad_tape(w.S, (size_t)(next / p.Hqk) * Hv + next % p.Hqk, tid, Sb);
+    if (next >= 0 && !(p.inflags & IN_QK_L2NORM)) fetch_qk_unit(p, next, tid, qkx);
     colsum = red_lg(colsum);
     // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r): the 10 lower
     // 16x16 tiles, wavefront w takes tiles w and w + 8
@@ -1527,12 +1551,11 @@ hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   const int units = p.NC * p.Hqk;
-  bf16x8 Sb[4];
-  if ((int)blockIdx.x < units)
-    load_grad_tape(w.S, (size_t)(blockIdx.x / p.Hqk) * p.Hv + blockIdx.x % p.Hqk, threadIdx.x, Sb);
+  u32x4 qkx[4];  // the q/k rows of the unit (inputs without the q/k L2 norm)
+  if ((int)blockIdx.x < units && !(p.inflags & IN_QK_L2NORM)) fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int next = unit + (int)gridDim.x < units ? unit + (int)gridDim.x : -1;
-    bwd_grad_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit, Sb, next);
+    bwd_grad_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit, qkx, next);
     lds_barrier();  // LDS is reused by the next unit
   }
 }
