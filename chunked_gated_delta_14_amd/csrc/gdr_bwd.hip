@@ -531,7 +531,7 @@ __device__ __forceinline__ void load_rows_transposed(u16 *dst, const u16 *src, s
   store_rows_transposed<PITCH>(dst, x, b);
 }
 
-// The raw q (threads 0..255) or k (256..511) rows of a KDA gradient unit, for
+// The raw q (threads 0..255) or k (256..511) rows of a gradient unit, for
 // store_rows_transposed (inputs without the q/k L2 norm).
 __device__ __forceinline__ void fetch_qk_unit(const Problem &p, int unit, int tid, u32x4 (&x)[4]) {
   const ChunkTable tb(p.table, p.NC, p.N);
@@ -1131,7 +1131,8 @@ __device__ __forceinline__ void add_tile(f32x4 (&acc)[4], int t, const f32x4 &x)
 }
 
 __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Workspace &w, const u16 *dout, u16 *dq,
-                                             u16 *dk, u16 *dv, float *dg, void *dbeta, int unit) {
+                                             u16 *dk, u16 *dv, float *dg, void *dbeta, int unit,
+                                             u32x4 (&qkx)[4], int next) {
   extern __shared__ __align__(16) unsigned char smem[];
   // Q/K heads vary fastest over the units (whole token rows per resident set)
   const int chunk = unit / p.Hqk, iqk = unit % p.Hqk;
@@ -1161,7 +1162,8 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
   const GateT<true> G{sG};
 
   // (the Y stage is free until the first iteration: scratch of the row norms)
-  load_qk_rows<QTP>(sQT, sKT, p, start, iqk, len, tid0, reinterpret_cast<float *>(sY), sNrm);
+  if (p.inflags & IN_QK_L2NORM) load_qk_rows<QTP>(sQT, sKT, p, start, iqk, len, tid0, reinterpret_cast<float *>(sY), sNrm);
+  else store_rows_transposed<QTP>((tid0 >> 8) ? sKT : sQT, qkx, tid0 & 255);
 
   f32x4 dqA[4], dkA[4];
 #pragma unroll
@@ -1341,6 +1343,9 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
         if (lg == 0) atomicAdd(&sRed[c], colsum);
       }
     }
+    // the next unit's q/k rows, once the last value head's tape products are done
+    // (qkx as in bwd_grad_unit)
+    if (jg == grp - 1 && next >= 0 && !(p.inflags & IN_QK_L2NORM)) fetch_qk_unit(p, next, tid, qkx);
     // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r), 16 x 16 tiles (mt, nt)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -1562,8 +1567,11 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                             u16 *dk, u16 *dv, float *dg, void *dbeta) {
   const int units = p.NC * p.Hqk;
+  u32x4 qkx[4];  // the q/k rows of the unit (inputs without the q/k L2 norm)
+  if ((int)blockIdx.x < units && !(p.inflags & IN_QK_L2NORM)) fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    bwd_grad_rows_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit);
+    const int next = unit + (int)gridDim.x < units ? unit + (int)gridDim.x : -1;
+    bwd_grad_rows_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit, qkx, next);
     lds_barrier();  // LDS is reused by the next unit
   }
 }
