@@ -1116,7 +1116,7 @@ constexpr int grad_rows_smem_bytes() {
   return 2 * HD * QTP * 2                   // sQT, sKT
          + CH * KP * 2                      // sY
          + 4 * CH * MP * 2                  // sDM, sDA, sDMT, sDAT
-         + (64 + 64 + 128 + 128 + 512) * 4  // sB, sDB, sRed, sDgam, sBT
+         + (64 + 4 * 64 + 4 * 128 + 128 + 512) * 4  // sB, sDB slots, sRed slots, sDgam, sBT
          + (128 + 64 * 4) * 4               // q, k row norms [2][64], row dots [64][2][2]
          + 64 * 4                           // sG
          + CH * HD * 2;                     // sVn: the value head's Vn tile, tape layout
@@ -1152,9 +1152,11 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
   u16 *sDMT = sDA + CH * MP;
   u16 *sDAT = sDMT + CH * MP;
   float *sB = reinterpret_cast<float *>(sDAT + CH * MP);
-  float *sDB = sB + 64;
-  float *sRed = sDB + 64;
-  float *sDgam = sRed + 128;
+  // Reductions across wavefronts go to one slot per contributing wavefront and
+  // are added in a fixed order, so every result is bitwise repeatable.
+  float *sDB = sB + 64;     // dbeta partial sums [4][64]: Y phase (column half 0, 1), then tape/dA phase (0, 1)
+  float *sRed = sDB + 256;  // K-bar column sums [4][128], one slot per row strip
+  float *sDgam = sRed + 512;
   float *sBT = sDgam + 128;  // [4][128] row-block totals of the gate gradient
   float *sG = sBT + 512;
   float *sNrm = sG + 64;  // q, k row norms [2][64], then row dots [64][2][2]
@@ -1191,9 +1193,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
         if (p.inflags & IN_BETA_SIGMOID) b = sigmoidf_(b);
       }
       sB[tid] = b;
-      sDB[tid] = 0.f;
     }
-    if (tid < 128) sRed[tid] = 0.f;
     // operands of Y = T^T dVn, v for dbeta and dv, and the dout / Vn rows of the tape
     // products, all issued before the barrier
     const u16 *dvt = w.dVnT + u * (CH * HD);
@@ -1283,7 +1283,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
         }
       }
       db1 = red_lg(db1);
-      if (lg == 0) atomicAdd(&sDB[ra], db1);
+      if (lg == 0) sDB[ch * 64 + ra] = db1;
     }
     lds_barrier();
 
@@ -1340,7 +1340,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
           dbp[jj] -= kt_ * aY[jj];
         }
         colsum = red_lg(colsum);
-        if (lg == 0) atomicAdd(&sRed[c], colsum);
+        if (lg == 0) sRed[mt * 128 + c] = colsum;
       }
     }
     // the next unit's q/k rows, once the last value head's tape products are done
@@ -1437,12 +1437,12 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const float x = red16(dbp[jj]);
-      if (lr == 0) atomicAdd(&sDB[r0 + jj], x);
+      if (lr == 0) sDB[(2 + ch) * 64 + r0 + jj] = x;
     }
     lds_barrier();  // also: sRed and sDgam complete
     if (tid < 64 && tid < len) {
       const size_t e = (size_t)(start + tid) * Hv + j;
-      float x = sDB[tid];
+      float x = ((sDB[tid] + sDB[64 + tid]) + sDB[128 + tid]) + sDB[192 + tid];
       if (p.inflags & IN_BETA_SIGMOID) x *= sB[tid] * (1.f - sB[tid]);  // to the logit
       reinterpret_cast<float *>(dbeta)[e] = x;
     }
@@ -1454,7 +1454,8 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int c = 16 * (4 * ch + t) + lr;
-        const float extra = sRed[c] + __expf(G.at(last, c)) * sDgam[c];
+        const float red = ((sRed[c] + sRed[128 + c]) + sRed[256 + c]) + sRed[384 + c];
+        const float extra = red + __expf(G.at(last, c)) * sDgam[c];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
           if (r0 + jj == last) dGA[t][jj] += extra;

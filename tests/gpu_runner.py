@@ -19,10 +19,13 @@ def to_dev(inp, device="cuda"):
     return {k: (v.to(device) if (torch.is_tensor(v) and k != "cu_seqlens") else v) for k, v in inp.items()}
 
 
-def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, nan_workspace=True, workspace=None,
+def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, ws_fill=0xFF, workspace=None,
             on_device=False, input_flags=0, walk_segments=0, walk_layout=0):
     """Forward (with tapes) and backward on the GPU.  Returns CPU fp32 tensors
-    (or the device tensors as computed, with on_device=True)."""
+    (or the device tensors as computed, with on_device=True).
+
+    ws_fill: byte written over the whole workspace first (0xFF: NaN in bf16 and
+    fp32; 0x00: zeros; None: left as it is)."""
     import torch
 
     import chunked_gated_delta_14_amd as gdr
@@ -33,8 +36,8 @@ def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, nan_workspace=
                        input_flags=input_flags, walk_segments=walk_segments, walk_layout=walk_layout)
     T, Hqk, Hv, N = prob.T, prob.H_qk, prob.H_v, prob.N
     ws = workspace if workspace is not None else prob.alloc_workspace(gdr.GDR_FWD_SAVE)
-    if nan_workspace:
-        ws.fill_(0xFF)  # all-ones bytes: NaN in bf16 and fp32
+    if ws_fill is not None:
+        ws.fill_(ws_fill)
     dev = d["q"].device
     bf, f32 = torch.bfloat16, torch.float32
     o = torch.full((T, Hv, 128), float("nan"), dtype=bf, device=dev)

@@ -137,37 +137,57 @@ def test_workload0_parity():
     compare(got, ref, label=w.name)
 
 
-def test_ckpt_equals_fwd_bwd_bitwise():
-    w = workloads.custom("kda", (150, 90), 2, 2, with_h0=True, seed=3)
+BITWISE = [
+    # (variant, docs, H_qk, H_v): ragged packs with h0 and dht
+    ("kda", (150, 90), 2, 2),
+    ("gdn", (150, 90, 1), 2, 6),
+]
+_bw_ids = lambda c: "%s_%s_h%d_%d" % (c[0], "-".join(map(str, c[1])), c[2], c[3])
+
+
+@pytest.mark.parametrize("case", BITWISE, ids=_bw_ids)
+def test_ckpt_equals_fwd_bwd_bitwise(case):
+    """The checkpointed step (forward, recompute without the output, backward on
+    the recompute's tapes) returns every output and gradient bitwise equal to a
+    forward with tapes followed by the backward."""
+    variant, docs, hqk, hv = case
+    w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=3)
     inp = workloads.make_inputs(w, device="cpu", dht=True)
-    a = run_gdr("kda", inp, dht=inp["dht"])
-    b = run_gdr("kda", inp, dht=inp["dht"], ckpt=True)
+    print("[case]", w.name, "ckpt vs fwd+bwd", flush=True)
+    a = run_gdr(variant, inp, dht=inp["dht"])
+    b = run_gdr(variant, inp, dht=inp["dht"], ckpt=True)
     for key in a:
         assert torch.equal(a[key], b[key]), key
 
 
-def test_recompute_without_output():
+@pytest.mark.parametrize("variant", ["kda", "gdn"])
+def test_recompute_without_output(variant):
     """GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT writes the same tapes as GDR_FWD_SAVE and
     leaves o untouched: the backward after it is bitwise the backward after a full
     forward."""
     import chunked_gated_delta_14_amd as gdr
     from gpu_runner import to_dev
 
-    w = workloads.custom("kda", (170, 64, 33), 2, 2, with_h0=True, seed=8)
+    hqk, hv = (2, 2) if variant == "kda" else (1, 3)
+    w = workloads.custom(variant, (170, 64, 33), hqk, hv, with_h0=True, seed=8)
     inp = workloads.make_inputs(w, device="cpu", dht=True)
-    a = run_gdr("kda", inp, dht=inp["dht"])
+    print("[case]", w.name, "recompute without output", flush=True)
+    a = run_gdr(variant, inp, dht=inp["dht"])
     d = to_dev(inp)
-    prob = gdr.Problem(gdr.GDR_KDA, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["h0"])
+    code = gdr.GDR_KDA if variant == "kda" else gdr.GDR_GDN
+    fwd = gdr.kda_fwd if variant == "kda" else gdr.gdn_fwd
+    bwd = gdr.kda_bwd if variant == "kda" else gdr.gdn_bwd
+    prob = gdr.Problem(code, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["h0"])
     ws = prob.alloc_workspace(gdr.GDR_FWD_SAVE)
     ws.fill_(0xFF)
     T, N = prob.T, prob.N
-    sentinel = torch.full((T, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda")
-    ht = torch.empty((N, 2, 128, 128), dtype=torch.float32, device="cuda")
-    gdr.kda_fwd(prob, sentinel, ht, ws, gdr.GDR_FWD_SAVE | gdr.GDR_FWD_SKIP_OUTPUT)
-    gdr.kda_fwd(prob, None, None, ws, gdr.GDR_FWD_SAVE | gdr.GDR_FWD_SKIP_OUTPUT)
+    sentinel = torch.full((T, hv, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty((N, hv, 128, 128), dtype=torch.float32, device="cuda")
+    fwd(prob, sentinel, ht, ws, gdr.GDR_FWD_SAVE | gdr.GDR_FWD_SKIP_OUTPUT)
+    fwd(prob, None, None, ws, gdr.GDR_FWD_SAVE | gdr.GDR_FWD_SKIP_OUTPUT)
     g = {k: torch.full_like(a[k], float("nan"), device="cuda").to(v.dtype) for k, v in
          dict(dq=d["q"], dk=d["k"], dv=d["v"], dg=d["g"], dbeta=d["beta"], dh0=ht).items()}
-    gdr.kda_bwd(prob, d["dout"], d["dht"], g["dq"], g["dk"], g["dv"], g["dg"], g["dbeta"], g["dh0"], ws)
+    bwd(prob, d["dout"], d["dht"], g["dq"], g["dk"], g["dv"], g["dg"], g["dbeta"], g["dh0"], ws)
     torch.cuda.synchronize()
     assert bool((sentinel == 7.0).all())
     assert torch.equal(ht.cpu(), a["ht"])
@@ -222,13 +242,199 @@ def test_ckpt_graph_replay(walk_layout):
             assert torch.equal(outs[k], eager[k]), (rep, k)
 
 
-def test_repeat_bitwise_and_nan_workspace():
-    w = workloads.custom("gdn", (100, 180), 1, 3, with_h0=True, seed=4)
+REPEAT = [
+    # (variant, docs, H_qk, H_v): ragged packs with h0 and dht; the second pair
+    # has more units than twice the compute units, so every workgroup of the
+    # persistent kernels walks several units
+    ("kda", (100, 180, 1), 2, 2),
+    ("gdn", (100, 180, 1), 1, 3),
+    ("kda", (3000, 1100, 64), 8, 8),
+    ("gdn", (4000, 1500, 64), 8, 24),
+]
+
+
+@pytest.mark.parametrize("case", REPEAT, ids=_bw_ids)
+def test_repeat_bitwise(case):
+    """The same call twice gives the same bits: every reduction runs in a fixed
+    order (the pages hold out, dq, dk, dv and dbeta bitwise across runs)."""
+    variant, docs, hqk, hv = case
+    w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=4)
     inp = workloads.make_inputs(w, device="cpu", dht=True)
-    a = run_gdr("gdn", inp, dht=inp["dht"], nan_workspace=True)
-    b = run_gdr("gdn", inp, dht=inp["dht"], nan_workspace=False)
+    print("[case]", w.name, "repeat", flush=True)
+    a = run_gdr(variant, inp, dht=inp["dht"])
+    b = run_gdr(variant, inp, dht=inp["dht"])
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("case", REPEAT[:2], ids=_bw_ids)
+def test_nan_workspace(case):
+    """Workspace contents on entry do not matter: a NaN-filled workspace and a
+    zero-filled one give the same bits."""
+    variant, docs, hqk, hv = case
+    w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=5)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    print("[case]", w.name, "NaN vs zero workspace", flush=True)
+    a = run_gdr(variant, inp, dht=inp["dht"], ws_fill=0xFF)
+    b = run_gdr(variant, inp, dht=inp["dht"], ws_fill=0x00)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+MULTI_UNIT = [
+    # (variant, docs, H_qk, H_v, input_flags): 528 KDA units and 704 GDN
+    # (chunk, Q/K head) units, over twice the 256 compute units, so the
+    # persistent kernels' carried next-unit loads are exercised
+    ("kda", (3000, 1100, 64), 8, 8, 0),
+    ("kda", (3000, 1100, 64), 8, 8, 3),
+    ("gdn", (4000, 1500, 64), 8, 24, 0),
+    ("gdn", (4000, 1500, 64), 8, 24, 3),
+]
+
+
+@pytest.mark.parametrize("case", MULTI_UNIT,
+                         ids=lambda c: "%s_%s_h%d_%d_f%d" % (c[0], "-".join(map(str, c[1])), c[2], c[3], c[4]))
+def test_multi_unit_persistent(case):
+    """Packs where every workgroup of prep and of the gradient kernels walks two
+    or three units: all heads and tokens against the oracle, with and without the
+    in-kernel q/k L2 norm and beta sigmoid."""
+    variant, docs, hqk, hv, flags = case
+    w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=sum(docs) + flags)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    if flags:
+        gen = torch.Generator().manual_seed(sum(docs))
+        for name in ("q", "k"):
+            x = inp[name].float()
+            inp[name] = (x * (0.25 + 4.0 * torch.rand((w.T, hqk, 1), generator=gen))).to(torch.bfloat16)
+        inp["beta"] = torch.randn(tuple(inp["beta"].shape), generator=gen).to(inp["beta"].dtype)
+    print("[case]", w.name, "multi-unit, input flags", flags, flush=True)
+    got = run_gdr(variant, inp, dht=inp["dht"], input_flags=flags)
+    ref = oracle_all(variant, inp, dht=inp["dht"], qk_l2norm=bool(flags & 1), beta_sigmoid=bool(flags & 2))
+    compare(got, ref, label="%s_f%d" % (w.name, flags))
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn"])
+def test_document_independence(variant):
+    """Perturbing every input of one document leaves every output and gradient of
+    the other documents bitwise unchanged (the state restarts at each boundary)."""
+    hqk, hv = (2, 2) if variant == "kda" else (1, 3)
+    docs = (300, 129, 77, 1)
+    w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=12)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    print("[case]", w.name, "document independence", flush=True)
+    a = run_gdr(variant, inp, dht=inp["dht"])
+    cu = inp["cu_seqlens"].tolist()
+    lo, hi = cu[1], cu[2]  # document 1
+    gen = torch.Generator().manual_seed(99)
+    pert = dict(inp)
+    for key in ("q", "k", "v", "g", "beta", "dout"):
+        x = inp[key].clone()
+        noise = torch.randn(tuple(x[lo:hi].shape), generator=gen)
+        if key in ("q", "k"):
+            y = x[lo:hi].float() + 0.5 * noise
+            x[lo:hi] = (y / y.norm(dim=-1, keepdim=True)).to(x.dtype)
+        elif key == "g":
+            x[lo:hi] = -5.0 * torch.rand(tuple(x[lo:hi].shape), generator=gen)
+        elif key == "beta":
+            x[lo:hi] = torch.sigmoid(noise).to(x.dtype)
+        else:
+            x[lo:hi] = noise.to(x.dtype)
+        pert[key] = x
+    for key in ("h0", "dht"):
+        x = inp[key].clone()
+        x[1] = 0.05 * torch.randn(tuple(x[1].shape), generator=gen)
+        pert[key] = x
+    b = run_gdr(variant, pert, dht=pert["dht"])
+    keep_t = torch.ones(w.T, dtype=torch.bool)
+    keep_t[lo:hi] = False
+    keep_n = torch.tensor([n != 1 for n in range(len(docs))])
+    for key in a:
+        sel = keep_n if key in ("ht", "dh0") else keep_t
+        assert torch.equal(a[key][sel], b[key][sel]), key
+        changed = ~sel
+        assert not torch.equal(a[key][changed], b[key][changed]), key + " of the perturbed document did not change"
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn"])
+def test_shared_workspace_across_packs(variant):
+    """One workspace, sized for the larger of two packs, serves both in turn: each
+    result is bitwise the result with a workspace of its own."""
+    import chunked_gated_delta_14_amd as gdr
+
+    hqk, hv = (2, 2) if variant == "kda" else (1, 3)
+    wa = workloads.custom(variant, (500, 77), hqk, hv, with_h0=True, seed=21)
+    wb = workloads.custom(variant, (64, 1, 190, 33), hqk, hv, with_h0=True, seed=22)
+    ia = workloads.make_inputs(wa, device="cpu", dht=True)
+    ib = workloads.make_inputs(wb, device="cpu", dht=True)
+    print("[case]", wa.name, wb.name, "shared workspace", flush=True)
+    ref_a = run_gdr(variant, ia, dht=ia["dht"])
+    ref_b = run_gdr(variant, ib, dht=ib["dht"])
+    code = gdr.GDR_KDA if variant == "kda" else gdr.GDR_GDN
+
+    def need(inp, w):
+        cu = inp["cu_seqlens"].numpy()
+        _, nc = gdr.plan_chunks(cu)
+        return gdr.workspace_bytes(code, w.T, len(w.docs), nc, hqk, hv, 128, 128, gdr.GDR_FWD_SAVE)
+
+    ws = torch.empty(max(need(ia, wa), need(ib, wb)), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    for inp, ref in ((ia, ref_a), (ib, ref_b), (ia, ref_a)):
+        got = run_gdr(variant, inp, dht=inp["dht"], workspace=ws, ws_fill=None)
+        for key in ref:
+            assert torch.equal(got[key], ref[key]), key
+
+
+@pytest.mark.parametrize("variant", ["kda", "gdn"])
+def test_steady_calls_neither_allocate_nor_block(variant):
+    """After a first call, forward, backward and the checkpointed step return to
+    the host while earlier work on the stream is still running (no
+    synchronisation), and device free memory is unchanged (no allocation)."""
+    import time
+
+    import chunked_gated_delta_14_amd as gdr
+    from gpu_runner import to_dev
+
+    hqk, hv = (2, 2) if variant == "kda" else (1, 3)
+    w = workloads.custom(variant, (300, 129), hqk, hv, with_h0=True, seed=31)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    d = to_dev(inp)
+    code = gdr.GDR_KDA if variant == "kda" else gdr.GDR_GDN
+    prob = gdr.Problem(code, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["h0"])
+    ws = prob.alloc_workspace(gdr.GDR_FWD_SAVE)
+    T, N = prob.T, prob.N
+    bf, f32 = torch.bfloat16, torch.float32
+    o = torch.empty((T, hv, 128), dtype=bf, device="cuda")
+    ht = torch.empty((N, hv, 128, 128), dtype=f32, device="cuda")
+    dq, dk = (torch.empty((T, hqk, 128), dtype=bf, device="cuda") for _ in range(2))
+    dv = torch.empty((T, hv, 128), dtype=bf, device="cuda")
+    dg = torch.empty(tuple(d["g"].shape), dtype=f32, device="cuda")
+    dbeta = torch.empty(tuple(d["beta"].shape), dtype=d["beta"].dtype, device="cuda")
+    dh0 = torch.empty((N, hv, 128, 128), dtype=f32, device="cuda")
+    fwd = gdr.kda_fwd if variant == "kda" else gdr.gdn_fwd
+    bwd = gdr.kda_bwd if variant == "kda" else gdr.gdn_bwd
+    ckpt = gdr.kda_ckpt if variant == "kda" else gdr.gdn_ckpt
+
+    def calls():
+        fwd(prob, o, ht, ws, 0)
+        fwd(prob, o, ht, ws, gdr.GDR_FWD_SAVE)
+        bwd(prob, d["dout"], d["dht"], dq, dk, dv, dg, dbeta, dh0, ws)
+        ckpt(prob, o, ht, d["dout"], d["dht"], dq, dk, dv, dg, dbeta, dh0, ws)
+
+    calls()  # first call: one-time kernel attributes
+    torch.cuda._sleep(1000)  # and the spin kernel's own first launch (loads its code object)
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    stream = torch.cuda.current_stream()
+    torch.cuda._sleep(200_000_000)  # a bounded spin kernel ahead of the calls
+    t0 = time.perf_counter()
+    calls()
+    host_s = time.perf_counter() - t0
+    pending = not stream.query()
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    print("[steady] host %.3f ms for 4 calls, stream pending after them: %s" % (1e3 * host_s, pending), flush=True)
+    assert pending, "a call waited for the stream"
+    assert free1 == free0, "device free memory changed by %d bytes" % (free0 - free1)
 
 
 def test_forward_without_tapes_matches():

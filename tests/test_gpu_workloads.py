@@ -2,14 +2,20 @@
 benchmark times.
 
 The GPU runs the whole pack (every head, every document).  The fp64 oracle
-checks sampled heads: for each document it runs the forward over the
-document's prefix (giving o there and the state entering the last WINDOW
-tokens), then forward + backward over that window entered with the prefix
-state and no final-state gradient.  That is exactly the document's
-gradient for the window's tokens, because a token's gradients depend only on
-the state entering it and on the tokens after it.  Workload 1 (a 32674-token
-shard entered with h0) runs the oracle over the whole sequence for three
-heads, which also checks ht and dh0.
+checks sampled heads in two ways:
+
+* full: one Q/K head (with its value heads) over the whole pack, every token of
+  every document, o, ht and every gradient.  This includes the deepest steps of
+  the adjoint walk (1386 chunks on the longest KDA document);
+* window: another head, o over every token, gradients over each document's last
+  WINDOW tokens.  The oracle runs the forward over the document's prefix (giving
+  o there and the state entering the window), then forward + backward over the
+  window entered with that state.  That is exactly the document's gradient for
+  the window's tokens, because a token's gradients depend only on the state
+  entering it and on the tokens after it.
+
+Workload 1 (a 32674-token shard entered with h0) runs the oracle over the
+whole sequence for three heads, which also checks ht and dh0.
 """
 import numpy as np
 import pytest
@@ -24,7 +30,7 @@ pytestmark = pytest.mark.gpu
 WINDOW = 512
 
 
-def _slice_heads(inp, variant, qk_heads, group):
+def _slice_heads(inp, qk_heads, group):
     vh = [i * group + g for i in qk_heads for g in range(group)]
     out = {}
     for key in ("q", "k"):
@@ -71,31 +77,60 @@ def _oracle_windows(sub, cu):
     return ref, grads, win_idx
 
 
-def _check_workload(w, ckpt=False, qk_heads=(0,), label=None):
+def _oracle_full(sub, cu):
+    """Forward and backward of the whole pack for the sliced heads."""
+    o, ht = oracle.forward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], cu, sub["h0"])
+    gr = oracle.backward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], cu, sub["dout"], sub["h0"], None)
+    return {"o": o, "ht": ht, **gr}
+
+
+def _heads_of(dev, qh, vh):
+    return {k: dev[k][:, qh if k in ("dq", "dk") else vh].float().cpu() for k in dev}
+
+
+def _check_workload(w, ckpt=False, full_qk_heads=(0,), window_qk_heads=(), also_ckpt=False):
+    """Run the whole pack on the GPU, then check sampled heads against the oracle.
+    With also_ckpt, the checkpointed step runs too and must be bitwise equal to
+    forward + backward on every head."""
     inp = workloads.make_inputs(w, device="cuda")
-    print("[case]", w.name, flush=True)
+    print("[case]", w.name, "ckpt" if ckpt else "fwd+bwd", flush=True)
     dev = run_gdr(w.variant, inp, ckpt=ckpt, on_device=True)
+    if also_ckpt:
+        print("[case]", w.name, "ckpt, bitwise against fwd+bwd", flush=True)
+        dev2 = run_gdr(w.variant, inp, ckpt=True, on_device=True)
+        for key in dev:
+            assert torch.equal(dev[key], dev2[key]), "%s: ckpt differs from fwd+bwd" % key
+        del dev2
     group = w.H_v // w.H_qk
-    qh = list(qk_heads)
-    sub, vh = _slice_heads(inp, w.variant, qh, group)
-    got = {k: dev[k][:, qh if k in ("dq", "dk") else vh].float().cpu() for k in dev}
+    cu = inp["cu_seqlens"].numpy()
+    sampled = {}
+    for qh in list(full_qk_heads) + list(window_qk_heads):
+        sub, vh = _slice_heads(inp, [qh], group)
+        sampled[qh] = (sub, _heads_of(dev, [qh], vh))
     del dev
     torch.cuda.empty_cache()
-    cu = inp["cu_seqlens"].numpy()
-    ref, grads, win_idx = _oracle_windows(sub, cu)
-    g = {"o": got["o"], "ht": got["ht"]}
-    compare(g, ref, names=["o", "ht"], label=(label or w.name) + " fwd")
-    gg = {k: got[k][torch.from_numpy(win_idx)] for k in ("dq", "dk", "dv", "dg", "dbeta")}
-    compare(gg, grads, names=["dq", "dk", "dv", "dg", "dbeta"], label=(label or w.name) + " bwd window")
+    for qh in full_qk_heads:
+        sub, got = sampled[qh]
+        print("[oracle] %s Q/K head %d, whole pack" % (w.name, qh), flush=True)
+        ref = _oracle_full(sub, cu)
+        compare(got, ref, names=["o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"], label="%s head %d full" % (w.name, qh))
+    for qh in window_qk_heads:
+        sub, got = sampled[qh]
+        print("[oracle] %s Q/K head %d, windows" % (w.name, qh), flush=True)
+        ref, grads, win_idx = _oracle_windows(sub, cu)
+        compare({"o": got["o"], "ht": got["ht"]}, ref, names=["o", "ht"], label="%s head %d fwd" % (w.name, qh))
+        gg = {k: got[k][torch.from_numpy(win_idx)] for k in ("dq", "dk", "dv", "dg", "dbeta")}
+        compare(gg, grads, names=["dq", "dk", "dv", "dg", "dbeta"], label="%s head %d bwd window" % (w.name, qh))
 
 
 def test_workload1_shard_with_initial_state():
     w = workloads.workload(1)
     inp = workloads.make_inputs(w, device="cuda")
+    print("[case]", w.name, flush=True)
     dev = run_gdr("kda", inp, on_device=True)
     heads = [0, 7, 15]
     got = {k: v[:, heads].float().cpu() for k, v in dev.items()}
-    sub, vh = _slice_heads(inp, "kda", heads, 1)
+    sub, vh = _slice_heads(inp, heads, 1)
     cu = inp["cu_seqlens"].numpy()
     o, ht = oracle.forward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], cu, sub["h0"])
     gr = oracle.backward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], cu, sub["dout"], sub["h0"], None)
@@ -105,12 +140,12 @@ def test_workload1_shard_with_initial_state():
 
 @pytest.mark.parametrize("H", [4, 16])
 def test_workload2_pack(H):
-    _check_workload(workloads.workload(2, H), qk_heads=(0, H - 1))
+    _check_workload(workloads.workload(2, H), full_qk_heads=(H - 1,), window_qk_heads=(0,))
 
 
-def test_workload3_gdn_pack():
-    _check_workload(workloads.workload(3), qk_heads=(0, 15))
+def test_workload3_gdn_pack_and_ckpt():
+    _check_workload(workloads.workload(3), full_qk_heads=(15,), window_qk_heads=(0,), also_ckpt=True)
 
 
 def test_workload4_pack_h64_ckpt():
-    _check_workload(workloads.workload(4), ckpt=True, qk_heads=(0, 63))
+    _check_workload(workloads.workload(4), ckpt=True, full_qk_heads=(63,), window_qk_heads=(0,))
