@@ -17,7 +17,8 @@ from . import _build
 
 __all__ = [
     "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GDR_IN_QK_L2NORM", "GDR_IN_BETA_SIGMOID", "GDR_WALK_AUTO", "GDR_WALK_SLICES", "GDR_WALK_RINGS", "GdrError", "lib", "plan_chunks", "max_doc_chunks", "workspace_bytes",
-    "Problem", "kda_fwd", "kda_bwd", "gdn_fwd", "gdn_bwd", "kda_ckpt", "gdn_ckpt", "status_string",
+    "Problem", "kda_fwd", "kda_bwd", "gdn_fwd", "gdn_bwd", "kda_ckpt", "gdn_ckpt", "kda_ckpt_noalloc",
+    "GDR_NOALLOC_SCRATCH_BYTES", "status_string",
     "check_device", "walk_layout_chosen", "timing_enable", "timing_read", "EXPORTED_SYMBOLS",
 ]
 
@@ -33,7 +34,9 @@ EXPORTED_SYMBOLS = (
     "gdr_plan_chunks", "gdr_workspace_bytes", "gdr_kda_fwd", "gdr_kda_bwd", "gdr_gdn_fwd",
     "gdr_gdn_bwd", "gdr_kda_ckpt", "gdr_gdn_ckpt", "gdr_check_device", "gdr_status_string",
     "gdr_last_error", "gdr_timing_enable", "gdr_timing_read", "gdr_walk_layout_chosen",
+    "gdr_kda_ckpt_noalloc",
 )
+GDR_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static workspace of gdr_kda_ckpt_noalloc
 
 
 class GdrError(RuntimeError):
@@ -87,6 +90,8 @@ def lib():
                 fn = getattr(L, name)
                 fn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
                 fn.restype = i32
+            L.gdr_kda_ckpt_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            L.gdr_kda_ckpt_noalloc.restype = i32
             L.gdr_timing_enable.argtypes = [i32]
             L.gdr_timing_enable.restype = i32
             L.gdr_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -276,3 +281,9 @@ def kda_ckpt(prob, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace, stre
 
 def gdn_ckpt(prob, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace, stream=None):
     _ckpt("gdr_gdn_ckpt", prob, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace, stream)
+
+
+def kda_ckpt_noalloc(prob, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, stream=None):
+    """gdr_kda_ckpt on the library's static per-device workspace (no workspace argument)."""
+    _check(lib().gdr_kda_ckpt_noalloc(prob.cstruct, _ptr(o), _ptr(ht), _ptr(dout), _ptr(dht), _ptr(dq), _ptr(dk),
+                                      _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _stream(stream)))

@@ -14,6 +14,12 @@
 
 #include "gdr_kernels.h"
 
+// Workspace of gdr_kda_ckpt_noalloc: one copy per device, held from the
+// library's load on that device until the process ends.  Host code never uses
+// this name as an address; it uses the pointer hipGetSymbolAddress returns for
+// the current device (scratch_of_device below).
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+
 namespace gdr {
 hipError_t set_dynamic_lds_once(const void *kernel, int bytes) {
   struct Entry {
@@ -346,6 +352,42 @@ int32_t ckpt_impl(int32_t variant, const gdr_problem *p, uint16_t *o, float *ht,
   return bwd_impl(variant, p, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
 }
 
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current and kept in a fixed table (no allocation).
+constexpr int kMaxDevices = 64;
+int32_t scratch_of_device(void **out) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GDR_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDR_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GDR_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return GDR_OK;
+}
+
+int32_t ckpt_noalloc_impl(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout, const float *dht,
+                          uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0, void *stream) {
+  int32_t rc = check_problem(GDR_KDA, p);
+  if (rc) return rc;
+  const Layout L = make_layout((int64_t)p->n_chunks * p->H_v, p->N, p->H_v);
+  if (L.full_bytes > GDR_NOALLOC_SCRATCH_BYTES)
+    return fail(GDR_ERR_WORKSPACE, "problem needs " + std::to_string(L.full_bytes) +
+                                       " bytes of workspace; the static scratch holds " +
+                                       std::to_string((int64_t)GDR_NOALLOC_SCRATCH_BYTES));
+  if ((rc = check_device_impl())) return rc;
+  void *ws = nullptr;
+  if ((rc = scratch_of_device(&ws))) return rc;
+  return ckpt_impl(GDR_KDA, p, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, GDR_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,6 +468,12 @@ int32_t gdr_gdn_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_
                      uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0, void *ws,
                      int64_t ws_bytes, void *stream) {
   return ckpt_impl(GDR_GDN, p, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws, ws_bytes, stream);
+}
+
+int32_t gdr_kda_ckpt_noalloc(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout, const float *dht,
+                             uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0,
+                             void *stream) {
+  return ckpt_noalloc_impl(p, o, ht, dout, dht, dq, dk, dv, dg, dbeta, dh0, stream);
 }
 
 int32_t gdr_walk_layout_chosen(int32_t variant, const gdr_problem *p, int32_t compute_units, int32_t *layout) {

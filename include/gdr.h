@@ -202,6 +202,28 @@ int32_t gdr_gdn_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_
                      void *dbeta, float *dh0, void *workspace, int64_t workspace_bytes,
                      void *stream);
 
+/* gdr_kda_ckpt without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a static device array inside the
+ * library of GDR_NOALLOC_SCRATCH_BYTES bytes: every device the library runs
+ * on holds its own copy from the library's load until the process ends.  The
+ * call allocates nothing (no hipMalloc, no hipFree) and, like every call here,
+ * does not synchronise.  Its address is looked up once per device, on the
+ * first call with that device current.
+ *   - Problems whose gdr_workspace_bytes(GDR_KDA, ..., GDR_FWD_SAVE) exceeds
+ *     GDR_NOALLOC_SCRATCH_BYTES are rejected with GDR_ERR_WORKSPACE before
+ *     anything is enqueued (64 MiB holds about 320 chunk-heads: e.g. 20 K
+ *     tokens at one head or 5 K tokens at four).
+ *   - Every call on one device uses that device's one array, which keeps the
+ *     last call's contents (nothing in it has to start at zero).  Calls that
+ *     overlap on one device (other streams, other host threads) race and give
+ *     undefined results; calls ordered on one stream are safe.
+ * Other arguments, outputs and errors as gdr_kda_ckpt. */
+#define GDR_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int32_t gdr_kda_ckpt_noalloc(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout,
+                             const float *dht, uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg,
+                             void *dbeta, float *dh0, void *stream);
+
 /* Kernel timing (diagnostics).  gdr_timing_enable(1) makes every later call
  * bracket each of its kernel launches with a pair of hipEvents recorded on the
  * call's stream (the events are created on first use and reused; this is the
