@@ -37,9 +37,36 @@ FLOOR_BYTES_PER_TOKEN_HEAD = {"kda": 5382.0, "gdn": 2840.0}
 FLUSH_BYTES = 512 << 20  # written before every timed call: larger than L2 (8 x 4 MB) and MALL (256 MB)
 
 
+def method_bytes(name, T, Hqk, Hv, NC, N, gdn, save=True):
+    """Algorithmic bytes of one launch: the bytes of the method's own inputs and
+    outputs (no workspace intermediates) that this kernel must read or write,
+    at the per-token-head figures of the path floor (q, k 256 B each per Q/K
+    token-head, v, dout, o, dv 256 B, g 512 B (KDA) or 4 B (GDN), beta 2 B
+    (KDA) or 4 B (GDN), one bf16 128 x 128 state tape per chunk-head, fp32
+    final states).  The gradient kernel alone reads every backward input (q, k,
+    v, g, beta, dout, the state tape) and writes every gradient: 3332 B per KDA
+    token-head, 1637.3 B per GDN value token-head."""
+    qk = 2 * T * Hqk * 256
+    v = T * Hv * 256
+    g = T * Hv * (4 if gdn else 512)
+    beta = T * Hv * (4 if gdn else 2)
+    tape = NC * Hv * 32768
+    states = N * Hv * 65536
+    if name == "fwd_prep":
+        return qk + v + g + beta
+    if name == "fwd_walk":
+        return v + states + (tape if save else 0)  # o, ht (+ the tape)
+    if name == "bwd_walk":
+        return v  # dout
+    if name == "bwd_grad":
+        return (qk + v + g + beta + v + tape) + (qk + v + g + beta)
+    raise KeyError(name)
+
+
 def kernel_bytes(name, T, Hqk, Hv, NC, N, gdn, save=True):
-    """Algorithmic bytes of one launch: every input and output byte of the
-    kernel's design counted once (q and k once per Q/K head)."""
+    """Design bytes of one launch: every input and output byte of the kernel as
+    built, workspace fragments and tapes included, counted once (q and k once
+    per Q/K head).  Reported beside the algorithmic bytes, never as them."""
     units = NC * Hv
     qk = 2 * T * Hqk * 256
     v = T * Hv * 256
@@ -406,11 +433,13 @@ def main():
         if n == 0:
             continue
         avg = ms / n
-        b = kernel_bytes(name, T, Hqk, Hv, NC, N, gdn)
+        b = method_bytes(name, T, Hqk, Hv, NC, N, gdn)
+        db = kernel_bytes(name, T, Hqk, Hv, NC, N, gdn)
         fl = kernel_flops(name, NC, Hv)
         total_flops += fl * n / args.steps
         kernels[name] = {"avg_ms": avg, "launches": n, "bytes": b, "GB_s": b / avg / 1e6,
-                         "hbm_frac": b / avg / 1e6 / HBM_PEAK_GBS, "mfma_TFLOPs": fl / avg / 1e9,
+                         "hbm_frac": b / avg / 1e6 / HBM_PEAK_GBS, "design_bytes": db,
+                         "design_GB_s": db / avg / 1e6, "mfma_TFLOPs": fl / avg / 1e9,
                          "mfma_frac": fl / avg / 1e9 / MFMA_BF16_PEAK_TFLOPS}
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
     # dependent steps of the walks: chunks of the longest document (unsegmented
@@ -444,7 +473,11 @@ def main():
                    "step": "forward with tapes + backward (prep, walk, adjoint walk, gradients)"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk_["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dk_["GB_s"] / HBM_PEAK_GBS, "traffic": traffic,
-                     "bytes_per_launch": dk_["bytes"], "avg_launch_ms": dk_["avg_ms"]},
+                     "bytes_per_launch": dk_["bytes"], "avg_launch_ms": dk_["avg_ms"],
+                     "traffic_over_algorithmic": traffic / dk_["bytes"] if traffic else None,
+                     "design_bytes_per_launch": dk_["design_bytes"], "design_GB_s": dk_["design_GB_s"],
+                     "note": "achieved = the method's bytes for this kernel (bytes_per_launch) / avg_launch_ms; "
+                             "design bytes add the workspace fragments and tapes the kernels pass each other"},
         "ms": {k: v["ms"] for k, v in ops.items()},
         "cells": ops,
         "path_floor": {"ms": floor_ms, "frac": floor_ms / ms_per_step,

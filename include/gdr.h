@@ -74,9 +74,10 @@ enum gdr_variant { GDR_KDA = 0, GDR_GDN = 1 };
 #define GDR_FWD_SAVE 1u
 /* Forward without the output: o is neither computed nor written (it may be
  * NULL) and prep skips the output's operands.  With GDR_FWD_SAVE this is the
- * recompute of a checkpointed step (PR #8218 section "ckpt": the backward
- * reuses the recompute's tapes, the output is already known).  ht is still
- * written when non-NULL. */
+ * recompute of a checkpointed step whose tapes the backward then reads, the
+ * output being already known (PR #8638 description: the checkpoint recompute
+ * hands its tapes to the backward instead of the backward re-running prep and
+ * the state walk).  ht is still written when non-NULL. */
 #define GDR_FWD_SKIP_OUTPUT 2u
 
 /* One packed problem.  Lifetime: read during the call that receives it. */
@@ -136,7 +137,11 @@ typedef struct gdr_problem {
 /* Chunk planner (host only).  Splits every document of cu_seqlens into
  * 64-token chunks (the last one of a document may be shorter; chunks never
  * straddle documents) and orders the documents for the state walks, longest
- * first.  Table layout (int32), NC = n_chunks:
+ * first.  The pages' kernels walk such a table of chunks and chunk lengths
+ * (PR #7723 description: the adjoint walk keeps its chunk table in a
+ * shared-memory ring; its sequence diagram publishes the chunk lengths) over
+ * one packed batch given by cu_seqlens (PR #8218, workload paragraph).  Table
+ * layout (int32), NC = n_chunks:
  *     [0, NC)             first token of each chunk
  *     [NC, 2NC)           tokens in each chunk (1..64)
  *     [2NC, 3NC)          document of each chunk
@@ -149,7 +154,10 @@ typedef struct gdr_problem {
 int32_t gdr_plan_chunks(const int32_t *cu_seqlens_host, int32_t N, int32_t *table_host,
                         int64_t capacity, int32_t *n_chunks_out, int64_t *table_len_out);
 
-/* Workspace bytes for a problem (host only).  flags = 0: forward without
+/* Workspace bytes for a problem (host only), the counterpart of the pages'
+ * workspace helpers that size the caller-held arena (PR #8218 description:
+ * every facade entry, the workspace helpers included; PR #8638 description of
+ * the change: workspace accounting).  flags = 0: forward without
  * tapes; flags = GDR_FWD_SAVE: forward with tapes followed by a backward (the
  * size every backward needs).  When the walks' chains (documents x value
  * heads, 8 wavefronts each) number fewer than 512 wavefronts and some document
@@ -187,10 +195,11 @@ int32_t gdr_gdn_bwd(const gdr_problem *p, const uint16_t *dout, const float *dht
                     uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0,
                     void *workspace, int64_t workspace_bytes, void *stream);
 
-/* The checkpointed training step as one call (PR #8218 "ckpt": forward,
- * recompute and backward): forward without tapes (writes o, ht), the
+/* The checkpointed training step as one call (PR #8218 ops paragraph, "ckpt":
+ * forward, recompute and backward): forward without tapes (writes o, ht), the
  * recompute with GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT (tapes only), then the
- * backward on the recompute's tapes.  Arguments as in the fwd and
+ * backward on the recompute's tapes (PR #8638 description: the recompute hands
+ * its tapes to the backward, outputs and gradients bitwise unchanged).  Arguments as in the fwd and
  * bwd calls of the variant; the workspace must hold gdr_workspace_bytes(...,
  * GDR_FWD_SAVE). */
 int32_t gdr_kda_ckpt(const gdr_problem *p, uint16_t *o, float *ht, const uint16_t *dout,

@@ -35,6 +35,24 @@ def test_kernel_bytes_per_unit():
         bench.kernel_bytes("nope", T, H, H, NC, N, gdn=False)
 
 
+def test_method_bytes_match_the_path_floor():
+    """The gradient kernel's algorithmic bytes are the backward's figure of the
+    path floor (3332 B per KDA token-head, 1637.3 B per GDN value token-head)
+    with exactly full chunks; the four kernels' method bytes add up to the
+    fwd + bwd floor plus the dout read twice (adjoint walk and gradients) and
+    the final states."""
+    for gdn, H_qk, H_v, per_th in ((False, 16, 16, 3332.0), (True, 16, 48, 1637.0 + 1 / 3)):
+        T, N = 64 * 1000, 4
+        NC = T // 64
+        b = bench.method_bytes("bwd_grad", T, H_qk, H_v, NC, N, gdn)
+        assert abs(b / (T * H_v) - per_th) < 1e-9
+        total = sum(bench.method_bytes(k, T, H_qk, H_v, NC, N, gdn)
+                    for k in ("fwd_prep", "fwd_walk", "bwd_walk", "bwd_grad"))
+        floor = bench.FLOOR_BYTES_PER_TOKEN_HEAD["gdn" if gdn else "kda"]
+        extra = T * H_v * 256 + N * H_v * 65536
+        assert abs((total - extra) / (T * H_v) - floor) < 0.5
+
+
 def test_traffic_summary_matches_workload_only():
     """A committed HBM-traffic summary is reported only for the workload it names."""
     t = bench.traffic_from_profiles("bwd_grad", "kda_pack4_T261392_H16")
