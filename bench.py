@@ -109,6 +109,8 @@ def parse_args():
                     help="gdr_problem.walk_segments: 0 = automatic, n = at most n segments per document walk")
     ap.add_argument("--walk-layout", type=int, default=0,
                     help="walk launch layout: 0 automatic, 1 slice wavefronts, 2 ring workgroups")
+    ap.add_argument("--walk-plan", type=int, default=0,
+                    help="segment plan of segmented walks: 0 balanced by document length, 1 equal")
     ap.add_argument("--input-flags", type=int, default=0,
                     help="gdr_problem.input_flags: 1 = in-kernel q/k L2 norm, 2 = beta sigmoid (logits as input)")
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="tokens per document in the CPU sample")
@@ -366,7 +368,7 @@ def main():
     inp = workloads.make_inputs(w, device=dev)
     prob = gdr.Problem(gdr.GDR_GDN if gdn else gdr.GDR_KDA, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                        inp["cu_seqlens"], inp["h0"], input_flags=args.input_flags, walk_segments=args.walk_segments,
-                       walk_layout=args.walk_layout)
+                       walk_layout=args.walk_layout, walk_plan=args.walk_plan)
     ws = prob.alloc_workspace(gdr.GDR_FWD_SAVE)
     T, Hqk, Hv, N, NC = prob.T, prob.H_qk, prob.H_v, prob.N, prob.n_chunks
     bf, f32 = torch.bfloat16, torch.float32
@@ -468,6 +470,7 @@ def main():
         "config": {"workload": w.name, "variant": w.variant, "T": T, "docs": list(w.docs), "H_qk": Hqk,
                    "H_v": Hv, "K": 128, "V": 128, "n_chunks": NC, "input_flags": args.input_flags,
                    "walk_segments": args.walk_segments, "walk_layout": args.walk_layout,
+                   "walk_plan": "equal" if args.walk_plan else "balanced",
                    "walk_layout_run": "rings" if gdr.walk_layout_chosen(gdr.GDR_GDN if gdn else gdr.GDR_KDA, prob)
                    == gdr.GDR_WALK_RINGS else "slices",
                    "step": "forward with tapes + backward (prep, walk, adjoint walk, gradients)"},

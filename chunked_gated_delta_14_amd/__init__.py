@@ -16,7 +16,7 @@ import numpy as np
 from . import _build
 
 __all__ = [
-    "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GDR_IN_QK_L2NORM", "GDR_IN_BETA_SIGMOID", "GDR_WALK_AUTO", "GDR_WALK_SLICES", "GDR_WALK_RINGS", "GdrError", "lib", "plan_chunks", "max_doc_chunks", "workspace_bytes",
+    "GDR_KDA", "GDR_GDN", "GDR_FWD_SAVE", "GDR_FWD_SKIP_OUTPUT", "GDR_IN_QK_L2NORM", "GDR_IN_BETA_SIGMOID", "GDR_WALK_AUTO", "GDR_WALK_SLICES", "GDR_WALK_RINGS", "GDR_PLAN_BALANCED", "GDR_PLAN_EQUAL", "GdrError", "lib", "plan_chunks", "max_doc_chunks", "workspace_bytes",
     "Problem", "kda_fwd", "kda_bwd", "gdn_fwd", "gdn_bwd", "kda_ckpt", "gdn_ckpt", "kda_ckpt_noalloc",
     "GDR_NOALLOC_SCRATCH_BYTES", "status_string",
     "check_device", "walk_layout_chosen", "timing_enable", "timing_read", "EXPORTED_SYMBOLS",
@@ -29,6 +29,7 @@ GDR_FWD_SKIP_OUTPUT = 2  # forward without the output (o may be None): the recom
 GDR_IN_QK_L2NORM = 1     # Problem input flag: q, k rows scaled to unit L2 norm inside the kernels
 GDR_IN_BETA_SIGMOID = 2  # Problem input flag: beta holds logits, sigmoid applied inside the kernels
 GDR_WALK_AUTO, GDR_WALK_SLICES, GDR_WALK_RINGS = 0, 1, 2  # Problem walk_layout
+GDR_PLAN_BALANCED, GDR_PLAN_EQUAL = 0, 1  # Problem walk_plan: segments shared by length, or equally
 
 EXPORTED_SYMBOLS = (
     "gdr_plan_chunks", "gdr_workspace_bytes", "gdr_kda_fwd", "gdr_kda_bwd", "gdr_gdn_fwd",
@@ -53,7 +54,7 @@ class _CProblem(ctypes.Structure):
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("chunk_table", ctypes.c_void_p), ("n_chunks", ctypes.c_int32), ("h0", ctypes.c_void_p),
         ("scale", ctypes.c_float), ("input_flags", ctypes.c_uint32), ("walk_segments", ctypes.c_int32),
-        ("max_doc_chunks", ctypes.c_int32), ("walk_layout", ctypes.c_int32),
+        ("max_doc_chunks", ctypes.c_int32), ("walk_layout", ctypes.c_int32), ("walk_plan", ctypes.c_int32),
     ]
 
 
@@ -199,10 +200,11 @@ class Problem:
     input_flags: GDR_IN_QK_L2NORM and/or GDR_IN_BETA_SIGMOID (activations applied in the kernels).
     walk_segments: 0 = automatic segmentation of the state walks, n >= 1 = at most n segments.
     walk_layout: GDR_WALK_AUTO, GDR_WALK_SLICES or GDR_WALK_RINGS (launch layout of the walks).
+    walk_plan: GDR_PLAN_BALANCED or GDR_PLAN_EQUAL (segments of segmented walks per document).
     """
 
     def __init__(self, variant, q, k, v, g, beta, cu_seqlens, h0=None, scale=None, input_flags=0, walk_segments=0,
-                 walk_layout=GDR_WALK_AUTO):
+                 walk_layout=GDR_WALK_AUTO, walk_plan=GDR_PLAN_BALANCED):
         import torch
 
         self.variant = variant
@@ -224,7 +226,8 @@ class Problem:
                             q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                             self.cu.data_ptr(), self.table.data_ptr(), nc,
                             h0.data_ptr() if h0 is not None else None, self.scale, int(input_flags),
-                            int(walk_segments), max_doc_chunks(table, self.N, nc), int(walk_layout))
+                            int(walk_segments), max_doc_chunks(table, self.N, nc), int(walk_layout),
+                            int(walk_plan))
         self.input_flags = int(input_flags)
 
     def workspace_bytes(self, flags=GDR_FWD_SAVE) -> int:

@@ -66,11 +66,18 @@ constexpr int64_t kRows = kChunk * kHD * 2;
 
 // Walk segments per document: more than one only when the chains (documents x
 // value heads, 8 wavefronts each) would leave the compute units underfilled and
-// some document spans two chunks.
+// some document spans two chunks.  This is the equal plan's count and the
+// balanced plan's average (its budget is N times it).
 int walk_segments(int64_t N, int64_t Hv, int64_t NC) {
   const int64_t waves = 8 * N * Hv;
   if (waves == 0 || waves >= 512 || NC <= N) return 1;
   return (int)std::min<int64_t>(4, std::max<int64_t>(1, 512 / waves));
+}
+// Most segments one document can get: the balanced plan may give a long document
+// up to twice the average (at most 8).
+int walk_segment_cap(int64_t N, int64_t Hv, int64_t NC) {
+  const int P = walk_segments(N, Hv, NC);
+  return P > 1 && N > 1 ? std::min(8, 2 * P) : P;
 }
 
 struct Layout {
@@ -92,7 +99,7 @@ Layout make_layout(int64_t units, int64_t N, int64_t Hv) {
     return at;
   };
   L.carry = off;
-  off += round_up((int64_t)(walk_segments(N, Hv, units / Hv) - 1) * N * Hv * 2 * kHD * kHD * 4);
+  off += round_up((int64_t)(walk_segment_cap(N, Hv, units / Hv) - 1) * N * Hv * 2 * kHD * kHD * 4);
   L.WfN = take(kFrag64x128);
   L.Pf = take(kFrag64x128);
   L.KbT = take(kFrag64x128);
@@ -197,6 +204,8 @@ int32_t check_problem(int32_t variant, const gdr_problem *p) {
     return fail(GDR_ERR_INVALID_ARG, "max_doc_chunks outside [0, n_chunks]");
   if (p->walk_layout != GDR_WALK_AUTO && p->walk_layout != GDR_WALK_SLICES && p->walk_layout != GDR_WALK_RINGS)
     return fail(GDR_ERR_INVALID_ARG, "unknown walk_layout");
+  if (p->walk_plan != GDR_PLAN_BALANCED && p->walk_plan != GDR_PLAN_EQUAL)
+    return fail(GDR_ERR_INVALID_ARG, "unknown walk_plan");
   return GDR_OK;
 }
 
@@ -228,8 +237,16 @@ gdr::Problem to_internal(const gdr_problem *p) {
   q.h0 = p->h0;
   q.scale = p->scale;
   q.inflags = (int)p->input_flags;
-  q.P = walk_segments(p->N, p->H_v, p->n_chunks);
-  if (p->walk_segments > 0 && p->walk_segments < q.P) q.P = p->walk_segments;
+  int P = walk_segments(p->N, p->H_v, p->n_chunks);  // the equal plan's count per document
+  if (p->walk_segments > 0 && p->walk_segments < P) P = p->walk_segments;
+  if (p->walk_plan == GDR_PLAN_BALANCED && P > 1 && p->N > 1) {
+    // per-document cap: twice the average, within the carry slots the workspace holds
+    q.P = std::min(2 * P, walk_segment_cap(p->N, p->H_v, p->n_chunks));
+    q.B = P * p->N;  // as many segments in all as the equal plan
+  } else {
+    q.P = P;
+    q.B = 0;
+  }
   q.L = p->max_doc_chunks > 0 ? p->max_doc_chunks : p->n_chunks;
   q.layout = p->walk_layout;
   return q;

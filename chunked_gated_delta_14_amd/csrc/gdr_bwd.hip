@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
   walk_block(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, chain, sl);
   const ChunkTable tb(p.table, p.NC, p.N);
   WalkChain wc;
-  if (!walk_chain(p, tb, chain, MODE == MODE_WALK ? p.P : p.P - 1, MODE != MODE_WALK, wc, MODE == MODE_WALK ? 0 : 1))
+  if (!walk_chain(p, tb, chain, MODE != MODE_WALK, wc, MODE == MODE_WALK ? 0 : 1))
     return;
   const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
   const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
   int chain, half;
   walk_block<NW>(blockIdx.x, chain, half);  // the 8 / NW workgroups of a chain on one XCD
   WalkChain wc;
-  if (!walk_chain(p, tb, chain, p.P, false, wc)) return;  // uniform over the workgroup
+  if (!walk_chain(p, tb, chain, false, wc)) return;  // uniform over the workgroup
   const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
   const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1535,19 +1535,19 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
 
 hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout, const float *dht, float *dh0,
                            hipStream_t st) {
-  const int chains = p.N * p.Hv;
-  if (chains == 0) return hipSuccess;
+  if (p.N * p.Hv == 0) return hipSuccess;
+  const int chains = walk_chains(p, false);
   if (p.P > 1) {  // pass 1: the segments' carries
-    const int g1 = ((chains * (p.P - 1) + 7) / 8) * 64;
+    const int g1 = ((walk_chains(p, true) + 7) / 8) * 64;
     bwd_walk_kernel<MODE_CARRY><<<2 * g1, 64, 0, st>>>(p, w, dout, nullptr, nullptr);
   }
   if (walk_uses_rings(p, compute_units())) {
     hipError_t e = set_dynamic_lds_once((const void *)bwd_walk_wg_kernel<WGB_NW>, WGB_SMEM);
     if (e != hipSuccess) return e;
-    bwd_walk_wg_kernel<WGB_NW><<<((chains * p.P + 7) / 8) * 64 / WGB_NW, 64 * WGB_NW, WGB_SMEM, st>>>(p, w, dout, dht, dh0);
+    bwd_walk_wg_kernel<WGB_NW><<<((chains + 7) / 8) * 64 / WGB_NW, 64 * WGB_NW, WGB_SMEM, st>>>(p, w, dout, dht, dh0);
     return hipGetLastError();
   }
-  bwd_walk_kernel<MODE_WALK><<<((chains * p.P + 7) / 8) * 64, 64, 0, st>>>(p, w, dout, dht, dh0);
+  bwd_walk_kernel<MODE_WALK><<<((chains + 7) / 8) * 64, 64, 0, st>>>(p, w, dout, dht, dh0);
   return hipGetLastError();
 }
 

@@ -559,7 +559,7 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
   walk_block<NS>(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, chain, grp);
   const ChunkTable tb(p.table, p.NC, p.N);
   WalkChain wc;
-  if (!walk_chain(p, tb, chain, MODE == MODE_WALK ? p.P : p.P - 1, MODE != MODE_WALK, wc)) return;
+  if (!walk_chain(p, tb, chain, MODE != MODE_WALK, wc)) return;
   const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
   const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
@@ -761,7 +761,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
   int chain, half;
   walk_block<NW>(blockIdx.x, chain, half);  // the 8 / NW workgroups of a chain on one XCD
   WalkChain wc;
-  if (!walk_chain(p, tb, chain, p.P, false, wc)) return;  // uniform over the workgroup
+  if (!walk_chain(p, tb, chain, false, wc)) return;  // uniform over the workgroup
   const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
   const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -950,12 +950,12 @@ hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool 
 
 hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, u16 *o, float *ht, bool save, bool out,
                            hipStream_t st) {
-  const int chains = p.N * p.Hv;
-  if (chains == 0) return hipSuccess;
+  if (p.N * p.Hv == 0) return hipSuccess;
   constexpr int NS = WALK_NS;
   static_assert(NS == 1, "segmented walks form entering states per 16-column slice");
+  const int chains = walk_chains(p, false);
   if (p.P > 1) {  // pass 1: the segments' carries
-    const int g1 = walk_grid(chains * (p.P - 1), 1);
+    const int g1 = walk_grid(walk_chains(p, true), 1);
     fwd_walk_kernel<1, false, false, MODE_CARRY><<<2 * g1, 64, 0, st>>>(p, w, nullptr, nullptr);
   }
   if (walk_uses_rings(p, compute_units())) {  // slice wavefronts of a chain in workgroups of WG_NW
@@ -964,14 +964,14 @@ hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, u16 *o, float *
                           : (out ? (const void *)fwd_walk_wg_kernel<false, true, NW> : (const void *)fwd_walk_wg_kernel<false, false, NW>);
     hipError_t e = set_dynamic_lds_once(fn, WG_SMEM);
     if (e != hipSuccess) return e;
-    const int g = walk_grid(chains * p.P, NW);
+    const int g = walk_grid(chains, NW);
     if (save && out) fwd_walk_wg_kernel<true, true, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
     else if (save) fwd_walk_wg_kernel<true, false, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
     else if (out) fwd_walk_wg_kernel<false, true, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
     else fwd_walk_wg_kernel<false, false, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
     return hipGetLastError();
   }
-  const int grid = walk_grid(chains * p.P, NS);
+  const int grid = walk_grid(chains, NS);
   if (save && out) fwd_walk_kernel<NS, true, true><<<grid, 64, 0, st>>>(p, w, o, ht);
   else if (save) fwd_walk_kernel<NS, true, false><<<grid, 64, 0, st>>>(p, w, o, ht);
   else if (out) fwd_walk_kernel<NS, false, true><<<grid, 64, 0, st>>>(p, w, o, ht);

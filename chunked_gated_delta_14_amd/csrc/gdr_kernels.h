@@ -46,7 +46,8 @@ struct Problem {
   const float *h0;
   float scale;
   int inflags;  // bit 0: q, k rows to unit L2 norm; bit 1: beta = sigmoid(beta)
-  int P;        // walk segments per document (1: one chain per document and head)
+  int P;        // walk segments per document at most (1: one chain per document and head)
+  int B;        // balanced segment plan: segments over all documents at most (0: equal plan, P each)
   int L;        // chunks of the longest document (an upper bound; only steers the walk layout)
   int layout;   // walk layout: 0 automatic, 1 slice wavefronts, 2 workgroup rings
 };
@@ -66,6 +67,13 @@ inline bool walk_uses_rings(const Problem &p, int cus) {
   const double slices = std::max(chain * 3.7, 8.0 * units / cus * 3.5);
   const double rings = std::max(chain * 6.5, 2.0 * units / cus * 8.5);
   return rings < slices;
+}
+// Chains of a walk launch, (document, segment, value head) triples: at most B
+// segments in all (equal plan: P per document), pass 1 without each document's
+// last.  Launches size their grids by this bound; triples past the plan's count exit.
+inline int walk_chains(const Problem &p, bool pass1) {
+  const int segs = p.B > 0 ? p.B : p.P * p.N;
+  return (pass1 ? segs - p.N : segs) * p.Hv;
 }
 constexpr int IN_QK_L2NORM = 1, IN_BETA_SIGMOID = 2;
 constexpr float L2NORM_EPS = 1e-6f;

@@ -6,8 +6,14 @@
 
 namespace gdr {
 
-// Segmented walks.  With P > 1 segments per document (P_d = min(P, chunks of
-// the document), at least 1, equal shares of its chunks), the walk over a segment is an
+// Segmented walks.  Document d of n_d chunks is cut into P_d segments of equal
+// shares of its chunks (at least one segment, at most min(P, n_d)):
+//  - equal plan (B = 0): P_d = min(P, n_d);
+//  - balanced plan (B > 0): P_d = ceil(n_d / L) with L the smallest segment
+//    length for which the segments of all documents number at most B, so the
+//    longest segment (the walks' critical path) is as short as the budget of
+//    segments allows: longer documents get more segments.
+// The walk over a segment is an
 // affine map of the state entering it: S_end = Phi S_start + Psi.  Pass 1
 // (MODE_CARRY) walks every segment but the last twice, in one launch: the first
 // half of the grid from a zero state (its end state is Psi), the second half
@@ -18,31 +24,76 @@ namespace gdr {
 // writes the outputs and tapes.
 constexpr int MODE_WALK = 0, MODE_CARRY = 1;
 
-// Chain c of a walk launch over Q segments per document: the document (walk
-// order), segment and value head, and the segment's chunk range; false if the
-// document has fewer segments.
+// Target segment length of the balanced plan: the smallest L >= 1 with
+// sum_d min(P, max(1, ceil(n_d / L))) <= B, by bisection over [1, longest
+// document] (at the upper end every document has one segment and N <= B).
+// Every wavefront of a walk computes the same value from the chunk table.
+__device__ __forceinline__ int plan_segment_len(const Problem &p, const ChunkTable &tb) {
+  int lo = 1, hi = tb.doc_ptr[tb.order[0] + 1] - tb.doc_ptr[tb.order[0]];
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    int total = 0;
+    for (int d = 0; d < p.N; ++d) {
+      const int n = tb.doc_ptr[d + 1] - tb.doc_ptr[d];
+      total += min(p.P, max(1, (n + mid - 1) / mid));
+    }
+    if (total <= p.B) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Segments of a document of n chunks under the problem's plan (L: the balanced
+// plan's target length, unused by the equal plan).
+__device__ __forceinline__ int doc_segments(const Problem &p, int n, int L) {
+  if (n <= 0) return 1;  // an empty document keeps one (empty) segment: ht = h0, dh0 = dht
+  const int cap = n < p.P ? n : p.P;
+  if (p.B == 0) return cap;
+  const int want = (n + L - 1) / L;
+  return want < cap ? want : cap;
+}
+
+// Chain c of a walk launch: the c-th (document, segment, value head) triple,
+// documents in walk order, then segments, then heads, counting only the
+// segments each document has under the plan (pass1: every segment but its last),
+// so the grid holds no idle chains.  Returns the document, segment and value
+// head and the segment's chunk range; false past the last triple.
 struct WalkChain {
   int d, s, j, Pd, first, nch, first_doc;
 };
-// pass1: only the segments with a carry to pass on (all but one per document);
-// shift 1 numbers them from 1 (the adjoint walk's carries flow toward the start).
-__device__ __forceinline__ bool walk_chain(const Problem &p, const ChunkTable &tb, int c, int Q, bool pass1,
+// shift 1 numbers pass 1's segments from 1 (the adjoint walk's carries flow
+// toward the start).
+__device__ __forceinline__ bool walk_chain(const Problem &p, const ChunkTable &tb, int c, bool pass1,
                                            WalkChain &wc, int shift = 0) {
-  const int per_doc = p.Hv * Q;
-  if (c >= p.N * per_doc) return false;
-  const int rank = c / per_doc, rem = c % per_doc;
-  wc.s = rem / p.Hv;
-  wc.j = rem % p.Hv;
-  wc.d = tb.order[rank];
-  wc.first_doc = tb.doc_ptr[wc.d];
-  const int n = tb.doc_ptr[wc.d + 1] - wc.first_doc;
-  wc.Pd = n < p.P ? (n > 0 ? n : 1) : p.P;  // an empty document keeps one (empty) segment: ht = h0, dh0 = dht
-  if (wc.s >= (pass1 ? wc.Pd - 1 : wc.Pd)) return false;
-  wc.s += shift;
-  const int a = (wc.s * n) / wc.Pd, b = ((wc.s + 1) * n) / wc.Pd;
-  wc.first = wc.first_doc + a;
-  wc.nch = b - a;
-  return true;
+  if (c >= p.N * p.Hv * p.P) return false;
+  int seg = c / p.Hv;
+  wc.j = c % p.Hv;
+  if (p.P == 1) {  // one segment per document (segmenting engages only with N H_v <= 32)
+    if (pass1) return false;
+    wc.d = tb.order[seg];
+    wc.first_doc = wc.first = tb.doc_ptr[wc.d];
+    wc.nch = tb.doc_ptr[wc.d + 1] - wc.first_doc;
+    wc.Pd = 1;
+    wc.s = 0;
+    return true;
+  }
+  const int L = p.B > 0 ? plan_segment_len(p, tb) : 1;
+  for (int r = 0; r < p.N; ++r) {
+    const int d = tb.order[r], first_doc = tb.doc_ptr[d], n = tb.doc_ptr[d + 1] - first_doc;
+    const int Pd = doc_segments(p, n, L), cnt = pass1 ? Pd - 1 : Pd;
+    if (seg < cnt) {
+      wc.d = d;
+      wc.first_doc = first_doc;
+      wc.Pd = Pd;
+      wc.s = seg + shift;
+      const int a = (wc.s * n) / Pd, b = ((wc.s + 1) * n) / Pd;
+      wc.first = first_doc + a;
+      wc.nch = b - a;
+      return true;
+    }
+    seg -= cnt;
+  }
+  return false;
 }
 
 // Carries of segment boundary b of (document d, value head j): Psi then Phi.

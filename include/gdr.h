@@ -105,7 +105,24 @@ typedef struct gdr_problem {
                                 per-document first-chunk section), or 0 = unknown (taken as n_chunks).
                                 A hint for the walks' launch layout: results never depend on it */
   int32_t walk_layout;       /* GDR_WALK_AUTO, GDR_WALK_SLICES or GDR_WALK_RINGS (below) */
+  int32_t walk_plan;         /* GDR_PLAN_BALANCED (0) or GDR_PLAN_EQUAL: how segmented walks share
+                                their segments among the documents (below) */
 } gdr_problem;
+
+/* Segment plan of segmented walks (gdr_problem.walk_plan).  Segmenting engages
+ * when the walks' chains leave the compute units underfilled (see
+ * gdr_workspace_bytes): with P segments per document on average, the pack gets
+ * P * N segments per value head in all.
+ * GDR_PLAN_EQUAL: every document gets min(P, its chunks) segments.
+ * GDR_PLAN_BALANCED: document d of n_d chunks gets ceil(n_d / L) segments (at
+ *   most 2P, 8 and n_d, at least one), L being the smallest segment length for
+ *   which the pack's segments stay within P * N: the longest segment, which
+ *   sets the walks' critical path, is as short as that budget allows (the
+ *   pages' longest-processing-time segment rule, PR #7723 description, solves
+ *   the same balance per rank).  With one document the two plans agree.
+ * Results differ between plans only by fp32 rounding of the carries. */
+#define GDR_PLAN_BALANCED 0
+#define GDR_PLAN_EQUAL 1
 
 /* Launch layout of the state walks (gdr_problem.walk_layout).  Both run the same
  * products in the same order for every 16-column slice of the state, so they
@@ -164,7 +181,8 @@ int32_t gdr_plan_chunks(const int32_t *cu_seqlens_host, int32_t N, int32_t *tabl
  * spans two chunks (n_chunks > N), each document's walk is split into
  * P = min(4, 512 / (8 N H_v)) segments run in parallel
  * (the segments' affine carries, 2 x 64 KB per segment boundary and value
- * head, are part of the workspace).  Returns the byte count (a multiple of 256), or
+ * head, are part of the workspace, sized for the balanced plan's cap: up to
+ * min(8, 2P) segments per document).  Returns the byte count (a multiple of 256), or
  * minus a gdr_status on invalid or unsupported sizes. */
 int64_t gdr_workspace_bytes(int32_t variant, int32_t T, int32_t N, int32_t n_chunks,
                             int32_t H_qk, int32_t H_v, int32_t K, int32_t V, uint32_t flags);

@@ -20,7 +20,7 @@ def to_dev(inp, device="cuda"):
 
 
 def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, ws_fill=0xFF, workspace=None,
-            on_device=False, input_flags=0, walk_segments=0, walk_layout=0):
+            on_device=False, input_flags=0, walk_segments=0, walk_layout=0, walk_plan=0):
     """Forward (with tapes) and backward on the GPU.  Returns CPU fp32 tensors
     (or the device tensors as computed, with on_device=True).
 
@@ -33,7 +33,8 @@ def run_gdr(variant, inp, *, backward=True, dht=None, ckpt=False, ws_fill=0xFF, 
     d = to_dev(inp)
     code = gdr.GDR_KDA if variant == "kda" else gdr.GDR_GDN
     prob = gdr.Problem(code, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d.get("h0"),
-                       input_flags=input_flags, walk_segments=walk_segments, walk_layout=walk_layout)
+                       input_flags=input_flags, walk_segments=walk_segments, walk_layout=walk_layout,
+                       walk_plan=walk_plan)
     T, Hqk, Hv, N = prob.T, prob.H_qk, prob.H_v, prob.N
     ws = workspace if workspace is not None else prob.alloc_workspace(gdr.GDR_FWD_SAVE)
     if ws_fill is not None:

@@ -78,19 +78,24 @@ SEGMENTED = [
 
 @pytest.mark.parametrize("case", SEGMENTED, ids=lambda c: "%s_%s_h%d_%d" % (c[0], "-".join(map(str, c[1])), c[2], c[3]))
 def test_segmented_walks(case):
-    """Walks split into 2, 3 and 4 segments per document (carry and transfer
-    walks, composed at the segment starts) against the oracle, and against the
-    unsegmented walk: the two differ only by fp32 rounding of the composition,
-    which reaches the bf16 outputs and tapes as rare last-place flips."""
+    """Walks split into 2, 3 and 4 segments per document on average (carry and
+    transfer walks, composed at the segment starts), with the segments shared
+    equally or by document length (the balanced plan gives the longest document
+    up to 8 segments here), against the oracle, and against the unsegmented
+    walk: the two differ only by fp32 rounding of the composition, which reaches
+    the bf16 outputs and tapes as rare last-place flips."""
+    import chunked_gated_delta_14_amd as gdr
+
     variant, docs, hqk, hv = case
     w = workloads.custom(variant, docs, hqk, hv, with_h0=True, seed=sum(docs) + 11 * hv)
     inp = workloads.make_inputs(w, device="cpu", dht=True)
     ref = oracle_all(variant, inp, dht=inp["dht"])
     base = None
-    for P in (1, 2, 3, 4):
-        print("[case]", w.name, "walk_segments", P, flush=True)
-        got = run_gdr(variant, inp, dht=inp["dht"], walk_segments=P)
-        compare(got, ref, label="%s_P%d" % (w.name, P))
+    runs = [(P, gdr.GDR_PLAN_BALANCED) for P in (1, 2, 3, 4)] + [(P, gdr.GDR_PLAN_EQUAL) for P in (2, 4)]
+    for P, plan in runs:
+        print("[case]", w.name, "walk_segments", P, "plan", plan, flush=True)
+        got = run_gdr(variant, inp, dht=inp["dht"], walk_segments=P, walk_plan=plan)
+        compare(got, ref, label="%s_P%d_plan%d" % (w.name, P, plan))
         if base is None:
             base = got
             continue
