@@ -84,13 +84,14 @@ struct Layout {
   int64_t carry;                          // segment carries (segmented walks only)
   int64_t WfN, Pf, KbT, Uacc, Oacc, gam;  // forward walk operands
   int64_t Kb, WTn, QGT, MTs, Tt, Et, S, Vn;  // tapes kept for the backward
+  int64_t qk_rstd;                           // q/k inverse norms (per token and Q/K head)
   int64_t fwd_bytes, full_bytes;
 };
 
 // Region order keeps WfN|Pf, KbT and Uacc adjacent so that the backward's
 // scratch tapes (dS: 32 KB, dVnT: 16 KB per unit) can overlay the
 // forward-walk operands, which are dead once the forward walk has run.
-Layout make_layout(int64_t units, int64_t N, int64_t Hv) {
+Layout make_layout(int64_t units, int64_t N, int64_t Hv, int64_t T, int64_t Hqk) {
   Layout L{};
   int64_t off = 0;
   auto take = [&](int64_t per_unit) {
@@ -115,6 +116,8 @@ Layout make_layout(int64_t units, int64_t N, int64_t Hv) {
   L.Et = take(kFrag64x64);
   L.S = take(kState);
   L.Vn = take(kRows);
+  L.qk_rstd = off;
+  off += round_up(T * Hqk * 2 * 4);
   L.full_bytes = off;
   return L;
 }
@@ -139,6 +142,7 @@ gdr::Workspace bind(const Layout &L, void *base) {
   w.dS = reinterpret_cast<uint16_t *>(b + L.WfN);   // over WfN|Pf
   w.dVnT = reinterpret_cast<uint16_t *>(b + L.Uacc);// over Uacc
   w.carry = reinterpret_cast<float *>(b + L.carry);
+  w.qk_rstd = reinterpret_cast<float *>(b + L.qk_rstd);
   return w;
 }
 
@@ -210,7 +214,7 @@ int32_t check_problem(int32_t variant, const gdr_problem *p) {
 }
 
 int32_t check_workspace(const gdr_problem *p, void *ws, int64_t ws_bytes, bool full, Layout &L) {
-  L = make_layout((int64_t)p->n_chunks * p->H_v, p->N, p->H_v);
+  L = make_layout((int64_t)p->n_chunks * p->H_v, p->N, p->H_v, p->T, p->H_qk);
   const int64_t need = full ? L.full_bytes : L.fwd_bytes;
   if (need > 0 && !ws) return fail(GDR_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(GDR_ERR_WORKSPACE, "workspace is not 256-byte aligned");
@@ -394,7 +398,7 @@ int32_t ckpt_noalloc_impl(const gdr_problem *p, uint16_t *o, float *ht, const ui
                           uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta, float *dh0, void *stream) {
   int32_t rc = check_problem(GDR_KDA, p);
   if (rc) return rc;
-  const Layout L = make_layout((int64_t)p->n_chunks * p->H_v, p->N, p->H_v);
+  const Layout L = make_layout((int64_t)p->n_chunks * p->H_v, p->N, p->H_v, p->T, p->H_qk);
   if (L.full_bytes > GDR_NOALLOC_SCRATCH_BYTES)
     return fail(GDR_ERR_WORKSPACE, "problem needs " + std::to_string(L.full_bytes) +
                                        " bytes of workspace; the static scratch holds " +
@@ -456,7 +460,7 @@ int64_t gdr_workspace_bytes(int32_t variant, int32_t T, int32_t N, int32_t n_chu
   const int32_t rc = check_sizes(variant, T, N, n_chunks, H_qk, H_v, K, V);
   if (rc) return -(int64_t)rc;
   if (flags & ~(GDR_FWD_SAVE | GDR_FWD_SKIP_OUTPUT)) return -(int64_t)fail(GDR_ERR_INVALID_ARG, "unknown flag");
-  const Layout L = make_layout((int64_t)n_chunks * H_v, N, H_v);
+  const Layout L = make_layout((int64_t)n_chunks * H_v, N, H_v, T, H_qk);
   return (flags & GDR_FWD_SAVE) ? L.full_bytes : L.fwd_bytes;
 }
 

@@ -540,60 +540,33 @@ __device__ __forceinline__ void fetch_qk_unit(const Problem &p, int unit, int ti
   fetch_rows(x, (isk ? p.k : p.q) + ((size_t)start * p.Hqk + iqk) * HD, (size_t)p.Hqk * HD, len, tid & 255);
 }
 
-// q and k rows of a chunk into the transposed LDS tiles, as load_rows_transposed
-// (threads 0..255: q, 256..511: k).  With IN_QK_L2NORM every row is first scaled
-// to unit L2 norm, x (sum x^2 + eps)^(-1/2), the 16 partial sums of squares of a
-// row (one per 8-channel group) added in a fixed order through sPart (2 x 64 x 16
-// floats of scratch), and the inverse norms kept in sRstd [2][64] for the
+// The raw q (threads 0..255) or k (256..511) rows of a unit (fetch_qk_unit) into
+// the transposed LDS tiles.  With IN_QK_L2NORM every row is first scaled by the
+// inverse norm prep kept (qk_rstd, rounded to bf16 after the product, as prep
+// forms its operands), and the inverse norms go to sRstd [q, k][64] for the
 // backward through the norm.
 template <int PITCH>
-__device__ __forceinline__ void load_qk_rows(u16 *sQT, u16 *sKT, const Problem &p, int start, int iqk, int len,
-                                             int tid, float *sPart, float *sRstd) {
+__device__ __forceinline__ void store_qk_rows(u16 *sQT, u16 *sKT, const Problem &p, const Workspace &w, int start,
+                                              int iqk, int len, const u32x4 (&xr)[4], int tid, float *sRstd) {
   const int isk = tid >> 8, b = tid & 255;
-  const u16 *src = (isk ? p.k : p.q) + ((size_t)start * p.Hqk + iqk) * HD;
-  const size_t ld = (size_t)p.Hqk * HD;
+  u16 *dst = isk ? sKT : sQT;
   if (!(p.inflags & IN_QK_L2NORM)) {
-    load_rows_transposed<PITCH>(isk ? sKT : sQT, src, ld, len, b);
+    store_rows_transposed<PITCH>(dst, xr, b);
     return;
   }
-  const int r0 = 4 * (b >> 4), c0 = 8 * (b & 15);
-  float x[4][8];
+  const int r0 = 4 * (b & 15), c0 = 8 * (b >> 4);
+  u32x4 y[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 raw = r0 + i < len ? *reinterpret_cast<const uint4 *>(src + (size_t)(r0 + i) * ld + c0)
-                                   : make_uint4(0, 0, 0, 0);
-    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-    float ss = 0.f;
+    const float rs = r0 + i < len ? w.qk_rstd[((size_t)(start + r0 + i) * p.Hqk + iqk) * 2 + isk] : 0.f;
+    if (c0 == 0) sRstd[isk * 64 + r0 + i] = rs;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[i][e] = bf2f((u16)((e & 1) ? (wd[e >> 1] >> 16) : (wd[e >> 1] & 0xffffu)));
-      ss += x[i][e] * x[i][e];
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t wd = xr[i][e];
+      y[i][e] = (uint32_t)f2bf(lo_bf(wd) * rs) | ((uint32_t)f2bf(hi_bf(wd) * rs) << 16);
     }
-    sPart[(isk * 64 + r0 + i) * 16 + (b & 15)] = ss;
   }
-  lds_barrier();
-  u16 *dst = isk ? sKT : sQT;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 *pp = reinterpret_cast<const float4 *>(sPart + (isk * 64 + r0 + i) * 16);
-    float t = 0.f;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 v4 = pp[q4];
-      t += v4.x; t += v4.y; t += v4.z; t += v4.w;
-    }
-    const float rs = rsqrtf(t + L2NORM_EPS);
-    if ((b & 15) == 0) sRstd[isk * 64 + r0 + i] = rs;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[i][e] *= rs;
-  }
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    uint2 pk;
-    pk.x = (uint32_t)f2bf(x[0][cc]) | ((uint32_t)f2bf(x[1][cc]) << 16);
-    pk.y = (uint32_t)f2bf(x[2][cc]) | ((uint32_t)f2bf(x[3][cc]) << 16);
-    *reinterpret_cast<uint2 *>(dst + (c0 + cc) * PITCH + r0) = pk;
-  }
+  store_rows_transposed<PITCH>(dst, y, b);
 }
 
 __device__ __forceinline__ float sigmoidf_(float b) { return 1.f / (1.f + __expf(-b)); }
@@ -609,7 +582,7 @@ __device__ __forceinline__ void load_grad_tape(const u16 *tape, size_t u, int ti
 // qkx arrives holding this unit's raw q/k rows (fetch_qk_unit) and leaves holding
 // those of unit `next` (if next >= 0), fetched once this unit's tape products are
 // done, so that their latency overlaps the rest of the unit.  With the q/k L2 norm
-// the unit loads its rows itself and qkx is unused.
+// the rows are scaled by the inverse norms prep kept as they go to LDS.
 __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace &w, const u16 *dout, u16 *dq,
                                              u16 *dk, u16 *dv, float *dg, void *dbeta, int unit,
                                              u32x4 (&qkx)[4], int next) {
@@ -641,9 +614,7 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
   const GateT<false> G{sG};
 
   float *sNrm = reinterpret_cast<float *>(smem + G_NRM);
-  // (the dout stage is free until the first iteration's loads: scratch of the row norms)
-  if (p.inflags & IN_QK_L2NORM) load_qk_rows<KQTP>(sQT, sKT, p, start, iqk, len, tid0, reinterpret_cast<float *>(smem + G_DO), sNrm);
-  else store_rows_transposed<KQTP>((tid0 >> 8) ? sKT : sQT, qkx, tid0 & 255);
+  store_qk_rows<KQTP>(sQT, sKT, p, w, start, iqk, len, qkx, tid0, sNrm);
 
   f32x4 dqA[4], dkA[4];  // [row block I]: rows 16I + 4lg + jj, column 16w + lr
 #pragma unroll
@@ -830,7 +801,7 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         if (lr == 0) sDB[(8 + wave) * 64 + r0 + jj] = x;  // slots 8..15
       }
     }
-    if (next >= 0 && !(p.inflags & IN_QK_L2NORM)) fetch_qk_unit(p, next, tid, qkx);
+    if (next >= 0) fetch_qk_unit(p, next, tid, qkx);
     colsum = red_lg(colsum);
     // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r): the 10 lower
     // 16x16 tiles, wavefront w takes tiles w and w + 8
@@ -1163,9 +1134,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
   u16 *sVn = reinterpret_cast<u16 *>(sNrm + 128 + 64 * 4);  // Vn tile of the current value head
   const GateT<true> G{sG};
 
-  // (the Y stage is free until the first iteration: scratch of the row norms)
-  if (p.inflags & IN_QK_L2NORM) load_qk_rows<QTP>(sQT, sKT, p, start, iqk, len, tid0, reinterpret_cast<float *>(sY), sNrm);
-  else store_rows_transposed<QTP>((tid0 >> 8) ? sKT : sQT, qkx, tid0 & 255);
+  store_qk_rows<QTP>(sQT, sKT, p, w, start, iqk, len, qkx, tid0, sNrm);
 
   f32x4 dqA[4], dkA[4];
 #pragma unroll
@@ -1345,7 +1314,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
     }
     // the next unit's q/k rows, once the last value head's tape products are done
     // (qkx as in bwd_grad_unit)
-    if (jg == grp - 1 && next >= 0 && !(p.inflags & IN_QK_L2NORM)) fetch_qk_unit(p, next, tid, qkx);
+    if (jg == grp - 1 && next >= 0) fetch_qk_unit(p, next, tid, qkx);
     // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r), 16 x 16 tiles (mt, nt)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -1557,8 +1526,8 @@ hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
   const int units = p.NC * p.Hqk;
-  u32x4 qkx[4];  // the q/k rows of the unit (inputs without the q/k L2 norm)
-  if ((int)blockIdx.x < units && !(p.inflags & IN_QK_L2NORM)) fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
+  u32x4 qkx[4];  // the raw q/k rows of the unit
+  if ((int)blockIdx.x < units) fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int next = unit + (int)gridDim.x < units ? unit + (int)gridDim.x : -1;
     bwd_grad_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit, qkx, next);
@@ -1568,8 +1537,8 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                             u16 *dk, u16 *dv, float *dg, void *dbeta) {
   const int units = p.NC * p.Hqk;
-  u32x4 qkx[4];  // the q/k rows of the unit (inputs without the q/k L2 norm)
-  if ((int)blockIdx.x < units && !(p.inflags & IN_QK_L2NORM)) fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
+  u32x4 qkx[4];  // the raw q/k rows of the unit
+  if ((int)blockIdx.x < units) fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int next = unit + (int)gridDim.x < units ? unit + (int)gridDim.x : -1;
     bwd_grad_rows_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit, qkx, next);

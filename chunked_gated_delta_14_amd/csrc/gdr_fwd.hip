@@ -205,6 +205,16 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         rq[h] = rsqrtf(tq + L2NORM_EPS);
         rk[h] = rsqrtf(tk + L2NORM_EPS);
       }
+      // kept for the backward, once per (token, Q/K head): by the group's first value head
+      const int grp = p.Hv / p.Hqk;
+      if (save && o == 0 && j % grp == 0) {
+        const int start = tb.start[chunk];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (rp + h < len)
+            *reinterpret_cast<float2 *>(w.qk_rstd + ((size_t)(start + rp + h) * p.Hqk + j / grp) * 2) =
+                make_float2(rq[h], rk[h]);
+      }
     }
     float gx[2][NG];
 #pragma unroll

@@ -35,6 +35,9 @@ struct Workspace {
   // affine carry of a segment, fp32 [128][128] each: Psi (end state from a zero
   // start) then Phi (the segment's transfer matrix)
   float *carry;
+  // inverse L2 norms of the q and k rows, fp32 [T][H_qk][q, k] (prep with GDR_FWD_SAVE
+  // and the q/k L2 norm; read by the gradient kernels)
+  float *qk_rstd;
 };
 
 struct Problem {
