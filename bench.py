@@ -113,7 +113,9 @@ def parse_args():
                     help="segment plan of segmented walks: 0 balanced by document length, 1 equal")
     ap.add_argument("--input-flags", type=int, default=0,
                     help="gdr_problem.input_flags: 1 = in-kernel q/k L2 norm, 2 = beta sigmoid (logits as input)")
-    ap.add_argument("--cpu-tokens", type=int, default=8192, help="tokens per document in the CPU sample")
+    ap.add_argument("--cpu-tokens", type=int, default=32768, help="tokens per document in the CPU sample")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time only the fp64 oracle on the whole workload (fwd, bwd, ckpt) on this host; no GPU")
     ap.add_argument("--no-op-timing", action="store_true", help="skip the separate fwd/bwd/ckpt timings")
     ap.add_argument("--no-smi", action="store_true", help="do not sample clock and power with amd-smi")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and HBM peak probes")
@@ -340,8 +342,42 @@ def cpu_baseline(inp, docs, tokens_per_doc):
                                                    t1 - t0, t2 - t1)}
 
 
+def cpu_full(w):
+    """The fp64 oracle (as it stands) on the whole workload on this host's cores:
+    one timed forward and one timed backward (which replays the forward from its
+    64-token checkpoints); ckpt = 2 x forward + backward."""
+    import oracle
+    from chunked_gated_delta_14_amd import workloads
+
+    t0 = time.perf_counter()
+    inp = workloads.make_inputs(w, device="cpu")
+    t_gen = time.perf_counter() - t0
+    cu = inp["cu_seqlens"].numpy()
+    threads = oracle.default_threads()
+    oracle.build()
+    print("[cpu-full] %s: inputs drawn in %.1f s; forward on %d threads" % (w.name, t_gen, threads),
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    oracle.forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cu, inp["h0"], threads=threads)
+    t1 = time.perf_counter()
+    print("[cpu-full] forward %.1f s; backward" % (t1 - t0), file=sys.stderr, flush=True)
+    oracle.backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cu, inp["dout"], inp["h0"], threads=threads)
+    t2 = time.perf_counter()
+    print("[cpu-full] backward %.1f s" % (t2 - t1), file=sys.stderr, flush=True)
+    th = w.T * w.H_v
+    fwd_s, bwd_s = t1 - t0, t2 - t1
+    return {"workload": w.name, "token_heads": th, "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
+            "fwd_s": fwd_s, "bwd_s": bwd_s, "ckpt_s": 2 * fwd_s + bwd_s,
+            "fwd_bwd_token_heads_per_s": th / (fwd_s + bwd_s), "input_generation_s": t_gen}
+
+
 def main():
     args = parse_args()
+    if args.cpu_full:
+        from chunked_gated_delta_14_amd import workloads
+
+        print(json.dumps(cpu_full(workloads.workload(args.workload, args.H))), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures a single GPU; libgdr has no multi-GPU path. Run with --gpus 1.",
               file=sys.stderr)
