@@ -1083,14 +1083,130 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
 // set fits without spilling; the gate factors there are exponentials of
 // per-row scalars.
 // ---------------------------------------------------------------------------
+// Operands of the next value head, staged in LDS by direct-to-LDS loads while
+// the current one computes (see stage_grad_rows): dout rows, dVn^T, T^T, E, beta
+// and g; v goes to the Y tile and Vn to sVn once those are dead.
+constexpr int GR_STAGE_DO = CH * HD * 2, GR_STAGE_DV = HD * CH * 2, GR_STAGE_T = CH * CH * 2;
+constexpr int GR_STAGE_E = 10 * 64 * 8, GR_STAGE_BG = 2 * 64 * 4;
 constexpr int grad_rows_smem_bytes() {
   return 2 * HD * QTP * 2                   // sQT, sKT
-         + CH * KP * 2                      // sY
+         + CH * KP * 2                      // sY (also the stage of the next value head's v)
          + 4 * CH * MP * 2                  // sDM, sDA, sDMT, sDAT
          + (64 + 4 * 64 + 4 * 128 + 128 + 512) * 4  // sB, sDB slots, sRed slots, sDgam, sBT
          + (128 + 64 * 4) * 4               // q, k row norms [2][64], row dots [64][2][2]
          + 64 * 4                           // sG
-         + CH * HD * 2;                     // sVn: the value head's Vn tile, tape layout
+         + CH * HD * 2                      // sVn: the value head's Vn tile, tape layout
+         + GR_STAGE_DO + GR_STAGE_DV + GR_STAGE_T + GR_STAGE_E + GR_STAGE_BG;
+}
+static_assert(grad_rows_smem_bytes() <= 160 * 1024, "GDN gradient LDS map");
+
+// Direct-to-LDS copy: every lane moves `BYTES` (4 or 16) from its own global
+// address to lds_byte + BYTES * lane.  Written as inline asm: the compiler would
+// otherwise make every later LDS access wait for it (it cannot tell the bytes
+// apart), which would serialise the copy with the work it is meant to overlap.
+// The compiler does not count these loads, so callers drain the vector-memory
+// counter before issuing them (no register load issued earlier is then waited for
+// behind them) and wait for them explicitly (s_waitcnt vmcnt(0) and a barrier)
+// before reading what they wrote.  M0 carries the LDS address; it is saved and
+// restored, with one wait state between its write and the load.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void *src, uint32_t lds_byte) {
+  uint32_t saved;
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS regions of the GDN gradient kernel (pointers into the dynamic LDS).
+struct GradRowsLds {
+  u16 *sQT, *sKT, *sY, *sDM, *sDA, *sDMT, *sDAT;
+  float *sB, *sDB, *sRed, *sDgam, *sBT, *sG, *sNrm;
+  u16 *sVn, *pDo, *pDv, *pT;
+  uint2 *pE;
+  float *pBG;
+  __device__ __forceinline__ explicit GradRowsLds(unsigned char *smem) {
+    sQT = reinterpret_cast<u16 *>(smem);
+    sKT = sQT + HD * QTP;
+    sY = sKT + HD * QTP;
+    sDM = sY + CH * KP;
+    sDA = sDM + CH * MP;
+    sDMT = sDA + CH * MP;
+    sDAT = sDMT + CH * MP;
+    sB = reinterpret_cast<float *>(sDAT + CH * MP);
+    // Reductions across wavefronts go to one slot per contributing wavefront and
+    // are added in a fixed order, so every result is bitwise repeatable.
+    sDB = sB + 64;     // dbeta partial sums [4][64]: Y phase (column half 0, 1), then tape/dA phase (0, 1)
+    sRed = sDB + 256;  // K-bar column sums [4][128], one slot per row strip
+    sDgam = sRed + 512;
+    sBT = sDgam + 128;  // [4][128] row-block totals of the gate gradient
+    sG = sBT + 512;
+    sNrm = sG + 64;  // q, k row norms [2][64], then row dots [64][2][2]
+    sVn = reinterpret_cast<u16 *>(sNrm + 128 + 64 * 4);  // Vn tile of the current value head
+    pDo = sVn + CH * HD;         // dout rows [64][16 pieces], piece p of row r at slot p ^ (r & 15)
+    pDv = pDo + CH * HD;         // dVn^T [128][8 pieces], piece p of row v at slot p ^ ((v >> 1) & 7)
+    pT = pDv + HD * CH;          // T^T [64][8 pieces], as dVn^T
+    pE = reinterpret_cast<uint2 *>(pT + CH * CH);  // E's 10 lower tiles [tile][lane]
+    pBG = reinterpret_cast<float *>(pE + 10 * 64);  // beta [64], g [64]
+  }
+};
+
+// Stage the operands of value-head unit u (chunk rows start..start+len-1, value
+// head j) in LDS with direct-to-LDS loads; every wavefront moves its own 1 KB
+// blocks.  rest: dout rows, dVn^T, T^T, E, beta and g into the stage regions;
+// late: v rows into the Y tile ([64][16 pieces], the dout swizzle) and the Vn tile
+// (as it lies in the tape) into sVn, once both are dead.  dout and v rows past len
+// repeat the last row (readers zero them); beta and g rows past len are read as
+// row 0 (likewise zeroed).  The swizzles put the 16 rows a 16-lane group reads in
+// 16 distinct bank groups.
+__device__ __forceinline__ void stage_grad_rows(const Problem &p, const Workspace &w, const u16 *dout,
+                                                const GradRowsLds &L, size_t u, int start, int len, int j,
+                                                bool late, bool rest) {
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const size_t Hv = p.Hv;
+  if (rest) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = 2 * wave + h;
+      {  // dout: rows 4k .. 4k+3, 16 pieces each
+        const int row = 4 * k + (lane >> 4), slot = lane & 15, pc = slot ^ (row & 15);
+        const size_t e = ((size_t)(start + (row < len ? row : len - 1)) * Hv + j) * HD + 8 * pc;
+        lds_dma<16>(dout + e, lds_addr(L.pDo + 512 * k));
+      }
+      {  // dVn^T: rows 8k .. 8k+7, 8 pieces each
+        const int v = 8 * k + (lane >> 3), slot = lane & 7, pc = slot ^ ((v >> 1) & 7);
+        lds_dma<16>(w.dVnT + u * (CH * HD) + v * CH + 8 * pc, lds_addr(L.pDv + 512 * k));
+      }
+    }
+    {  // T^T: rows 8w .. 8w+7
+      const int r = 8 * wave + (lane >> 3), slot = lane & 7, pc = slot ^ ((r >> 1) & 7);
+      lds_dma<16>(reinterpret_cast<const u16 *>(w.Tt + u * FRAG_64x64_U4) + r * CH + 8 * pc, lds_addr(L.pT + 512 * wave));
+    }
+    if (wave < 5)  // E: 5 KB, contiguous
+      lds_dma<16>(reinterpret_cast<const u16 *>(w.Et + u * FRAG_64x64_U4) + 512 * wave + 8 * lane,
+                  lds_addr(L.pE + 128 * wave));
+    if (wave == 0) {  // beta and g of rows 0..63
+      const size_t e = (size_t)(start + (lane < len ? lane : 0)) * Hv + j;
+      lds_dma<4>(reinterpret_cast<const float *>(p.beta) + e, lds_addr(L.pBG));
+      lds_dma<4>(p.g + e, lds_addr(L.pBG + 64));
+    }
+  }
+  if (late) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = 2 * wave + h;
+      const int row = 4 * k + (lane >> 4), slot = lane & 15, pc = slot ^ (row & 15);
+      lds_dma<16>(p.v + ((size_t)(start + (row < len ? row : len - 1)) * Hv + j) * HD + 8 * pc,
+                  lds_addr(L.sY + 512 * k));
+      lds_dma<16>(w.Vn + u * (CH * HD) + 512 * k + 8 * lane, lds_addr(L.sVn + 512 * k));
+    }
+  }
 }
 
 // acc[t] += x for a run-time tile index t, without indexing a register array
@@ -1115,23 +1231,10 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
   const float scale = p.scale;
   const size_t Hv = p.Hv;
 
-  u16 *sQT = reinterpret_cast<u16 *>(smem);
-  u16 *sKT = sQT + HD * QTP;
-  u16 *sY = sKT + HD * QTP;
-  u16 *sDM = sY + CH * KP;
-  u16 *sDA = sDM + CH * MP;
-  u16 *sDMT = sDA + CH * MP;
-  u16 *sDAT = sDMT + CH * MP;
-  float *sB = reinterpret_cast<float *>(sDAT + CH * MP);
-  // Reductions across wavefronts go to one slot per contributing wavefront and
-  // are added in a fixed order, so every result is bitwise repeatable.
-  float *sDB = sB + 64;     // dbeta partial sums [4][64]: Y phase (column half 0, 1), then tape/dA phase (0, 1)
-  float *sRed = sDB + 256;  // K-bar column sums [4][128], one slot per row strip
-  float *sDgam = sRed + 512;
-  float *sBT = sDgam + 128;  // [4][128] row-block totals of the gate gradient
-  float *sG = sBT + 512;
-  float *sNrm = sG + 64;  // q, k row norms [2][64], then row dots [64][2][2]
-  u16 *sVn = reinterpret_cast<u16 *>(sNrm + 128 + 64 * 4);  // Vn tile of the current value head
+  const GradRowsLds L(smem);
+  u16 *sQT = L.sQT, *sKT = L.sKT, *sY = L.sY, *sDM = L.sDM, *sDA = L.sDA, *sDMT = L.sDMT, *sDAT = L.sDAT;
+  float *sB = L.sB, *sDB = L.sDB, *sRed = L.sRed, *sDgam = L.sDgam, *sBT = L.sBT, *sG = L.sG, *sNrm = L.sNrm;
+  u16 *sVn = L.sVn;
   const GateT<true> G{sG};
 
   store_qk_rows<QTP>(sQT, sKT, p, w, start, iqk, len, qkx, tid0, sNrm);
@@ -1152,51 +1255,57 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
     const size_t u = (size_t)chunk * Hv + j;
     const int r0 = 16 * mt + 4 * lg;  // first of the 4 accumulator rows of this lane
     const int ra = 16 * mt + lr;      // operand row of this lane
-
-    // ---- per value head: beta, cleared sums, the cumulative gate ----
-    if (tid < 64) {
-      float b = 0.f;
-      if (tid < len) {
-        const size_t e = (size_t)(start + tid) * Hv + j;
-        b = reinterpret_cast<const float *>(p.beta)[e];
-        if (p.inflags & IN_BETA_SIGMOID) b = sigmoidf_(b);
-      }
-      sB[tid] = b;
+    // the value head after this one: the next of the group, else the first of unit `next`
+    const bool more = jg + 1 < grp || next >= 0;
+    int nstart = start, nlen = len, nj = j + 1;
+    size_t nu = u + 1;
+    if (jg + 1 == grp && next >= 0) {
+      const int nchunk = next / p.Hqk;
+      nstart = tb.start[nchunk];
+      nlen = tb.len[nchunk];
+      nj = (next % p.Hqk) * grp;
+      nu = (size_t)nchunk * Hv + nj;
     }
-    // operands of Y = T^T dVn, v for dbeta and dv, and the dout / Vn rows of the tape
-    // products, all issued before the barrier
-    const u16 *dvt = w.dVnT + u * (CH * HD);
+
+    // ---- this value head's operands, staged in LDS one value head earlier ----
+    drain_vmem();
+    lds_barrier();
     bf16x8 bT[2], aDV[4][2], dOa[4];
     uint2 vvs[4], e4s[2];
-    // E tiles (mt, ch + 2q) of the dA products (read only where ch + 2q <= mt; every index
-    // lies in the 10 lower tiles)
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      e4s[q] = reinterpret_cast<const uint2 *>(w.Et + u * FRAG_64x64_U4)[(mt * (mt + 1) / 2 + ch + 2 * q) * 64 + lane];
-    // the Vn tile (16 KB) for the LDS stage: 32 contiguous bytes per thread
-    const uint4 *vnsrc = reinterpret_cast<const uint4 *>(w.Vn + u * (CH * HD));
-    const uint4 vn0 = vnsrc[2 * tid], vn1 = vnsrc[2 * tid + 1];
-    {
-      const u16 *dr = dout + ((size_t)(start + ra) * Hv + j) * HD;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) dOa[kt] = ra < len ? ld8(dr + 32 * kt + 8 * lg) : as_bf16x8(make_uint4(0, 0, 0, 0));
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        vvs[t] = ra < len ? *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + ra) * Hv + j) * HD + 16 * (4 * ch + t) + 4 * lg)
-                          : make_uint2(0u, 0u);
+    if (tid < 64) {
+      float b = L.pBG[tid];
+      if (p.inflags & IN_BETA_SIGMOID) b = sigmoidf_(b);
+      sB[tid] = tid < len ? b : 0.f;
     }
+    // E tiles (mt, ch + 2q) of the dA products (used only where ch + 2q <= mt; every
+    // index lies in the 10 lower tiles)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) e4s[q] = L.pE[(mt * (mt + 1) / 2 + ch + 2 * q) * 64 + lane];
     {
-      const uint4 *TT = w.Tt + u * FRAG_64x64_U4;  // T^T, bf16 row-major 64 x 64
+      const bf16x8 z = as_bf16x8(make_uint4(0, 0, 0, 0));
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) bT[kt] = as_bf16x8(TT[ra * 8 + 4 * kt + lg]);
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8 x = ld8(L.pDo + ra * HD + 8 * ((4 * kt + lg) ^ (ra & 15)));
+        dOa[kt] = ra < len ? x : z;
+      }
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        const int c = 16 * (4 * ch + t) + 4 * lg;  // 8 bytes: half (c >> 2) & 1 of piece c >> 3
+        const uint2 x = *reinterpret_cast<const uint2 *>(sY + ra * HD + 8 * ((c >> 3) ^ (ra & 15)) + (c & 7));
+        vvs[t] = ra < len ? x : make_uint2(0u, 0u);
+      }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) aDV[t][kt] = ld8(dvt + (16 * (4 * ch + t) + lr) * CH + 32 * kt + 8 * lg);
+      for (int kt = 0; kt < 2; ++kt) bT[kt] = ld8(L.pT + ra * CH + 8 * ((4 * kt + lg) ^ ((ra >> 1) & 7)));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int vr = 16 * (4 * ch + t) + lr;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) aDV[t][kt] = ld8(L.pDv + vr * CH + 8 * ((4 * kt + lg) ^ ((vr >> 1) & 7)));
+      }
     }
     {
       if (tid < 64) {
-        float x = tid < len ? p.g[(size_t)(start + tid) * Hv + j] : 0.f;
+        float x = tid < len ? L.pBG[64 + tid] : 0.f;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const float y = __shfl_up(x, o, 64);
@@ -1204,9 +1313,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
         }
         sG[tid] = x;
       }
-      reinterpret_cast<uint4 *>(sVn)[2 * tid] = vn0;
-      reinterpret_cast<uint4 *>(sVn)[2 * tid + 1] = vn1;
-      lds_barrier();
+      lds_barrier();  // also: every wavefront has read the stage (its regions may be refilled)
     }
 
     // the state tapes' first tile of the tape products below, fetched once the Y
@@ -1312,8 +1419,15 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
         if (lg == 0) sRed[mt * 128 + c] = colsum;
       }
     }
-    // the next unit's q/k rows, once the last value head's tape products are done
-    // (qkx as in bwd_grad_unit)
+    // Stage the next value head's operands (the stage regions were read at the top
+    // of this iteration, before a barrier), then the next unit's q/k rows once the
+    // last value head's tape products are done (qkx as in bwd_grad_unit).  No
+    // register load issued before the staging is still in flight after it
+    // (drained), so none is waited for behind it.
+    if (more) {
+      drain_vmem();
+      stage_grad_rows(p, w, dout, L, nu, nstart, nlen, nj, false, true);
+    }
     if (jg == grp - 1 && next >= 0) fetch_qk_unit(p, next, tid, qkx);
     // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r), 16 x 16 tiles (mt, nt)
 #pragma unroll
@@ -1353,6 +1467,9 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
       *reinterpret_cast<uint2 *>(sDAT + s * MP + r0) = pack4(a[0], a[1], a[2], a[3]);
     }
     lds_barrier();
+    // the Y tile and sVn are dead (last read by the tape and dM/dA products, before
+    // the barrier above): the next value head's v rows and Vn tile
+    if (more) stage_grad_rows(p, w, dout, L, nu, nstart, nlen, nj, true, false);
 
     {
       // ---- gated products with the decay and beta folded into the tiles:
@@ -1536,9 +1653,17 @@ __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, c
 }
 __global__ __launch_bounds__(GNT) void bwd_grad_rows_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                             u16 *dk, u16 *dv, float *dg, void *dbeta) {
+  extern __shared__ __align__(16) unsigned char smem[];
   const int units = p.NC * p.Hqk;
   u32x4 qkx[4];  // the raw q/k rows of the unit
-  if ((int)blockIdx.x < units) fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
+  if ((int)blockIdx.x < units) {
+    // the first unit's first value head, staged as every later one is by its predecessor
+    const ChunkTable tb(p.table, p.NC, p.N);
+    const int chunk = blockIdx.x / p.Hqk, j = (blockIdx.x % p.Hqk) * (p.Hv / p.Hqk);
+    stage_grad_rows(p, w, dout, GradRowsLds(smem), (size_t)chunk * p.Hv + j, tb.start[chunk], tb.len[chunk], j,
+                    true, true);
+    fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
+  }
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int next = unit + (int)gridDim.x < units ? unit + (int)gridDim.x : -1;
     bwd_grad_rows_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit, qkx, next);
