@@ -409,20 +409,54 @@ constexpr int DMP = 68;   // dM, dA, dM^T, dA^T
 constexpr int G_QT = 0;                     // q^T bf16 [128][KQTP]
 constexpr int G_KT = G_QT + HD * KQTP * 2;  // k^T bf16 [128][KQTP]
 constexpr int G_GT = G_KT + HD * KQTP * 2;  // cumulative gate: KDA fp32 [128][GTP], GDN [64]
-constexpr int G_DO = G_GT + HD * GTP * 4;   // dout bf16 [64][KP]      (tape products)
-constexpr int G_VN = G_DO + CH * KP * 2;    // Vn
-constexpr int G_Y = G_VN + CH * KP * 2;     // Y
+constexpr int G_DO = G_GT + HD * GTP * 4;   // dout bf16 [64][128], sw128 layout  (tape products)
+constexpr int G_VN = G_DO + CH * HD * 2;    // Vn, sw128
+constexpr int G_Y = G_VN + CH * HD * 2;     // Y, sw128
 constexpr int G_DM = G_DO;                  // dM, dA, dM^T, dA^T bf16 [64][DMP] (gated products)
 constexpr int G_DA = G_DM + CH * DMP * 2;
 constexpr int G_DMT = G_DA + CH * DMP * 2;
 constexpr int G_DAT = G_DMT + CH * DMP * 2;
-constexpr int G_TT = G_Y + CH * KP * 2;     // T^T bf16 [64][MP]             (Y product)
-constexpr int G_B = G_TT + CH * MP * 2;     // beta [64]
+constexpr int G_TT = G_Y + CH * HD * 2;     // T^T bf16 [64][64], sw64 layout    (Y product)
+constexpr int G_B = G_TT + CH * CH * 2;     // beta [64]
 constexpr int G_DB = G_B + 64 * 4;          // dbeta partial sums [20][64], added in a fixed order
 constexpr int G_NRM = G_DB + 20 * 64 * 4;   // q, k row norms [2][64], then row dots [64][2][8]
-constexpr int G_SMEM = G_NRM + (128 + 64 * 16) * 4;
-static_assert(G_DAT + CH * DMP * 2 <= G_B, "grad LDS map");
+constexpr int G_DV = G_NRM + (128 + 64 * 16) * 4;  // dVn^T bf16 [128][64], sw64 (Y product)
+constexpr int G_SMEM = G_DV + HD * CH * 2;
+static_assert(G_DAT + CH * DMP * 2 <= G_TT, "grad LDS map: dM, dA overlay dout, Vn and Y only");
+static_assert(G_SMEM <= 160 * 1024, "grad LDS map");
 
+// Unpadded row-major bf16 tiles in LDS.  The 16-byte piece p of row r of a
+// 128-column tile sits at slot p ^ (r & 15); of a 64-column tile at slot
+// p ^ ((r >> 1) & 7).  Either way the 16 rows a 16-lane group reads in one
+// instruction fall in 16 distinct bank groups, and every piece stays 16 contiguous
+// bytes, so direct-to-LDS loads can fill the tiles 1 KB at a time.
+__device__ __forceinline__ int sw128(int r, int col) { return r * HD + 8 * ((col >> 3) ^ (r & 15)) + (col & 7); }
+__device__ __forceinline__ int sw64(int r, int col) { return r * CH + 8 * ((col >> 3) ^ ((r >> 1) & 7)) + (col & 7); }
+
+
+// Direct-to-LDS copy: every lane moves `BYTES` (4 or 16) from its own global
+// address to lds_byte + BYTES * lane.  Written as inline asm: the compiler would
+// otherwise make every later LDS access wait for it (it cannot tell the bytes
+// apart), which would serialise the copy with the work it is meant to overlap.
+// The compiler does not count these loads, so callers drain the vector-memory
+// counter before issuing them (no register load issued earlier is then waited for
+// behind them) and wait for them explicitly (s_waitcnt vmcnt(0) and a barrier)
+// before reading what they wrote.  M0 carries the LDS address; it is saved and
+// restored, with one wait state between its write and the load.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void *src, uint32_t lds_byte) {
+  uint32_t saved;
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Cumulative gate: per-channel tile [channel][row] (KDA) or one value per row.
 template <bool SCALAR>
@@ -579,6 +613,42 @@ __device__ __forceinline__ void load_grad_tape(const u16 *tape, size_t u, int ti
   for (int kt = 0; kt < 4; ++kt) Sb[kt] = ld8(Sg + tape_s(c, 32 * kt + 8 * lg));
 }
 
+// Stage operands of the KDA gradient unit `unit` in LDS with direct-to-LDS loads
+// (lds_dma), every wavefront moving its own 1 KB blocks.  early: T^T and dVn^T
+// (sw64), whose tiles are dead once the tape products are done; late: the dout and
+// Vn rows (sw128, Vn gathered from its tape layout), whose tiles carry dM and dA
+// until the gated products are done.  dout rows past the chunk repeat its last
+// row (readers zero them).
+__device__ __forceinline__ void stage_grad_kda(const Problem &p, const Workspace &w, const u16 *dout,
+                                               unsigned char *smem, int unit, bool early, bool late) {
+  const ChunkTable tb(p.table, p.NC, p.N);
+  const int chunk = unit / p.Hqk, j = unit % p.Hqk;
+  const int start = tb.start[chunk], len = tb.len[chunk];
+  const size_t Hv = p.Hv, u = (size_t)chunk * Hv + j;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  if (early) {
+    {  // T^T: rows 8w .. 8w+7
+      const int r = 8 * wave + (lane >> 3), slot = lane & 7, pc = slot ^ ((r >> 1) & 7);
+      lds_dma<16>(reinterpret_cast<const u16 *>(w.Tt + u * FRAG_64x64_U4) + r * CH + 8 * pc,
+                  lds_addr(smem + G_TT + 1024 * wave));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // dVn^T: rows 8k .. 8k+7
+      const int k = 2 * wave + h, v = 8 * k + (lane >> 3), slot = lane & 7, pc = slot ^ ((v >> 1) & 7);
+      lds_dma<16>(w.dVnT + u * (CH * HD) + v * CH + 8 * pc, lds_addr(smem + G_DV + 1024 * k));
+    }
+  }
+  if (late) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // dout and Vn: rows 4k .. 4k+3
+      const int k = 2 * wave + h, row = 4 * k + (lane >> 4), slot = lane & 15, pc = slot ^ (row & 15);
+      lds_dma<16>(dout + ((size_t)(start + (row < len ? row : len - 1)) * Hv + j) * HD + 8 * pc,
+                  lds_addr(smem + G_DO + 1024 * k));
+      lds_dma<16>(w.Vn + u * (CH * HD) + tape_r(row, 8 * pc), lds_addr(smem + G_VN + 1024 * k));
+    }
+  }
+}
+
 // qkx arrives holding this unit's raw q/k rows (fetch_qk_unit) and leaves holding
 // those of unit `next` (if next >= 0), fetched once this unit's tape products are
 // done, so that their latency overlaps the rest of the unit.  With the q/k L2 norm
@@ -631,7 +701,12 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
     const size_t u = (size_t)chunk * Hv + j;
     const int c = 16 * wave + lr;  // this lane's key/value column
 
-    // ---- every load of the iteration, issued up front in the order of use and
+    // T^T, dVn^T, dout and Vn were staged in LDS by the previous unit (or before the
+    // loop): each wavefront waits for its own copies here, and the barrier before
+    // the Y product makes all of them visible.
+    drain_vmem();
+
+    // ---- every other load of the iteration, issued up front in the order of use and
     // unconditionally (rows past the chunk read its last row, zeroed at use) ----
     float graw[2][8];
     uint32_t braw = 0u;
@@ -650,31 +725,12 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
       const size_t e = (size_t)(start + (tid < len ? tid : last)) * Hv + j;
       braw = reinterpret_cast<const u16 *>(p.beta)[e];
     }
-    // Y operands: T^T (one 16-byte piece per thread, for the LDS stage), this
-    // wavefront's value tile of dVn^T, and v at the accumulator positions
-    const u32x4 stT = reinterpret_cast<const u32x4 *>(w.Tt + u * FRAG_64x64_U4)[tid];
-    bf16x8 aDV[2];
+    // v at the accumulator positions (dbeta and dv)
     uint2 vv[4];
-    {
-      const u16 *dvt = w.dVnT + u * (CH * HD) + (size_t)c * CH;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) aDV[kt] = ld8(dvt + 32 * kt + 8 * lg);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int rl = 16 * mt + lr < len ? 16 * mt + lr : last;
-        vv[mt] = *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + rl) * Hv + j) * HD + 16 * wave + 4 * lg);
-      }
-    }
-    // dout and Vn rows for the LDS stage: thread -> rows (tid>>4) and +32, 16-byte segment tid&15
-    u32x4 stDo[2], stVn[2];
-    {
-      const u16 *Vng = w.Vn + u * (CH * HD);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = (tid >> 4) + 32 * h, rc = r < len ? r : last, sg = 8 * (tid & 15);
-        stDo[h] = *reinterpret_cast<const u32x4 *>(dout + ((size_t)(start + rc) * Hv + j) * HD + sg);
-        stVn[h] = *reinterpret_cast<const u32x4 *>(Vng + tape_r(r, sg));
-      }
+    for (int mt = 0; mt < 4; ++mt) {
+      const int rl = 16 * mt + lr < len ? 16 * mt + lr : last;
+      vv[mt] = *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + rl) * Hv + j) * HD + 16 * wave + 4 * lg);
     }
     // ---- beta, cleared sums, the cumulative gate ----
     if (tid < 64) {
@@ -683,7 +739,6 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
       sB[tid] = tid < len ? b : 0.f;
     }
     if (tid < 256) sDB[16 * 64 + tid] = 0.f;  // E-term slots (not every row block writes every slot)
-    *reinterpret_cast<u32x4 *>(sTT + (tid >> 3) * MP + 8 * (tid & 7)) = stT;
     {
       // the 32 lanes of a half wavefront scan their channel octet's 64 rows
 #pragma unroll
@@ -712,15 +767,18 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
     uint2 dvv[4];
     {
       const int v0 = 16 * wave + 4 * lg;
+      bf16x8 aDV[2];  // this wavefront's value tile of dVn^T
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) aDV[kt] = ld8(reinterpret_cast<const u16 *>(smem + G_DV) + sw64(c, 32 * kt + 8 * lg));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int ra = 16 * mt + lr;
         f32x4 acc = zero4();
 #pragma unroll
         for (int kt = (mt >= 2 ? 1 : 0); kt < 2; ++kt)  // T^T[r][r'] = 0 for r' < r
-          acc = mfma(aDV[kt], ld8(sTT + ra * MP + 32 * kt + 8 * lg), acc);
+          acc = mfma(aDV[kt], ld8(sTT + sw64(ra, 32 * kt + 8 * lg)), acc);
         // acc[jj] = Y[ra][v0 + jj]
-        *reinterpret_cast<uint2 *>(sY + ra * KP + v0) = pack4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<uint2 *>(sY + sw128(ra, v0)) = pack4(acc[0], acc[1], acc[2], acc[3]);
         float db1 = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) db1 += acc[jj] * bf_at(vv[mt], jj);
@@ -729,12 +787,6 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         const float br = sB[ra];
         dvv[mt] = pack4(br * acc[0], br * acc[1], br * acc[2], br * acc[3]);
       }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = (tid >> 4) + 32 * h, sg = 8 * (tid & 15);
-      *reinterpret_cast<u32x4 *>(sDo + r * KP + sg) = r < len ? stDo[h] : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(sVn + r * KP + sg) = stVn[h];
     }
 
     // ---- gate factors of this lane's column c and rows 16I + 4lg + jj ----
@@ -769,8 +821,9 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         __builtin_amdgcn_sched_barrier(0);  // one k-step of operands in flight at a time
-        const int o = rA * KP + 32 * kt + 8 * lg;
-        aQ = mfma(ld8(sDo + o), Sb[kt], aQ);
+        const int o = sw128(rA, 32 * kt + 8 * lg);
+        const bf16x8 dor = ld8(sDo + o);
+        aQ = mfma(rA < len ? dor : as_bf16x8(make_uint4(0, 0, 0, 0)), Sb[kt], aQ);
         aY = mfma(ld8(sY + o), Sb[kt], aY);
         aK = mfma(ld8(sVn + o), dSb[kt], aK);
       }
@@ -801,7 +854,15 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         if (lr == 0) sDB[(8 + wave) * 64 + r0 + jj] = x;  // slots 8..15
       }
     }
-    if (next >= 0) fetch_qk_unit(p, next, tid, qkx);
+    // The next unit's T^T and dVn^T into their tiles (read by this unit's Y product,
+    // before the barrier ahead of the tape products), then its q/k rows.  No
+    // register load issued before the staging is still in flight after it
+    // (drained), so none is waited for behind it.
+    if (next >= 0) {
+      drain_vmem();
+      stage_grad_kda(p, w, dout, smem, next, true, false);
+      fetch_qk_unit(p, next, tid, qkx);
+    }
     colsum = red_lg(colsum);
     // dM = scale dout Vn^T (s <= r) and dA = -Y Vn^T (s < r): the 10 lower
     // 16x16 tiles, wavefront w takes tiles w and w + 8
@@ -815,9 +876,10 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         block_pair(pt, I, J);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 vb = ld8(sVn + (16 * J + lr) * KP + 32 * kt + 8 * lg);
-          const int o = (16 * I + lr) * KP + 32 * kt + 8 * lg;
-          tM[q] = mfma(ld8(sDo + o), vb, tM[q]);
+          const bf16x8 vb = ld8(sVn + sw128(16 * J + lr, 32 * kt + 8 * lg));
+          const int o = sw128(16 * I + lr, 32 * kt + 8 * lg);
+          const bf16x8 dor = ld8(sDo + o);
+          tM[q] = mfma(16 * I + lr < len ? dor : as_bf16x8(make_uint4(0, 0, 0, 0)), vb, tM[q]);
           tA[q] = mfma(ld8(sY + o), vb, tA[q]);
         }
         float db3[4];
@@ -1012,7 +1074,9 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
         below += blk[I];
       }
     }
-    lds_barrier();  // dbeta partial sums complete (and GDN row sums)
+    lds_barrier();  // dbeta partial sums complete; dM, dA and their transposes are dead
+    // the next unit's dout and Vn rows into the tiles dM and dA occupied
+    if (next >= 0) stage_grad_kda(p, w, dout, smem, next, false, true);
     if (tid < 64 && tid < len) {
       float x = 0.f;
 #pragma unroll
@@ -1099,30 +1163,6 @@ constexpr int grad_rows_smem_bytes() {
          + GR_STAGE_DO + GR_STAGE_DV + GR_STAGE_T + GR_STAGE_E + GR_STAGE_BG;
 }
 static_assert(grad_rows_smem_bytes() <= 160 * 1024, "GDN gradient LDS map");
-
-// Direct-to-LDS copy: every lane moves `BYTES` (4 or 16) from its own global
-// address to lds_byte + BYTES * lane.  Written as inline asm: the compiler would
-// otherwise make every later LDS access wait for it (it cannot tell the bytes
-// apart), which would serialise the copy with the work it is meant to overlap.
-// The compiler does not count these loads, so callers drain the vector-memory
-// counter before issuing them (no register load issued earlier is then waited for
-// behind them) and wait for them explicitly (s_waitcnt vmcnt(0) and a barrier)
-// before reading what they wrote.  M0 carries the LDS address; it is saved and
-// restored, with one wait state between its write and the load.
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(const void *src, uint32_t lds_byte) {
-  uint32_t saved;
-  if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
-  else
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
-}
-__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS regions of the GDN gradient kernel (pointers into the dynamic LDS).
 struct GradRowsLds {
@@ -1642,9 +1682,13 @@ hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout
 // workgroups take consecutive units, as a one-unit-per-workgroup grid would.
 __global__ __launch_bounds__(GNT) void bwd_grad_kernel(Problem p, Workspace w, const u16 *dout, u16 *dq,
                                                        u16 *dk, u16 *dv, float *dg, void *dbeta) {
+  extern __shared__ __align__(16) unsigned char smem[];
   const int units = p.NC * p.Hqk;
   u32x4 qkx[4];  // the raw q/k rows of the unit
-  if ((int)blockIdx.x < units) fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
+  if ((int)blockIdx.x < units) {
+    stage_grad_kda(p, w, dout, smem, blockIdx.x, true, true);  // as every later unit is staged by its predecessor
+    fetch_qk_unit(p, blockIdx.x, threadIdx.x, qkx);
+  }
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int next = unit + (int)gridDim.x < units ? unit + (int)gridDim.x : -1;
     bwd_grad_unit(p, w, dout, dq, dk, dv, dg, dbeta, unit, qkx, next);
