@@ -126,9 +126,9 @@ def parse_args():
 
 def traffic_from_profiles(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this
-    kernel (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), if
-    one exists for this workload."""
-    path = os.path.join(ROOT, "profiles", "%s_traffic.md" % kernel)
+    kernel on this workload (profiles/<kernel>_<workload>_traffic.md: FETCH_SIZE
+    + WRITE_SIZE, scaled by the copy-kernel calibration), if one exists."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (kernel, workload))
     if not os.path.exists(path):
         return None
     text = open(path).read()

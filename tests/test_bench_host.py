@@ -57,5 +57,7 @@ def test_traffic_summary_matches_workload_only():
     """A committed HBM-traffic summary is reported only for the workload it names."""
     t = bench.traffic_from_profiles("bwd_grad", "kda_pack4_T261392_H16")
     assert t is not None and t > 1e10
-    assert bench.traffic_from_profiles("bwd_grad", "gdn_pack6_T241817_Hqk16_Hv48") is None
+    g = bench.traffic_from_profiles("bwd_grad", "gdn_pack6_T241817_Hqk16_Hv48")
+    assert g is not None and g != t
+    assert bench.traffic_from_profiles("bwd_grad", "kda_pack4_T261392_H4") is None
     assert bench.traffic_from_profiles("no_such_kernel", "kda_pack4_T261392_H16") is None
