@@ -26,9 +26,13 @@ METRIC = "KDA fwd+bwd token-heads/s, H=16, T=261392 (1 GPU); % MFMA & HBM peak"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
-# Per (chunk, value head) unit bytes of the workspace regions.
-FWD_OPERANDS = 16384 * 3 + 16384 * 2 + 512   # -W, P, Kbar^T fragments; U, Oi; gamma
-BWD_OPERANDS = 16384 * 3 + 8192               # Kbar, -W^T, (q Gamma)^T fragments; M^T
+# Per (chunk, value head) unit bytes of the workspace regions; the Kbar^T, Kbar and
+# (q Gamma)^T fragments are per (chunk, Q/K head) (with one gate per row they are a
+# Q/K head's K^T, K and scale Q^T, shared by its value heads; KDA has H_qk = H_v).
+SHARED_FWD = 16384                             # Kbar^T
+SHARED_BWD = 16384 * 2                         # Kbar, (q Gamma)^T
+FWD_OPERANDS = 16384 * 2 + 16384 * 2 + 512   # -W, P fragments; U, Oi; gamma
+BWD_OPERANDS = 16384 + 8192                   # -W^T fragments; M^T
 TE_SAVED = 8192 + 5120                         # T^T (bf16 64 x 64) and E's 10 lower tiles (bf16)
 S_TAPE, ROW_TAPE = 32768, 16384
 # Bytes per token-head that the method must move for fwd + bwd with bf16 state
@@ -67,17 +71,19 @@ def kernel_bytes(name, T, Hqk, Hv, NC, N, gdn, save=True):
     """Design bytes of one launch: every input and output byte of the kernel as
     built, workspace fragments and tapes included, counted once (q and k once
     per Q/K head).  Reported beside the algorithmic bytes, never as them."""
-    units = NC * Hv
+    units, qk_units = NC * Hv, NC * Hqk
     qk = 2 * T * Hqk * 256
     v = T * Hv * 256
     g = T * Hv * (4 if gdn else 512)
     beta = T * Hv * (4 if gdn else 2)
+    fwd_ops = units * FWD_OPERANDS + qk_units * SHARED_FWD
+    bwd_ops = units * BWD_OPERANDS + qk_units * SHARED_BWD
     if name == "fwd_prep":
-        return qk + v + g + beta + units * (FWD_OPERANDS + ((BWD_OPERANDS + TE_SAVED) if save else 0))
+        return qk + v + g + beta + fwd_ops + ((bwd_ops + units * TE_SAVED) if save else 0)
     if name == "fwd_walk":
-        return units * FWD_OPERANDS + v + units * ((S_TAPE + ROW_TAPE) if save else 0) + N * Hv * 65536
+        return fwd_ops + v + units * ((S_TAPE + ROW_TAPE) if save else 0) + N * Hv * 65536
     if name == "bwd_walk":
-        return units * (BWD_OPERANDS + 512 + S_TAPE + ROW_TAPE) + v + N * Hv * 65536
+        return bwd_ops + units * (512 + S_TAPE + ROW_TAPE) + v + N * Hv * 65536
     if name == "bwd_grad":
         return (2 * qk + 3 * v + g * 2 + beta * 2) + units * (2 * S_TAPE + 2 * ROW_TAPE + TE_SAVED)
     raise KeyError(name)

@@ -88,9 +88,9 @@ struct Layout {
   int64_t fwd_bytes, full_bytes;
 };
 
-// Region order keeps WfN|Pf, KbT and Uacc adjacent so that the backward's
-// scratch tapes (dS: 32 KB, dVnT: 16 KB per unit) can overlay the
-// forward-walk operands, which are dead once the forward walk has run.
+// The backward's scratch tapes overlay forward-walk operands, which are dead once
+// the forward walk has run: dS (32 KB per unit) the adjacent WfN|Pf, dVnT (16 KB)
+// Uacc.  KbT, Kb and QGT are per (chunk, Q/K head).
 Layout make_layout(int64_t units, int64_t N, int64_t Hv, int64_t T, int64_t Hqk) {
   Layout L{};
   int64_t off = 0;
@@ -99,18 +99,25 @@ Layout make_layout(int64_t units, int64_t N, int64_t Hv, int64_t T, int64_t Hqk)
     off += round_up(per_unit * units);
     return at;
   };
+  // per (chunk, Q/K head): the K fragments a Q/K head's value heads share
+  const int64_t qk_units = Hv > 0 ? units / Hv * Hqk : 0;
+  auto take_qk = [&](int64_t per_unit) {
+    const int64_t at = off;
+    off += round_up(per_unit * qk_units);
+    return at;
+  };
   L.carry = off;
   off += round_up((int64_t)(walk_segment_cap(N, Hv, units / Hv) - 1) * N * Hv * 2 * kHD * kHD * 4);
   L.WfN = take(kFrag64x128);
   L.Pf = take(kFrag64x128);
-  L.KbT = take(kFrag64x128);
+  L.KbT = take_qk(kFrag64x128);
   L.Uacc = take(kAcc64x128);
   L.Oacc = take(kAcc64x128);
   L.gam = take(kGamma);
   L.fwd_bytes = off;
-  L.Kb = take(kFrag64x128);
+  L.Kb = take_qk(kFrag64x128);
   L.WTn = take(kFrag64x128);
-  L.QGT = take(kFrag64x128);
+  L.QGT = take_qk(kFrag64x128);
   L.MTs = take(kFrag64x64);
   L.Tt = take(kFrag64x64);
   L.Et = take(kFrag64x64);
@@ -326,7 +333,7 @@ int32_t fwd_impl(int32_t variant, const gdr_problem *p, uint16_t *o, float *ht, 
   if ((rc = hip_status(timed(0, st, [&] { return gdr::launch_fwd_prep(variant == GDR_GDN, q, w, save, out, st); }),
                        "prep launch")))
     return rc;
-  if ((rc = hip_status(timed(1, st, [&] { return gdr::launch_fwd_walk(q, w, out ? o : nullptr, ht, save, out, st); }), "walk launch")))
+  if ((rc = hip_status(timed(1, st, [&] { return gdr::launch_fwd_walk(variant == GDR_GDN, q, w, out ? o : nullptr, ht, save, out, st); }), "walk launch")))
     return rc;
   g_last_error.clear();
   return GDR_OK;
@@ -345,7 +352,7 @@ int32_t bwd_impl(int32_t variant, const gdr_problem *p, const uint16_t *dout, co
   const gdr::Problem q = to_internal(p);
   const gdr::Workspace w = bind(L, ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = hip_status(timed(2, st, [&] { return gdr::launch_bwd_walk(q, w, dout, dht, dh0, st); }),
+  if ((rc = hip_status(timed(2, st, [&] { return gdr::launch_bwd_walk(variant == GDR_GDN, q, w, dout, dht, dh0, st); }),
                        "adjoint walk launch")))
     return rc;
   if ((rc = hip_status(

@@ -38,7 +38,9 @@ namespace gdr {
 // start, dout as given; second half: identity start, dout = 0); pass 2 starts
 // segment s from dht carried back
 // through segments P_d - 1 .. s + 1 and writes the tapes; dh0 comes from segment 0.
-template <int MODE = MODE_WALK>
+// SG: one gate per row (GDN): the Q/K head's scale Q^T and K fragments, with dout's
+// rows scaled by exp(G_r) for the first and K dS' rows by exp(G_last - G_r).
+template <int MODE = MODE_WALK, bool SG = false>
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
@@ -53,7 +55,8 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
   const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int vcol = 16 * sl + lr;
-  const size_t Hv = p.Hv;
+  const size_t Hv = p.Hv, Hqk = p.Hqk;
+  const int jq = j / (p.Hv / p.Hqk);  // the value head's Q/K head: slot of the shared fragments
   const uint32_t row_bytes = (uint32_t)(Hv * HD * 2);
   const s16x4 eye = eye16(lane);
 
@@ -91,14 +94,15 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
   float2 gq = make_float2(0.f, 0.f);  // gamma of keys 2*lane, 2*lane+1 (next chunk)
   if (nch > 0) {  // issued in the loop's own order: the counter waits at the loop head see one history
     const size_t u = (size_t)(first + nch - 1) * Hv + j;
+    const size_t uq = SG ? (size_t)(first + nch - 1) * Hqk + jq : u;  // KDA: H_qk = H_v, the unit's own slot
     gq = *reinterpret_cast<const float2 *>(w.gam + u * HD + 2 * lane);
     fetch_dout(nch - 1);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) QG[t >> 1][t & 1] = as_bf16x8(w.QGT[u * FRAG_64x128_U4 + t * 64 + lane]);
+    for (int t = 0; t < 16; ++t) QG[t >> 1][t & 1] = as_bf16x8(w.QGT[uq * FRAG_64x128_U4 + t * 64 + lane]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) MT[t >> 1][t & 1] = as_bf16x8(w.MTs[u * FRAG_64x64_U4 + t * 64 + lane]);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) Kb[t >> 2][t & 3] = as_bf16x8(w.Kb[u * FRAG_64x128_U4 + t * 64 + lane]);
+    for (int t = 0; t < 16; ++t) Kb[t >> 2][t & 3] = as_bf16x8(w.Kb[uq * FRAG_64x128_U4 + t * 64 + lane]);
 #pragma unroll
     for (int t = 0; t < 16; ++t) WT[t >> 1][t & 1] = as_bf16x8(w.WTn[u * FRAG_64x128_U4 + t * 64 + lane]);
   }
@@ -106,15 +110,23 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
   for (int n = nch - 1; n >= 0; --n) {
     const size_t u = (size_t)(first + n) * Hv + j;
     const size_t un = n > 0 ? u - Hv : u;
+    const size_t uqn = SG ? (size_t)(n > 0 ? first + n - 1 : first + n) * Hqk + jq : un;
 
     *reinterpret_cast<float2 *>(sgam + 2 * lane) = gq;
     float4 gm[8];
+    if constexpr (SG) {
+      const float gl = sgam[CH - 1];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(sgam + 16 * mt + 4 * lg);
+      for (int mt = 0; mt < 8; ++mt) gm[mt] = make_float4(gl, gl, gl, gl);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(sgam + 16 * mt + 4 * lg);
+    }
     gq = *reinterpret_cast<const float2 *>(w.gam + un * HD + 2 * lane);
 
-    // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns)
-    bf16x8 dOb[2];
+    // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns);
+    // dOq: the operand of the (q Gamma)^T product (SG: dout's rows scaled by exp(G_r))
+    bf16x8 dOb[2], dOq[2];
     {
       f32x4 dO[4];
 #pragma unroll
@@ -127,6 +139,15 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
       }
       dOb[0] = acc_pair_to_b(dO[0], dO[1]);
       dOb[1] = acc_pair_to_b(dO[2], dO[3]);
+      if constexpr (SG) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float4 e = *reinterpret_cast<const float4 *>(sgam + 16 * t + 4 * lg);
+          dO[t][0] *= e.x; dO[t][1] *= e.y; dO[t][2] *= e.z; dO[t][3] *= e.w;
+        }
+        dOq[0] = acc_pair_to_b(dO[0], dO[1]);
+        dOq[1] = acc_pair_to_b(dO[2], dO[3]);
+      }
     }
     fetch_dout(n > 0 ? n - 1 : 0);
 
@@ -152,28 +173,50 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        dS[mt] = mfma(QG[mt][kt], dOb[kt], dS[mt]);
-        QG[mt][kt] = as_bf16x8(w.QGT[un * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
+        dS[mt] = mfma(QG[mt][kt], SG ? dOq[kt] : dOb[kt], dS[mt]);
+        QG[mt][kt] = as_bf16x8(w.QGT[uqn * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
       }
 
     __builtin_amdgcn_sched_barrier(0);
     f32x4 dV[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) dV[mt] = zero4();
+    if constexpr (SG) {  // K dS' first, its rows scaled by exp(G_last - G_r), then scale M^T dout
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          dV[mt] = mfma(Kb[mt][kt], dSb[kt], dV[mt]);
+          Kb[mt][kt] = as_bf16x8(w.Kb[uqn * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
+        }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        dV[mt] = mfma(MT[mt][kt], dOb[kt], dV[mt]);
-        MT[mt][kt] = as_bf16x8(w.MTs[un * FRAG_64x64_U4 + (mt * 2 + kt) * 64 + lane]);
+        const float4 e = *reinterpret_cast<const float4 *>(sgam + CH + 16 * mt + 4 * lg);
+        dV[mt][0] *= e.x; dV[mt][1] *= e.y; dV[mt][2] *= e.z; dV[mt][3] *= e.w;
       }
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        dV[mt] = mfma(Kb[mt][kt], dSb[kt], dV[mt]);
-        Kb[mt][kt] = as_bf16x8(w.Kb[un * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
-      }
+        for (int mt = 0; mt < 4; ++mt) {
+          dV[mt] = mfma(MT[mt][kt], dOb[kt], dV[mt]);
+          MT[mt][kt] = as_bf16x8(w.MTs[un * FRAG_64x64_U4 + (mt * 2 + kt) * 64 + lane]);
+        }
+    } else {  // dV = scale M^T dout + Kbar dS'
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          dV[mt] = mfma(MT[mt][kt], dOb[kt], dV[mt]);
+          MT[mt][kt] = as_bf16x8(w.MTs[un * FRAG_64x64_U4 + (mt * 2 + kt) * 64 + lane]);
+        }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          dV[mt] = mfma(Kb[mt][kt], dSb[kt], dV[mt]);
+          Kb[mt][kt] = as_bf16x8(w.Kb[uqn * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
+        }
+    }
     if (MODE == MODE_WALK) {  // dVn^T rows of this slice's columns: 8 consecutive chunk rows 32h + 8lg.. per lane
       u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 8 * lg;
 #pragma unroll
@@ -220,7 +263,7 @@ constexpr int WGB_SLOT = WGB_TILES * FRAG_TILE_U4 * 16 + HD * 4;  // bytes per r
 constexpr int WGB_SMEM = 2 * WGB_SLOT;
 constexpr int WGB_NW = 4;
 
-template <int NW>
+template <int NW, bool SG = false>
 __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspace w, const u16 *dout,
                                                               const float *dht, float *dh0) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -235,7 +278,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
   const int sl = NW * half + wv;  // this wavefront's slice
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int vcol = 16 * sl + lr;
-  const size_t Hv = p.Hv;
+  const size_t Hv = p.Hv, Hqk = p.Hqk;
+  const int jq = j / (p.Hv / p.Hqk);  // the value head's Q/K head: slot of the shared fragments
   const uint32_t row_bytes = (uint32_t)(Hv * HD * 2);
   const s16x4 eye = eye16(lane);
   constexpr int PER = WGB_TILES / NW;
@@ -259,16 +303,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
     for (int h = 0; h < 2; ++h) pdo[h] = src.get16((uint32_t)(32 * h + prow) * row_bytes + 2 * pcol);
   };
-  auto tile_src = [&](size_t u, int t) -> const uint4 * {
-    if (t < 16) return w.QGT + u * FRAG_64x128_U4 + t * 64 + lane;
+  // tile t of unit u: (q Gamma)^T and Kbar from the Q/K head's slot uq, M^T and -W^T the unit's
+  auto tile_src = [&](size_t u, size_t uq, int t) -> const uint4 * {
+    if (t < 16) return w.QGT + uq * FRAG_64x128_U4 + t * 64 + lane;
     if (t < 24) return w.MTs + u * FRAG_64x64_U4 + (t - 16) * 64 + lane;
-    return (t < 40 ? w.Kb : w.WTn) + u * FRAG_64x128_U4 + ((t - 24) & 15) * 64 + lane;
+    return (t < 40 ? w.Kb + uq * FRAG_64x128_U4 : w.WTn + u * FRAG_64x128_U4) + ((t - 24) & 15) * 64 + lane;
   };
   u32x4 stage[PER];
   float4 gst = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto fetch = [&](size_t u) {
+  // chunk c's operands (u = c H_v + j; KDA: H_qk = H_v, the unit's own slot)
+  auto fetch = [&](int c, size_t u) {
+    const size_t uq = SG ? (size_t)c * Hqk + jq : u;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) stage[i] = __builtin_bit_cast(u32x4, *tile_src(u, wv + NW * i));
+    for (int i = 0; i < PER; ++i) stage[i] = __builtin_bit_cast(u32x4, *tile_src(u, uq, wv + NW * i));
     if (wv == 0 && lane < 32) gst = *reinterpret_cast<const float4 *>(w.gam + u * HD + 4 * lane);
   };
   auto put = [&](int slot) {
@@ -282,7 +329,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
   };
 
   if (nch > 0) {
-    fetch((size_t)(first + nch - 1) * Hv + j);
+    fetch(first + nch - 1, (size_t)(first + nch - 1) * Hv + j);
     fetch_dout(nch - 1);
     put(0);
   }
@@ -292,14 +339,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
     const size_t u = (size_t)(first + n) * Hv + j;
     const size_t un = n > 0 ? u - Hv : u;
     const int slot = it & 1;
-    if (n > 0) fetch(un);
+    if (n > 0) fetch(first + n - 1, un);
 
+    const float *sg = reinterpret_cast<const float *>(smem + slot * WGB_SLOT + WGB_TILES * 1024);
     float4 gm[8];
+    if constexpr (SG) {
+      const float gl = sg[CH - 1];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      gm[mt] = *reinterpret_cast<const float4 *>(smem + slot * WGB_SLOT + WGB_TILES * 1024 + (16 * mt + 4 * lg) * 4);
+      for (int mt = 0; mt < 8; ++mt) gm[mt] = make_float4(gl, gl, gl, gl);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(sg + 16 * mt + 4 * lg);
+    }
 
-    bf16x8 dOb[2];  // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns)
+    // dout as B operand (k: chunk rows in kwalk order, n: this slice's columns); dOq:
+    // the operand of the (q Gamma)^T product (SG: dout's rows scaled by exp(G_r))
+    bf16x8 dOb[2], dOq[2];
     {
       f32x4 dO[4];
 #pragma unroll
@@ -311,6 +366,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
       }
       dOb[0] = acc_pair_to_b(dO[0], dO[1]);
       dOb[1] = acc_pair_to_b(dO[2], dO[3]);
+      if constexpr (SG) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float4 e = *reinterpret_cast<const float4 *>(sg + 16 * t + 4 * lg);
+          dO[t][0] *= e.x; dO[t][1] *= e.y; dO[t][2] *= e.z; dO[t][3] *= e.w;
+        }
+        dOq[0] = acc_pair_to_b(dO[0], dO[1]);
+        dOq[1] = acc_pair_to_b(dO[2], dO[3]);
+      }
     }
     fetch_dout(n > 0 ? n - 1 : 0);
 
@@ -331,19 +395,35 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(frag(slot, mt * 2 + kt), dOb[kt], dS[mt]);
+      for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(frag(slot, mt * 2 + kt), SG ? dOq[kt] : dOb[kt], dS[mt]);
 
     f32x4 dV[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) dV[mt] = zero4();
+    if constexpr (SG) {  // K dS' first, its rows scaled by exp(G_last - G_r), then scale M^T dout
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 16 + mt * 2 + kt), dOb[kt], dV[mt]);
+        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 24 + mt * 4 + kt), dSb[kt], dV[mt]);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int mt = 0; mt < 4; ++mt) {
+        const float4 e = *reinterpret_cast<const float4 *>(sg + CH + 16 * mt + 4 * lg);
+        dV[mt][0] *= e.x; dV[mt][1] *= e.y; dV[mt][2] *= e.z; dV[mt][3] *= e.w;
+      }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 24 + mt * 4 + kt), dSb[kt], dV[mt]);
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 16 + mt * 2 + kt), dOb[kt], dV[mt]);
+    } else {  // dV = scale M^T dout + Kbar dS'
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 16 + mt * 2 + kt), dOb[kt], dV[mt]);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 24 + mt * 4 + kt), dSb[kt], dV[mt]);
+    }
     {  // dVn^T rows of this slice's columns: 8 consecutive chunk rows 32h + 8lg.. per lane
       u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 8 * lg;
 #pragma unroll
@@ -1659,22 +1739,28 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
 }
 
 
-hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const u16 *dout, const float *dht, float *dh0,
-                           hipStream_t st) {
-  if (p.N * p.Hv == 0) return hipSuccess;
+template <bool SG>
+static hipError_t launch_bwd_walk_t(const Problem &p, const Workspace &w, const u16 *dout, const float *dht,
+                                    float *dh0, hipStream_t st) {
   const int chains = walk_chains(p, false);
   if (p.P > 1) {  // pass 1: the segments' carries
-    const int g1 = ((walk_chains(p, true) + 7) / 8) * 64;
-    bwd_walk_kernel<MODE_CARRY><<<2 * g1, 64, 0, st>>>(p, w, dout, nullptr, nullptr);
+    const int g1 = walk_grid(walk_chains(p, true), 1);
+    bwd_walk_kernel<MODE_CARRY, SG><<<2 * g1, 64, 0, st>>>(p, w, dout, nullptr, nullptr);
   }
   if (walk_uses_rings(p, compute_units())) {
-    hipError_t e = set_dynamic_lds_once((const void *)bwd_walk_wg_kernel<WGB_NW>, WGB_SMEM);
+    hipError_t e = set_dynamic_lds_once((const void *)bwd_walk_wg_kernel<WGB_NW, SG>, WGB_SMEM);
     if (e != hipSuccess) return e;
-    bwd_walk_wg_kernel<WGB_NW><<<((chains + 7) / 8) * 64 / WGB_NW, 64 * WGB_NW, WGB_SMEM, st>>>(p, w, dout, dht, dh0);
+    bwd_walk_wg_kernel<WGB_NW, SG><<<walk_grid(chains, WGB_NW), 64 * WGB_NW, WGB_SMEM, st>>>(p, w, dout, dht, dh0);
     return hipGetLastError();
   }
-  bwd_walk_kernel<MODE_WALK><<<((chains + 7) / 8) * 64, 64, 0, st>>>(p, w, dout, dht, dh0);
+  bwd_walk_kernel<MODE_WALK, SG><<<walk_grid(chains, 1), 64, 0, st>>>(p, w, dout, dht, dh0);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_walk(bool gdn, const Problem &p, const Workspace &w, const u16 *dout, const float *dht,
+                           float *dh0, hipStream_t st) {
+  if (p.N * p.Hv == 0) return hipSuccess;
+  return gdn ? launch_bwd_walk_t<true>(p, w, dout, dht, dh0, st) : launch_bwd_walk_t<false>(p, w, dout, dht, dh0, st);
 }
 
 // Persistent gradient kernels: one workgroup per compute unit (the LDS map allows

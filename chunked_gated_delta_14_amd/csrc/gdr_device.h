@@ -242,7 +242,7 @@ struct ChunkTable {
 // and the wavefront's group of NS adjacent 16-column value slices from the
 // block index, placing all groups of one chain on the same XCD (block ids are
 // dealt to the 8 XCDs round-robin), so they share that XCD's L2 copy of the
-// chain's per-chunk operands.  The grid is ceil(chains / 8) * 64 / NS blocks.
+// chain's per-chunk operands.  The grid is walk_grid(chains, NS) blocks.
 template <int NS = 1>
 __device__ __forceinline__ void walk_block(int b, int &chain, int &group) {
   constexpr int G = 8 / NS;  // slice groups per chain

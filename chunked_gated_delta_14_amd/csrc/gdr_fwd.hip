@@ -14,6 +14,13 @@
 //     Vn = U - W S,   o = Oi + P S,   S <- diag(gamma) S + Kbar^T Vn.
 // (o = scale[(q exp G) S + M Vn] regrouped so that the output needs no second
 // pass over q, k and the gates.)
+// With one gate per row (GDN) exp(G) is a row scale: Kbar = diag(exp(G_last - G)) K
+// and (q exp G)^T = Q^T diag(exp G).  The walks then take the Q/K head's plain k,
+// k^T and scale q^T fragments, stored once per (chunk, Q/K head) for the group's
+// value heads, and apply the row scales to the operands they form themselves
+// (Vn before the state update, dout and K dS' in the adjoint walk); the gamma
+// slot of a GDN unit holds exp(G_r) (rows 0..63) and exp(G_last - G_r) (rows
+// 64..127), and gamma = exp(G_63), padded rows keeping the last row's gate.
 #include "gdr_device.h"
 #include "gdr_kernels.h"
 #include "gdr_walk.h"
@@ -57,7 +64,8 @@ constexpr int P_T = P_E + CH * SP * 4;     // T fp32 [64][SP]
 constexpr int P_M = P_T + CH * SP * 4;     // M bf16 [64][MP]
 constexpr int P_B = P_M + CH * MP * 2;     // beta [64]
 constexpr int P_D = P_B + 64 * 4;          // D_IJ [6][128]
-constexpr int P_SMEM = P_D + 768 * 4;
+constexpr int P_EG = P_D + 768 * 4;       // exp(G_r) [64] (scalar gate: P's row scale)
+constexpr int P_SMEM = P_EG + 64 * 4;
 static_assert(P_KFI + CH * GP * 4 <= P_E, "prep LDS map");
 
 __device__ __forceinline__ uint32_t pack2bf(float a, float b) {
@@ -158,6 +166,13 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   u16 *sM = reinterpret_cast<u16 *>(smem + P_M);
   float *sB = reinterpret_cast<float *>(smem + P_B);
   float *sD = reinterpret_cast<float *>(smem + P_D);
+  float *sEG = reinterpret_cast<float *>(smem + P_EG);
+  // fragments shared by a Q/K head's value heads (K^T, K, scale Q^T with one gate per
+  // row; Kbar^T, Kbar, scale (Q Gamma)^T per channel, where H_qk = H_v): slot of
+  // (chunk, Q/K head), written by the group's first value head
+  const int grp = p.Hv / p.Hqk;
+  const bool lead = j % grp == 0;
+  const size_t uq = (size_t)chunk * p.Hqk + j / grp;
 
   // ---- 1. thread = (channel octet o, row pair pr): rows 2pr, 2pr+1 of
   // channels 8o..8o+7, read as 16-byte pieces.  The 32 lanes of a half
@@ -165,6 +180,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   // reference gates are in-wave shuffles. ----
   const int o = tid >> 5, pr = tid & 31, c0 = 8 * o, rp = 2 * pr;
   uint32_t pkBKG[8], pkBV[8], pkQG[8], pkKL[8];  // channel c0+ii: rows rp, rp+1 as a bf16 pair
+  float rowg[2], rowl[2];  // one gate per row: exp(G_r), exp(G_last - G_r) of rows rp, rp+1
   {
     constexpr int NG = SCALAR ? 1 : 8;  // gate values per row held by a thread
     const bf16x8 *kx = in.k, *qx = in.q, *vx = in.v;
@@ -206,8 +222,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         rk[h] = rsqrtf(tk + L2NORM_EPS);
       }
       // kept for the backward, once per (token, Q/K head): by the group's first value head
-      const int grp = p.Hv / p.Hqk;
-      if (save && o == 0 && j % grp == 0) {
+      if (save && o == 0 && lead) {
         const int start = tb.start[chunk];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -253,7 +268,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 #pragma unroll
       for (int cc = (SCALAR ? 0 : ic); cc < (SCALAR ? 8 : ic + 1); ++cc) {
         if (pr < 6) sD[pr * 128 + c0 + cc] = e;
-        else if (pr == 6) w.gam[u * HD + c0 + cc] = e;
+        else if (pr == 6 && !SCALAR) w.gam[u * HD + c0 + cc] = e;
       }
     }
 #pragma unroll
@@ -275,13 +290,25 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         const float el = Fi * elr[ic];  // exp(G_last - G_r)
         pkBKG[ii] |= (uint32_t)f2bf(bt[h] * kv * eg) << sh;
         pkBV[ii] |= (uint32_t)f2bf(bt[h] * vv) << sh;
-        pkQG[ii] |= (uint32_t)f2bf(scale * qv * eg) << sh;
-        pkKL[ii] |= (uint32_t)f2bf(kv * el) << sh;
+        pkQG[ii] |= (uint32_t)f2bf(SCALAR ? scale * qv : scale * qv * eg) << sh;
+        pkKL[ii] |= (uint32_t)f2bf(SCALAR ? kv : kv * el) << sh;
+        if (ii == 0) {
+          rowg[h] = eg;
+          rowl[h] = el;
+        }
       }
       *reinterpret_cast<bf16x8 *>(sKF + r * KP + c0) = kf;
       *reinterpret_cast<bf16x8 *>(sQF + r * KP + c0) = qf;
       *reinterpret_cast<float4 *>(sKFi + r * GP + c0) = make_float4(kfi[0], kfi[1], kfi[2], kfi[3]);
       *reinterpret_cast<float4 *>(sKFi + r * GP + c0 + 4) = make_float4(kfi[4], kfi[5], kfi[6], kfi[7]);
+    }
+  }
+  if (SCALAR && o == 0) {  // the row scales: P's (LDS) and the walks' (gamma slot)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sEG[rp + h] = rowg[h];
+      w.gam[u * HD + rp + h] = rowg[h];
+      w.gam[u * HD + CH + rp + h] = rowl[h];
     }
   }
   lds_barrier();
@@ -449,13 +476,14 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int mt = 2 * kp + h, r = 16 * mt + lr;
+      const float eg = SCALAR ? sEG[r] : 1.f;  // sQG holds scale q without the row's gate
       f32x4 pt[2];
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int cc = 16 * (2 * cg + n) + 4 * lg + jj;
-          pt[n][jj] = bf2f(sQG[cc * CTP + r]) - scale * PT[n][h][jj];
+          pt[n][jj] = bf2f(sQG[cc * CTP + r]) * eg - scale * PT[n][h][jj];
         }
       w.Pf[u * FRAG_64x128_U4 + (mt * 4 + cg) * 64 + lane] = as_u4(acc_pair_to_b(pt[0], pt[1]));
 #pragma unroll
@@ -467,17 +495,17 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     }
   }
 
-  // ---- remaining walk operands from the column-form tiles ----
-  for (int slot = tid; slot < 1024; slot += PNT) {
+  // ---- remaining walk operands from the column-form tiles (shared by the group) ----
+  for (int slot = tid; lead && slot < 1024; slot += PNT) {
     const int tile = slot >> 6, ln = slot & 63, r_ = ln & 15, g_ = ln >> 4;
     {  // rows: key (16 mt + r_), k: chunk (32 kt + kwalk): two 4-row runs of a column-form row
       const int mt = tile >> 1, kt = tile & 1, key = 16 * mt + r_;
       const int o = key * CTP + 32 * kt + 4 * g_;
       const uint2 a = *reinterpret_cast<const uint2 *>(sKL + o), b = *reinterpret_cast<const uint2 *>(sKL + o + 16);
-      w.KbT[u * FRAG_64x128_U4 + slot] = make_uint4(a.x, a.y, b.x, b.y);
+      w.KbT[uq * FRAG_64x128_U4 + slot] = make_uint4(a.x, a.y, b.x, b.y);
       if (save) {
         const uint2 qa = *reinterpret_cast<const uint2 *>(sQG + o), qb = *reinterpret_cast<const uint2 *>(sQG + o + 16);
-        w.QGT[u * FRAG_64x128_U4 + slot] = make_uint4(qa.x, qa.y, qb.x, qb.y);
+        w.QGT[uq * FRAG_64x128_U4 + slot] = make_uint4(qa.x, qa.y, qb.x, qb.y);
       }
     }
     if (save) {  // rows: chunk (16 mt + r_), k: key (32 kt + kwalk)
@@ -485,7 +513,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
       bf16x8 kb;
 #pragma unroll
       for (int ii = 0; ii < 8; ++ii) kb[ii] = __builtin_bit_cast(__bf16, sKL[(32 * kt + kwalk(g_, ii)) * CTP + row]);
-      w.Kb[u * FRAG_64x128_U4 + slot] = as_u4(kb);
+      w.Kb[uq * FRAG_64x128_U4 + slot] = as_u4(kb);
     }
   }
   if (save && tid < CH * CH / 8) {  // T^T, bf16 row-major, for the gradient kernel
@@ -559,8 +587,9 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
 constexpr int WALK_NS = 1;
 
 // MODE_CARRY launches run the carry walks in the first half of the grid and the
-// transfer walks in the second, so the two proceed together.
-template <int NS, bool SAVE, bool OUT, int MODE = MODE_WALK>
+// transfer walks in the second, so the two proceed together.  SG: one gate per row
+// (GDN): the Q/K head's K^T fragments with Vn's rows scaled by exp(G_last - G_r).
+template <int NS, bool SAVE, bool OUT, int MODE = MODE_WALK, bool SG = false>
 __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u16 *o, float *ht) {
   static_assert(MODE == MODE_WALK || (NS == 1 && !SAVE && !OUT), "pass-1 walks carry one slice, no outputs");
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
@@ -574,7 +603,8 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
   const int tok0 = p.cu[d] + CH * (first - wc.first_doc), tok1 = p.cu[d + 1];
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int sl0 = NS * grp;  // first slice of this wavefront
-  const size_t Hv = p.Hv;
+  const size_t Hv = p.Hv, Hqk = p.Hqk;
+  const int jq = j / (p.Hv / p.Hqk);  // the value head's Q/K head: slot of the shared K fragments
   const uint32_t row_bytes = (uint32_t)(Hv * HD * 2);
   const s16x4 eye = eye16(lane);
 
@@ -619,21 +649,29 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
 #pragma unroll
       for (int t = 0; t < 16; ++t) Pf[t >> 2][t & 3] = as_bf16x8(w.Pf[u * FRAG_64x128_U4 + t * 64 + lane]);
     }
+    const size_t uq = SG ? (size_t)first * Hqk + jq : u;  // KDA: H_qk = H_v, the unit's own slot
 #pragma unroll
-    for (int t = 0; t < 16; ++t) KT[t >> 1][t & 1] = as_bf16x8(w.KbT[u * FRAG_64x128_U4 + t * 64 + lane]);
+    for (int t = 0; t < 16; ++t) KT[t >> 1][t & 1] = as_bf16x8(w.KbT[uq * FRAG_64x128_U4 + t * 64 + lane]);
   }
 
   for (int n = 0; n < nch; ++n) {
     const size_t u = (size_t)(first + n) * Hv + j;
     const size_t un = n + 1 < nch ? u + Hv : u;
+    const size_t uqn = SG ? (size_t)(n + 1 < nch ? first + n + 1 : first + n) * Hqk + jq : un;
     const int row0 = tok0 + CH * n;
     const int len = min(CH, tok1 - row0);
 
     // This chunk's gate factors, laid out as each lane's accumulator rows need them.
     *reinterpret_cast<float2 *>(sgam + 2 * lane) = gq;
     float4 gm[8];
+    if constexpr (SG) {
+      const float gl = sgam[CH - 1];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(sgam + 16 * mt + 4 * lg);
+      for (int mt = 0; mt < 8; ++mt) gm[mt] = make_float4(gl, gl, gl, gl);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(sgam + 16 * mt + 4 * lg);
+    }
     gq = *reinterpret_cast<const float2 *>(w.gam + un * HD + 2 * lane);
 
     bf16x8 Sb[NS][4];
@@ -689,11 +727,25 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
         }
     }
 
-    bf16x8 Vb[NS][2];
+    bf16x8 Vb[NS][2], Vs[NS][2];  // Vn; the state update's operand (SG: Vn's rows scaled)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       Vb[s][0] = acc_pair_to_b(Vn[s][0], Vn[s][1]);
       Vb[s][1] = acc_pair_to_b(Vn[s][2], Vn[s][3]);
+      if constexpr (SG) {
+        f32x4 x[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const float4 e = *reinterpret_cast<const float4 *>(sgam + CH + 16 * mt + 4 * lg);
+          x[mt][0] = Vn[s][mt][0] * e.x; x[mt][1] = Vn[s][mt][1] * e.y;
+          x[mt][2] = Vn[s][mt][2] * e.z; x[mt][3] = Vn[s][mt][3] * e.w;
+        }
+        Vs[s][0] = acc_pair_to_b(x[0], x[1]);
+        Vs[s][1] = acc_pair_to_b(x[2], x[3]);
+      } else {
+        Vs[s][0] = Vb[s][0];
+        Vs[s][1] = Vb[s][1];
+      }
     }
     if (OUT) {  // o rows of this chunk; rows past len fall outside the sink's range
       const RowSink ob(o + ((size_t)row0 * Hv + j) * HD + 16 * sl0, (uint32_t)len * row_bytes);
@@ -727,8 +779,8 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) S[s][mt] = mfma(KT[mt][kt], Vb[s][kt], S[s][mt]);
-        KT[mt][kt] = as_bf16x8(w.KbT[un * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
+        for (int s = 0; s < NS; ++s) S[s][mt] = mfma(KT[mt][kt], Vs[s][kt], S[s][mt]);
+        KT[mt][kt] = as_bf16x8(w.KbT[uqn * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
       }
   }
 
@@ -764,7 +816,7 @@ constexpr int WG_NW = 4;    // slice wavefronts per ring workgroup (two workgrou
 constexpr int WG_RING = 3;  // slots: the chunk in use, the next one, the one after in flight
 constexpr int WG_SMEM = WG_RING * WG_SLOT;
 
-template <bool SAVE, bool OUT, int NW>
+template <bool SAVE, bool OUT, int NW, bool SG = false>
 __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspace w, u16 *o, float *ht) {
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
@@ -777,7 +829,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sl0 = NW * half + wv;  // this wavefront's slice
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const size_t Hv = p.Hv;
+  const size_t Hv = p.Hv, Hqk = p.Hqk;
+  const int jq = j / (p.Hv / p.Hqk);  // the value head's Q/K head: slot of the shared K fragments
   const uint32_t row_bytes = (uint32_t)(Hv * HD * 2);
   const s16x4 eye = eye16(lane);
   constexpr int NT = OUT ? 48 : 32;  // tiles fetched per chunk (P only with the output)
@@ -794,18 +847,20 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
     apply_carry(S, cb, cb + HD * HD, 16 * sl0, lane);
   }
 
-  // tile t of a chunk: -W (0..15), Kbar^T (16..31), P (32..47); wavefront w takes t = w + 8i
-  auto tile_src = [&](size_t u, int t) -> const uint4 * {
+  // tile t of chunk c: -W (0..15), Kbar^T (16..31, the Q/K head's), P (32..47); wavefront w
+  // takes t = w + 8i
+  auto tile_src = [&](int c, int t) -> const uint4 * {
+    const size_t u = SG && t >= 16 && t < 32 ? (size_t)c * Hqk + jq : (size_t)c * Hv + j;
     const uint4 *base = t < 16 ? w.WfN : (t < 32 ? w.KbT : w.Pf);
     return base + u * FRAG_64x128_U4 + (t & 15) * 64 + lane;
   };
   // two register stage sets: the chunk after next is fetched while the next one waits for its slot
   u32x4 stA[PER], stB[PER];
   float4 gA = make_float4(0.f, 0.f, 0.f, 0.f), gB = gA;
-  auto fetch = [&](size_t u, u32x4 (&st)[PER], float4 &gs) {
+  auto fetch = [&](int c, u32x4 (&st)[PER], float4 &gs) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) st[i] = __builtin_bit_cast(u32x4, *tile_src(u, wv + NW * i));
-    if (wv == 0 && lane < 32) gs = *reinterpret_cast<const float4 *>(w.gam + u * HD + 4 * lane);
+    for (int i = 0; i < PER; ++i) st[i] = __builtin_bit_cast(u32x4, *tile_src(c, wv + NW * i));
+    if (wv == 0 && lane < 32) gs = *reinterpret_cast<const float4 *>(w.gam + ((size_t)c * Hv + j) * HD + 4 * lane);
   };
   auto put = [&](int slot, const u32x4 (&st)[PER], const float4 &gs) {
     unsigned char *base = smem + slot * WG_SLOT;
@@ -820,8 +875,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
   uint2 Ua[4], Oa[4];
   if (nch > 0) {
     const size_t u = (size_t)first * Hv + j;
-    fetch(u, stA, gA);
-    if (nch > 1) fetch(u + Hv, stB, gB);
+    fetch(first, stA, gA);
+    if (nch > 1) fetch(first + 1, stB, gB);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const size_t off = u * ACC_64x128_U16 + ((sl0 * 4 + mt) * 64 + lane) * 4;
@@ -841,12 +896,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
     const int slot = n % WG_RING;
     const int row0 = tok0 + CH * n;
     const int len = min(CH, tok1 - row0);
-    if (n + 2 < nch) fetch(u + 2 * Hv, st_after, g_after);
+    if (n + 2 < nch) fetch(first + n + 2, st_after, g_after);
 
+    const float *sg = reinterpret_cast<const float *>(smem + slot * WG_SLOT + WG_TILES * 1024);
     float4 gm[8];
+    if constexpr (SG) {
+      const float gl = sg[CH - 1];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      gm[mt] = *reinterpret_cast<const float4 *>(smem + slot * WG_SLOT + WG_TILES * 1024 + (16 * mt + 4 * lg) * 4);
+      for (int mt = 0; mt < 8; ++mt) gm[mt] = make_float4(gl, gl, gl, gl);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) gm[mt] = *reinterpret_cast<const float4 *>(sg + 16 * mt + 4 * lg);
+    }
 
     bf16x8 Sb[4];
 #pragma unroll
@@ -883,9 +944,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
         for (int mt = 0; mt < 4; ++mt) Oc[mt] = mfma(frag(slot, 32 + mt * 4 + kt), Sb[kt], Oc[mt]);
     }
 
-    bf16x8 Vb[2];
+    bf16x8 Vb[2], Vs[2];  // Vn; the state update's operand (SG: Vn's rows scaled)
     Vb[0] = acc_pair_to_b(Vn[0], Vn[1]);
     Vb[1] = acc_pair_to_b(Vn[2], Vn[3]);
+    if constexpr (SG) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float4 e = *reinterpret_cast<const float4 *>(sg + CH + 16 * mt + 4 * lg);
+        Vn[mt][0] *= e.x; Vn[mt][1] *= e.y; Vn[mt][2] *= e.z; Vn[mt][3] *= e.w;
+      }
+      Vs[0] = acc_pair_to_b(Vn[0], Vn[1]);
+      Vs[1] = acc_pair_to_b(Vn[2], Vn[3]);
+    } else {
+      Vs[0] = Vb[0];
+      Vs[1] = Vb[1];
+    }
     if (OUT) {  // o rows of this chunk; rows past len fall outside the sink's range
       const RowSink ob(o + ((size_t)row0 * Hv + j) * HD + 16 * sl0, (uint32_t)len * row_bytes);
 #pragma unroll
@@ -908,7 +981,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) S[mt] = mfma(frag(slot, 16 + mt * 2 + kt), Vb[kt], S[mt]);
+      for (int mt = 0; mt < 8; ++mt) S[mt] = mfma(frag(slot, 16 + mt * 2 + kt), Vs[kt], S[mt]);
 
     if (n + 1 < nch) put((n + 1) % WG_RING, st_next, g_next);
     lds_barrier();
@@ -927,7 +1000,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
   }
 }
 
-static int walk_grid(int chains, int ns) { return ((chains + 7) / 8) * 64 / ns; }
 
 int compute_units() {
   static int cached[64] = {0};
@@ -958,35 +1030,43 @@ hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool 
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, u16 *o, float *ht, bool save, bool out,
-                           hipStream_t st) {
-  if (p.N * p.Hv == 0) return hipSuccess;
+template <bool SG>
+static hipError_t launch_fwd_walk_t(const Problem &p, const Workspace &w, u16 *o, float *ht, bool save, bool out,
+                                    hipStream_t st) {
   constexpr int NS = WALK_NS;
   static_assert(NS == 1, "segmented walks form entering states per 16-column slice");
   const int chains = walk_chains(p, false);
   if (p.P > 1) {  // pass 1: the segments' carries
     const int g1 = walk_grid(walk_chains(p, true), 1);
-    fwd_walk_kernel<1, false, false, MODE_CARRY><<<2 * g1, 64, 0, st>>>(p, w, nullptr, nullptr);
+    fwd_walk_kernel<1, false, false, MODE_CARRY, SG><<<2 * g1, 64, 0, st>>>(p, w, nullptr, nullptr);
   }
   if (walk_uses_rings(p, compute_units())) {  // slice wavefronts of a chain in workgroups of WG_NW
     constexpr int NW = WG_NW;
-    const void *fn = save ? (out ? (const void *)fwd_walk_wg_kernel<true, true, NW> : (const void *)fwd_walk_wg_kernel<true, false, NW>)
-                          : (out ? (const void *)fwd_walk_wg_kernel<false, true, NW> : (const void *)fwd_walk_wg_kernel<false, false, NW>);
+    const void *fn = save ? (out ? (const void *)fwd_walk_wg_kernel<true, true, NW, SG>
+                                 : (const void *)fwd_walk_wg_kernel<true, false, NW, SG>)
+                          : (out ? (const void *)fwd_walk_wg_kernel<false, true, NW, SG>
+                                 : (const void *)fwd_walk_wg_kernel<false, false, NW, SG>);
     hipError_t e = set_dynamic_lds_once(fn, WG_SMEM);
     if (e != hipSuccess) return e;
     const int g = walk_grid(chains, NW);
-    if (save && out) fwd_walk_wg_kernel<true, true, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
-    else if (save) fwd_walk_wg_kernel<true, false, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
-    else if (out) fwd_walk_wg_kernel<false, true, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
-    else fwd_walk_wg_kernel<false, false, NW><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
+    if (save && out) fwd_walk_wg_kernel<true, true, NW, SG><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
+    else if (save) fwd_walk_wg_kernel<true, false, NW, SG><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
+    else if (out) fwd_walk_wg_kernel<false, true, NW, SG><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
+    else fwd_walk_wg_kernel<false, false, NW, SG><<<g, 64 * NW, WG_SMEM, st>>>(p, w, o, ht);
     return hipGetLastError();
   }
   const int grid = walk_grid(chains, NS);
-  if (save && out) fwd_walk_kernel<NS, true, true><<<grid, 64, 0, st>>>(p, w, o, ht);
-  else if (save) fwd_walk_kernel<NS, true, false><<<grid, 64, 0, st>>>(p, w, o, ht);
-  else if (out) fwd_walk_kernel<NS, false, true><<<grid, 64, 0, st>>>(p, w, o, ht);
-  else fwd_walk_kernel<NS, false, false><<<grid, 64, 0, st>>>(p, w, o, ht);
+  if (save && out) fwd_walk_kernel<NS, true, true, MODE_WALK, SG><<<grid, 64, 0, st>>>(p, w, o, ht);
+  else if (save) fwd_walk_kernel<NS, true, false, MODE_WALK, SG><<<grid, 64, 0, st>>>(p, w, o, ht);
+  else if (out) fwd_walk_kernel<NS, false, true, MODE_WALK, SG><<<grid, 64, 0, st>>>(p, w, o, ht);
+  else fwd_walk_kernel<NS, false, false, MODE_WALK, SG><<<grid, 64, 0, st>>>(p, w, o, ht);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_walk(bool gdn, const Problem &p, const Workspace &w, u16 *o, float *ht, bool save, bool out,
+                           hipStream_t st) {
+  if (p.N * p.Hv == 0) return hipSuccess;
+  return gdn ? launch_fwd_walk_t<true>(p, w, o, ht, save, out, st) : launch_fwd_walk_t<false>(p, w, o, ht, save, out, st);
 }
 
 }  // namespace gdr

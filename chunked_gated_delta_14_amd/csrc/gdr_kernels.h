@@ -14,10 +14,13 @@ struct Workspace {
   // forward-walk operands (written by the prep kernel, read by the forward walk)
   uint4 *WfN;   // -W, A fragments (rows: chunk, k: key), 16 tiles
   uint4 *Pf;    // scale * (Q.Gamma - M W), A fragments (rows: chunk, k: key)
+  // KbT, Kb and QGT are indexed by (chunk, Q/K head), uq = chunk * H_qk + Q/K head
+  // (KDA: H_qk = H_v, so uq = u); with one gate per row (GDN) they hold K^T, K and
+  // scale * Q^T, shared by the group's value heads, and the walks apply the rows' gates
   uint4 *KbT;   // Kbar^T, A fragments (rows: key, k: chunk)
   uint16_t *Uacc;  // U in accumulator order, [u][vslice 8][mtile 4][lane 64][4]
   uint16_t *Oacc;  // scale * M U in accumulator order
-  float *gam;      // exp(G_last) per channel, [u][128]
+  float *gam;      // exp(G_last) per channel, [u][128]; GDN: exp(G_r), then exp(G_last - G_r), 64 rows each
   // backward-walk operands (written by the prep kernel with GDR_FWD_SAVE)
   uint4 *Kb;    // Kbar, A fragments (rows: chunk, k: key)
   uint4 *WTn;   // -W^T, A fragments (rows: key, k: chunk)
@@ -78,6 +81,11 @@ inline int walk_chains(const Problem &p, bool pass1) {
   const int segs = p.B > 0 ? p.B : p.P * p.N;
   return (pass1 ? segs - p.N : segs) * p.Hv;
 }
+// Blocks of a walk launch over `chains` chains (walk_block) with NS slices per
+// wavefront: every XCD gets ceil(chains / 8) chain slots, each chain 8 / NS
+// blocks of 64 threads (ring layouts divide by their wavefronts per block);
+// chains past the plan exit.
+inline int walk_grid(int chains, int ns) { return ((chains + 7) / 8) * 64 / ns; }
 constexpr int IN_QK_L2NORM = 1, IN_BETA_SIGMOID = 2;
 constexpr float L2NORM_EPS = 1e-6f;
 
@@ -90,9 +98,10 @@ hipError_t set_dynamic_lds_once(const void *kernel, int bytes);
 int compute_units();
 
 hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, bool out, hipStream_t st);
-hipError_t launch_fwd_walk(const Problem &p, const Workspace &w, uint16_t *o, float *ht, bool save, bool out,
-                           hipStream_t st);
-hipError_t launch_bwd_walk(const Problem &p, const Workspace &w, const uint16_t *dout, const float *dht,
+// gdn: one gate per row, the walks' K fragments shared by a Q/K head's value heads
+hipError_t launch_fwd_walk(bool gdn, const Problem &p, const Workspace &w, uint16_t *o, float *ht, bool save,
+                           bool out, hipStream_t st);
+hipError_t launch_bwd_walk(bool gdn, const Problem &p, const Workspace &w, const uint16_t *dout, const float *dht,
                            float *dh0, hipStream_t st);
 hipError_t launch_bwd_grad(bool gdn, const Problem &p, const Workspace &w, const uint16_t *dout,
                            uint16_t *dq, uint16_t *dk, uint16_t *dv, float *dg, void *dbeta,

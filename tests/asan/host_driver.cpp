@@ -21,8 +21,8 @@ static int g_launches = 0;
 namespace gdr {
 int compute_units() { return 256; }
 hipError_t launch_fwd_prep(bool, const Problem &, const Workspace &, bool, bool, hipStream_t) { ++g_launches; return hipErrorUnknown; }
-hipError_t launch_fwd_walk(const Problem &, const Workspace &, uint16_t *, float *, bool, bool, hipStream_t) { ++g_launches; return hipErrorUnknown; }
-hipError_t launch_bwd_walk(const Problem &, const Workspace &, const uint16_t *, const float *, float *, hipStream_t) { ++g_launches; return hipErrorUnknown; }
+hipError_t launch_fwd_walk(bool, const Problem &, const Workspace &, uint16_t *, float *, bool, bool, hipStream_t) { ++g_launches; return hipErrorUnknown; }
+hipError_t launch_bwd_walk(bool, const Problem &, const Workspace &, const uint16_t *, const float *, float *, hipStream_t) { ++g_launches; return hipErrorUnknown; }
 hipError_t launch_bwd_grad(bool, const Problem &, const Workspace &, const uint16_t *, uint16_t *, uint16_t *, uint16_t *, float *, void *, hipStream_t) { ++g_launches; return hipErrorUnknown; }
 }  // namespace gdr
 

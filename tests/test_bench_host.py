@@ -27,7 +27,12 @@ def test_kernel_bytes_per_unit():
     prep = bench.kernel_bytes("fwd_prep", T, H, H, NC, N, gdn=False)
     # inputs q, k, v, g, beta per token-head, then the walk operands and saved tapes per unit
     assert prep == 2 * T * H * 256 + T * H * 256 + T * H * 512 + T * H * 2 + units * (
-        bench.FWD_OPERANDS + bench.BWD_OPERANDS + bench.TE_SAVED)
+        bench.FWD_OPERANDS + bench.BWD_OPERANDS + bench.TE_SAVED + bench.SHARED_FWD + bench.SHARED_BWD)
+    # GDN: the K fragments once per (chunk, Q/K head), for 3 value heads each
+    Hqk, Hv = 16, 48
+    gprep = bench.kernel_bytes("fwd_prep", T, Hqk, Hv, NC, N, gdn=True)
+    kda_like = bench.kernel_bytes("fwd_prep", T, Hv, Hv, NC, N, gdn=True)
+    assert kda_like - gprep == 2 * T * (Hv - Hqk) * 256 + NC * (Hv - Hqk) * (bench.SHARED_FWD + bench.SHARED_BWD)
     grad = bench.kernel_bytes("bwd_grad", T, H, H, NC, N, gdn=False)
     per_unit = grad / units
     assert 280e3 < per_unit < 300e3  # ~173 KB + q, k read, ~80 KB written per full chunk

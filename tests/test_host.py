@@ -84,12 +84,15 @@ def test_workspace_bytes_monotone_and_aligned():
         fwd = gdr.workspace_bytes(gdr.GDR_KDA, 64 * nc, 1, nc, 4, 4, 128, 128, 0)
         assert full > fwd and full > prev
         prev = full
-    # GDN sizes by value heads, except the q/k inverse norms: one pair per (token, Q/K head)
+    # GDN sizes by value heads, except what a Q/K head's value heads share: the q/k
+    # inverse norms (one pair per (token, Q/K head)) and the walks' K^T, K and scale Q^T
+    # fragments (16 KB each per (chunk, Q/K head))
     a = gdr.workspace_bytes(gdr.GDR_GDN, 640, 1, 10, 16, 48, 128, 128, 1)
     b = gdr.workspace_bytes(gdr.GDR_KDA, 640, 1, 10, 48, 48, 128, 128, 1)
-    assert b - a == 640 * (48 - 16) * 2 * 4
-    assert gdr.workspace_bytes(gdr.GDR_GDN, 640, 1, 10, 16, 48, 128, 128, 0) == \
-        gdr.workspace_bytes(gdr.GDR_KDA, 640, 1, 10, 48, 48, 128, 128, 0)
+    assert b - a == 640 * (48 - 16) * 2 * 4 + 3 * 16384 * 10 * (48 - 16)
+    # forward only: the shared K^T fragments
+    assert gdr.workspace_bytes(gdr.GDR_KDA, 640, 1, 10, 48, 48, 128, 128, 0) - \
+        gdr.workspace_bytes(gdr.GDR_GDN, 640, 1, 10, 16, 48, 128, 128, 0) == 16384 * 10 * (48 - 16)
     assert gdr.workspace_bytes(gdr.GDR_KDA, 0, 1, 0, 1, 1, 128, 128, 1) == 0
 
 
