@@ -900,7 +900,7 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
       f32x4 aQ = zero4(), aY = zero4(), aK = zero4();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        __builtin_amdgcn_sched_barrier(0);  // one k-step of operands in flight at a time
+        if ((kt & 1) == 0) __builtin_amdgcn_sched_barrier(0);  // two k-steps of operands in flight at a time
         const int o = sw128(rA, 32 * kt + 8 * lg);
         const bf16x8 dor = ld8(sDo + o);
         aQ = mfma(rA < len ? dor : as_bf16x8(make_uint4(0, 0, 0, 0)), Sb[kt], aQ);
@@ -1038,7 +1038,7 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
       }
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        __builtin_amdgcn_sched_barrier(0);
+        if ((I & 1) == 0) __builtin_amdgcn_sched_barrier(0);  // two row blocks' operands in flight at a time
         const int rA = 16 * I + lr;
         f32x4 accM = zero4(), accA = zero4();
 #pragma unroll
@@ -1076,7 +1076,7 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
       for (int I = 0; I < 4; ++I) accT[I] = zero4();
 #pragma unroll
       for (int K = 0; K < 4; ++K) {
-        __builtin_amdgcn_sched_barrier(0);
+        if ((K & 1) == 0) __builtin_amdgcn_sched_barrier(0);  // two blocks' operands in flight at a time
         const int r0 = 16 * K + 4 * lg;
         const uint2 q4 = *reinterpret_cast<const uint2 *>(sQT + c * KQTP + r0);
         const uint2 k4 = *reinterpret_cast<const uint2 *>(sKT + c * KQTP + r0);
@@ -1157,13 +1157,17 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
     lds_barrier();  // dbeta partial sums complete; dM, dA and their transposes are dead
     // the next unit's dout and Vn rows into the tiles dM and dA occupied
     if (next >= 0) stage_grad_kda(p, w, dout, smem, next, false, true);
-    if (tid < 64 && tid < len) {
+    if (wave < 4) {  // dbeta of row 16w + lr: lane group lg adds slots 5lg..5lg+4, then the groups' sums
+      const int row = 16 * wave + lr;
       float x = 0.f;
 #pragma unroll
-      for (int k = 0; k < 20; ++k) x += sDB[k * 64 + tid];
-      if (p.inflags & IN_BETA_SIGMOID) x *= sB[tid] * (1.f - sB[tid]);  // to the logit
-      const size_t e = (size_t)(start + tid) * Hv + j;
-      reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
+      for (int k = 0; k < 5; ++k) x += sDB[(5 * lg + k) * 64 + row];
+      x = red_lg(x);
+      if (lg == 0 && row < len) {
+        if (p.inflags & IN_BETA_SIGMOID) x *= sB[row] * (1.f - sB[row]);  // to the logit
+        const size_t e = (size_t)(start + row) * Hv + j;
+        reinterpret_cast<u16 *>(dbeta)[e] = f2bf(x);
+      }
     }
     {  // dv: pairs of row blocks regrouped into 16-byte row pieces
       const uint32_t rowb = (uint32_t)(Hv * HD * 2);
