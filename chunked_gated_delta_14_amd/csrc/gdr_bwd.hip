@@ -555,6 +555,13 @@ struct GateT {
 // Butterfly sums without the LDS crossbar: each step adds the value of a partner
 // lane (lane ^ 1, ^ 2, then the neighbouring quad, then the other half row), and
 // since a + b == b + a every lane of a 16-lane row ends with the same bits.
+// Inclusive scan over the 64 lanes of a wavefront (lane l: sum of lanes 0..l):
+// each half by DPP, then the lower half's total added to the upper half.
+__device__ __forceinline__ float scan64(float x, int lane) {
+  x = scan32(x);
+  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  return lane >= 32 ? x + lo : x;
+}
 __device__ __forceinline__ float red16(float x) {  // sum over the 16 lanes sharing lg
   x += dpp_move<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
   x += dpp_move<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
@@ -1428,15 +1435,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
       }
     }
     {
-      if (tid < 64) {
-        float x = tid < len ? L.pBG[64 + tid] : 0.f;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float y = __shfl_up(x, o, 64);
-          if (tid >= o) x += y;
-        }
-        sG[tid] = x;
-      }
+      if (tid < 64) sG[tid] = scan64(tid < len ? L.pBG[64 + tid] : 0.f, tid);
       lds_barrier();  // also: every wavefront has read the stage (its regions may be refilled)
     }
 
@@ -1681,12 +1680,7 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
       }
       lds_barrier();
       if (tid < 64) {
-        float y = sBT[63 - tid] + sBT[64 + 63 - tid];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float z = __shfl_up(y, o, 64);
-          if (tid >= o) y += z;
-        }
+        const float y = scan64(sBT[63 - tid] + sBT[64 + 63 - tid], tid);
         const int rr = 63 - tid;  // y = sum of rows rr..63
         if (rr < len) dg[(size_t)(start + rr) * Hv + j] = y;
       }
