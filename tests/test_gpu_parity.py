@@ -442,6 +442,20 @@ def test_steady_calls_neither_allocate_nor_block(variant):
     assert free1 == free0, "device free memory changed by %d bytes" % (free0 - free1)
 
 
+@pytest.mark.parametrize("variant,hqk,hv", [("kda", 2, 2), ("gdn", 1, 3)])
+@pytest.mark.parametrize("ckpt", [False, True], ids=["fwd_bwd", "ckpt"])
+def test_all_empty_pack(variant, hqk, hv, ckpt):
+    """A pack of empty documents (T = 0): no chunk to process, so the state passes
+    through unchanged (ht = h0) and so does its adjoint (dh0 = dht), bit for bit."""
+    w = workloads.custom(variant, (0, 0, 0), hqk, hv, with_h0=True, seed=3)
+    inp = workloads.make_inputs(w, device="cpu", dht=True)
+    print("[case]", w.name, "ckpt" if ckpt else "fwd+bwd", flush=True)
+    got = run_gdr(variant, inp, dht=inp["dht"], ckpt=ckpt)
+    assert got["o"].shape == (0, hv, 128) and got["dq"].shape == (0, hqk, 128)
+    assert torch.equal(got["ht"], inp["h0"].float())
+    assert torch.equal(got["dh0"], inp["dht"].float())
+
+
 def test_forward_without_tapes_matches():
     w = workloads.custom("kda", (300, 45), 2, 2, with_h0=True, seed=5)
     inp = workloads.make_inputs(w, device="cpu")
