@@ -46,7 +46,8 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
   const bool transfer = MODE == MODE_CARRY && blockIdx.x >= gridDim.x / 2;
   int chain, sl;
-  walk_block(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, chain, sl);
+  walk_block(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, MODE == MODE_CARRY ? gridDim.x / 2 : gridDim.x,
+             p.wq, chain, sl);
   const ChunkTable tb(p.table, p.NC, p.N);
   WalkChain wc;
   if (!walk_chain(p, tb, chain, MODE != MODE_WALK, wc, MODE == MODE_WALK ? 0 : 1))
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
   int chain, half;
-  walk_block<NW>(blockIdx.x, chain, half);  // the 8 / NW workgroups of a chain on one XCD
+  walk_block<NW>(blockIdx.x, gridDim.x, 0, chain, half);  // the 8 / NW workgroups of a chain on one XCD
   WalkChain wc;
   if (!walk_chain(p, tb, chain, false, wc)) return;  // uniform over the workgroup
   const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
@@ -1738,8 +1739,10 @@ __device__ __forceinline__ void bwd_grad_rows_unit(const Problem &p, const Works
 
 
 template <bool SG>
-static hipError_t launch_bwd_walk_t(const Problem &p, const Workspace &w, const u16 *dout, const float *dht,
+static hipError_t launch_bwd_walk_t(const Problem &p0, const Workspace &w, const u16 *dout, const float *dht,
                                     float *dh0, hipStream_t st) {
+  Problem p = p0;
+  p.wq = compute_units() / 64;  // chain slots whose slice wavefronts fill an XCD's compute units once
   const int chains = walk_chains(p, false);
   if (p.P > 1) {  // pass 1: the segments' carries
     const int g1 = walk_grid(walk_chains(p, true), 1);

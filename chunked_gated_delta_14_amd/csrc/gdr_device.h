@@ -242,13 +242,30 @@ struct ChunkTable {
 // and the wavefront's group of NS adjacent 16-column value slices from the
 // block index, placing all groups of one chain on the same XCD (block ids are
 // dealt to the 8 XCDs round-robin), so they share that XCD's L2 copy of the
-// chain's per-chunk operands.  The grid is walk_grid(chains, NS) blocks.
+// chain's per-chunk operands.  The grid is `nblocks` = walk_grid(chains, NS)
+// blocks: every XCD holds nblocks / 64 * NS chain slots, slot s taking chain
+// 8 s + XCD.
+//
+// An XCD hands out its blocks in order, one to each of its compute units
+// before a second one to any, so with wq slots filling its units once (wq =
+// units per XCD * NS / 64; 0: keep the plain order), a unit holds slots i,
+// i + wq, i + 2 wq, ...  Chains are numbered longest first, so in that order a
+// unit would pair long chains with long ones and, once the short chains end,
+// half the units would sit idle while the others still carry two.  Odd passes
+// therefore take their slots in reverse order: a unit holds a long chain next
+// to a short one, and the chains' lengths even out over the units.
 template <int NS = 1>
-__device__ __forceinline__ void walk_block(int b, int &chain, int &group) {
+__device__ __forceinline__ void walk_block(int b, int nblocks, int wq, int &chain, int &group) {
   constexpr int G = 8 / NS;  // slice groups per chain
   const int x = b & 7, m = b >> 3;
   group = m % G;
-  chain = (m / G) * 8 + x;
+  int slot = m / G;
+  if (wq > 0) {
+    const int slots = nblocks / (8 * G), pass = slot / wq, base = pass * wq;
+    const int n = slots - base < wq ? slots - base : wq;
+    if (pass & 1) slot = base + n - 1 - (slot - base);
+  }
+  chain = slot * 8 + x;
 }
 
 // ---------------------------------------------------------------------------

@@ -595,7 +595,8 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
   const bool transfer = MODE == MODE_CARRY && blockIdx.x >= gridDim.x / 2;
   int chain, grp;
-  walk_block<NS>(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, chain, grp);
+  walk_block<NS>(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, MODE == MODE_CARRY ? gridDim.x / 2 : gridDim.x,
+                 p.wq, chain, grp);
   const ChunkTable tb(p.table, p.NC, p.N);
   WalkChain wc;
   if (!walk_chain(p, tb, chain, MODE != MODE_WALK, wc)) return;
@@ -821,7 +822,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
   int chain, half;
-  walk_block<NW>(blockIdx.x, chain, half);  // the 8 / NW workgroups of a chain on one XCD
+  walk_block<NW>(blockIdx.x, gridDim.x, 0, chain, half);  // the 8 / NW workgroups of a chain on one XCD
   WalkChain wc;
   if (!walk_chain(p, tb, chain, false, wc)) return;  // uniform over the workgroup
   const int d = wc.d, j = wc.j, first = wc.first, nch = wc.nch;
@@ -1031,10 +1032,12 @@ hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool 
 }
 
 template <bool SG>
-static hipError_t launch_fwd_walk_t(const Problem &p, const Workspace &w, u16 *o, float *ht, bool save, bool out,
+static hipError_t launch_fwd_walk_t(const Problem &p0, const Workspace &w, u16 *o, float *ht, bool save, bool out,
                                     hipStream_t st) {
   constexpr int NS = WALK_NS;
   static_assert(NS == 1, "segmented walks form entering states per 16-column slice");
+  Problem p = p0;
+  p.wq = compute_units() * NS / 64;  // chain slots whose slice wavefronts fill an XCD's compute units once
   const int chains = walk_chains(p, false);
   if (p.P > 1) {  // pass 1: the segments' carries
     const int g1 = walk_grid(walk_chains(p, true), 1);

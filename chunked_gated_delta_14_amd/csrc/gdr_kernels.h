@@ -56,6 +56,7 @@ struct Problem {
   int B;        // balanced segment plan: segments over all documents at most (0: equal plan, P each)
   int L;        // chunks of the longest document (an upper bound; only steers the walk layout)
   int layout;   // walk layout: 0 automatic, 1 slice wavefronts, 2 workgroup rings
+  int wq;       // slice walks: chain slots that fill an XCD's compute units once (walk_block)
 };
 
 // Walk layout.  Slice wavefronts finish a chain step in about 3.7 K cycles, but a
