@@ -256,9 +256,10 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 // fwd_walk_wg_kernel: the chain's shared per-chunk operands ((q Gamma)^T, M^T,
 // Kbar, -W^T fragments and the gate factors: 56 tiles) pass once per chunk
 // through a two-slot LDS ring (three slots would not fit); each wavefront
-// fetches 56 / NW tiles of the next chunk into registers at the top of a step
-// and writes them to the free slot at its end.  dout stays a per-slice register
-// prefetch.  Same products in the same order as bwd_walk_kernel.
+// copies 56 / NW tiles of the next chunk straight into the free slot
+// (direct-to-LDS loads) during a step and waits for them at its end.  dout stays
+// a per-slice register prefetch.  Same products in the same order as
+// bwd_walk_kernel.
 constexpr int WGB_TILES = 56;                                    // QGT 0..15, MTs 16..23, Kb 24..39, WTn 40..55
 constexpr int WGB_SLOT = WGB_TILES * FRAG_TILE_U4 * 16 + HD * 4;  // bytes per ring slot (+ gamma)
 constexpr int WGB_SMEM = 2 * WGB_SLOT;
@@ -310,37 +311,30 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
     if (t < 24) return w.MTs + u * FRAG_64x64_U4 + (t - 16) * 64 + lane;
     return (t < 40 ? w.Kb + uq * FRAG_64x128_U4 : w.WTn + u * FRAG_64x128_U4) + ((t - 24) & 15) * 64 + lane;
   };
-  u32x4 stage[PER];
-  float4 gst = make_float4(0.f, 0.f, 0.f, 0.f);
-  // chunk c's operands (u = c H_v + j; KDA: H_qk = H_v, the unit's own slot)
-  auto fetch = [&](int c, size_t u) {
-    const size_t uq = SG ? (size_t)c * Hqk + jq : u;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) stage[i] = __builtin_bit_cast(u32x4, *tile_src(u, uq, wv + NW * i));
-    if (wv == 0 && lane < 32) gst = *reinterpret_cast<const float4 *>(w.gam + u * HD + 4 * lane);
-  };
-  auto put = [&](int slot) {
+  // chunk c's operands (u = c H_v + j; KDA: H_qk = H_v, the unit's own slot) into ring
+  // slot `slot`: every wavefront copies its tiles (t = w + NW i) and wavefront 0 the gate
+  // factors straight into LDS (direct-to-LDS loads, no registers)
+  auto stage = [&](int c, int slot) {
+    const size_t u = (size_t)c * Hv + j, uq = SG ? (size_t)c * Hqk + jq : u;
     unsigned char *base = smem + slot * WGB_SLOT;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) *reinterpret_cast<u32x4 *>(base + (wv + NW * i) * 1024 + lane * 16) = stage[i];
-    if (wv == 0 && lane < 32) *reinterpret_cast<float4 *>(base + WGB_TILES * 1024 + lane * 16) = gst;
+    for (int i = 0; i < PER; ++i) lds_dma<16>(tile_src(u, uq, wv + NW * i), lds_addr(base + (wv + NW * i) * 1024));
+    if (wv == 0 && lane < 32) lds_dma<16>(w.gam + u * HD + 4 * lane, lds_addr(base + WGB_TILES * 1024));
   };
   auto frag = [&](int slot, int t) -> bf16x8 {
     return *reinterpret_cast<const bf16x8 *>(smem + slot * WGB_SLOT + t * 1024 + lane * 16);
   };
 
   if (nch > 0) {
-    fetch(first + nch - 1, (size_t)(first + nch - 1) * Hv + j);
+    stage(first + nch - 1, 0);
     fetch_dout(nch - 1);
-    put(0);
   }
+  drain_vmem();
   lds_barrier();
 
   for (int n = nch - 1, it = 0; n >= 0; --n, ++it) {
     const size_t u = (size_t)(first + n) * Hv + j;
-    const size_t un = n > 0 ? u - Hv : u;
     const int slot = it & 1;
-    if (n > 0) fetch(first + n - 1, un);
 
     const float *sg = reinterpret_cast<const float *>(smem + slot * WGB_SLOT + WGB_TILES * 1024);
     float4 gm[8];
@@ -377,6 +371,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
         dOq[1] = acc_pair_to_b(dO[2], dO[3]);
       }
     }
+    // dout's registers are settled before the copies go out (the compiler's wait for them
+    // counts only its own instructions, and would otherwise wait for the copies too);
+    // the next chunk goes to the slot every wavefront finished reading a step ago
+#pragma unroll
+    for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(pdo[h]));
+    if (n > 0) stage(first + n - 1, slot ^ 1);
     fetch_dout(n > 0 ? n - 1 : 0);
 
     bf16x8 dSb[4];
@@ -440,9 +440,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(frag(slot, 40 + mt * 2 + kt), dVb[kt], dS[mt]);
 
-    if (n > 0) put(slot ^ 1);  // the slot every wavefront finished reading a step ago
+    // the next chunk's copies: behind them this step issued 2 dout loads, 4 dS-tape and
+    // 2 dVn^T stores, which may stay in flight
+    vm_wait<8>();
     lds_barrier();
   }
+  drain_vmem();  // no copy may still be writing this workgroup's LDS when it ends
 
   if (dh0 && wc.s == 0) {
     float *hp = dh0 + ((size_t)d * Hv + j) * HD * HD;
@@ -515,29 +518,7 @@ __device__ __forceinline__ int sw128(int r, int col) { return r * HD + 8 * ((col
 __device__ __forceinline__ int sw64(int r, int col) { return r * CH + 8 * ((col >> 3) ^ ((r >> 1) & 7)) + (col & 7); }
 
 
-// Direct-to-LDS copy: every lane moves `BYTES` (4 or 16) from its own global
-// address to lds_byte + BYTES * lane.  Written as inline asm: the compiler would
-// otherwise make every later LDS access wait for it (it cannot tell the bytes
-// apart), which would serialise the copy with the work it is meant to overlap.
-// The compiler does not count these loads, so callers drain the vector-memory
-// counter before issuing them (no register load issued earlier is then waited for
-// behind them) and wait for them explicitly (s_waitcnt vmcnt(0) and a barrier)
-// before reading what they wrote.  M0 carries the LDS address; it is saved and
-// restored, with one wait state between its write and the load.
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(const void *src, uint32_t lds_byte) {
-  uint32_t saved;
-  if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
-  else
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
-}
-__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 
 // Cumulative gate: per-channel tile [channel][row] (KDA) or one value per row.
 template <bool SCALAR>

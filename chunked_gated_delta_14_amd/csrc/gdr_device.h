@@ -177,6 +177,36 @@ __device__ __forceinline__ bf16x8 cvt8(float4 a, float4 b) {
 // memory clobber keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Direct-to-LDS copy: every lane moves `BYTES` (4 or 16) from its own global
+// address to lds_byte + BYTES * lane.  Written as inline asm: the compiler would
+// otherwise make every later LDS access wait for it (it cannot tell the bytes
+// apart), which would serialise the copy with the work it is meant to overlap.
+// The compiler does not count these loads.  A register load issued before them
+// and waited for after them would, by the compiler's count, wait for them too
+// (vector-memory instructions complete in issue order), so callers drain the
+// counter or settle those registers before issuing the copies, and wait for the
+// copies explicitly (vmcnt and a barrier) before reading what they wrote.  M0
+// carries the LDS address; it is saved and restored, with one wait state between
+// its write and the load.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void *src, uint32_t lds_byte) {
+  uint32_t saved;
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_byte), "v"(src) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most K vector-memory instructions of this wavefront are in flight
+// (they complete in issue order).
+template <int K>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory"); }
+
 // Stores of 16-byte row pieces through a buffer resource whose record count
 // ends at the last valid byte: the hardware drops stores past it, so a ragged
 // final chunk needs no branch (a branch would split the walk's step into

@@ -805,16 +805,16 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
 // NW slice wavefronts (wavefront w of workgroup h walks the 16-column value
 // slice NW h + w), and the chain's shared per-chunk operands (-W, P, Kbar^T
 // fragments and the gate factors) pass once per chunk and workgroup through a
-// three-slot LDS ring instead of once per slice wavefront through its own
-// memory pipeline.  At the top of step n each wavefront fetches 1 / NW of chunk
-// n + 2's fragment tiles into one of two register stage sets; at the end it
-// writes the other set (chunk n + 1, fetched a step earlier) to that chunk's
-// slot, and one LDS barrier per step hands it over.  Per-slice operands (U, Oi)
-// stay a register prefetch, and the outputs leave as in fwd_walk_kernel.
+// two-slot LDS ring instead of once per slice wavefront through its own memory
+// pipeline.  During step n each wavefront copies 1 / NW of chunk n + 1's
+// fragment tiles straight into the other slot (direct-to-LDS loads: no
+// registers, no LDS stores), waits for its copies at the end of the step, and
+// one LDS barrier hands the slot over.  Per-slice operands (U, Oi) stay a
+// register prefetch, and the outputs leave as in fwd_walk_kernel.
 constexpr int WG_TILES = 48;                                  // -W, P, Kbar^T: 16 tiles each
 constexpr int WG_SLOT = WG_TILES * FRAG_TILE_U4 * 16 + HD * 4;  // bytes per ring slot (+ gamma)
 constexpr int WG_NW = 4;    // slice wavefronts per ring workgroup (two workgroups per chain)
-constexpr int WG_RING = 3;  // slots: the chunk in use, the next one, the one after in flight
+constexpr int WG_RING = 2;  // slots: the chunk in use, the next one in flight
 constexpr int WG_SMEM = WG_RING * WG_SLOT;
 
 template <bool SAVE, bool OUT, int NW, bool SG = false>
@@ -855,19 +855,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
     const uint4 *base = t < 16 ? w.WfN : (t < 32 ? w.KbT : w.Pf);
     return base + u * FRAG_64x128_U4 + (t & 15) * 64 + lane;
   };
-  // two register stage sets: the chunk after next is fetched while the next one waits for its slot
-  u32x4 stA[PER], stB[PER];
-  float4 gA = make_float4(0.f, 0.f, 0.f, 0.f), gB = gA;
-  auto fetch = [&](int c, u32x4 (&st)[PER], float4 &gs) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) st[i] = __builtin_bit_cast(u32x4, *tile_src(c, wv + NW * i));
-    if (wv == 0 && lane < 32) gs = *reinterpret_cast<const float4 *>(w.gam + ((size_t)c * Hv + j) * HD + 4 * lane);
-  };
-  auto put = [&](int slot, const u32x4 (&st)[PER], const float4 &gs) {
+  // chunk c into ring slot `slot`: every wavefront copies its tiles (t = w + NW i) and
+  // wavefront 0 the gate factors straight into LDS (direct-to-LDS loads, no registers)
+  auto stage = [&](int c, int slot) {
     unsigned char *base = smem + slot * WG_SLOT;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) *reinterpret_cast<u32x4 *>(base + (wv + NW * i) * 1024 + lane * 16) = st[i];
-    if (wv == 0 && lane < 32) *reinterpret_cast<float4 *>(base + WG_TILES * 1024 + lane * 16) = gs;
+    for (int i = 0; i < PER; ++i) lds_dma<16>(tile_src(c, wv + NW * i), lds_addr(base + (wv + NW * i) * 1024));
+    if (wv == 0 && lane < 32) lds_dma<16>(w.gam + ((size_t)c * Hv + j) * HD + 4 * lane, lds_addr(base + WG_TILES * 1024));
   };
   auto frag = [&](int slot, int t) -> bf16x8 {
     return *reinterpret_cast<const bf16x8 *>(smem + slot * WG_SLOT + t * 1024 + lane * 16);
@@ -876,28 +870,26 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
   uint2 Ua[4], Oa[4];
   if (nch > 0) {
     const size_t u = (size_t)first * Hv + j;
-    fetch(first, stA, gA);
-    if (nch > 1) fetch(first + 1, stB, gB);
+    stage(first, 0);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const size_t off = u * ACC_64x128_U16 + ((sl0 * 4 + mt) * 64 + lane) * 4;
       Ua[mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
       if (OUT) Oa[mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
     }
-    put(0, stA, gA);
   }
+  drain_vmem();
   lds_barrier();
 
-  // step n: chunk n in slot n % 3; chunk n + 1 in one stage set (fetched a step
-  // ago), chunk n + 2 fetched into the other; at the end chunk n + 1 goes to its
-  // slot, which every wavefront finished reading two steps ago.
-  auto step = [&](int n, u32x4 (&st_next)[PER], float4 &g_next, u32x4 (&st_after)[PER], float4 &g_after) {
+  // step n: chunk n in slot n % 2; chunk n + 1 is copied into the other slot (which
+  // every wavefront finished reading at the end of step n - 1) while this one computes,
+  // and each wavefront waits for its copies before the barrier that ends the step.
+  auto step = [&](int n) {
     const size_t u = (size_t)(first + n) * Hv + j;
     const size_t un = n + 1 < nch ? u + Hv : u;
     const int slot = n % WG_RING;
     const int row0 = tok0 + CH * n;
     const int len = min(CH, tok1 - row0);
-    if (n + 2 < nch) fetch(first + n + 2, st_after, g_after);
 
     const float *sg = reinterpret_cast<const float *>(smem + slot * WG_SLOT + WG_TILES * 1024);
     float4 gm[8];
@@ -926,13 +918,24 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
     for (int mt = 0; mt < 4; ++mt) {
       Vn[mt][0] = bf2f(Ua[mt].x & 0xffff); Vn[mt][1] = bf2f(Ua[mt].x >> 16);
       Vn[mt][2] = bf2f(Ua[mt].y & 0xffff); Vn[mt][3] = bf2f(Ua[mt].y >> 16);
-      const size_t off = un * ACC_64x128_U16 + ((sl0 * 4 + mt) * 64 + lane) * 4;
-      Ua[mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
       if (OUT) {
         Oc[mt][0] = bf2f(Oa[mt].x & 0xffff); Oc[mt][1] = bf2f(Oa[mt].x >> 16);
         Oc[mt][2] = bf2f(Oa[mt].y & 0xffff); Oc[mt][3] = bf2f(Oa[mt].y >> 16);
-        Oa[mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
       }
+    }
+    // the U / Oi registers are settled before the copies go out (the compiler's wait for
+    // them counts only its own instructions, and would otherwise wait for the copies too)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      asm volatile("" ::"v"(Ua[mt]));
+      if (OUT) asm volatile("" ::"v"(Oa[mt]));
+    }
+    if (n + 1 < nch) stage(first + n + 1, (n + 1) % WG_RING);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const size_t off = un * ACC_64x128_U16 + ((sl0 * 4 + mt) * 64 + lane) * 4;
+      Ua[mt] = *reinterpret_cast<const uint2 *>(w.Uacc + off);
+      if (OUT) Oa[mt] = *reinterpret_cast<const uint2 *>(w.Oacc + off);
     }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -984,13 +987,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) S[mt] = mfma(frag(slot, 16 + mt * 2 + kt), Vs[kt], S[mt]);
 
-    if (n + 1 < nch) put((n + 1) % WG_RING, st_next, g_next);
+    // chunk n + 1's copies: behind them this step issued the U (+ Oi) loads, the o
+    // stores (OUT) and the Vn-tape stores (SAVE), which may stay in flight
+    vm_wait<4 + (OUT ? 6 : 0) + (SAVE ? 2 : 0)>();
     lds_barrier();
   };
-  for (int n = 0; n < nch; n += 2) {  // unrolled by two: the stage sets swap roles
-    step(n, stB, gB, stA, gA);
-    if (n + 1 < nch) step(n + 1, stA, gA, stB, gB);
-  }
+  for (int n = 0; n < nch; ++n) step(n);
+  drain_vmem();  // no copy may still be writing this workgroup's LDS when it ends
 
   if (ht && wc.s == wc.Pd - 1) {
     float *hp = ht + ((size_t)d * Hv + j) * HD * HD;
