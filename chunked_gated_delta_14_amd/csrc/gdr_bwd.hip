@@ -505,7 +505,8 @@ constexpr int G_B = G_TT + CH * CH * 2;     // beta [64]
 constexpr int G_DB = G_B + 64 * 4;          // dbeta partial sums [20][64], added in a fixed order
 constexpr int G_NRM = G_DB + 20 * 64 * 4;   // q, k row norms [2][64], then row dots [64][2][8]
 constexpr int G_DV = G_NRM + (128 + 64 * 16) * 4;  // dVn^T bf16 [128][64], sw64 (Y product)
-constexpr int G_SMEM = G_DV + HD * CH * 2;
+constexpr int G_E = G_DV + HD * CH * 2;             // E, staged: its 10 tiles in accumulator order
+constexpr int G_SMEM = G_E + 10 * 64 * 8;
 static_assert(G_DAT + CH * DMP * 2 <= G_TT, "grad LDS map: dM, dA overlay dout, Vn and Y only");
 static_assert(G_SMEM <= 160 * 1024, "grad LDS map");
 
@@ -684,10 +685,11 @@ __device__ __forceinline__ void load_grad_tape(const u16 *tape, size_t u, int ti
 
 // Stage operands of the KDA gradient unit `unit` in LDS with direct-to-LDS loads
 // (lds_dma), every wavefront moving its own 1 KB blocks.  early: T^T and dVn^T
-// (sw64), whose tiles are dead once the tape products are done; late: the dout and
-// Vn rows (sw128, Vn gathered from its tape layout), whose tiles carry dM and dA
-// until the gated products are done.  dout rows past the chunk repeat its last
-// row (readers zero them).
+// (sw64), whose tiles are dead once the tape products are done; late: the dout,
+// Vn and v rows (sw128, Vn gathered from its tape layout) into the tiles that carry
+// dM, dA and Y until the gated products are done, the raw gate rows into the
+// gate tile (dead once dg is out) and E into its own tile.  Rows past the chunk
+// repeat its last row (readers zero them).
 __device__ __forceinline__ void stage_grad_kda(const Problem &p, const Workspace &w, const u16 *dout,
                                                unsigned char *smem, int unit, bool early, bool late) {
   const ChunkTable tb(p.table, p.NC, p.N);
@@ -709,12 +711,23 @@ __device__ __forceinline__ void stage_grad_kda(const Problem &p, const Workspace
   }
   if (late) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {  // dout and Vn: rows 4k .. 4k+3
+    for (int h = 0; h < 2; ++h) {  // dout, Vn and v: rows 4k .. 4k+3
       const int k = 2 * wave + h, row = 4 * k + (lane >> 4), slot = lane & 15, pc = slot ^ (row & 15);
-      lds_dma<16>(dout + ((size_t)(start + (row < len ? row : len - 1)) * Hv + j) * HD + 8 * pc,
-                  lds_addr(smem + G_DO + 1024 * k));
+      const size_t tok = (size_t)(start + (row < len ? row : len - 1)) * Hv + j;
+      lds_dma<16>(dout + tok * HD + 8 * pc, lds_addr(smem + G_DO + 1024 * k));
       lds_dma<16>(w.Vn + u * (CH * HD) + tape_r(row, 8 * pc), lds_addr(smem + G_VN + 1024 * k));
+      lds_dma<16>(p.v + tok * HD + 8 * pc, lds_addr(smem + G_Y + 1024 * k));
     }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {  // raw gate rows 2k, 2k+1 (512 bytes each): 16-byte piece q of
+                                   // row r at slot q ^ (r >> 1), so the scan's reads spread over the banks
+      const int k = 4 * wave + b, row = 2 * k + (lane >> 5), slot = lane & 31, q = slot ^ k;
+      lds_dma<16>(p.g + ((size_t)(start + (row < len ? row : len - 1)) * Hv + j) * HD + 4 * q,
+                  lds_addr(smem + G_GT + 1024 * k));
+    }
+    if (wave < 5)  // E: 5 KB
+      lds_dma<16>(reinterpret_cast<const unsigned char *>(w.Et + u * FRAG_64x64_U4) + 1024 * wave + 16 * lane,
+                  lds_addr(smem + G_E + 1024 * wave));
   }
 }
 
@@ -770,22 +783,21 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
     const size_t u = (size_t)chunk * Hv + j;
     const int c = 16 * wave + lr;  // this lane's key/value column
 
-    // T^T, dVn^T, dout and Vn were staged in LDS by the previous unit (or before the
-    // loop): each wavefront waits for its own copies here, and the barrier before
-    // the Y product makes all of them visible.
+    // T^T, dVn^T, dout, Vn, v, the raw gate and E were staged in LDS by the previous
+    // unit (or before the loop): each wavefront waits for its own copies, and a barrier
+    // makes all of them visible.
     drain_vmem();
+    lds_barrier();
 
-    // ---- every other load of the iteration, issued up front in the order of use and
-    // unconditionally (rows past the chunk read its last row, zeroed at use) ----
     float graw[2][8];
     uint32_t braw = 0u;
-    const int o8 = tid >> 5, pr = tid & 31, c0g = 8 * o8, rp = 2 * pr;  // gate loader coordinates
+    const int o8 = tid >> 5, pr = tid & 31, c0g = 8 * o8, rp = 2 * pr;  // gate scan coordinates
     {
+      const unsigned char *src = smem + G_GT + rp * 512;  // rows rp, rp + 1: pieces 2 o8, 2 o8 + 1 at slots ^ pr
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int r = rp + h < len ? rp + h : last;
-        const float *src = p.g + ((size_t)(start + r) * Hv + j) * HD + c0g;
-        const float4 ga = *reinterpret_cast<const float4 *>(src), gb = *reinterpret_cast<const float4 *>(src + 4);
+        const float4 ga = *reinterpret_cast<const float4 *>(src + h * 512 + 16 * ((2 * o8) ^ pr));
+        const float4 gb = *reinterpret_cast<const float4 *>(src + h * 512 + 16 * ((2 * o8 + 1) ^ pr));
         graw[h][0] = ga.x; graw[h][1] = ga.y; graw[h][2] = ga.z; graw[h][3] = ga.w;
         graw[h][4] = gb.x; graw[h][5] = gb.y; graw[h][6] = gb.z; graw[h][7] = gb.w;
       }
@@ -794,13 +806,18 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
       const size_t e = (size_t)(start + (tid < len ? tid : last)) * Hv + j;
       braw = reinterpret_cast<const u16 *>(p.beta)[e];
     }
-    // v at the accumulator positions (dbeta and dv)
+    // v at the accumulator positions (dbeta and dv), from the Y tile it was staged in
     uint2 vv[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int rl = 16 * mt + lr < len ? 16 * mt + lr : last;
-      vv[mt] = *reinterpret_cast<const uint2 *>(p.v + ((size_t)(start + rl) * Hv + j) * HD + 16 * wave + 4 * lg);
+    for (int mt = 0; mt < 4; ++mt) vv[mt] = *reinterpret_cast<const uint2 *>(sY + sw128(16 * mt + lr, 16 * wave + 4 * lg));
+    // E (accumulator order) of the dM, dA tiles of this wavefront: p = w and p = w + 8
+    uint2 eT[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pt = wave + 8 * q < 10 ? wave + 8 * q : wave;
+      eT[q] = *reinterpret_cast<const uint2 *>(smem + G_E + (pt * 64 + lane) * 8);
     }
+    lds_barrier();  // the raw gate and v are read: the cumulative gate and Y take their tiles
     // ---- beta, cleared sums, the cumulative gate ----
     if (tid < 64) {
       float b = bf2f((u16)braw);
@@ -821,13 +838,6 @@ __device__ __forceinline__ void bwd_grad_unit(const Problem &p, const Workspace 
     bf16x8 Sb[4], dSb[4];
     load_grad_tape(w.S, u, tid, Sb);
     load_grad_tape(w.dS, u, tid, dSb);
-    // E (accumulator order) of the dM, dA tiles of this wavefront: p = w and p = w + 8
-    uint2 eT[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int pt = wave + 8 * q < 10 ? wave + 8 * q : wave;
-      eT[q] = reinterpret_cast<const uint2 *>(w.Et + u * FRAG_64x64_U4)[pt * 64 + lane];
-    }
 
     lds_barrier();
 
