@@ -296,6 +296,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
     const float *cb = carry_of(p, w, d, t - 1, j);
     apply_carry(dS, cb, cb + HD * HD, 16 * sl, lane);
   }
+  // the entering adjoint settled here: the loop's first use of it then waits for nothing
+  // on its way in from this prologue (the compiler merges the two paths into the loop)
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) asm volatile("" ::"v"(dS[mt]));
 
   const int prow = 16 * (lg >> 1) + lr, pcol = 8 * (lg & 1);
   u32x4 pdo[2];
@@ -335,6 +339,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
   for (int n = nch - 1, it = 0; n >= 0; --n, ++it) {
     const size_t u = (size_t)(first + n) * Hv + j;
     const int slot = it & 1;
+    // the adjoint-state tape first: its stores then sit between the previous step's dout
+    // loads and their use on every path into the loop, so the wait for dout leaves them
+    // in flight
+    bf16x8 dSb[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) dSb[kt] = acc_pair_to_b(dS[2 * kt], dS[2 * kt + 1]);
+    {  // this slice's block [key][16] of the adjoint-state tape
+      u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + prow * 16 + pcol;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        *reinterpret_cast<u32x4 *>(tp + kt * 512) = rows8_from_pair(tile_row4(dSb[kt], 0, eye), tile_row4(dSb[kt], 1, eye));
+    }
 
     const float *sg = reinterpret_cast<const float *>(smem + slot * WGB_SLOT + WGB_TILES * 1024);
     float4 gm[8];
@@ -379,15 +395,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
     if (n > 0) stage(first + n - 1, slot ^ 1);
     fetch_dout(n > 0 ? n - 1 : 0);
 
-    bf16x8 dSb[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) dSb[kt] = acc_pair_to_b(dS[2 * kt], dS[2 * kt + 1]);
-    {  // this slice's block [key][16] of the adjoint-state tape
-      u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + prow * 16 + pcol;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        *reinterpret_cast<u32x4 *>(tp + kt * 512) = rows8_from_pair(tile_row4(dSb[kt], 0, eye), tile_row4(dSb[kt], 1, eye));
-    }
 
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
@@ -440,9 +447,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(frag(slot, 40 + mt * 2 + kt), dVb[kt], dS[mt]);
 
-    // the next chunk's copies: behind them this step issued 2 dout loads, 4 dS-tape and
-    // 2 dVn^T stores, which may stay in flight
-    vm_wait<8>();
+    // the next chunk's copies: behind them this step issued 2 dout loads and 2 dVn^T
+    // stores, which may stay in flight
+    vm_wait<4>();
     lds_barrier();
   }
   drain_vmem();  // no copy may still be writing this workgroup's LDS when it ends
