@@ -88,18 +88,21 @@ def _heads_of(dev, qh, vh):
     return {k: dev[k][:, qh if k in ("dq", "dk") else vh].float().cpu() for k in dev}
 
 
-def _check_workload(w, ckpt=False, full_qk_heads=(0,), window_qk_heads=(), also_ckpt=False):
+def _check_workload(w, ckpt=False, full_qk_heads=(0,), window_qk_heads=(), also_ckpt=False, also_repeat=False):
     """Run the whole pack on the GPU, then check sampled heads against the oracle.
     With also_ckpt, the checkpointed step runs too and must be bitwise equal to
-    forward + backward on every head."""
+    forward + backward on every head; with also_repeat, the same call runs again
+    (on a NaN-filled workspace and outputs) and must give the same bits."""
     inp = workloads.make_inputs(w, device="cuda")
     print("[case]", w.name, "ckpt" if ckpt else "fwd+bwd", flush=True)
     dev = run_gdr(w.variant, inp, ckpt=ckpt, on_device=True)
-    if also_ckpt:
-        print("[case]", w.name, "ckpt, bitwise against fwd+bwd", flush=True)
-        dev2 = run_gdr(w.variant, inp, ckpt=True, on_device=True)
+    for again, label in ((also_ckpt, "ckpt, bitwise against fwd+bwd"), (also_repeat, "again, bitwise")):
+        if not again:
+            continue
+        print("[case]", w.name, label, flush=True)
+        dev2 = run_gdr(w.variant, inp, ckpt=ckpt or label.startswith("ckpt"), on_device=True)
         for key in dev:
-            assert torch.equal(dev[key], dev2[key]), "%s: ckpt differs from fwd+bwd" % key
+            assert torch.equal(dev[key], dev2[key]), "%s: %s" % (key, label)
         del dev2
     group = w.H_v // w.H_qk
     cu = inp["cu_seqlens"].numpy()
@@ -140,7 +143,7 @@ def test_workload1_shard_with_initial_state():
 
 @pytest.mark.parametrize("H", [4, 16])
 def test_workload2_pack(H):
-    _check_workload(workloads.workload(2, H), full_qk_heads=(H - 1,), window_qk_heads=(0,))
+    _check_workload(workloads.workload(2, H), full_qk_heads=(H - 1,), window_qk_heads=(0,), also_repeat=True)
 
 
 def test_workload3_gdn_pack_and_ckpt():
@@ -148,4 +151,4 @@ def test_workload3_gdn_pack_and_ckpt():
 
 
 def test_workload4_pack_h64_ckpt():
-    _check_workload(workloads.workload(4), ckpt=True, full_qk_heads=(63,), window_qk_heads=(0,))
+    _check_workload(workloads.workload(4), ckpt=True, full_qk_heads=(63,), window_qk_heads=(0,), also_repeat=True)
