@@ -138,8 +138,8 @@ __device__ __forceinline__ void prep_load(PrepIn &in, const Problem &p, const Ch
   }
 }
 
-template <bool SCALAR, bool ACT>
-__device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, int save, int out, int unit,
+template <bool SCALAR, bool ACT, bool SAVE, bool OUT>
+__device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, int unit,
                                           const PrepIn &in, PrepIn &next, int next_unit, bool next_same_qk,
                                           unsigned char *smem) {
   // heads vary fastest over the units, so the workgroups working together
@@ -222,7 +222,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         rk[h] = rsqrtf(tk + L2NORM_EPS);
       }
       // kept for the backward, once per (token, Q/K head): by the group's first value head
-      if (save && o == 0 && lead) {
+      if (SAVE && o == 0 && lead) {
         const int start = tb.start[chunk];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -366,10 +366,10 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         ev[jj] = e;
         ms[h][jj] = scale * m;
       }
-      if (save && I >= J)  // E for the gradient kernel, accumulator order of tile (I, J)
+      if (SAVE && I >= J)  // E for the gradient kernel, accumulator order of tile (I, J)
         reinterpret_cast<uint2 *>(w.Et + u * FRAG_64x64_U4)[((I * (I + 1)) / 2 + J) * 64 + lane] = pack4bf(ev);
     }
-    if (save) w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane] = as_u4(acc_pair_to_b(ms[0], ms[1]));
+    if (SAVE) w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane] = as_u4(acc_pair_to_b(ms[0], ms[1]));
   }
   lds_barrier();
   if (has_next) prep_load<SCALAR, PF_B>(next, p, tb, next_unit, tid, reuse_in);
@@ -427,7 +427,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         *reinterpret_cast<uint2 *>(w.Uacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4) = pack4bf(Ud[h][n]);
       }
     }
-    if (save)
+    if (SAVE)
 #pragma unroll
       for (int n = 0; n < 2; ++n)  // -W^T: rows key 16nt.., k: chunk 32kp + kwalk
         w.WTn[u * FRAG_64x128_U4 + ((2 * cg + n) * 2 + kp) * 64 + lane] = as_u4(acc_pair_to_b(-Wd[0][n], -Wd[1][n]));
@@ -446,7 +446,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 
   // ---- 5. P^T = scale (q exp G)^T - scale W^T M^T,  Oi = scale M U (the output's
   // operands; a recompute that skips the output skips them) ----
-  if (out) {
+  if (OUT) {
     bf16x8 aM[2][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -503,12 +503,12 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
       const int o = key * CTP + 32 * kt + 4 * g_;
       const uint2 a = *reinterpret_cast<const uint2 *>(sKL + o), b = *reinterpret_cast<const uint2 *>(sKL + o + 16);
       w.KbT[uq * FRAG_64x128_U4 + slot] = make_uint4(a.x, a.y, b.x, b.y);
-      if (save) {
+      if (SAVE) {
         const uint2 qa = *reinterpret_cast<const uint2 *>(sQG + o), qb = *reinterpret_cast<const uint2 *>(sQG + o + 16);
         w.QGT[uq * FRAG_64x128_U4 + slot] = make_uint4(qa.x, qa.y, qb.x, qb.y);
       }
     }
-    if (save) {  // rows: chunk (16 mt + r_), k: key (32 kt + kwalk)
+    if (SAVE) {  // rows: chunk (16 mt + r_), k: key (32 kt + kwalk)
       const int mt = tile >> 2, kt = tile & 3, row = 16 * mt + r_;
       bf16x8 kb;
 #pragma unroll
@@ -516,7 +516,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
       w.Kb[uq * FRAG_64x128_U4 + slot] = as_u4(kb);
     }
   }
-  if (save && tid < CH * CH / 8) {  // T^T, bf16 row-major, for the gradient kernel
+  if (SAVE && tid < CH * CH / 8) {  // T^T, bf16 row-major, for the gradient kernel
     const int r = tid >> 3, c8 = (tid & 7) * 8;
     bf16x8 tv;
 #pragma unroll
@@ -530,9 +530,14 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 // ... and fetches the next unit's inputs into registers while it works on
 // the current one (in parts, from the end of the current unit's first phase on).
 // ACT: input activations requested (q/k L2 norm, beta sigmoid); the instantiation
-// without them carries none of their code.
-template <bool SCALAR, bool ACT>
-__global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, int save, int out) {
+// without them carries none of their code.  SAVE, OUT: the backward's operands
+// and the output's (P, Oi) are written.  Both are compile-time: with them known,
+// the compiler counts every store behind the last prefetch part, and the wait for
+// that part at the end of a unit leaves the unit's last stores in flight (with
+// run-time flags it merged the paths with and without the stores and waited for
+// all of them).
+template <bool SCALAR, bool ACT, bool SAVE, bool OUT>
+__global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w) {
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
   const int total = p.NC * p.Hv, tid = threadIdx.x;
@@ -543,7 +548,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
     settle(nxt);  // so that no path into the loop carries an outstanding load
     for (; unit < total; unit += gridDim.x) {
       const PrepIn cur = nxt;
-      prep_unit<SCALAR, ACT>(p, w, save, out, unit, cur, nxt, unit + gridDim.x, false, smem);
+      prep_unit<SCALAR, ACT, SAVE, OUT>(p, w, unit, cur, nxt, unit + gridDim.x, false, smem);
       lds_barrier();  // LDS is reused by the next unit
     }
     return;
@@ -561,7 +566,7 @@ __global__ __launch_bounds__(PNT) void fwd_prep_kernel(Problem p, Workspace w, i
     int ng = g, nj = jg + 1;
     if (nj == grp) { ng = g + gridDim.x; nj = 0; }
     const PrepIn cur = nxt;
-    prep_unit<SCALAR, ACT>(p, w, save, out, unit_of(g, jg), cur, nxt, ng < groups ? unit_of(ng, nj) : total, nj != 0,
+    prep_unit<SCALAR, ACT, SAVE, OUT>(p, w, unit_of(g, jg), cur, nxt, ng < groups ? unit_of(ng, nj) : total, nj != 0,
                            smem);
     lds_barrier();  // LDS is reused by the next unit
     g = ng;
@@ -1017,21 +1022,32 @@ int compute_units() {
   return cached[dev];
 }
 
+// One instantiation per (variant, activations, SAVE, OUT).
+template <bool SCALAR, bool ACT, bool SAVE, bool OUT>
+static hipError_t launch_fwd_prep_k(const Problem &p, const Workspace &w, dim3 grid, dim3 block, hipStream_t st) {
+  hipError_t e = set_dynamic_lds_once((const void *)fwd_prep_kernel<SCALAR, ACT, SAVE, OUT>, P_SMEM);
+  if (e != hipSuccess) return e;
+  fwd_prep_kernel<SCALAR, ACT, SAVE, OUT><<<grid, block, P_SMEM, st>>>(p, w);
+  return hipGetLastError();
+}
+template <bool SCALAR, bool ACT>
+static hipError_t launch_fwd_prep_t(const Problem &p, const Workspace &w, bool save, bool out, dim3 grid, dim3 block,
+                                    hipStream_t st) {
+  if (save) return out ? launch_fwd_prep_k<SCALAR, ACT, true, true>(p, w, grid, block, st)
+                       : launch_fwd_prep_k<SCALAR, ACT, true, false>(p, w, grid, block, st);
+  return out ? launch_fwd_prep_k<SCALAR, ACT, false, true>(p, w, grid, block, st)
+             : launch_fwd_prep_k<SCALAR, ACT, false, false>(p, w, grid, block, st);
+}
+
 hipError_t launch_fwd_prep(bool gdn, const Problem &p, const Workspace &w, bool save, bool out, hipStream_t st) {
   if (p.NC == 0) return hipSuccess;
   const int items = gdn ? p.NC * p.Hqk : p.NC * p.Hv;  // GDN: (chunk, Q/K head) groups; KDA: units
   const dim3 grid(items < compute_units() ? items : compute_units()), block(PNT);
   const bool act = p.inflags != 0;
-  const void *fn = gdn ? (act ? (const void *)fwd_prep_kernel<true, true> : (const void *)fwd_prep_kernel<true, false>)
-                       : (act ? (const void *)fwd_prep_kernel<false, true> : (const void *)fwd_prep_kernel<false, false>);
-  hipError_t e = set_dynamic_lds_once(fn, P_SMEM);
-  if (e != hipSuccess) return e;
-  const int sv = save ? 1 : 0, ov = out ? 1 : 0;
-  if (gdn && act) fwd_prep_kernel<true, true><<<grid, block, P_SMEM, st>>>(p, w, sv, ov);
-  else if (gdn) fwd_prep_kernel<true, false><<<grid, block, P_SMEM, st>>>(p, w, sv, ov);
-  else if (act) fwd_prep_kernel<false, true><<<grid, block, P_SMEM, st>>>(p, w, sv, ov);
-  else fwd_prep_kernel<false, false><<<grid, block, P_SMEM, st>>>(p, w, sv, ov);
-  return hipGetLastError();
+  if (gdn) return act ? launch_fwd_prep_t<true, true>(p, w, save, out, grid, block, st)
+                      : launch_fwd_prep_t<true, false>(p, w, save, out, grid, block, st);
+  return act ? launch_fwd_prep_t<false, true>(p, w, save, out, grid, block, st)
+             : launch_fwd_prep_t<false, false>(p, w, save, out, grid, block, st);
 }
 
 template <bool SG>

@@ -200,6 +200,38 @@ def test_recompute_without_output(variant):
         assert torch.equal(g[key].float().cpu(), a[key]), key
 
 
+@pytest.mark.parametrize("variant", ["kda", "gdn"])
+@pytest.mark.parametrize("walk_layout", [1, 2], ids=["slices", "rings"])
+def test_final_states_only_forward(variant, walk_layout):
+    """GDR_FWD_SKIP_OUTPUT alone (no tapes, no o): ht is bitwise the full forward's,
+    o is left untouched, and a workspace sized without GDR_FWD_SAVE suffices."""
+    import chunked_gated_delta_14_amd as gdr
+    from gpu_runner import to_dev
+
+    hqk, hv = (2, 2) if variant == "kda" else (1, 3)
+    w = workloads.custom(variant, (170, 64, 33, 0), hqk, hv, with_h0=True, seed=9)
+    inp = workloads.make_inputs(w, device="cpu")
+    print("[case]", w.name, "final states only, layout", walk_layout, flush=True)
+    d = to_dev(inp)
+    code = gdr.GDR_KDA if variant == "kda" else gdr.GDR_GDN
+    fwd = gdr.kda_fwd if variant == "kda" else gdr.gdn_fwd
+    prob = gdr.Problem(code, d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["h0"],
+                       walk_layout=walk_layout)
+    T, N = prob.T, prob.N
+    ws = prob.alloc_workspace(0)
+    ws.fill_(0xFF)
+    o = torch.empty((T, hv, 128), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty((N, hv, 128, 128), dtype=torch.float32, device="cuda")
+    fwd(prob, o, ht, ws, 0)
+    ws.fill_(0xFF)
+    sentinel = torch.full((T, hv, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    ht2 = torch.full_like(ht, float("nan"))
+    fwd(prob, sentinel, ht2, ws, gdr.GDR_FWD_SKIP_OUTPUT)
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all())
+    assert torch.equal(ht2, ht)
+
+
 @pytest.mark.parametrize("walk_layout", [1, 2], ids=["slices", "rings"])
 def test_ckpt_graph_replay(walk_layout):
     """The checkpointed step captured in a HIP graph, with either walk layout:
