@@ -82,15 +82,16 @@ int walk_segment_cap(int64_t N, int64_t Hv, int64_t NC) {
 
 struct Layout {
   int64_t carry;                          // segment carries (segmented walks only)
-  int64_t WfN, Pf, KbT, Uacc, Oacc, gam;  // forward walk operands
-  int64_t Kb, WTn, QGT, MTs, Tt, Et, S, Vn;  // tapes kept for the backward
+  int64_t WfN, KbT, Pf, Oacc, Uacc, gam;  // forward walk operands
+  int64_t QGT, MTs, Tt, Et, S, Vn;        // tapes kept for the backward
   int64_t qk_rstd;                           // q/k inverse norms (per token and Q/K head)
   int64_t fwd_bytes, full_bytes;
 };
 
 // The backward's scratch tapes overlay forward-walk operands, which are dead once
-// the forward walk has run: dS (32 KB per unit) the adjacent WfN|Pf, dVnT (16 KB)
-// Uacc.  KbT, Kb and QGT are per (chunk, Q/K head).
+// the forward walk has run: dS (32 KB per unit) the adjacent Pf|Oacc, dVnT (16 KB)
+// Uacc.  WfN and KbT stay: the adjoint walk reads them transposed.  KbT and QGT are
+// per (chunk, Q/K head).
 Layout make_layout(int64_t units, int64_t N, int64_t Hv, int64_t T, int64_t Hqk) {
   Layout L{};
   int64_t off = 0;
@@ -109,14 +110,12 @@ Layout make_layout(int64_t units, int64_t N, int64_t Hv, int64_t T, int64_t Hqk)
   L.carry = off;
   off += round_up((int64_t)(walk_segment_cap(N, Hv, units / Hv) - 1) * N * Hv * 2 * kHD * kHD * 4);
   L.WfN = take(kFrag64x128);
-  L.Pf = take(kFrag64x128);
   L.KbT = take_qk(kFrag64x128);
+  L.Pf = take(kFrag64x128);
+  L.Oacc = take(kAcc64x128);  // right after Pf: the two carry the dS tape
   L.Uacc = take(kAcc64x128);
-  L.Oacc = take(kAcc64x128);
   L.gam = take(kGamma);
   L.fwd_bytes = off;
-  L.Kb = take_qk(kFrag64x128);
-  L.WTn = take(kFrag64x128);
   L.QGT = take_qk(kFrag64x128);
   L.MTs = take(kFrag64x64);
   L.Tt = take(kFrag64x64);
@@ -138,15 +137,13 @@ gdr::Workspace bind(const Layout &L, void *base) {
   w.Uacc = reinterpret_cast<uint16_t *>(b + L.Uacc);
   w.Oacc = reinterpret_cast<uint16_t *>(b + L.Oacc);
   w.gam = reinterpret_cast<float *>(b + L.gam);
-  w.Kb = reinterpret_cast<uint4 *>(b + L.Kb);
-  w.WTn = reinterpret_cast<uint4 *>(b + L.WTn);
   w.QGT = reinterpret_cast<uint4 *>(b + L.QGT);
   w.MTs = reinterpret_cast<uint4 *>(b + L.MTs);
   w.Tt = reinterpret_cast<uint4 *>(b + L.Tt);
   w.Et = reinterpret_cast<uint4 *>(b + L.Et);
   w.S = reinterpret_cast<uint16_t *>(b + L.S);
   w.Vn = reinterpret_cast<uint16_t *>(b + L.Vn);
-  w.dS = reinterpret_cast<uint16_t *>(b + L.WfN);   // over WfN|Pf
+  w.dS = reinterpret_cast<uint16_t *>(b + L.Pf);    // over Pf|Oacc
   w.dVnT = reinterpret_cast<uint16_t *>(b + L.Uacc);// over Uacc
   w.carry = reinterpret_cast<float *>(b + L.carry);
   w.qk_rstd = reinterpret_cast<float *>(b + L.qk_rstd);

@@ -25,11 +25,12 @@ namespace gdr {
 // ---------------------------------------------------------------------------
 // Adjoint walk: one wavefront per (document, value head, 16-column slice),
 // chunks in reverse.  dS lives in eight accumulator tiles; 56 MFMAs per chunk.
-// Operands are fetched one chunk ahead in the loop's own issue order.  dout
+// Operands are fetched one chunk ahead in the loop's own issue order.  Kbar and
+// -W^T come from the forward walk's Kbar^T and -W tiles: each tile is written
+// to LDS (slots permuted) where it is used and read back transposed.  dout
 // arrives as 16-byte row pieces (rows past the chunk read as zeros) and the dS
 // tape leaves as 16-byte row pieces, both through lane regrouping and tile
-// products with the identity on the matrix cores, so the step has no LDS
-// round trip besides the broadcast of the gate factors.
+// products with the identity on the matrix cores.
 // ---------------------------------------------------------------------------
 // Segmented like the forward walk (gdr_walk.h), in reverse: the adjoint walk over
 // segment s maps the adjoint entering it at its last chunk to the one leaving it
@@ -44,6 +45,7 @@ template <int MODE = MODE_WALK, bool SG = false>
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
   __shared__ __align__(16) float sgam[HD];  // gate factors of the current chunk
+  __shared__ __align__(16) unsigned char sfr[32 * 1024];  // Kbar^T tiles, then -W tiles (slots permuted)
   const bool transfer = MODE == MODE_CARRY && blockIdx.x >= gridDim.x / 2;
   int chain, sl;
   walk_block(transfer ? blockIdx.x - gridDim.x / 2 : blockIdx.x, MODE == MODE_CARRY ? gridDim.x / 2 : gridDim.x,
@@ -91,8 +93,18 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
     for (int h = 0; h < 2; ++h) pdo[h] = src.get16((uint32_t)(32 * h + prow) * row_bytes + 2 * pcol);
   };
 
-  bf16x8 Kb[4][4], MT[4][2], QG[8][2], WT[8][2];
+  bf16x8 KT[16], MT[4][2], QG[8][2], WF[16];  // KT: Kbar^T tiles, WF: -W tiles
   float2 gq = make_float2(0.f, 0.f);  // gamma of keys 2*lane, 2*lane+1 (next chunk)
+  // Kbar (rows chunk, k key) and -W^T (rows key, k chunk) fragments, read transposed
+  const uint32_t wpos = tr_slot(lane) * 16, troff = tr_lane_off(lane);
+  auto kb_frag = [&](int mt, int kt) -> bf16x8 {
+    const unsigned char *b = sfr + troff + 8 * (mt & 1);
+    return tr_frag(b + (4 * kt + (mt >> 1)) * 1024, b + (2 + 4 * kt + (mt >> 1)) * 1024);
+  };
+  auto wt_frag = [&](int mt, int kt) -> bf16x8 {
+    const unsigned char *b = sfr + 16 * 1024 + troff + 8 * (mt & 1);
+    return tr_frag(b + (8 * kt + (mt >> 1)) * 1024, b + (4 + 8 * kt + (mt >> 1)) * 1024);
+  };
   if (nch > 0) {  // issued in the loop's own order: the counter waits at the loop head see one history
     const size_t u = (size_t)(first + nch - 1) * Hv + j;
     const size_t uq = SG ? (size_t)(first + nch - 1) * Hqk + jq : u;  // KDA: H_qk = H_v, the unit's own slot
@@ -103,9 +115,9 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 #pragma unroll
     for (int t = 0; t < 8; ++t) MT[t >> 1][t & 1] = as_bf16x8(w.MTs[u * FRAG_64x64_U4 + t * 64 + lane]);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) Kb[t >> 2][t & 3] = as_bf16x8(w.Kb[uq * FRAG_64x128_U4 + t * 64 + lane]);
+    for (int t = 0; t < 16; ++t) KT[t] = as_bf16x8(w.KbT[uq * FRAG_64x128_U4 + t * 64 + lane]);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) WT[t >> 1][t & 1] = as_bf16x8(w.WTn[u * FRAG_64x128_U4 + t * 64 + lane]);
+    for (int t = 0; t < 16; ++t) WF[t] = as_bf16x8(w.WfN[u * FRAG_64x128_U4 + t * 64 + lane]);
   }
 
   for (int n = nch - 1; n >= 0; --n) {
@@ -184,12 +196,14 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
     for (int mt = 0; mt < 4; ++mt) dV[mt] = zero4();
     if constexpr (SG) {  // K dS' first, its rows scaled by exp(G_last - G_r), then scale M^T dout
 #pragma unroll
+      for (int t = 0; t < 16; ++t) {  // this chunk's Kbar^T tiles to LDS, the next chunk's fetched
+        *reinterpret_cast<bf16x8 *>(sfr + t * 1024 + wpos) = KT[t];
+        KT[t] = as_bf16x8(w.KbT[uqn * FRAG_64x128_U4 + t * 64 + lane]);
+      }
+#pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          dV[mt] = mfma(Kb[mt][kt], dSb[kt], dV[mt]);
-          Kb[mt][kt] = as_bf16x8(w.Kb[uqn * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
-        }
+        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(kb_frag(mt, kt), dSb[kt], dV[mt]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const float4 e = *reinterpret_cast<const float4 *>(sgam + CH + 16 * mt + 4 * lg);
@@ -211,12 +225,14 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
           MT[mt][kt] = as_bf16x8(w.MTs[un * FRAG_64x64_U4 + (mt * 2 + kt) * 64 + lane]);
         }
 #pragma unroll
+      for (int t = 0; t < 16; ++t) {  // this chunk's Kbar^T tiles to LDS, the next chunk's fetched
+        *reinterpret_cast<bf16x8 *>(sfr + t * 1024 + wpos) = KT[t];
+        KT[t] = as_bf16x8(w.KbT[uqn * FRAG_64x128_U4 + t * 64 + lane]);
+      }
+#pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          dV[mt] = mfma(Kb[mt][kt], dSb[kt], dV[mt]);
-          Kb[mt][kt] = as_bf16x8(w.Kb[uqn * FRAG_64x128_U4 + (mt * 4 + kt) * 64 + lane]);
-        }
+        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(kb_frag(mt, kt), dSb[kt], dV[mt]);
     }
     if (MODE == MODE_WALK) {  // dVn^T rows of this slice's columns: 8 consecutive chunk rows 32h + 8lg.. per lane
       u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 8 * lg;
@@ -230,12 +246,14 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
     dVb[0] = acc_pair_to_b(dV[0], dV[1]);
     dVb[1] = acc_pair_to_b(dV[2], dV[3]);
 #pragma unroll
+    for (int t = 0; t < 16; ++t) {  // this chunk's -W tiles to LDS, the next chunk's fetched
+      *reinterpret_cast<bf16x8 *>(sfr + 16 * 1024 + t * 1024 + wpos) = WF[t];
+      WF[t] = as_bf16x8(w.WfN[un * FRAG_64x128_U4 + t * 64 + lane]);
+    }
+#pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        dS[mt] = mfma(WT[mt][kt], dVb[kt], dS[mt]);
-        WT[mt][kt] = as_bf16x8(w.WTn[un * FRAG_64x128_U4 + (mt * 2 + kt) * 64 + lane]);
-      }
+      for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(wt_frag(mt, kt), dVb[kt], dS[mt]);
   }
 
   float *hp = nullptr;
@@ -253,21 +271,25 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
 }
 
 // Adjoint walk with the slice wavefronts of a chain in workgroups of NW, as
-// fwd_walk_wg_kernel: the chain's shared per-chunk operands ((q Gamma)^T, M^T,
-// Kbar, -W^T fragments and the gate factors: 56 tiles) pass once per chunk
-// through a two-slot LDS ring (three slots would not fit); each wavefront
-// copies 56 / NW tiles of the next chunk straight into the free slot
-// (direct-to-LDS loads) during a step and waits for them at its end.  dout stays
-// a per-slice register prefetch.  Same products in the same order as
+// fwd_walk_wg_kernel: the chain's shared per-chunk operands ((q Gamma)^T and M^T
+// fragments, the forward walk's Kbar^T and -W fragments, and the gate factors:
+// 56 tiles) pass once per chunk through a two-slot LDS ring (three slots would
+// not fit); each wavefront copies 56 / NW tiles of the next chunk straight into
+// the free slot (direct-to-LDS loads) during a step and waits for them at its
+// end.  Kbar and -W^T are read transposed out of their tiles.  dout stays a
+// per-slice register prefetch.  Same products in the same order as
 // bwd_walk_kernel.
-constexpr int WGB_TILES = 56;                                    // QGT 0..15, MTs 16..23, Kb 24..39, WTn 40..55
+constexpr int WGB_TILES = 56;                                    // QGT 0..15, MTs 16..23, KbT 24..39, WfN 40..55
 constexpr int WGB_SLOT = WGB_TILES * FRAG_TILE_U4 * 16 + HD * 4;  // bytes per ring slot (+ gamma)
 constexpr int WGB_SMEM = 2 * WGB_SLOT;
 constexpr int WGB_NW = 4;
 
+// Its LDS ring leaves room for one workgroup per compute unit, so one wavefront per
+// SIMD: the compiler may use the whole register file and keep more LDS fragment
+// reads in flight ahead of the products.
 template <int NW, bool SG = false>
-__global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspace w, const u16 *dout,
-                                                              const float *dht, float *dh0) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_walk_wg_kernel(Problem p, Workspace w, const u16 *dout, const float *dht, float *dh0) {
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
   int chain, half;
@@ -309,11 +331,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
     for (int h = 0; h < 2; ++h) pdo[h] = src.get16((uint32_t)(32 * h + prow) * row_bytes + 2 * pcol);
   };
-  // tile t of unit u: (q Gamma)^T and Kbar from the Q/K head's slot uq, M^T and -W^T the unit's
+  // tile t of unit u: (q Gamma)^T and Kbar^T from the Q/K head's slot uq, M^T and -W the
+  // unit's; the forward walk's Kbar^T and -W tiles with their slots permuted (tr_slot), for
+  // the transposed reads that give Kbar and -W^T
   auto tile_src = [&](size_t u, size_t uq, int t) -> const uint4 * {
     if (t < 16) return w.QGT + uq * FRAG_64x128_U4 + t * 64 + lane;
     if (t < 24) return w.MTs + u * FRAG_64x64_U4 + (t - 16) * 64 + lane;
-    return (t < 40 ? w.Kb + uq * FRAG_64x128_U4 : w.WTn + u * FRAG_64x128_U4) + ((t - 24) & 15) * 64 + lane;
+    return (t < 40 ? w.KbT + uq * FRAG_64x128_U4 : w.WfN + u * FRAG_64x128_U4) + ((t - 24) & 15) * 64 + tr_slot(lane);
   };
   // chunk c's operands (u = c H_v + j; KDA: H_qk = H_v, the unit's own slot) into ring
   // slot `slot`: every wavefront copies its tiles (t = w + NW i) and wavefront 0 the gate
@@ -327,6 +351,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
   };
   auto frag = [&](int slot, int t) -> bf16x8 {
     return *reinterpret_cast<const bf16x8 *>(smem + slot * WGB_SLOT + t * 1024 + lane * 16);
+  };
+  // Kbar (rows chunk, k key) and -W^T (rows key, k chunk) fragments, read transposed out of
+  // the Kbar^T and -W tiles
+  const uint32_t troff = tr_lane_off(lane);
+  auto kb_frag = [&](int slot, int mt, int kt) -> bf16x8 {
+    const unsigned char *b = smem + slot * WGB_SLOT + troff + 8 * (mt & 1);
+    return tr_frag(b + (24 + 4 * kt + (mt >> 1)) * 1024, b + (26 + 4 * kt + (mt >> 1)) * 1024);
+  };
+  auto wt_frag = [&](int slot, int mt, int kt) -> bf16x8 {
+    const unsigned char *b = smem + slot * WGB_SLOT + troff + 8 * (mt & 1);
+    return tr_frag(b + (40 + 8 * kt + (mt >> 1)) * 1024, b + (44 + 8 * kt + (mt >> 1)) * 1024);
   };
 
   if (nch > 0) {
@@ -412,7 +447,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 24 + mt * 4 + kt), dSb[kt], dV[mt]);
+        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(kb_frag(slot, mt, kt), dSb[kt], dV[mt]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const float4 e = *reinterpret_cast<const float4 *>(sg + CH + 16 * mt + 4 * lg);
@@ -430,7 +465,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(frag(slot, 24 + mt * 4 + kt), dSb[kt], dV[mt]);
+        for (int mt = 0; mt < 4; ++mt) dV[mt] = mfma(kb_frag(slot, mt, kt), dSb[kt], dV[mt]);
     }
     {  // dVn^T rows of this slice's columns: 8 consecutive chunk rows 32h + 8lg.. per lane
       u16 *tr = w.dVnT + u * (CH * HD) + (size_t)vcol * CH + 8 * lg;
@@ -445,7 +480,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_wg_kernel(Problem p, Workspa
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(frag(slot, 40 + mt * 2 + kt), dVb[kt], dS[mt]);
+      for (int mt = 0; mt < 8; ++mt) dS[mt] = mfma(wt_frag(slot, mt, kt), dVb[kt], dS[mt]);
 
     // the next chunk's copies: behind them this step issued 2 dout loads and 2 dVn^T
     // stores, which may stay in flight

@@ -123,6 +123,39 @@ __device__ __forceinline__ bf16x8 acc_pair_to_b(f32x4 hi, f32x4 lo) {
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// Transposed fragments.  A tile of a kwalk-ordered A fragment of a matrix X
+// (rows r, reduction c) holds in slot s (lane s, 16 bytes) row 16 mt + (s & 15)
+// and two runs of four consecutive c: 32 kt + 4 (s >> 4) + 0..3 (bytes 0..7) and
+// 32 kt + 16 + 4 (s >> 4) + 0..3 (bytes 8..15).  The kwalk-ordered A fragment of
+// X^T (rows c, reduction r) is built from two such tiles in LDS by gfx950's
+// transposed read, ds_read_b64_tr_b16: within each 16-lane row of the
+// wavefront it hands lane 4a + e element e of the 8-byte pieces that lanes a,
+// 4 + a, 8 + a and 12 + a address, in that order (measured on the device).  So
+// lane (lr, lg) addresses slot 4 lg + (lr >> 2) + 16 (lr & 3) and receives four
+// consecutive reduction rows of its X^T row:
+//   X^T tile (mt', kt'): half 0 from X tile (2 kt', mt' >> 1), half 1 from X tile
+//   (2 kt' + 1, mt' >> 1), both at byte 8 (mt' & 1) of the addressed slots.
+// In LDS the slots of a tile are permuted (position p holds slot tr_slot(p), an
+// involution), so that the 16 lanes of a row address 16 different 16-byte
+// positions modulo 256 bytes instead of 4 groups of 4 on the same banks.
+__device__ __forceinline__ int tr_slot(int p) { return p ^ (((p >> 4) & 3) << 2); }
+// byte offset, within a permuted tile, of the piece this lane addresses (half 0)
+__device__ __forceinline__ uint32_t tr_lane_off(int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  return (uint32_t)(tr_slot(4 * lg + (lr >> 2) + 16 * (lr & 3)) * 16);
+}
+typedef __bf16 bf16x4v __attribute__((__vector_size__(8)));
+// The X^T fragment from LDS: lo and hi point at this lane's pieces (tile base +
+// tr_lane_off + 8 (mt' & 1)) of the two X tiles.
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *lo, const unsigned char *hi) {
+  typedef __attribute__((address_space(3))) bf16x4v *lds_v4;
+  const bf16x4v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4)(const_cast<unsigned char *>(lo)));
+  const bf16x4v b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4)(const_cast<unsigned char *>(hi)));
+  const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+  return __builtin_bit_cast(bf16x8, u32x4{x.x, x.y, y.x, y.y});
+}
+
 // x ~= hi + lo with both parts bf16: a product against an exact bf16 operand
 // then carries about 16 significant bits instead of 8.
 __device__ __forceinline__ void split_bf16(float x, bf16x8 &hi, bf16x8 &lo, int i) {

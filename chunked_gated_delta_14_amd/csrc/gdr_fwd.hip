@@ -167,8 +167,8 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   float *sB = reinterpret_cast<float *>(smem + P_B);
   float *sD = reinterpret_cast<float *>(smem + P_D);
   float *sEG = reinterpret_cast<float *>(smem + P_EG);
-  // fragments shared by a Q/K head's value heads (K^T, K, scale Q^T with one gate per
-  // row; Kbar^T, Kbar, scale (Q Gamma)^T per channel, where H_qk = H_v): slot of
+  // fragments shared by a Q/K head's value heads (K^T and scale Q^T with one gate per
+  // row; Kbar^T and scale (Q Gamma)^T per channel, where H_qk = H_v): slot of
   // (chunk, Q/K head), written by the group's first value head
   const int grp = p.Hv / p.Hqk;
   const bool lead = j % grp == 0;
@@ -427,10 +427,6 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         *reinterpret_cast<uint2 *>(w.Uacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4) = pack4bf(Ud[h][n]);
       }
     }
-    if (SAVE)
-#pragma unroll
-      for (int n = 0; n < 2; ++n)  // -W^T: rows key 16nt.., k: chunk 32kp + kwalk
-        w.WTn[u * FRAG_64x128_U4 + ((2 * cg + n) * 2 + kp) * 64 + lane] = as_u4(acc_pair_to_b(-Wd[0][n], -Wd[1][n]));
     lds_barrier();  // beta k exp(G) and beta v are dead
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -507,13 +503,6 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         const uint2 qa = *reinterpret_cast<const uint2 *>(sQG + o), qb = *reinterpret_cast<const uint2 *>(sQG + o + 16);
         w.QGT[uq * FRAG_64x128_U4 + slot] = make_uint4(qa.x, qa.y, qb.x, qb.y);
       }
-    }
-    if (SAVE) {  // rows: chunk (16 mt + r_), k: key (32 kt + kwalk)
-      const int mt = tile >> 2, kt = tile & 3, row = 16 * mt + r_;
-      bf16x8 kb;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) kb[ii] = __builtin_bit_cast(__bf16, sKL[(32 * kt + kwalk(g_, ii)) * CTP + row]);
-      w.Kb[uq * FRAG_64x128_U4 + slot] = as_u4(kb);
     }
   }
   if (SAVE && tid < CH * CH / 8) {  // T^T, bf16 row-major, for the gradient kernel
@@ -822,8 +811,12 @@ constexpr int WG_NW = 4;    // slice wavefronts per ring workgroup (two workgrou
 constexpr int WG_RING = 2;  // slots: the chunk in use, the next one in flight
 constexpr int WG_SMEM = WG_RING * WG_SLOT;
 
+// Its LDS ring leaves room for one workgroup per compute unit, so one wavefront per
+// SIMD: the compiler may use the whole register file and keep more LDS fragment
+// reads in flight ahead of the products.
 template <bool SAVE, bool OUT, int NW, bool SG = false>
-__global__ __launch_bounds__(64 * NW) void fwd_walk_wg_kernel(Problem p, Workspace w, u16 *o, float *ht) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_walk_wg_kernel(Problem p, Workspace w, u16 *o, float *ht) {
   extern __shared__ __align__(16) unsigned char smem[];
   const ChunkTable tb(p.table, p.NC, p.N);
   int chain, half;

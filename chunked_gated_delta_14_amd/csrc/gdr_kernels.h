@@ -14,16 +14,15 @@ struct Workspace {
   // forward-walk operands (written by the prep kernel, read by the forward walk)
   uint4 *WfN;   // -W, A fragments (rows: chunk, k: key), 16 tiles
   uint4 *Pf;    // scale * (Q.Gamma - M W), A fragments (rows: chunk, k: key)
-  // KbT, Kb and QGT are indexed by (chunk, Q/K head), uq = chunk * H_qk + Q/K head
-  // (KDA: H_qk = H_v, so uq = u); with one gate per row (GDN) they hold K^T, K and
-  // scale * Q^T, shared by the group's value heads, and the walks apply the rows' gates
+  // KbT and QGT are indexed by (chunk, Q/K head), uq = chunk * H_qk + Q/K head
+  // (KDA: H_qk = H_v, so uq = u); with one gate per row (GDN) they hold K^T and
+  // scale * Q^T, shared by the group's value heads, and the walks apply the rows' gates.
+  // The adjoint walk reads Kbar and -W^T transposed out of KbT and WfN (tr_frag).
   uint4 *KbT;   // Kbar^T, A fragments (rows: key, k: chunk)
   uint16_t *Uacc;  // U in accumulator order, [u][vslice 8][mtile 4][lane 64][4]
   uint16_t *Oacc;  // scale * M U in accumulator order
   float *gam;      // exp(G_last) per channel, [u][128]; GDN: exp(G_r), then exp(G_last - G_r), 64 rows each
   // backward-walk operands (written by the prep kernel with GDR_FWD_SAVE)
-  uint4 *Kb;    // Kbar, A fragments (rows: chunk, k: key)
-  uint4 *WTn;   // -W^T, A fragments (rows: key, k: chunk)
   uint4 *QGT;   // scale * (Q.Gamma)^T, A fragments (rows: key, k: chunk)
   uint4 *MTs;   // scale * M^T, A fragments (rows: chunk, k: chunk), 8 tiles
   uint4 *Tt;    // T^T, T = (I + diag(beta) E)^-1, bf16 row-major 64 x 64

@@ -85,11 +85,11 @@ def test_workspace_bytes_monotone_and_aligned():
         assert full > fwd and full > prev
         prev = full
     # GDN sizes by value heads, except what a Q/K head's value heads share: the q/k
-    # inverse norms (one pair per (token, Q/K head)) and the walks' K^T, K and scale Q^T
-    # fragments (16 KB each per (chunk, Q/K head))
+    # inverse norms (one pair per (token, Q/K head)) and the walks' K^T and scale Q^T
+    # fragments (16 KB each per (chunk, Q/K head); the adjoint walk reads K out of K^T)
     a = gdr.workspace_bytes(gdr.GDR_GDN, 640, 1, 10, 16, 48, 128, 128, 1)
     b = gdr.workspace_bytes(gdr.GDR_KDA, 640, 1, 10, 48, 48, 128, 128, 1)
-    assert b - a == 640 * (48 - 16) * 2 * 4 + 3 * 16384 * 10 * (48 - 16)
+    assert b - a == 640 * (48 - 16) * 2 * 4 + 2 * 16384 * 10 * (48 - 16)
     # forward only: the shared K^T fragments
     assert gdr.workspace_bytes(gdr.GDR_KDA, 640, 1, 10, 48, 48, 128, 128, 0) - \
         gdr.workspace_bytes(gdr.GDR_GDN, 640, 1, 10, 16, 48, 128, 128, 0) == 16384 * 10 * (48 - 16)
