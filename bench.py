@@ -26,13 +26,15 @@ METRIC = "KDA fwd+bwd token-heads/s, H=16, T=261392 (1 GPU); % MFMA & HBM peak"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
-# Per (chunk, value head) unit bytes of the workspace regions; the Kbar^T, Kbar and
+# Per (chunk, value head) unit bytes of the workspace regions; the Kbar^T and
 # (q Gamma)^T fragments are per (chunk, Q/K head) (with one gate per row they are a
-# Q/K head's K^T, K and scale Q^T, shared by its value heads; KDA has H_qk = H_v).
+# Q/K head's K^T and scale Q^T, shared by its value heads; KDA has H_qk = H_v).
 SHARED_FWD = 16384                             # Kbar^T
-SHARED_BWD = 16384 * 2                         # Kbar, (q Gamma)^T
+SHARED_BWD = 16384                             # (q Gamma)^T
 FWD_OPERANDS = 16384 * 2 + 16384 * 2 + 512   # -W, P fragments; U, Oi; gamma
-BWD_OPERANDS = 16384 + 8192                   # -W^T fragments; M^T
+BWD_OPERANDS = 8192                            # M^T
+# the adjoint walk also reads the forward walk's -W (per unit) and Kbar^T (shared)
+# fragments, for Kbar and -W^T by transposed reads, and gamma
 TE_SAVED = 8192 + 5120                         # T^T (bf16 64 x 64) and E's 10 lower tiles (bf16)
 S_TAPE, ROW_TAPE = 32768, 16384
 # Bytes per token-head that the method must move for fwd + bwd with bf16 state
@@ -83,7 +85,8 @@ def kernel_bytes(name, T, Hqk, Hv, NC, N, gdn, save=True):
     if name == "fwd_walk":
         return fwd_ops + v + units * ((S_TAPE + ROW_TAPE) if save else 0) + N * Hv * 65536
     if name == "bwd_walk":
-        return bwd_ops + units * (512 + S_TAPE + ROW_TAPE) + v + N * Hv * 65536
+        return (bwd_ops + units * 16384 + qk_units * SHARED_FWD + units * (512 + S_TAPE + ROW_TAPE) + v
+                + N * Hv * 65536)
     if name == "bwd_grad":
         return (2 * qk + 3 * v + g * 2 + beta * 2) + units * (2 * S_TAPE + 2 * ROW_TAPE + TE_SAVED)
     raise KeyError(name)
