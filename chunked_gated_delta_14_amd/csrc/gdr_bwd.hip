@@ -39,8 +39,9 @@ namespace gdr {
 // start, dout as given; second half: identity start, dout = 0); pass 2 starts
 // segment s from dht carried back
 // through segments P_d - 1 .. s + 1 and writes the tapes; dh0 comes from segment 0.
-// SG: one gate per row (GDN): the Q/K head's scale Q^T and K fragments, with dout's
-// rows scaled by exp(G_r) for the first and K dS' rows by exp(G_last - G_r).
+// SG: one gate per row (GDN): the Q/K head's scale Q^T and K^T fragments (K read
+// transposed), with dout's rows scaled by exp(G_r) for the first and K dS' rows by
+// exp(G_last - G_r).
 template <int MODE = MODE_WALK, bool SG = false>
 __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, const u16 *dout,
                                                       const float *dht, float *dh0) {
