@@ -1,7 +1,7 @@
-// Peak probes for the measurement script (not part of libgdr's ABI): a
+// Probes for the measurement script and the tests (not part of libgdr's ABI): a
 // pure-MFMA loop and stream kernels over device buffers, so that achieved
 // rates can be set beside rates measured on the same device, not only beside
-// the published peaks.
+// the published peaks; and the lane layout of the transposed LDS read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,9 +76,34 @@ __global__ __launch_bounds__(256) void fill_kernel(uint4 *dst, size_t n) {
     dst[i] = make_uint4(1u, 2u, 3u, 4u);
 }
 
+// Lane layout of gfx950's transposed LDS read (ds_read_b64_tr_b16), which the
+// adjoint walk's fragment transposes rely on.  An LDS block holds the u16 values
+// 0..511 in order, so the 8-byte piece p holds 4p..4p+3; lane l addresses piece
+// l (mode 0) or 63 - l (mode 1), and out[4 l + e] is element e of its result.
+// Every address lies inside the 1 KB block.
+__global__ __launch_bounds__(64) void tr16_kernel(uint16_t *out, int mode) {
+  typedef __bf16 bf16x4v __attribute__((__vector_size__(8)));
+  __shared__ __align__(16) uint16_t lds[512];
+  const int l = threadIdx.x;
+  for (int i = l; i < 512; i += 64) lds[i] = (uint16_t)i;
+  __syncthreads();
+  const int piece = mode == 0 ? l : 63 - l;
+  const bf16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4v *)(lds + 4 * piece));
+  uint16_t v[4];
+  __builtin_memcpy(v, &r, 8);
+  for (int e = 0; e < 4; ++e) out[4 * l + e] = v[e];
+}
+
 }  // namespace
 
 extern "C" {
+
+// One 64-lane transposed LDS read (tr16_kernel): out is a device uint16_t[256].
+int gdr_probe_tr16(uint16_t *out, int mode, hipStream_t st) {
+  if (!out || mode < 0 || mode > 1) return (int)hipErrorInvalidValue;
+  tr16_kernel<<<1, 64, 0, st>>>(out, mode);
+  return (int)hipGetLastError();
+}
 
 // Launches blocks x 256 threads of a pure-MFMA loop (below).  sink: device
 // float[blocks * 256], never written in practice.  Returns a hipError_t code.
