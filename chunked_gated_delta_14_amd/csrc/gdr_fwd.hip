@@ -374,7 +374,25 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   lds_barrier();
   if (has_next) prep_load<SCALAR, PF_B>(next, p, tb, next_unit, tid, reuse_in);
 
-  // ---- 3. column-form operands (over the step-1 space), then T ----
+  // ---- 3. column-form operands (over the step-1 space), then T.  While wavefront 0
+  // inverts T's diagonal blocks, the others zero its upper blocks and store the walk
+  // operands that come straight from the column-form tiles (K-bar^T and scale (q Gamma)^T,
+  // shared by the group).  With the input activations (ACT) the register budget has
+  // no room for that overlap (the kernel would spill): those stores stay at the end of
+  // the unit. ----
+  // slot of the K-bar^T and scale (q Gamma)^T fragments: rows key (16 mt + r_), k: chunk
+  // (32 kt + kwalk), two 4-row runs of a column-form row
+  auto store_shared_frag = [&](int slot) {
+    const int tile = slot >> 6, ln = slot & 63, r_ = ln & 15, g_ = ln >> 4;
+    const int mt = tile >> 1, kt = tile & 1, key = 16 * mt + r_;
+    const int o = key * CTP + 32 * kt + 4 * g_;
+    const uint2 a = *reinterpret_cast<const uint2 *>(sKL + o), b = *reinterpret_cast<const uint2 *>(sKL + o + 16);
+    w.KbT[uq * FRAG_64x128_U4 + slot] = make_uint4(a.x, a.y, b.x, b.y);
+    if (SAVE) {
+      const uint2 qa = *reinterpret_cast<const uint2 *>(sQG + o), qb = *reinterpret_cast<const uint2 *>(sQG + o + 16);
+      w.QGT[uq * FRAG_64x128_U4 + slot] = make_uint4(qa.x, qa.y, qb.x, qb.y);
+    }
+  };
 #pragma unroll
   for (int ii = 0; ii < 8; ++ii) {
     const int off = (c0 + ii) * CTP + rp;
@@ -383,7 +401,21 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     *reinterpret_cast<uint32_t *>(sQG + off) = pkQG[ii];
     *reinterpret_cast<uint32_t *>(sKL + off) = pkKL[ii];
   }
-  tri_inverse<PNT>(sT, sE, sB, tid);  // ends with a barrier
+  if constexpr (!ACT) {
+    lds_barrier();  // the column-form tiles are complete
+    if (wave == 0) {
+      tri_inverse_diag(sT, sE, sB, lane);
+    } else {
+      tri_zero_upper(sT, tid - 64, PNT - 64);
+#pragma unroll 1
+      for (int slot = tid - 64; lead && slot < 1024; slot += PNT - 64) store_shared_frag(slot);
+    }
+  } else {
+    tri_zero_upper(sT, tid, PNT);
+    if (wave == 0) tri_inverse_diag(sT, sE, sB, lane);
+  }
+  lds_barrier();
+  tri_inverse_levels(sT, sE, sB, tid);  // ends with a barrier
   if (has_next) prep_load<SCALAR, PF_C>(next, p, tb, next_unit, tid, reuse_in);
 
   // ---- 4. W = T (beta k exp G), W^T, U = T (beta v).  Wavefront: row blocks
@@ -491,20 +523,8 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     }
   }
 
-  // ---- remaining walk operands from the column-form tiles (shared by the group) ----
-  for (int slot = tid; lead && slot < 1024; slot += PNT) {
-    const int tile = slot >> 6, ln = slot & 63, r_ = ln & 15, g_ = ln >> 4;
-    {  // rows: key (16 mt + r_), k: chunk (32 kt + kwalk): two 4-row runs of a column-form row
-      const int mt = tile >> 1, kt = tile & 1, key = 16 * mt + r_;
-      const int o = key * CTP + 32 * kt + 4 * g_;
-      const uint2 a = *reinterpret_cast<const uint2 *>(sKL + o), b = *reinterpret_cast<const uint2 *>(sKL + o + 16);
-      w.KbT[uq * FRAG_64x128_U4 + slot] = make_uint4(a.x, a.y, b.x, b.y);
-      if (SAVE) {
-        const uint2 qa = *reinterpret_cast<const uint2 *>(sQG + o), qb = *reinterpret_cast<const uint2 *>(sQG + o + 16);
-        w.QGT[uq * FRAG_64x128_U4 + slot] = make_uint4(qa.x, qa.y, qb.x, qb.y);
-      }
-    }
-  }
+  if constexpr (ACT)
+    for (int slot = tid; lead && slot < 1024; slot += PNT) store_shared_frag(slot);
   if (SAVE && tid < CH * CH / 8) {  // T^T, bf16 row-major, for the gradient kernel
     const int r = tid >> 3, c8 = (tid & 7) * 8;
     bf16x8 tv;
