@@ -131,9 +131,9 @@ typedef struct gdr_problem {
  *   per-chunk operands through its own memory pipeline: the shortest chain step,
  *   but a compute unit retires about one slice step at a time.
  * GDR_WALK_RINGS: the slice wavefronts of a chain in workgroups of four that
- *   pass each chunk's shared operands through an LDS ring (forward walk: three
- *   slots, 146 KB; adjoint walk: two slots, 113 KB): a longer chain step, about
- *   four times the work per compute unit.
+ *   pass each chunk's shared operands through an LDS ring of two slots (forward
+ *   walk 97 KB, adjoint walk 113 KB): a longer chain step, about four times the
+ *   work per compute unit.
  * GDR_WALK_AUTO: the layout with the smaller estimated walk time, from the
  *   longest chain (max_doc_chunks) and the work per compute unit; segmented
  *   walks (see walk_segments) always use slices. */
