@@ -363,14 +363,15 @@ __device__ __forceinline__ f32x4 tile_row4_f32(f32x4 x, int lane) {
 }
 
 // T = (I + diag(beta) E)^-1 (unit lower triangular, fp32) for a strictly
-// lower 64 x 64 E (pitch SP) in blocks of 16, in three pieces:
+// lower 64 x 64 E, given as sA = -diag(beta) E (pitch SP), in blocks of 16,
+// in three pieces:
 //  - tri_zero_upper: the six strictly upper blocks of T, by any threads;
 //  - tri_inverse_diag (wavefront 0): the four diagonal blocks by right-looking
 //    forward substitution, one lane per column; it ends without a barrier, so
 //    the other wavefronts can work meanwhile;
 //  - tri_inverse_levels (after a barrier): the off-diagonal blocks level by
 //    level (I - J = 1, 2, 3) as
-//      T_IJ = -T_II sum_{J <= K < I} diag(beta_I) E_IK T_KJ,
+//      T_IJ = T_II sum_{J <= K < I} A_IK T_KJ,
 //    one wavefront per block with fp32 MFMAs.  The inner sum uses reduction
 //    index k = 4q + lg in step q; the product with T_II uses k = 4lg + q, so
 //    the sum's accumulator is its B operand as it stands.  Ends with a barrier.
@@ -382,39 +383,35 @@ __device__ __forceinline__ void tri_zero_upper(float *sT, int t0, int nt) {
     sT[(16 * I + (idx >> 4)) * SP + 16 * J + (idx & 15)] = 0.f;
   }
 }
-__device__ __forceinline__ void tri_inverse_diag(float *sT, const float *sE, const float *sB, int lane) {
+__device__ __forceinline__ void tri_inverse_diag(float *sT, const float *sA, int lane) {
   const int base = 16 * (lane >> 4), s = lane & 15;
-  float x[16], nb[16];
+  float x[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    x[r] = (r == s) ? 1.f : 0.f;
-    nb[r] = -sB[base + r];
-  }
+  for (int r = 0; r < 16; ++r) x[r] = (r == s) ? 1.f : 0.f;
 #pragma unroll
   for (int t = 0; t < 15; ++t)
 #pragma unroll
-    for (int r = t + 1; r < 16; ++r) x[r] += nb[r] * sE[(base + r) * SP + base + t] * x[t];
+    for (int r = t + 1; r < 16; ++r) x[r] += sA[(base + r) * SP + base + t] * x[t];
 #pragma unroll
   for (int r = 0; r < 16; ++r) sT[(base + r) * SP + base + s] = x[r];
 }
-__device__ __forceinline__ void tri_inverse_levels(float *sT, const float *sE, const float *sB, int tid) {
+__device__ __forceinline__ void tri_inverse_levels(float *sT, const float *sA, int tid) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   for (int d = 1; d < 4; ++d) {
     if (wave < 4 - d) {
       const int J = wave, I = J + d, row = 16 * I + lr;
-      const float br = sB[row];
       f32x4 X = zero4();
       for (int K = J; K < I; ++K)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int k = 4 * q + lg;
-          X = mfma4(br * sE[row * SP + 16 * K + k], sT[(16 * K + k) * SP + 16 * J + lr], X);
+          X = mfma4(sA[row * SP + 16 * K + k], sT[(16 * K + k) * SP + 16 * J + lr], X);
         }
       f32x4 Y = zero4();
 #pragma unroll
       for (int q = 0; q < 4; ++q) Y = mfma4(sT[row * SP + 16 * I + 4 * lg + q], X[q], Y);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sT[(16 * I + 4 * lg + jj) * SP + 16 * J + lr] = -Y[jj];
+      for (int jj = 0; jj < 4; ++jj) sT[(16 * I + 4 * lg + jj) * SP + 16 * J + lr] = Y[jj];
     }
     lds_barrier();
   }

@@ -59,7 +59,7 @@ constexpr int P_QG = P_BV + HD * CTP * 2;  // scale q exp(G)
 constexpr int P_KL = P_QG + HD * CTP * 2;  // Kbar = k exp(G_last - G)
 constexpr int P_WT = P_BKG;                // W (column form)
 constexpr int P_UT = P_BV;                 // U (column form)
-constexpr int P_E = P_KL + HD * CTP * 2;   // E fp32 [64][SP]
+constexpr int P_E = P_KL + HD * CTP * 2;   // A = -diag(beta) E fp32 [64][SP]
 constexpr int P_T = P_E + CH * SP * 4;     // T fp32 [64][SP]
 constexpr int P_M = P_T + CH * SP * 4;     // M bf16 [64][MP]
 constexpr int P_B = P_M + CH * MP * 2;     // beta [64]
@@ -161,7 +161,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   u16 *sKL = reinterpret_cast<u16 *>(smem + P_KL);
   u16 *sWT = reinterpret_cast<u16 *>(smem + P_WT);
   u16 *sUT = reinterpret_cast<u16 *>(smem + P_UT);
-  float *sE = reinterpret_cast<float *>(smem + P_E);
+  float *sA = reinterpret_cast<float *>(smem + P_E);
   float *sT = reinterpret_cast<float *>(smem + P_T);
   u16 *sM = reinterpret_cast<u16 *>(smem + P_M);
   float *sB = reinterpret_cast<float *>(smem + P_B);
@@ -355,13 +355,15 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int I = 2 * kt2 + h;
+      const float4 b4 = *reinterpret_cast<const float4 *>(sB + 16 * I + 4 * lg);
+      const float nb[4] = {-b4.x, -b4.y, -b4.z, -b4.w};
       f32x4 ev;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * I + 4 * lg + jj;
         const float e = (I >= J && s < r) ? aE[h][jj] : 0.f;
         const float m = (I >= J && s <= r) ? aMc[h][jj] : 0.f;
-        sE[r * SP + s] = e;
+        sA[r * SP + s] = nb[jj] * e;
         sM[r * MP + s] = f2bf(m);
         ev[jj] = e;
         ms[h][jj] = scale * m;
@@ -377,9 +379,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   // ---- 3. column-form operands (over the step-1 space), then T.  While wavefront 0
   // inverts T's diagonal blocks, the others zero its upper blocks and store the walk
   // operands that come straight from the column-form tiles (K-bar^T and scale (q Gamma)^T,
-  // shared by the group).  With the input activations (ACT) the register budget has
-  // no room for that overlap (the kernel would spill): those stores stay at the end of
-  // the unit. ----
+  // shared by the group). ----
   // slot of the K-bar^T and scale (q Gamma)^T fragments: rows key (16 mt + r_), k: chunk
   // (32 kt + kwalk), two 4-row runs of a column-form row
   auto store_shared_frag = [&](int slot) {
@@ -401,21 +401,16 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     *reinterpret_cast<uint32_t *>(sQG + off) = pkQG[ii];
     *reinterpret_cast<uint32_t *>(sKL + off) = pkKL[ii];
   }
-  if constexpr (!ACT) {
-    lds_barrier();  // the column-form tiles are complete
-    if (wave == 0) {
-      tri_inverse_diag(sT, sE, sB, lane);
-    } else {
-      tri_zero_upper(sT, tid - 64, PNT - 64);
-#pragma unroll 1
-      for (int slot = tid - 64; lead && slot < 1024; slot += PNT - 64) store_shared_frag(slot);
-    }
+  lds_barrier();  // the column-form tiles are complete
+  if (wave == 0) {
+    tri_inverse_diag(sT, sA, lane);
   } else {
-    tri_zero_upper(sT, tid, PNT);
-    if (wave == 0) tri_inverse_diag(sT, sE, sB, lane);
+    tri_zero_upper(sT, tid - 64, PNT - 64);
+#pragma unroll 1
+    for (int slot = tid - 64; lead && slot < 1024; slot += PNT - 64) store_shared_frag(slot);
   }
   lds_barrier();
-  tri_inverse_levels(sT, sE, sB, tid);  // ends with a barrier
+  tri_inverse_levels(sT, sA, tid);  // ends with a barrier
   if (has_next) prep_load<SCALAR, PF_C>(next, p, tb, next_unit, tid, reuse_in);
 
   // ---- 4. W = T (beta k exp G), W^T, U = T (beta v).  Wavefront: row blocks
@@ -523,8 +518,6 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     }
   }
 
-  if constexpr (ACT)
-    for (int slot = tid; lead && slot < 1024; slot += PNT) store_shared_frag(slot);
   if (SAVE && tid < CH * CH / 8) {  // T^T, bf16 row-major, for the gradient kernel
     const int r = tid >> 3, c8 = (tid & 7) * 8;
     bf16x8 tv;
