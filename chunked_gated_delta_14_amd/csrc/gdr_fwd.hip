@@ -66,6 +66,14 @@ constexpr int P_B = P_M + CH * MP * 2;     // beta [64]
 constexpr int P_D = P_B + 64 * 4;          // D_IJ [6][128]
 constexpr int P_EG = P_D + 768 * 4;       // exp(G_r) [64] (scalar gate: P's row scale)
 constexpr int P_SMEM = P_EG + 64 * 4;
+// One gate per row (GDN) only: the cumulative gate G_r, and K K^T, Q K^T of the
+// Q/K head (fp32, lower blocks), formed by the group's first value head and kept
+// for the others.
+constexpr int P_GR = P_SMEM;               // G_r [64]
+constexpr int P_KK = P_GR + 64 * 4;        // K K^T fp32 [64][SP]
+constexpr int P_QK = P_KK + CH * SP * 4;   // Q K^T fp32 [64][SP]
+constexpr int P_SMEM_SCALAR = P_QK + CH * SP * 4;
+static_assert(P_SMEM_SCALAR <= 160 * 1024, "prep LDS map (one gate per row)");
 static_assert(P_KFI + CH * GP * 4 <= P_E, "prep LDS map");
 
 __device__ __forceinline__ uint32_t pack2bf(float a, float b) {
@@ -167,6 +175,9 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   float *sB = reinterpret_cast<float *>(smem + P_B);
   float *sD = reinterpret_cast<float *>(smem + P_D);
   float *sEG = reinterpret_cast<float *>(smem + P_EG);
+  float *sGR = reinterpret_cast<float *>(smem + P_GR);
+  float *sKK = reinterpret_cast<float *>(smem + P_KK);
+  float *sQK = reinterpret_cast<float *>(smem + P_QK);
   // fragments shared by a Q/K head's value heads (K^T and scale Q^T with one gate per
   // row; Kbar^T and scale (Q Gamma)^T per channel, where H_qk = H_v): slot of
   // (chunk, Q/K head), written by the group's first value head
@@ -180,7 +191,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
   // reference gates are in-wave shuffles. ----
   const int o = tid >> 5, pr = tid & 31, c0 = 8 * o, rp = 2 * pr;
   uint32_t pkBKG[8], pkBV[8], pkQG[8], pkKL[8];  // channel c0+ii: rows rp, rp+1 as a bf16 pair
-  float rowg[2], rowl[2];  // one gate per row: exp(G_r), exp(G_last - G_r) of rows rp, rp+1
+  float rowg[2], rowl[2], rowG[2];  // one gate per row: exp(G_r), exp(G_last - G_r), G_r of rows rp, rp+1
   {
     constexpr int NG = SCALAR ? 1 : 8;  // gate values per row held by a thread
     const bf16x8 *kx = in.k, *qx = in.q, *vx = in.v;
@@ -265,10 +276,9 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
       const float a = pr == 6 ? gl : (I == 1 ? gr[1] : (I == 2 ? gr[2] : gr[3]));
       const float b = pr == 6 ? 0.f : (J == 0 ? gr[0] : (J == 1 ? gr[1] : gr[2]));
       const float e = __expf(a - b);
-#pragma unroll
-      for (int cc = (SCALAR ? 0 : ic); cc < (SCALAR ? 8 : ic + 1); ++cc) {
-        if (pr < 6) sD[pr * 128 + c0 + cc] = e;
-        else if (pr == 6 && !SCALAR) w.gam[u * HD + c0 + cc] = e;
+      if constexpr (!SCALAR) {
+        if (pr < 6) sD[pr * 128 + c0 + ic] = e;
+        else if (pr == 6) w.gam[u * HD + c0 + ic] = e;
       }
     }
 #pragma unroll
@@ -283,8 +293,8 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         const int ic = SCALAR ? 0 : ii;
         const float F = __expf(G[h][ic] - go[ic]), Fi = __builtin_amdgcn_rcpf(F);
         const float kv = (float)kx[h][ii] * rk[h], qv = (float)qx[h][ii] * rq[h], vv = (float)vx[h][ii];
-        kf[ii] = (__bf16)(kv * F);
-        qf[ii] = (__bf16)(qv * F);
+        kf[ii] = (__bf16)(SCALAR ? kv : kv * F);  // one gate per row: the raw rows
+        qf[ii] = (__bf16)(SCALAR ? qv : qv * F);
         kfi[ii] = kv * Fi;
         const float eg = F * eref[ic];  // exp(G_r)
         const float el = Fi * elr[ic];  // exp(G_last - G_r)
@@ -295,18 +305,24 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         if (ii == 0) {
           rowg[h] = eg;
           rowl[h] = el;
+          rowG[h] = G[h][0];
         }
       }
-      *reinterpret_cast<bf16x8 *>(sKF + r * KP + c0) = kf;
-      *reinterpret_cast<bf16x8 *>(sQF + r * KP + c0) = qf;
-      *reinterpret_cast<float4 *>(sKFi + r * GP + c0) = make_float4(kfi[0], kfi[1], kfi[2], kfi[3]);
-      *reinterpret_cast<float4 *>(sKFi + r * GP + c0 + 4) = make_float4(kfi[4], kfi[5], kfi[6], kfi[7]);
+      if (!SCALAR || lead) {
+        *reinterpret_cast<bf16x8 *>(sKF + r * KP + c0) = kf;
+        *reinterpret_cast<bf16x8 *>(sQF + r * KP + c0) = qf;
+      }
+      if constexpr (!SCALAR) {
+        *reinterpret_cast<float4 *>(sKFi + r * GP + c0) = make_float4(kfi[0], kfi[1], kfi[2], kfi[3]);
+        *reinterpret_cast<float4 *>(sKFi + r * GP + c0 + 4) = make_float4(kfi[4], kfi[5], kfi[6], kfi[7]);
+      }
     }
   }
   if (SCALAR && o == 0) {  // the row scales: P's (LDS) and the walks' (gamma slot)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       sEG[rp + h] = rowg[h];
+      sGR[rp + h] = rowG[h];
       w.gam[u * HD + rp + h] = rowg[h];
       w.gam[u * HD + CH + rp + h] = rowl[h];
     }
@@ -325,30 +341,80 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 
   // ---- 2. gated products.  Wavefront w: column block J = w >> 1 and row
   // blocks I in {2kt, 2kt+1}, kt = w & 1; the two accumulator tiles of M are
-  // then exactly the scale M^T fragment (J, kt). ----
+  // then exactly the scale M^T fragment (J, kt).  With one gate per row,
+  // E = (K K^T) exp(G_r - G_s) and M = (Q K^T) exp(G_r - G_s): the group's first
+  // value head forms K K^T and Q K^T and keeps them in LDS, where each lane
+  // finds its own elements again in the group's other value heads. ----
   {
     const int J = wave >> 1, kt2 = wave & 1, s = 16 * J + lr;
     f32x4 aE[2] = {zero4(), zero4()}, aMc[2] = {zero4(), zero4()};
+    if constexpr (SCALAR) {
+      if (lead) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int c0 = 32 * kc + 8 * lg;
-      const float4 fa = *reinterpret_cast<const float4 *>(sKFi + s * GP + c0);
-      const float4 fb = *reinterpret_cast<const float4 *>(sKFi + s * GP + c0 + 4);
+        for (int kc = 0; kc < 4; ++kc) {
+          const int c0 = 32 * kc + 8 * lg;
+          const bf16x8 bk = ld8(sKF + s * KP + c0);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int I = 2 * kt2 + h;
+            if (I < J) continue;
+            aE[h] = mfma(ld8(sKF + (16 * I + lr) * KP + c0), bk, aE[h]);
+            aMc[h] = mfma(ld8(sQF + (16 * I + lr) * KP + c0), bk, aMc[h]);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * (2 * kt2 + h) + 4 * lg + jj;
+            sKK[r * SP + s] = aE[h][jj];
+            sQK[r * SP + s] = aMc[h][jj];
+          }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r = 16 * (2 * kt2 + h) + 4 * lg + jj;
+            aE[h][jj] = sKK[r * SP + s];
+            aMc[h][jj] = sQK[r * SP + s];
+          }
+      }
+      const float gs = sGR[s];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int I = 2 * kt2 + h;
-        if (I < J) continue;
-        bf16x8 bk;
-        if (I == J) {
-          bk = cvt8(fa, fb);
-        } else {
-          const float *d = sD + ((I * (I - 1)) / 2 + J) * 128 + c0;
-          const float4 da = *reinterpret_cast<const float4 *>(d), db = *reinterpret_cast<const float4 *>(d + 4);
-          bk = cvt8(make_float4(fa.x * da.x, fa.y * da.y, fa.z * da.z, fa.w * da.w),
-                    make_float4(fb.x * db.x, fb.y * db.y, fb.z * db.z, fb.w * db.w));
+        const float4 g4 = *reinterpret_cast<const float4 *>(sGR + 16 * (2 * kt2 + h) + 4 * lg);
+        const float gr[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 16 * (2 * kt2 + h) + 4 * lg + jj;
+          const float f = s <= r ? __expf(gr[jj] - gs) : 0.f;
+          aE[h][jj] *= f;
+          aMc[h][jj] *= f;
         }
-        aE[h] = mfma(ld8(sKF + (16 * I + lr) * KP + c0), bk, aE[h]);
-        aMc[h] = mfma(ld8(sQF + (16 * I + lr) * KP + c0), bk, aMc[h]);
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const int c0 = 32 * kc + 8 * lg;
+        const float4 fa = *reinterpret_cast<const float4 *>(sKFi + s * GP + c0);
+        const float4 fb = *reinterpret_cast<const float4 *>(sKFi + s * GP + c0 + 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int I = 2 * kt2 + h;
+          if (I < J) continue;
+          bf16x8 bk;
+          if (I == J) {
+            bk = cvt8(fa, fb);
+          } else {
+            const float *d = sD + ((I * (I - 1)) / 2 + J) * 128 + c0;
+            const float4 da = *reinterpret_cast<const float4 *>(d), db = *reinterpret_cast<const float4 *>(d + 4);
+            bk = cvt8(make_float4(fa.x * da.x, fa.y * da.y, fa.z * da.z, fa.w * da.w),
+                      make_float4(fb.x * db.x, fb.y * db.y, fb.z * db.z, fb.w * db.w));
+          }
+          aE[h] = mfma(ld8(sKF + (16 * I + lr) * KP + c0), bk, aE[h]);
+          aMc[h] = mfma(ld8(sQF + (16 * I + lr) * KP + c0), bk, aMc[h]);
+        }
       }
     }
     f32x4 ms[2];
@@ -1031,9 +1097,10 @@ int compute_units() {
 // One instantiation per (variant, activations, SAVE, OUT).
 template <bool SCALAR, bool ACT, bool SAVE, bool OUT>
 static hipError_t launch_fwd_prep_k(const Problem &p, const Workspace &w, dim3 grid, dim3 block, hipStream_t st) {
-  hipError_t e = set_dynamic_lds_once((const void *)fwd_prep_kernel<SCALAR, ACT, SAVE, OUT>, P_SMEM);
+  constexpr int lds = SCALAR ? P_SMEM_SCALAR : P_SMEM;
+  hipError_t e = set_dynamic_lds_once((const void *)fwd_prep_kernel<SCALAR, ACT, SAVE, OUT>, lds);
   if (e != hipSuccess) return e;
-  fwd_prep_kernel<SCALAR, ACT, SAVE, OUT><<<grid, block, P_SMEM, st>>>(p, w);
+  fwd_prep_kernel<SCALAR, ACT, SAVE, OUT><<<grid, block, lds, st>>>(p, w);
   return hipGetLastError();
 }
 template <bool SCALAR, bool ACT>
