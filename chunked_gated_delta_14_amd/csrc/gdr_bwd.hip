@@ -172,7 +172,7 @@ __global__ __launch_bounds__(64) void bwd_walk_kernel(Problem p, Workspace w, co
       u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + prow * 16 + pcol;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        *reinterpret_cast<u32x4 *>(tp + kt * 512) = rows8_from_pair(tile_row4(dSb[kt], 0, eye), tile_row4(dSb[kt], 1, eye));
+        st_stream(reinterpret_cast<u32x4 *>(tp + kt * 512), rows8_from_pair(tile_row4(dSb[kt], 0, eye), tile_row4(dSb[kt], 1, eye)));
     }
 
     // dS' = gamma dS + scale (q Gamma)^T dout first (needs only dout), then dVn, then - W^T dVn.
@@ -385,7 +385,7 @@ void bwd_walk_wg_kernel(Problem p, Workspace w, const u16 *dout, const float *dh
       u16 *tp = w.dS + u * (HD * HD) + sl * (HD * 16) + prow * 16 + pcol;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        *reinterpret_cast<u32x4 *>(tp + kt * 512) = rows8_from_pair(tile_row4(dSb[kt], 0, eye), tile_row4(dSb[kt], 1, eye));
+        st_stream(reinterpret_cast<u32x4 *>(tp + kt * 512), rows8_from_pair(tile_row4(dSb[kt], 0, eye), tile_row4(dSb[kt], 1, eye)));
     }
 
     const float *sg = reinterpret_cast<const float *>(smem + slot * WGB_SLOT + WGB_TILES * 1024);

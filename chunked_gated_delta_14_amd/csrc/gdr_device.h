@@ -240,6 +240,20 @@ __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)"
 template <int K>
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory"); }
 
+// Streaming stores of workspace fragments and tapes that a later kernel reads
+// back.  They carry the nontemporal hint only where every instruction covers
+// whole 128-byte lines (a wavefront's 1 KB or 512 B contiguous block); stores
+// of row pieces (outputs, the transposed dVn tape) keep the default policy:
+// with the hint, partial-line stores made the kernels 15-40 % slower.
+__device__ __forceinline__ void st_stream(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_stream(uint4 *p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void st_stream(uint2 *p, uint2 v) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2 *>(p));
+}
+
 // Stores of 16-byte row pieces through a buffer resource whose record count
 // ends at the last valid byte: the hardware drops stores past it, so a ragged
 // final chunk needs no branch (a branch would split the walk's step into

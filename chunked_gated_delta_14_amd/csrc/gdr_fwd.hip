@@ -435,9 +435,9 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         ms[h][jj] = scale * m;
       }
       if (SAVE && I >= J)  // E for the gradient kernel, accumulator order of tile (I, J)
-        reinterpret_cast<uint2 *>(w.Et + u * FRAG_64x64_U4)[((I * (I + 1)) / 2 + J) * 64 + lane] = pack4bf(ev);
+        st_stream(reinterpret_cast<uint2 *>(w.Et + u * FRAG_64x64_U4) + ((I * (I + 1)) / 2 + J) * 64 + lane, pack4bf(ev));
     }
-    if (SAVE) w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane] = as_u4(acc_pair_to_b(ms[0], ms[1]));
+    if (SAVE) st_stream(&w.MTs[u * FRAG_64x64_U4 + (J * 2 + kt2) * 64 + lane], as_u4(acc_pair_to_b(ms[0], ms[1])));
   }
   lds_barrier();
   if (has_next) prep_load<SCALAR, PF_B>(next, p, tb, next_unit, tid, reuse_in);
@@ -453,10 +453,10 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     const int mt = tile >> 1, kt = tile & 1, key = 16 * mt + r_;
     const int o = key * CTP + 32 * kt + 4 * g_;
     const uint2 a = *reinterpret_cast<const uint2 *>(sKL + o), b = *reinterpret_cast<const uint2 *>(sKL + o + 16);
-    w.KbT[uq * FRAG_64x128_U4 + slot] = make_uint4(a.x, a.y, b.x, b.y);
+    st_stream(&w.KbT[uq * FRAG_64x128_U4 + slot], make_uint4(a.x, a.y, b.x, b.y));
     if (SAVE) {
       const uint2 qa = *reinterpret_cast<const uint2 *>(sQG + o), qb = *reinterpret_cast<const uint2 *>(sQG + o + 16);
-      w.QGT[uq * FRAG_64x128_U4 + slot] = make_uint4(qa.x, qa.y, qb.x, qb.y);
+      st_stream(&w.QGT[uq * FRAG_64x128_U4 + slot], make_uint4(qa.x, qa.y, qb.x, qb.y));
     }
   };
 #pragma unroll
@@ -513,11 +513,11 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // -W: rows chunk 16mt.., k: key 32cg + kwalk
       const int mt = 2 * kp + h;
-      w.WfN[u * FRAG_64x128_U4 + (mt * 4 + cg) * 64 + lane] = as_u4(acc_pair_to_b(-WTd[0][h], -WTd[1][h]));
+      st_stream(&w.WfN[u * FRAG_64x128_U4 + (mt * 4 + cg) * 64 + lane], as_u4(acc_pair_to_b(-WTd[0][h], -WTd[1][h])));
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int nt = 2 * cg + n;
-        *reinterpret_cast<uint2 *>(w.Uacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4) = pack4bf(Ud[h][n]);
+        st_stream(reinterpret_cast<uint2 *>(w.Uacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4), pack4bf(Ud[h][n]));
       }
     }
     lds_barrier();  // beta k exp(G) and beta v are dead
@@ -574,12 +574,12 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
           const int cc = 16 * (2 * cg + n) + 4 * lg + jj;
           pt[n][jj] = bf2f(sQG[cc * CTP + r]) * eg - scale * PT[n][h][jj];
         }
-      w.Pf[u * FRAG_64x128_U4 + (mt * 4 + cg) * 64 + lane] = as_u4(acc_pair_to_b(pt[0], pt[1]));
+      st_stream(&w.Pf[u * FRAG_64x128_U4 + (mt * 4 + cg) * 64 + lane], as_u4(acc_pair_to_b(pt[0], pt[1])));
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int nt = 2 * cg + n;
-        *reinterpret_cast<uint2 *>(w.Oacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4) =
-            pack4bf(scale * Oi[h][n]);
+        st_stream(reinterpret_cast<uint2 *>(w.Oacc + u * ACC_64x128_U16 + ((nt * 4 + mt) * 64 + lane) * 4),
+                  pack4bf(scale * Oi[h][n]));
       }
     }
   }
@@ -589,7 +589,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     bf16x8 tv;
 #pragma unroll
     for (int ii = 0; ii < 8; ++ii) tv[ii] = (__bf16)sT[(c8 + ii) * SP + r];
-    w.Tt[u * FRAG_64x64_U4 + tid] = as_u4(tv);
+    st_stream(&w.Tt[u * FRAG_64x64_U4 + tid], as_u4(tv));
   }
   settle(next);  // no path into the next unit carries an outstanding load
 }
@@ -762,7 +762,7 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
         u16 *st = w.S + u * (HD * HD) + (sl0 + s) * (HD * 16) + prow * 16 + pcol;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-          *reinterpret_cast<u32x4 *>(st + kt * 512) = rows8_from_pair(tile_row4(Sb[s][kt], 0, eye), tile_row4(Sb[s][kt], 1, eye));
+          st_stream(reinterpret_cast<u32x4 *>(st + kt * 512), rows8_from_pair(tile_row4(Sb[s][kt], 0, eye), tile_row4(Sb[s][kt], 1, eye)));
       }
     }
 
@@ -838,7 +838,7 @@ __global__ __launch_bounds__(64) void fwd_walk_kernel(Problem p, Workspace w, u1
         u16 *vt = w.Vn + u * (CH * HD) + (sl0 + s) * (CH * 16) + prow * 16 + pcol;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<u32x4 *>(vt + h * 512) = rows8_from_pair(tile_row4(Vb[s][h], 0, eye), tile_row4(Vb[s][h], 1, eye));
+          st_stream(reinterpret_cast<u32x4 *>(vt + h * 512), rows8_from_pair(tile_row4(Vb[s][h], 0, eye), tile_row4(Vb[s][h], 1, eye)));
       }
     }
 
@@ -987,7 +987,7 @@ void fwd_walk_wg_kernel(Problem p, Workspace w, u16 *o, float *ht) {
       u16 *st = w.S + u * (HD * HD) + sl0 * (HD * 16) + prow * 16 + pcol;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        *reinterpret_cast<u32x4 *>(st + kt * 512) = rows8_from_pair(tile_row4(Sb[kt], 0, eye), tile_row4(Sb[kt], 1, eye));
+        st_stream(reinterpret_cast<u32x4 *>(st + kt * 512), rows8_from_pair(tile_row4(Sb[kt], 0, eye), tile_row4(Sb[kt], 1, eye)));
     }
 
     f32x4 Vn[4], Oc[4];
@@ -1052,7 +1052,7 @@ void fwd_walk_wg_kernel(Problem p, Workspace w, u16 *o, float *ht) {
       u16 *vt = w.Vn + u * (CH * HD) + sl0 * (CH * 16) + prow * 16 + pcol;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4 *>(vt + h * 512) = rows8_from_pair(tile_row4(Vb[h], 0, eye), tile_row4(Vb[h], 1, eye));
+        st_stream(reinterpret_cast<u32x4 *>(vt + h * 512), rows8_from_pair(tile_row4(Vb[h], 0, eye), tile_row4(Vb[h], 1, eye)));
     }
 
 #pragma unroll
