@@ -624,8 +624,8 @@ __device__ __forceinline__ float bf_at(uint2 x, int jj) {
 }
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   uint2 r;
-  r.x = f2bf(a) | ((uint32_t)f2bf(b) << 16);
-  r.y = f2bf(c) | ((uint32_t)f2bf(d) << 16);
+  r.x = pk2bf(a, b);
+  r.y = pk2bf(c, d);
   return r;
 }
 // x ~= hi + lo, both bf16, four values packed per part
@@ -710,7 +710,7 @@ __device__ __forceinline__ void store_qk_rows(u16 *sQT, u16 *sKT, const Problem 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t wd = xr[i][e];
-      y[i][e] = (uint32_t)f2bf(lo_bf(wd) * rs) | ((uint32_t)f2bf(hi_bf(wd) * rs) << 16);
+      y[i][e] = pk2bf(lo_bf(wd) * rs, hi_bf(wd) * rs);
     }
   }
   store_rows_transposed<PITCH>(dst, y, b);

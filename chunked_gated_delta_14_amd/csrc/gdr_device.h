@@ -45,6 +45,13 @@ __device__ __forceinline__ u16 f2bf(float f) {
   __bf16 h = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(u16, h);
 }
+// Two floats to a bf16 pair (a in the low half) by one v_cvt_pk_bf16_f32; the
+// form f2bf(a) | f2bf(b) << 16 costs two conversions, a shift and an or.
+__device__ __forceinline__ uint32_t pk2bf(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

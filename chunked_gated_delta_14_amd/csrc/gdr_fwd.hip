@@ -76,13 +76,10 @@ constexpr int P_SMEM_SCALAR = P_QK + CH * SP * 4;
 static_assert(P_SMEM_SCALAR <= 160 * 1024, "prep LDS map (one gate per row)");
 static_assert(P_KFI + CH * GP * 4 <= P_E, "prep LDS map");
 
-__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
-  return f2bf(a) | ((uint32_t)f2bf(b) << 16);
-}
 __device__ __forceinline__ uint2 pack4bf(const f32x4 &x) {
   uint2 r;
-  r.x = pack2bf(x[0], x[1]);
-  r.y = pack2bf(x[2], x[3]);
+  r.x = pk2bf(x[0], x[1]);
+  r.y = pk2bf(x[2], x[3]);
   return r;
 }
 // One thread's share of a unit's inputs: rows 2pr, 2pr+1 of channels 8o..8o+7
@@ -281,40 +278,50 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         else if (pr == 6) w.gam[u * HD + c0 + ic] = e;
       }
     }
+    // channels c0 + ii of rows rp, rp + 1, in two halves of four channels whose LDS
+    // pieces are stored as soon as they are formed (the rows copied to registers first:
+    // `in` lives in memory, since the next unit may take q and k from it)
+    const bf16x8 kr[2] = {kx[0], kx[1]}, qr[2] = {qx[0], qx[1]}, vr[2] = {vx[0], vx[1]};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pkBKG[i] = pkBV[i] = pkQG[i] = pkKL[i] = 0u;
+    for (int half = 0; half < 2; ++half) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      __bf16 kf[2][4], qf[2][4];
+      float kfi[2][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = rp + h, sh = 16 * h;
-      bf16x8 kf, qf;
-      float kfi[8];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int ii = 4 * half + i4, ic = SCALAR ? 0 : ii;
+        float bk[2], bv[2], qg[2], kl[2];
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii) {
-        const int ic = SCALAR ? 0 : ii;
-        const float F = __expf(G[h][ic] - go[ic]), Fi = __builtin_amdgcn_rcpf(F);
-        const float kv = (float)kx[h][ii] * rk[h], qv = (float)qx[h][ii] * rq[h], vv = (float)vx[h][ii];
-        kf[ii] = (__bf16)(SCALAR ? kv : kv * F);  // one gate per row: the raw rows
-        qf[ii] = (__bf16)(SCALAR ? qv : qv * F);
-        kfi[ii] = kv * Fi;
-        const float eg = F * eref[ic];  // exp(G_r)
-        const float el = Fi * elr[ic];  // exp(G_last - G_r)
-        pkBKG[ii] |= (uint32_t)f2bf(bt[h] * kv * eg) << sh;
-        pkBV[ii] |= (uint32_t)f2bf(bt[h] * vv) << sh;
-        pkQG[ii] |= (uint32_t)f2bf(SCALAR ? scale * qv : scale * qv * eg) << sh;
-        pkKL[ii] |= (uint32_t)f2bf(SCALAR ? kv : kv * el) << sh;
-        if (ii == 0) {
-          rowg[h] = eg;
-          rowl[h] = el;
-          rowG[h] = G[h][0];
+        for (int h = 0; h < 2; ++h) {
+          const float F = __expf(G[h][ic] - go[ic]), Fi = __builtin_amdgcn_rcpf(F);
+          const float kv = (float)kr[h][ii] * rk[h], qv = (float)qr[h][ii] * rq[h], vv = (float)vr[h][ii];
+          kf[h][i4] = (__bf16)(SCALAR ? kv : kv * F);  // one gate per row: the raw rows
+          qf[h][i4] = (__bf16)(SCALAR ? qv : qv * F);
+          kfi[h][i4] = kv * Fi;
+          const float eg = F * eref[ic];  // exp(G_r)
+          const float el = Fi * elr[ic];  // exp(G_last - G_r)
+          bk[h] = bt[h] * kv * eg;
+          bv[h] = bt[h] * vv;
+          qg[h] = SCALAR ? scale * qv : scale * qv * eg;
+          kl[h] = SCALAR ? kv : kv * el;
+          if (ii == 0) {
+            rowg[h] = eg;
+            rowl[h] = el;
+            rowG[h] = G[h][0];
+          }
         }
+        pkBKG[ii] = pk2bf(bk[0], bk[1]);
+        pkBV[ii] = pk2bf(bv[0], bv[1]);
+        pkQG[ii] = pk2bf(qg[0], qg[1]);
+        pkKL[ii] = pk2bf(kl[0], kl[1]);
       }
-      if (!SCALAR || lead) {
-        *reinterpret_cast<bf16x8 *>(sKF + r * KP + c0) = kf;
-        *reinterpret_cast<bf16x8 *>(sQF + r * KP + c0) = qf;
-      }
-      if constexpr (!SCALAR) {
-        *reinterpret_cast<float4 *>(sKFi + r * GP + c0) = make_float4(kfi[0], kfi[1], kfi[2], kfi[3]);
-        *reinterpret_cast<float4 *>(sKFi + r * GP + c0 + 4) = make_float4(kfi[4], kfi[5], kfi[6], kfi[7]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = rp + h, c = c0 + 4 * half;
+        *reinterpret_cast<bf16x4 *>(sKF + r * KP + c) = bf16x4{kf[h][0], kf[h][1], kf[h][2], kf[h][3]};
+        *reinterpret_cast<bf16x4 *>(sQF + r * KP + c) = bf16x4{qf[h][0], qf[h][1], qf[h][2], qf[h][3]};
+        if constexpr (!SCALAR)
+          *reinterpret_cast<float4 *>(sKFi + r * GP + c) = make_float4(kfi[h][0], kfi[h][1], kfi[h][2], kfi[h][3]);
       }
     }
   }
