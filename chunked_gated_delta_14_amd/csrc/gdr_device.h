@@ -251,7 +251,7 @@ __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :
 // back.  They carry the nontemporal hint only where every instruction covers
 // whole 128-byte lines (a wavefront's 1 KB or 512 B contiguous block); stores
 // of row pieces (outputs, the transposed dVn tape) keep the default policy:
-// with the hint, partial-line stores made the kernels 15-40 % slower.
+// with the hint, partial-line stores made the kernels 15-45 % slower.
 __device__ __forceinline__ void st_stream(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ void st_stream(uint4 *p, uint4 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
