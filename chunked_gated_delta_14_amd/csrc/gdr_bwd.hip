@@ -630,15 +630,8 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 }
 // x ~= hi + lo, both bf16, four values packed per part
 __device__ __forceinline__ void split4(const f32x4 &x, uint2 &hi, uint2 &lo) {
-  float h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const __bf16 b = (__bf16)x[i];
-    h[i] = (float)b;
-    l[i] = x[i] - h[i];
-  }
-  hi = pack4(h[0], h[1], h[2], h[3]);
-  lo = pack4(l[0], l[1], l[2], l[3]);
+  hi = pack4(x[0], x[1], x[2], x[3]);
+  lo = pack4(x[0] - lo_bf(hi.x), x[1] - hi_bf(hi.x), x[2] - lo_bf(hi.y), x[3] - hi_bf(hi.y));
 }
 
 // 64 rows x 128 bf16 (row stride ld) -> LDS [channel][row] (pitch QTP), rows

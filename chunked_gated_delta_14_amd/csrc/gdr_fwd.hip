@@ -284,9 +284,7 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
     const bf16x8 kr[2] = {kx[0], kx[1]}, qr[2] = {qx[0], qx[1]}, vr[2] = {vx[0], vx[1]};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      __bf16 kf[2][4], qf[2][4];
-      float kfi[2][4];
+      float kf[2][4], qf[2][4], kfi[2][4];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int ii = 4 * half + i4, ic = SCALAR ? 0 : ii;
@@ -295,8 +293,8 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
         for (int h = 0; h < 2; ++h) {
           const float F = __expf(G[h][ic] - go[ic]), Fi = __builtin_amdgcn_rcpf(F);
           const float kv = (float)kr[h][ii] * rk[h], qv = (float)qr[h][ii] * rq[h], vv = (float)vr[h][ii];
-          kf[h][i4] = (__bf16)(SCALAR ? kv : kv * F);  // one gate per row: the raw rows
-          qf[h][i4] = (__bf16)(SCALAR ? qv : qv * F);
+          kf[h][i4] = SCALAR ? kv : kv * F;  // one gate per row: the raw rows
+          qf[h][i4] = SCALAR ? qv : qv * F;
           kfi[h][i4] = kv * Fi;
           const float eg = F * eref[ic];  // exp(G_r)
           const float el = Fi * elr[ic];  // exp(G_last - G_r)
@@ -318,8 +316,8 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = rp + h, c = c0 + 4 * half;
-        *reinterpret_cast<bf16x4 *>(sKF + r * KP + c) = bf16x4{kf[h][0], kf[h][1], kf[h][2], kf[h][3]};
-        *reinterpret_cast<bf16x4 *>(sQF + r * KP + c) = bf16x4{qf[h][0], qf[h][1], qf[h][2], qf[h][3]};
+        *reinterpret_cast<uint2 *>(sKF + r * KP + c) = make_uint2(pk2bf(kf[h][0], kf[h][1]), pk2bf(kf[h][2], kf[h][3]));
+        *reinterpret_cast<uint2 *>(sQF + r * KP + c) = make_uint2(pk2bf(qf[h][0], qf[h][1]), pk2bf(qf[h][2], qf[h][3]));
         if constexpr (!SCALAR)
           *reinterpret_cast<float4 *>(sKFi + r * GP + c) = make_float4(kfi[h][0], kfi[h][1], kfi[h][2], kfi[h][3]);
       }
@@ -593,10 +591,11 @@ __device__ __forceinline__ void prep_unit(const Problem &p, const Workspace &w, 
 
   if (SAVE && tid < CH * CH / 8) {  // T^T, bf16 row-major, for the gradient kernel
     const int r = tid >> 3, c8 = (tid & 7) * 8;
-    bf16x8 tv;
+    float tv[8];
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii) tv[ii] = (__bf16)sT[(c8 + ii) * SP + r];
-    st_stream(&w.Tt[u * FRAG_64x64_U4 + tid], as_u4(tv));
+    for (int ii = 0; ii < 8; ++ii) tv[ii] = sT[(c8 + ii) * SP + r];
+    st_stream(&w.Tt[u * FRAG_64x64_U4 + tid],
+              make_uint4(pk2bf(tv[0], tv[1]), pk2bf(tv[2], tv[3]), pk2bf(tv[4], tv[5]), pk2bf(tv[6], tv[7])));
   }
   settle(next);  // no path into the next unit carries an outstanding load
 }
