@@ -50,9 +50,9 @@ constexpr int CTP = 72;  // LDS pitch (bf16) of column-form tiles [channel][row]
 
 // LDS map (bytes).  Steps 1-2 use KF, QF, KFi; steps 3-5 reuse that space for
 // the column-form operands, and W, U replace beta k exp(G), beta v in step 4.
-constexpr int P_KF = 0;                    // k F   bf16 [64][KP]
-constexpr int P_QF = P_KF + CH * KP * 2;   // q F   bf16 [64][KP]
-constexpr int P_KFI = P_QF + CH * KP * 2;  // k Fi  fp32 [64][GP]
+constexpr int P_KF = 0;                    // k F   bf16 [64][KP] (one gate per row: k)
+constexpr int P_QF = P_KF + CH * KP * 2;   // q F   bf16 [64][KP] (one gate per row: q)
+constexpr int P_KFI = P_QF + CH * KP * 2;  // k Fi  fp32 [64][GP] (per-channel gate only)
 constexpr int P_BKG = 0;                   // beta k exp(G)          bf16 [128][CTP]
 constexpr int P_BV = P_BKG + HD * CTP * 2; // beta v
 constexpr int P_QG = P_BV + HD * CTP * 2;  // scale q exp(G)
